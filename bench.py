@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Compressed-KV decode attention throughput on one MI355X.
+
+A step is one pass of the whole hot path over every layer of the workload:
+for each layer, quantise-on-append of the q_len new K and V tokens per
+sequence (the MTP-verify tokens of the 256k workload), then decode attention
+of the layer's queries over the compressed cache.  Inputs and compressed
+caches are resident in HBM before timing starts.
+
+Default workload: 64 layers x 8 KV / 64 query heads, head_dim 128, 262144
+cached tokens, q_len 2, K and V 3-bit MSE, bf16 inputs with per-channel
+outliers (13.96 GB of compressed state read per step).
+
+Prints one JSON line (see the repository's design notes for every field).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="l64_d128_n256k_mse3_mtp2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=262144)
+    ap.add_argument("--layers", type=int, default=0, help="override the number of layer buffers")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, sample_tokens: int) -> dict:
+    """The oracle's decode (dequantise K and V, softmax attention, float64) on
+    one KV head of layer 0 of the same workload, in KV tokens/s."""
+    from oracle import attention as oatt
+    from oracle import codec as ocodec
+    from oracle import quant as oquant
+    from quantized_decode_attention_04_amd import workloads as wl
+
+    cores = len(os.sched_getaffinity(0))
+    n = min(sample_tokens, w.n)
+    sub = wl.Workload(w.name, 1, 1, w.hq // w.hkv, w.d, n, w.q_len, w.kbits, w.kmode, w.vbits, w.vmode, w.bf16,
+                      outliers=w.outliers)
+    k, v = wl.kv_tensors(sub, 0)
+    q = wl.queries(sub, 0).astype(np.float64)
+    kc = ocodec.make_codec(w.d, w.kbits, 0, w.kmode)
+    vc = ocodec.make_codec(w.d, w.vbits, 1, w.vmode)
+    ks = oquant.quantize(k.astype(np.float64), kc)
+    vs = oquant.quantize(v.astype(np.float64), vc)
+    lens = np.array([n])
+    t0 = time.perf_counter()
+    kd = oatt.dequantize_cache(ks, kc)
+    vd = oatt.dequantize_cache(vs, vc)
+    oatt.decode_attention(q, kd, vd, lens, 1.0 / math.sqrt(w.d))
+    dt = time.perf_counter() - t0
+    # n token-heads of one KV head; a token position of the layer holds hkv of them
+    return {
+        "value": n / dt / w.hkv,
+        "unit": "KV tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"layer 0, KV head 0 of {w.name}: {n} tokens x {w.hq // w.hkv * w.q_len} query rows; "
+                  f"oracle dequantise + float64 attention took {dt:.2f} s; rate = tokens / time / {w.hkv} KV heads",
+    }
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a single GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_decode_attention_04_amd as tq
+    from quantized_decode_attention_04_amd import _binding
+    from quantized_decode_attention_04_amd import workloads as wl
+
+    w = wl.configs()[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kc = tq.tq_codec_create(w.d, w.kbits, 0, w.kmode)
+    vc = tq.tq_codec_create(w.d, w.vbits, 1, w.vmode)
+    tq.tq_codec_upload(kc)
+    tq.tq_codec_upload(vc)
+    lens_h = w.lens()
+    append = w.q_len
+    B, hkv, hq, d, qlen = w.batch, w.hkv, w.hq, w.d, w.q_len
+    max_len = int(lens_h.max())
+    state_bytes_tok = kc.info["bytes_per_token"] + vc.info["bytes_per_token"]
+    layer_state_bytes = int(lens_h.sum()) * hkv * state_bytes_tok
+    layers = w.layers if w.layers > 1 else max(1, min(64, math.ceil(1e9 / layer_state_bytes)))
+    if args.layers:
+        layers = args.layers
+
+    # ---- set-up (not timed): per-layer compressed caches, queries, new tokens
+    kcs, vcs, qs, kn, vn = [], [], [], [], []
+    pos0 = torch.zeros(B, dtype=torch.int32, device=dev)
+    for l in range(layers):
+        K = tq.allocate_cache(kc, B, hkv, max_len, dev)
+        V = tq.allocate_cache(vc, B, hkv, max_len, dev)
+        ksc = wl.outlier_scales(0, l, hkv, d, 0) if w.outliers else None
+        vsc = wl.outlier_scales(0, l, hkv, d, 1) if w.outliers else None
+        hist = max_len - append
+        step_tok = 65536
+        for s0 in range(0, hist, step_tok):
+            n = min(step_tok, hist - s0)
+            pos = torch.full((B,), s0, dtype=torch.int32, device=dev)
+            kx = wl.device_normal((B, hkv, n, d), 0, l, 100 + s0 // step_tok, w.bf16, dev, ksc)
+            vx = wl.device_normal((B, hkv, n, d), 0, l, 200000 + s0 // step_tok, w.bf16, dev, vsc)
+            tq.tq_quantize_append(kc, kx, K, pos)
+            tq.tq_quantize_append(vc, vx, V, pos)
+            del kx, vx
+        kcs.append(K)
+        vcs.append(V)
+        qs.append(wl.device_normal((B, hq, qlen, d), 0, l, wl.STREAM_Q, w.bf16, dev))
+        kn.append(wl.device_normal((B, hkv, append, d), 0, l, wl.STREAM_KNEW, w.bf16, dev, ksc))
+        vn.append(wl.device_normal((B, hkv, append, d), 0, l, wl.STREAM_VNEW, w.bf16, dev, vsc))
+    torch.cuda.synchronize()
+    # the new tokens go to len-append .. len-1 of each sequence; the history
+    # beyond a ragged sequence's length is never attended
+    pos_new = torch.tensor(lens_h - append, dtype=torch.int32, device=dev)
+    lens = torch.tensor(lens_h, dtype=torch.int32, device=dev)
+    ws_bytes = tq.tq_decode_workspace_size(kc, vc, B, hq, hkv, qlen, max_len)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, hq, qlen, d), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d)
+
+    # ---- pre-marshalled C calls (the same entry points the binding wraps)
+    lib = _binding._lib
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    dt_code = tq.TQ_BF16 if w.bf16 else tq.TQ_F32
+    calls = []
+    for l in range(layers):
+        ks_, vs_ = kcs[l].as_struct(), vcs[l].as_struct()
+        kstr = (ctypes.c_int64 * 4)(*kn[l].stride())
+        vstr = (ctypes.c_int64 * 4)(*vn[l].stride())
+        calls.append((ks_, vs_, kstr, vstr,
+                      (kc.handle, ctypes.c_void_p(kn[l].data_ptr()), dt_code, B, hkv, append, kstr,
+                       ctypes.byref(ks_), ctypes.c_void_p(pos_new.data_ptr()), sp),
+                      (vc.handle, ctypes.c_void_p(vn[l].data_ptr()), dt_code, B, hkv, append, vstr,
+                       ctypes.byref(vs_), ctypes.c_void_p(pos_new.data_ptr()), sp),
+                      (kc.handle, vc.handle, ctypes.c_void_p(qs[l].data_ptr()), dt_code, B, hq, hkv, qlen,
+                       ctypes.byref(ks_), ctypes.byref(vs_), ctypes.c_void_p(lens.data_ptr()), max_len,
+                       ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                       ws_bytes, sp)))
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError(tq.tq_last_error())
+
+    def step(events=None):
+        for i, c in enumerate(calls):
+            check(lib.tq_quantize_append(*c[4]))
+            check(lib.tq_quantize_append(*c[5]))
+            if events is not None:
+                events[i][0].record(stream)
+            check(lib.tq_decode_attention(*c[6]))
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    dec_ms = [e0.elapsed_time(e1) for row in events for (e0, e1) in row]
+    dec_ms_avg = float(np.mean(dec_ms))
+
+    tokens_per_step = float(lens_h.sum()) * layers
+    value = tokens_per_step / (ms_per_step / 1000.0)
+    # algorithmic bytes of one decode call: the packed state of every attended
+    # token-head, the queries, the output and the two rotations it reads
+    q_bytes = B * hq * qlen * d * (2 if w.bf16 else 4)
+    out_bytes = B * hq * qlen * d * 4
+    table_bytes = 2 * d * d * 4 + (d * d * 4 if w.kmode == 1 else 0)
+    alg_bytes = layer_state_bytes + q_bytes + out_bytes + table_bytes
+    achieved = alg_bytes / (dec_ms_avg / 1000.0) / 1e9
+
+    res = {
+        "metric": "compressed-KV decode attn: KV tokens/s + HBM GB/s (% peak) at 256k ctx",
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded N(0,1)*0.02 bf16 K/V/q" + (" with per-channel outliers" if w.outliers else ""),
+        "config": {
+            "workload": w.name,
+            "layers": layers,
+            "batch": B,
+            "kv_heads": hkv,
+            "q_heads": hq,
+            "head_dim": d,
+            "cached_tokens": int(lens_h.sum()),
+            "q_len": qlen,
+            "k_codec": f"{w.kbits}-bit {'Prod' if w.kmode == 1 else 'MSE'}",
+            "v_codec": f"{w.vbits}-bit {'group32' if w.vmode == 2 else 'MSE'}",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+        },
+        "detail": {
+            "decode_call_us": dec_ms_avg * 1000.0,
+            "decode_alg_bytes_per_call": alg_bytes,
+            "state_bytes_per_step": layer_state_bytes * layers,
+            "step_gbps_state": layer_state_bytes * layers / (ms_per_step / 1000.0) / 1e9,
+            "ws_bytes": ws_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

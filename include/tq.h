@@ -1,0 +1,197 @@
+/*
+ * tq.h -- TurboQuant compressed KV cache for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libtq.so.  Three operations:
+ *   tq_codec_create       build a codec (rotation, Lloyd-Max codebook, QJL sketch)
+ *   tq_quantize_append    compress new K or V head vectors into a cache
+ *   tq_decode_attention   decode attention of queries over a compressed cache
+ *
+ * Sources ("the pages"):
+ *   [plan]   "lightning-mlx plan.md": feasibility of TurboQuant at 256k
+ *            context; decode is bound by reading the whole KV of every layer
+ *            each step; decompression = unpack + Lloyd-Max lookup,
+ *            denormalise, inverse rotation; a fused attention kernel over
+ *            the codes is what makes it viable.
+ *   [omlx]   "omlx turboquant_kv.py": BatchTurboQuantKVCache; the state
+ *            types TurboQuantMSEState(norms, indices) and
+ *            TurboQuantProdState(norms, mse_indices, residual_norms,
+ *            qjl_signs); packed width ceil(head_dim*bits/32) uint32 words
+ *            (_infer_head_dim); codecs rebuilt from (head_dim, bits, seed)
+ *            with the K codec on seed s and the V codec on seed s+1
+ *            (_rebuild_codecs); new tokens are written at the written end
+ *            (update_and_fetch) and see the cache causally (make_mask);
+ *            mixed (bits, seed) caches are refused (merge).
+ *   [val]    "turboquant validate_moe_phase2.py": TurboQuantProd keys
+ *            (3-bit = 2-bit MSE + 1-bit QJL), value group quantisation
+ *            quantize_values(v, bits, group_size=32) -> data, scales, zeros;
+ *            attention scores scaled by 1/sqrt(head_dim); Pi and S are
+ *            d x d float32 matrices.
+ *
+ * Conventions
+ *   - All device pointers are caller-owned device memory on the current HIP
+ *     device.  The library owns only codec objects and their tables.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every device operation is asynchronous on that stream; nothing
+ *     synchronises implicitly (except the one-time table upload of a codec
+ *     on a device, which uses hipMemcpy).
+ *   - Arguments are validated on the host before any launch; a failing call
+ *     launches nothing and returns a status, with a message retrievable via
+ *     tq_last_error() on the same thread.  No exception crosses the ABI.
+ *   - head_dim is a multiple of 32, at most 256.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = 1,     /* null pointer, bad size, bad stride */
+  TQ_ERR_UNSUPPORTED = 2,     /* parameter combination not implemented */
+  TQ_ERR_CONFIG_MISMATCH = 3, /* K/V codecs or caches disagree ([omlx] merge) */
+  TQ_ERR_CAPACITY = 4,        /* a length exceeds the cache capacity */
+  TQ_ERR_WORKSPACE = 5,       /* workspace missing or too small */
+  TQ_ERR_HIP = 6,             /* a HIP runtime call or launch failed */
+  TQ_ERR_NO_DEVICE = 7        /* no usable HIP device */
+} tq_status;
+
+/* Quantiser modes.
+ *   MSE:   rotate, store the float32 norm and the packed nearest-centroid
+ *          indices of the normalised rotated vector ([omlx] TurboQuantMSEState).
+ *          bits 1..4.
+ *   PROD:  MSE at bits-1 plus 1-bit QJL signs of the rotated residual and its
+ *          float32 norm ([omlx] TurboQuantProdState; [val] 3-bit keys =
+ *          MSE + QJL).  bits 2..5.  Keys only.
+ *   GROUP: asymmetric min-max quantisation of the unrotated vector in groups
+ *          of 32 coordinates with float32 scale and minimum per group ([val]
+ *          quantize_values).  bits 1..4.  Values only.                      */
+typedef enum { TQ_MODE_MSE = 0, TQ_MODE_PROD = 1, TQ_MODE_GROUP = 2 } tq_mode;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+typedef struct tq_codec tq_codec; /* opaque, immutable after creation */
+
+typedef struct {
+  int32_t head_dim;
+  int32_t bits;        /* bits per coordinate as requested (Prod includes the sign bit) */
+  int32_t mode;        /* tq_mode */
+  int32_t mse_bits;    /* bits of the packed index stream: bits (MSE, GROUP) or bits-1 (PROD) */
+  int32_t levels;      /* 2^mse_bits (MSE, PROD); 0 in GROUP mode */
+  int32_t idx_words;   /* W = head_dim*mse_bits/32 words per token-head ([omlx] _infer_head_dim) */
+  int32_t sign_words;  /* head_dim/32 in PROD mode, else 0 */
+  int32_t groups;      /* head_dim/32 in GROUP mode, else 0 */
+  int32_t grid_exp;    /* E: every centroid is an integer multiple of 2^-E (|c| 2^E <= 16256) */
+  int32_t reserved;
+  uint64_t seed;
+  uint64_t bytes_per_token; /* compressed bytes per token-head (state only) */
+} tq_codec_info;
+
+/* A compressed cache for one of K or V: caller-owned device arrays laid out
+ * [batch][heads][cap][...] in row-major order.  Which arrays are used
+ * depends on the codec's mode; unused ones may be NULL.
+ *   idx    uint32 [..][cap][idx_words]   MSE indices / Prod mse_indices / group data
+ *   norm   float  [..][cap]              MSE and Prod: vector norm
+ *   rnorm  float  [..][cap]              Prod: residual norm
+ *   sign   uint32 [..][cap][sign_words]  Prod: QJL sign bits, bit j = coordinate j
+ *   scale  float  [..][cap][groups]      GROUP: (max-min)/(2^bits-1) per group
+ *   gmin   float  [..][cap][groups]      GROUP: minimum per group ("zeros")
+ * Packed layout of idx: see the codec section of the library's design notes;
+ * for 1, 2 and 4 bits it is an LSB-first stream (index j at bits
+ * [b*j, b*j+b) of the word stream); 3-bit indices use a byte-lane layout
+ * in which each 32 coordinates own three words. */
+typedef struct {
+  uint32_t* idx;
+  float* norm;
+  float* rnorm;
+  uint32_t* sign;
+  float* scale;
+  float* gmin;
+  int32_t batch;
+  int32_t heads;
+  int64_t cap;
+} tq_cache;
+
+/* Build a codec, deterministic in (head_dim, bits, seed, mode) ([omlx]
+ * _rebuild_codecs).  Host-only: tables are uploaded to a device on first
+ * use there (or by tq_codec_upload).  Caller owns *out; release it with
+ * tq_codec_destroy.  Errors: INVALID_ARG (out == NULL), UNSUPPORTED (head_dim
+ * not a multiple of 32 in 32..256, bits out of range for the mode). */
+tq_status tq_codec_create(int32_t head_dim, int32_t bits, uint64_t seed, int32_t mode, tq_codec** out);
+
+/* Free a codec and its device tables.  NULL is a no-op.  The caller must make
+ * sure no work using it is still queued on any stream. */
+void tq_codec_destroy(tq_codec* codec);
+
+/* Describe a codec (sizes of the state it produces). */
+tq_status tq_codec_get_info(const tq_codec* codec, tq_codec_info* info);
+
+/* Copy the codec's float32 tables to host memory.  Any pointer may be NULL.
+ *   rot        [head_dim][head_dim] Pi, row-major; the rotation is y = Pi x
+ *   centroids  [levels] ascending
+ *   boundaries [levels-1] midpoints of neighbouring centroids
+ *   sketch     [head_dim][head_dim] S (PROD only; left untouched otherwise)
+ * GROUP codecs have no tables (returns OK and writes nothing). */
+tq_status tq_codec_export(const tq_codec* codec, float* rot, float* centroids, float* boundaries, float* sketch);
+
+/* Upload the codec's tables to the current device now (otherwise done on
+ * first use, with a blocking hipMemcpy).  Idempotent per device. */
+tq_status tq_codec_upload(const tq_codec* codec);
+
+/* Quantise-on-append ([omlx] update_and_fetch: only the new tokens are
+ * quantised and written at the written end; [plan]: append incremental per
+ * token).
+ *   x        device, n_new new head vectors per (batch, head), element
+ *            (b, h, t, j) at x + b*s0 + h*s1 + t*s2 + j*s3 (element strides
+ *            x_strides[0..3], s3 == 1 required), dtype x_dtype
+ *   dst      the cache to write; dst->batch == batch, dst->heads == heads
+ *   d_pos    device int32[batch]: token t of sequence b goes to position
+ *            d_pos[b] + t.  Positions outside [0, cap) are skipped (nothing
+ *            is written for them); validate positions on the host.
+ * Errors: INVALID_ARG, CONFIG_MISMATCH (cache shape), HIP. */
+tq_status tq_quantize_append(const tq_codec* codec, const void* x, int32_t x_dtype, int32_t batch, int32_t heads,
+                             int32_t n_new, const int64_t* x_strides, const tq_cache* dst, const int32_t* d_pos,
+                             void* stream);
+
+/* Bytes of device workspace tq_decode_attention needs for these sizes. */
+tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t q_len, int64_t max_len, size_t* bytes);
+
+/* Decode attention over the compressed cache ([val] Tests 1 and 5: scaled
+ * scores, softmax, weighted values, compared in the original domain; [plan]:
+ * a fused kernel over the codes instead of dequantising K and V).
+ *   q        device [batch][n_q_heads][q_len][head_dim], dtype q_dtype
+ *   k, v     caches written by tq_quantize_append with kc and vc
+ *            (kc: MSE or PROD; vc: MSE or GROUP; equal head_dim)
+ *   d_len    device int32[batch]: attended length N_b of each sequence
+ *            (after the q_len new tokens were appended); clamped to cap;
+ *            every N_b must be <= max_len (tokens beyond max_len are ignored)
+ *   max_len  host bound on the lengths, 1 <= max_len <= cap; sizes the grid
+ *   scale    softmax scale (1/sqrt(head_dim) in [val])
+ *   out      device float [batch][n_q_heads][q_len][head_dim]
+ *   ws       device workspace of ws_bytes >= tq_decode_workspace_size(...)
+ * Query head h reads KV head h / (n_q_heads / n_kv_heads); row i of q_len
+ * sees tokens t <= N_b - q_len + i ([omlx] make_mask: causal for new tokens).
+ * A row that sees no token gets zeros.
+ * Errors: INVALID_ARG, UNSUPPORTED, CONFIG_MISMATCH, CAPACITY (max_len > cap),
+ * WORKSPACE, HIP. */
+tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void* q, int32_t q_dtype, int32_t batch,
+                              int32_t n_q_heads, int32_t n_kv_heads, int32_t q_len, const tq_cache* k,
+                              const tq_cache* v, const int32_t* d_len, int64_t max_len, float scale, float* out,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* tq_last_error(void);
+
+/* Name of a status code. */
+const char* tq_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -1,0 +1,30 @@
+"""TurboQuant compressed KV cache and decode attention for AMD MI355X.
+
+Thin Python binding over the C ABI of ``libtq.so`` (``include/tq.h``): the
+functions keep the C names and only marshal arguments (torch tensors to device
+pointers, the current HIP stream, status codes to exceptions).  Every step of
+the hot path runs in the library's HIP kernels; there is no Python or CPU
+fallback -- importing the binding fails if the library is not built.
+"""
+from ._binding import (  # noqa: F401
+    TQ_BF16,
+    TQ_F32,
+    TQ_MODE_GROUP,
+    TQ_MODE_MSE,
+    TQ_MODE_PROD,
+    Cache,
+    Codec,
+    TQError,
+    allocate_cache,
+    lib_path,
+    tq_codec_create,
+    tq_codec_destroy,
+    tq_codec_export,
+    tq_codec_get_info,
+    tq_codec_upload,
+    tq_decode_attention,
+    tq_decode_workspace_size,
+    tq_last_error,
+    tq_quantize_append,
+    tq_status_string,
+)

@@ -1,0 +1,378 @@
+// C ABI of libtq.so: argument validation, codec objects, per-device table
+// upload and workspace planning.  Every device operation is a kernel launch
+// on the caller's stream; nothing here computes on the host except the codec
+// build.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "tq_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+tq_status fail(tq_status s, const std::string& msg) {
+  g_error = msg;
+  return s;
+}
+
+tq_status hip_fail(hipError_t e, const char* what) {
+  std::string m = std::string(what) + ": " + hipGetErrorString(e);
+  return fail(TQ_ERR_HIP, m);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int idx_words(const tq::HostCodec& h) { return h.d * h.mse_bits / 32; }
+int sign_words(const tq::HostCodec& h) { return h.mode == TQ_MODE_PROD ? h.d / 32 : 0; }
+int group_count(const tq::HostCodec& h) { return h.mode == TQ_MODE_GROUP ? h.d / 32 : 0; }
+
+uint64_t bytes_per_token(const tq::HostCodec& h) {
+  uint64_t b = 4ull * idx_words(h);
+  if (h.mode == TQ_MODE_MSE) b += 4;
+  if (h.mode == TQ_MODE_PROD) b += 8 + 4ull * sign_words(h);
+  if (h.mode == TQ_MODE_GROUP) b += 8ull * group_count(h);
+  return b;
+}
+
+// Upload the codec's tables to the current device (once per device).
+tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out) {
+  tq_codec* c = const_cast<tq_codec*>(cc);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TQ_ERR_NO_DEVICE, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= tq::kMaxDevices) return fail(TQ_ERR_UNSUPPORTED, "device index above 15");
+  std::lock_guard<std::mutex> lock(c->mu);
+  tq::DevTables& t = c->dev[dev];
+  if (!c->uploaded[dev] && c->h.mode != TQ_MODE_GROUP) {
+    const int d = c->h.d;
+    const size_t dd = (size_t)d * d;
+    const size_t nfl = 3 * dd + 32;
+    void* block = nullptr;
+    e = hipMalloc(&block, nfl * sizeof(float));
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(codec tables)");
+    std::vector<float> host(nfl, 0.0f);
+    float* pit = host.data();
+    float* pi = pit + dd;
+    float* st = pi + dd;
+    float* cent = st + dd;
+    float* bnd = cent + 16;
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) {
+        pit[(size_t)j * d + i] = c->h.rot[(size_t)i * d + j];
+        pi[(size_t)i * d + j] = c->h.rot[(size_t)i * d + j];
+        if (!c->h.sketch.empty()) st[(size_t)j * d + i] = c->h.sketch[(size_t)i * d + j];
+      }
+    for (int k = 0; k < c->h.levels; ++k) cent[k] = c->h.centroids[k];
+    for (int k = 0; k + 1 < c->h.levels; ++k) bnd[k] = c->h.boundaries[k];
+    e = hipMemcpy(block, host.data(), nfl * sizeof(float), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(block);
+      return hip_fail(e, "hipMemcpy(codec tables)");
+    }
+    float* base = static_cast<float*>(block);
+    t.block = block;
+    t.pit = base;
+    t.pi = base + dd;
+    t.st = base + 2 * dd;
+    t.cent = base + 3 * dd;
+    t.bnd = base + 3 * dd + 16;
+    c->uploaded[dev] = true;
+  }
+  *out = &t;
+  return TQ_OK;
+}
+
+bool cache_ok(const tq_cache* c, const tq::HostCodec& h, std::string* why) {
+  if (!c->idx) { *why = "cache idx is NULL"; return false; }
+  if (h.mode != TQ_MODE_GROUP && !c->norm) { *why = "cache norm is NULL"; return false; }
+  if (h.mode == TQ_MODE_PROD && (!c->rnorm || !c->sign)) { *why = "Prod cache needs rnorm and sign"; return false; }
+  if (h.mode == TQ_MODE_GROUP && (!c->scale || !c->gmin)) { *why = "group cache needs scale and gmin"; return false; }
+  if (c->batch <= 0 || c->heads <= 0 || c->cap <= 0) { *why = "cache batch, heads and cap must be positive"; return false; }
+  return true;
+}
+
+}  // namespace
+
+namespace tq {
+
+DecodePlan plan_decode(int batch, int hkv, int rows, int d, int64_t max_len, bool prod) {
+  DecodePlan p{};
+  p.rows = rows;
+  const int64_t tile = 256;
+  const int64_t target_items = 1024;
+  const int64_t total = (int64_t)batch * hkv * max_len;
+  int64_t chunk = (total + target_items - 1) / target_items;
+  chunk = ((chunk + tile - 1) / tile) * tile;
+  chunk = std::max<int64_t>(tile, std::min<int64_t>(chunk, 16384));
+  p.chunk = (int)chunk;
+  p.n_chunks = (int)((max_len + chunk - 1) / chunk);
+  const size_t bg = (size_t)batch * hkv;
+  size_t off = 0;
+  p.off_counters = off;
+  off = align256(off + bg * sizeof(uint32_t));
+  p.off_qrot = off;
+  off = align256(off + bg * rows * d * sizeof(float));
+  p.off_qs = off;
+  if (prod) off = align256(off + bg * rows * d * sizeof(float));
+  p.off_part_o = off;
+  off = align256(off + bg * p.n_chunks * rows * d * sizeof(float));
+  p.off_part_ml = off;
+  off = align256(off + bg * p.n_chunks * rows * 2 * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+}  // namespace tq
+
+extern "C" {
+
+const char* tq_last_error(void) { return g_error.c_str(); }
+
+const char* tq_status_string(int32_t s) {
+  switch (s) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_ERR_INVALID_ARG: return "TQ_ERR_INVALID_ARG";
+    case TQ_ERR_UNSUPPORTED: return "TQ_ERR_UNSUPPORTED";
+    case TQ_ERR_CONFIG_MISMATCH: return "TQ_ERR_CONFIG_MISMATCH";
+    case TQ_ERR_CAPACITY: return "TQ_ERR_CAPACITY";
+    case TQ_ERR_WORKSPACE: return "TQ_ERR_WORKSPACE";
+    case TQ_ERR_HIP: return "TQ_ERR_HIP";
+    case TQ_ERR_NO_DEVICE: return "TQ_ERR_NO_DEVICE";
+    default: return "TQ_ERR_UNKNOWN";
+  }
+}
+
+tq_status tq_codec_create(int32_t head_dim, int32_t bits, uint64_t seed, int32_t mode, tq_codec** out) {
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "tq_codec_create: out is NULL");
+  *out = nullptr;
+  tq::HostCodec h;
+  std::string err;
+  if (!tq::build_codec(head_dim, bits, seed, mode, &h, &err)) return fail(TQ_ERR_UNSUPPORTED, "tq_codec_create: " + err);
+  tq_codec* c = new (std::nothrow) tq_codec();
+  if (!c) return fail(TQ_ERR_INVALID_ARG, "tq_codec_create: out of host memory");
+  c->h = std::move(h);
+  *out = c;
+  g_error.clear();
+  return TQ_OK;
+}
+
+void tq_codec_destroy(tq_codec* c) {
+  if (!c) return;
+  for (int i = 0; i < tq::kMaxDevices; ++i)
+    if (c->uploaded[i] && c->dev[i].block) (void)hipFree(c->dev[i].block);
+  delete c;
+}
+
+tq_status tq_codec_get_info(const tq_codec* c, tq_codec_info* info) {
+  if (!c || !info) return fail(TQ_ERR_INVALID_ARG, "tq_codec_get_info: NULL argument");
+  const tq::HostCodec& h = c->h;
+  std::memset(info, 0, sizeof(*info));
+  info->head_dim = h.d;
+  info->bits = h.bits;
+  info->mode = h.mode;
+  info->mse_bits = h.mse_bits;
+  info->levels = h.levels;
+  info->idx_words = idx_words(h);
+  info->sign_words = sign_words(h);
+  info->groups = group_count(h);
+  info->grid_exp = h.grid_exp;
+  info->seed = h.seed;
+  info->bytes_per_token = bytes_per_token(h);
+  return TQ_OK;
+}
+
+tq_status tq_codec_export(const tq_codec* c, float* rot, float* centroids, float* boundaries, float* sketch) {
+  if (!c) return fail(TQ_ERR_INVALID_ARG, "tq_codec_export: codec is NULL");
+  const tq::HostCodec& h = c->h;
+  if (h.mode == TQ_MODE_GROUP) return TQ_OK;
+  if (rot) std::memcpy(rot, h.rot.data(), h.rot.size() * sizeof(float));
+  if (centroids) std::memcpy(centroids, h.centroids.data(), h.centroids.size() * sizeof(float));
+  if (boundaries) std::memcpy(boundaries, h.boundaries.data(), h.boundaries.size() * sizeof(float));
+  if (sketch && !h.sketch.empty()) std::memcpy(sketch, h.sketch.data(), h.sketch.size() * sizeof(float));
+  return TQ_OK;
+}
+
+tq_status tq_codec_upload(const tq_codec* c) {
+  if (!c) return fail(TQ_ERR_INVALID_ARG, "tq_codec_upload: codec is NULL");
+  tq::DevTables* t = nullptr;
+  return ensure_tables(c, &t);
+}
+
+tq_status tq_quantize_append(const tq_codec* c, const void* x, int32_t x_dtype, int32_t batch, int32_t heads,
+                             int32_t n_new, const int64_t* x_strides, const tq_cache* dst, const int32_t* d_pos,
+                             void* stream) {
+  if (!c || !x || !dst || !d_pos) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: NULL argument");
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: bad x_dtype");
+  if (batch <= 0 || heads <= 0 || n_new < 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: batch and heads must be positive, n_new >= 0");
+  const tq::HostCodec& h = c->h;
+  std::string why;
+  if (!cache_ok(dst, h, &why)) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: " + why);
+  if (dst->batch != batch || dst->heads != heads)
+    return fail(TQ_ERR_CONFIG_MISMATCH, "tq_quantize_append: cache batch/heads differ from the input's");
+  int64_t s0, s1, s2;
+  if (x_strides) {
+    if (x_strides[3] != 1) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: coordinate stride must be 1");
+    s0 = x_strides[0];
+    s1 = x_strides[1];
+    s2 = x_strides[2];
+    if (s0 < 0 || s1 < 0 || s2 < 0) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: negative stride");
+  } else {
+    s2 = h.d;
+    s1 = (int64_t)n_new * h.d;
+    s0 = (int64_t)heads * s1;
+  }
+  if (n_new == 0) return TQ_OK;
+  tq::DevTables* t = nullptr;
+  if (h.mode != TQ_MODE_GROUP) {
+    tq_status st = ensure_tables(c, &t);
+    if (st != TQ_OK) return st;
+  }
+  tq::QuantizeParams p{};
+  p.x = x;
+  p.x_bf16 = x_dtype == TQ_BF16;
+  p.s0 = s0;
+  p.s1 = s1;
+  p.s2 = s2;
+  p.batch = batch;
+  p.heads = heads;
+  p.n_new = n_new;
+  p.d = h.d;
+  p.mode = h.mode;
+  p.mse_bits = h.mse_bits;
+  p.levels = h.levels;
+  p.words = idx_words(h);
+  p.sign_words = sign_words(h);
+  p.groups = group_count(h);
+  p.gbits = h.mode == TQ_MODE_GROUP ? h.bits : 0;
+  if (t) {
+    p.pit = t->pit;
+    p.st = t->st;
+    p.cent = t->cent;
+    p.bnd = t->bnd;
+  }
+  p.idx = dst->idx;
+  p.norm = dst->norm;
+  p.rnorm = dst->rnorm;
+  p.sign = dst->sign;
+  p.scale = dst->scale;
+  p.gmin = dst->gmin;
+  p.cap = dst->cap;
+  p.pos = d_pos;
+  hipError_t e = tq::launch_quantize(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tq_quantize_append launch");
+  return TQ_OK;
+}
+
+static tq_status check_decode_shapes(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
+                                     int32_t q_len, int64_t max_len) {
+  if (!kc || !vc) return fail(TQ_ERR_INVALID_ARG, "decode: codec is NULL");
+  if (kc->h.mode != TQ_MODE_MSE && kc->h.mode != TQ_MODE_PROD)
+    return fail(TQ_ERR_UNSUPPORTED, "decode: the key codec must be MSE or Prod");
+  if (vc->h.mode != TQ_MODE_MSE && vc->h.mode != TQ_MODE_GROUP)
+    return fail(TQ_ERR_UNSUPPORTED, "decode: the value codec must be MSE or group");
+  if (kc->h.d != vc->h.d) return fail(TQ_ERR_CONFIG_MISMATCH, "decode: key and value codecs have different head_dim");
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || q_len <= 0)
+    return fail(TQ_ERR_INVALID_ARG, "decode: batch, heads and q_len must be positive");
+  if (hq % hkv) return fail(TQ_ERR_INVALID_ARG, "decode: n_q_heads must be a multiple of n_kv_heads");
+  if (max_len <= 0) return fail(TQ_ERR_INVALID_ARG, "decode: max_len must be positive");
+  const int rows = (hq / hkv) * q_len;
+  const int rmax = kc->h.d <= 128 ? 16 : 8;
+  if (rows > rmax)
+    return fail(TQ_ERR_UNSUPPORTED, "decode: (n_q_heads/n_kv_heads)*q_len above " + std::to_string(rmax) +
+                                        " for this head_dim");
+  return TQ_OK;
+}
+
+tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
+                                   int32_t q_len, int64_t max_len, size_t* bytes) {
+  if (!bytes) return fail(TQ_ERR_INVALID_ARG, "tq_decode_workspace_size: bytes is NULL");
+  tq_status st = check_decode_shapes(kc, vc, batch, hq, hkv, q_len, max_len);
+  if (st != TQ_OK) return st;
+  const int rows = (hq / hkv) * q_len;
+  *bytes = tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, kc->h.mode == TQ_MODE_PROD).total;
+  return TQ_OK;
+}
+
+tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void* q, int32_t q_dtype, int32_t batch,
+                              int32_t hq, int32_t hkv, int32_t q_len, const tq_cache* k, const tq_cache* v,
+                              const int32_t* d_len, int64_t max_len, float scale, float* out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  tq_status st = check_decode_shapes(kc, vc, batch, hq, hkv, q_len, max_len);
+  if (st != TQ_OK) return st;
+  if (!q || !k || !v || !d_len || !out) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: NULL argument");
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: bad q_dtype");
+  if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: scale is not finite");
+  std::string why;
+  if (!cache_ok(k, kc->h, &why)) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: key " + why);
+  if (!cache_ok(v, vc->h, &why)) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: value " + why);
+  if (k->batch != batch || v->batch != batch || k->heads != hkv || v->heads != hkv)
+    return fail(TQ_ERR_CONFIG_MISMATCH, "tq_decode_attention: cache batch/heads differ from the call's");
+  if (k->cap != v->cap) return fail(TQ_ERR_CONFIG_MISMATCH, "tq_decode_attention: key and value caps differ");
+  if (max_len > k->cap) return fail(TQ_ERR_CAPACITY, "tq_decode_attention: max_len exceeds the cache capacity");
+  const int rows = (hq / hkv) * q_len;
+  const bool prod = kc->h.mode == TQ_MODE_PROD;
+  const tq::DecodePlan plan = tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, prod);
+  if (!ws || ws_bytes < plan.total)
+    return fail(TQ_ERR_WORKSPACE, "tq_decode_attention: workspace needs " + std::to_string(plan.total) + " bytes");
+  tq::DevTables* kt = nullptr;
+  tq::DevTables* vt = nullptr;
+  st = ensure_tables(kc, &kt);
+  if (st != TQ_OK) return st;
+  if (vc->h.mode != TQ_MODE_GROUP) {
+    st = ensure_tables(vc, &vt);
+    if (st != TQ_OK) return st;
+  }
+  char* w = static_cast<char*>(ws);
+  tq::DecodeParams p{};
+  p.q = q;
+  p.q_bf16 = q_dtype == TQ_BF16;
+  p.batch = batch;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.q_len = q_len;
+  p.group = hq / hkv;
+  p.rows = rows;
+  p.d = kc->h.d;
+  p.scale = scale;
+  p.kmode = kc->h.mode;
+  p.kbits = kc->h.mse_bits;
+  p.kwords = idx_words(kc->h);
+  p.ksign_words = sign_words(kc->h);
+  p.k_pit = kt->pit;
+  p.k_st = kt->st;
+  p.k_cent = kt->cent;
+  p.k_idx = k->idx;
+  p.k_norm = k->norm;
+  p.k_rnorm = k->rnorm;
+  p.k_sign = k->sign;
+  p.vmode = vc->h.mode;
+  p.vbits = vc->h.mse_bits;
+  p.vwords = idx_words(vc->h);
+  p.vgroups = group_count(vc->h);
+  p.v_pi = vt ? vt->pi : nullptr;
+  p.v_cent = vt ? vt->cent : nullptr;
+  p.v_idx = v->idx;
+  p.v_norm = v->norm;
+  p.v_scale = v->scale;
+  p.v_gmin = v->gmin;
+  p.cap = k->cap;
+  p.len = d_len;
+  p.chunk = plan.chunk;
+  p.n_chunks = plan.n_chunks;
+  p.counters = reinterpret_cast<uint32_t*>(w + plan.off_counters);
+  p.qrot = reinterpret_cast<float*>(w + plan.off_qrot);
+  p.qs = prod ? reinterpret_cast<float*>(w + plan.off_qs) : nullptr;
+  p.part_o = reinterpret_cast<float*>(w + plan.off_part_o);
+  p.part_ml = reinterpret_cast<float*>(w + plan.off_part_ml);
+  p.out = out;
+  hipError_t e = tq::launch_decode(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tq_decode_attention launch");
+  return TQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// Internal declarations shared by the C ABI, the host codec builder and the
+// HIP kernels of libtq.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "tq.h"
+
+namespace tq {
+
+constexpr int kMaxDevices = 16;
+constexpr int kGridMax = 16256;  // 127 * 128: |centroid| * 2^E bound
+constexpr float kQjlConstNumer = 1.2533141373155003f;  // sqrt(pi/2)
+
+// Host tables of a codec (float32 as stored; see tq_codec_export).
+struct HostCodec {
+  int d = 0, bits = 0, mode = 0, mse_bits = 0, levels = 0, grid_exp = 0;
+  uint64_t seed = 0;
+  std::vector<float> rot;         // Pi [d][d] row-major, y = Pi x
+  std::vector<float> sketch;      // S  [d][d] row-major (Prod)
+  std::vector<float> centroids;   // [levels]
+  std::vector<float> boundaries;  // [levels-1]
+};
+
+// Builds the codec; returns false with a message on unsupported parameters.
+bool build_codec(int d, int bits, uint64_t seed, int mode, HostCodec* out, std::string* err);
+
+// Device copies of the tables on one device.
+struct DevTables {
+  float* pit = nullptr;   // Pi^T [d][d]: pit[j*d + i] = Pi[i][j]
+  float* pi = nullptr;    // Pi   [d][d] row-major
+  float* st = nullptr;    // S^T  [d][d]: st[j*d + i] = S[i][j] (Prod)
+  float* cent = nullptr;  // centroids [16]
+  float* bnd = nullptr;   // boundaries [16]
+  void* block = nullptr;  // single allocation holding all of the above
+};
+
+}  // namespace tq
+
+struct tq_codec {
+  tq::HostCodec h;
+  std::mutex mu;
+  bool uploaded[tq::kMaxDevices] = {};
+  tq::DevTables dev[tq::kMaxDevices];
+};
+
+namespace tq {
+
+// ---- kernel launch parameters -------------------------------------------
+
+struct QuantizeParams {
+  const void* x;
+  int x_bf16;
+  int64_t s0, s1, s2;  // element strides of batch, head, token (coordinate stride 1)
+  int batch, heads, n_new;
+  int d, mode, mse_bits, levels, words, sign_words, groups, gbits;
+  const float* pit;   // Pi^T
+  const float* st;    // S^T (Prod)
+  const float* cent;  // centroids
+  const float* bnd;   // boundaries
+  uint32_t* idx;
+  float* norm;
+  float* rnorm;
+  uint32_t* sign;
+  float* scale;
+  float* gmin;
+  int64_t cap;
+  const int32_t* pos;
+};
+
+hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);
+
+struct DecodeParams {
+  // query
+  const void* q;
+  int q_bf16;
+  int batch, hq, hkv, q_len, group, rows;  // rows = group * q_len
+  int d;
+  float scale;
+  // key codec / cache
+  int kmode, kbits, kwords, ksign_words;
+  const float* k_pit;   // Pi_k^T
+  const float* k_st;    // S^T
+  const float* k_cent;
+  const uint32_t* k_idx;
+  const float* k_norm;
+  const float* k_rnorm;
+  const uint32_t* k_sign;
+  // value codec / cache
+  int vmode, vbits, vwords, vgroups;
+  const float* v_pi;    // Pi_v row-major (inverse rotation of the output)
+  const float* v_cent;
+  const uint32_t* v_idx;
+  const float* v_norm;
+  const float* v_scale;
+  const float* v_gmin;
+  int64_t cap;
+  const int32_t* len;
+  // split over the token axis
+  int chunk, n_chunks;
+  // workspace pieces
+  uint32_t* counters;  // [batch*hkv]
+  float* qrot;         // [batch*hkv][rows][d]
+  float* qs;           // [batch*hkv][rows][d] (Prod)
+  float* part_o;       // [batch*hkv][n_chunks][rows][d]
+  float* part_ml;      // [batch*hkv][n_chunks][rows][2]
+  float* out;          // [batch][hq][q_len][d]
+};
+
+// Chunk length of the token split and the workspace layout for it.
+struct DecodePlan {
+  int rows, chunk, n_chunks;
+  size_t off_counters, off_qrot, off_qs, off_part_o, off_part_ml, total;
+};
+DecodePlan plan_decode(int batch, int hkv, int rows, int d, int64_t max_len, bool prod);
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace tq
