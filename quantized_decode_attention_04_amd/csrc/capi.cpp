@@ -126,7 +126,71 @@ DecodePlan plan_decode(int batch, int hkv, int rows, int d, int64_t max_len, boo
   return p;
 }
 
+// Compute units of the current device (256 on MI355X; the fallback when no
+// device answers keeps workspace sizing usable on hosts without a GPU).
+static int device_cus() {
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+DecodePlan plan_decode_fast(int batch, int hkv, int rows, int d, int64_t max_len) {
+  DecodePlan p{};
+  p.rows = rows;
+  p.fast = true;
+  const int64_t step = 512;                 // eight waves x 64-token tiles
+  const int64_t heads = (int64_t)batch * hkv;
+  const int64_t per_head = std::max<int64_t>(1, (device_cus() + heads - 1) / heads);  // one workgroup per CU
+  int64_t chunk = (max_len + per_head - 1) / per_head;
+  chunk = ((chunk + step - 1) / step) * step;
+  chunk = std::max<int64_t>(step, chunk);
+  chunk = std::max<int64_t>(chunk, ((max_len + 127) / 128 + step - 1) / step * step);  // <= 128 chunks
+  p.chunk = (int)chunk;
+  p.n_chunks = (int)((max_len + chunk - 1) / chunk);
+  const size_t bg = (size_t)batch * hkv;
+  size_t off = 0;
+  p.off_counters = off;
+  off = align256(off + bg * sizeof(uint32_t));
+  p.off_qop = off;
+  off = align256(off + bg * 6144);
+  p.off_qconst = off;
+  off = align256(off + bg * 16 * sizeof(float));
+  p.off_part_o = off;
+  off = align256(off + bg * p.n_chunks * rows * d * sizeof(float));
+  p.off_part_ml = off;
+  off = align256(off + bg * p.n_chunks * rows * 2 * sizeof(float));
+  p.total = off;
+  return p;
+}
+
 }  // namespace tq
+
+namespace {
+
+// int8 piece tables of an 8-level codebook: centroid * 2^E = 256*hi + lo with
+// lo in [-128, 127]; bytes hi[0..3], hi[4..7], lo[0..3], lo[4..7].
+void piece_tables(const tq::HostCodec& h, uint32_t* lut) {
+  lut[0] = lut[1] = lut[2] = lut[3] = 0;
+  for (int k = 0; k < h.levels && k < 8; ++k) {
+    const int c = (int)std::ldexp((double)h.centroids[k], h.grid_exp);
+    const int hi = (int)std::floor((c + 128) / 256.0);
+    const int lo = c - 256 * hi;
+    lut[k / 4] |= ((uint32_t)hi & 0xffu) << (8 * (k % 4));
+    lut[2 + k / 4] |= ((uint32_t)lo & 0xffu) << (8 * (k % 4));
+  }
+}
+
+bool use_fast(const tq_codec* kc, const tq_codec* vc, int rows) {
+  return tq::fast_decode_supported(kc->h.d, kc->h.mode, kc->h.mse_bits, vc->h.mode, vc->h.mse_bits, rows);
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -294,7 +358,8 @@ tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32
   tq_status st = check_decode_shapes(kc, vc, batch, hq, hkv, q_len, max_len);
   if (st != TQ_OK) return st;
   const int rows = (hq / hkv) * q_len;
-  *bytes = tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, kc->h.mode == TQ_MODE_PROD).total;
+  *bytes = use_fast(kc, vc, rows) ? tq::plan_decode_fast(batch, hkv, rows, kc->h.d, max_len).total
+                                  : tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, kc->h.mode == TQ_MODE_PROD).total;
   return TQ_OK;
 }
 
@@ -316,7 +381,9 @@ tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void
   if (max_len > k->cap) return fail(TQ_ERR_CAPACITY, "tq_decode_attention: max_len exceeds the cache capacity");
   const int rows = (hq / hkv) * q_len;
   const bool prod = kc->h.mode == TQ_MODE_PROD;
-  const tq::DecodePlan plan = tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, prod);
+  const bool fast = use_fast(kc, vc, rows);
+  const tq::DecodePlan plan = fast ? tq::plan_decode_fast(batch, hkv, rows, kc->h.d, max_len)
+                                   : tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, prod);
   if (!ws || ws_bytes < plan.total)
     return fail(TQ_ERR_WORKSPACE, "tq_decode_attention: workspace needs " + std::to_string(plan.total) + " bytes");
   tq::DevTables* kt = nullptr;
@@ -365,12 +432,23 @@ tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void
   p.chunk = plan.chunk;
   p.n_chunks = plan.n_chunks;
   p.counters = reinterpret_cast<uint32_t*>(w + plan.off_counters);
-  p.qrot = reinterpret_cast<float*>(w + plan.off_qrot);
-  p.qs = prod ? reinterpret_cast<float*>(w + plan.off_qs) : nullptr;
   p.part_o = reinterpret_cast<float*>(w + plan.off_part_o);
   p.part_ml = reinterpret_cast<float*>(w + plan.off_part_ml);
   p.out = out;
-  hipError_t e = tq::launch_decode(p, static_cast<hipStream_t>(stream));
+  hipError_t e;
+  if (fast) {
+    p.qop = reinterpret_cast<uint32_t*>(w + plan.off_qop);
+    p.qconst = reinterpret_cast<float*>(w + plan.off_qconst);
+    piece_tables(kc->h, p.klut);
+    piece_tables(vc->h, p.vlut);
+    p.kgrid = kc->h.grid_exp;
+    p.vgrid = vc->h.grid_exp;
+    e = tq::launch_decode_fast(p, static_cast<hipStream_t>(stream));
+  } else {
+    p.qrot = reinterpret_cast<float*>(w + plan.off_qrot);
+    p.qs = prod ? reinterpret_cast<float*>(w + plan.off_qs) : nullptr;
+    e = tq::launch_decode(p, static_cast<hipStream_t>(stream));
+  }
   if (e != hipSuccess) return hip_fail(e, "tq_decode_attention launch");
   return TQ_OK;
 }

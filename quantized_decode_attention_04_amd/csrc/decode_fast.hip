@@ -1,0 +1,608 @@
+// Decode attention over the compressed cache on the gfx950 matrix cores.
+//
+// Covers head_dim 128 with 3-bit MSE keys and values and up to 16 query rows
+// per KV head (the 256k-context MTP-verify workload: 8 query heads per KV head
+// x 2 new tokens).  Same split over the token axis and the same cross-chunk
+// merge as the general kernel; the per-token work is reorganised so that both
+// products run as exact int8 matrix-core operations:
+//
+//   scores  S^T[token][row] = C_k[token][coord] . Q^T[coord][row]
+//   values  O^T[coord][row] = V^T[coord][token] . P'^T[token][row]
+//
+// * Centroids are integers on the codec's dyadic grid (|c| 2^E <= 16256), so
+//   each is exactly hi*256 + lo with int8 pieces.  The rotated queries and the
+//   probabilities p*n_v are quantised to 24 bits (three balanced base-256 int8
+//   digits, 2^-23 of the row maximum / the value-norm reference), so that the
+//   rounding noise summed over many small probabilities stays far below the
+//   output of a sharp softmax.  The int8 v_mfma_i32_16x16x64_i8 products of
+//   the digits accumulate exactly in int32: five per K-step of the scores and
+//   five per tile of the values (every digit pair above 2^-24 of a product).
+// * Packed indices become int8 operands with no per-coordinate loop: the 3-bit
+//   byte-lane layout yields four indices per shift-and-mask ("selector"
+//   dwords), and v_perm_b32 looks four of them up at once in 8-byte tables.
+// * Keys are used token-major (one lane per token and 32-coordinate group).
+//   Values must enter the matrix core coordinate-major: each wave writes its
+//   tile's value selectors to LDS as [token][coordinate] bytes and reads them
+//   back transposed with ds_read_b64_tr_b8 (lane j of a 16-lane group gets,
+//   as byte i, column j%8 of the row addressed by lane 2i + j/8).
+// * The score tile's token order is permuted so that a lane's score
+//   accumulators are exactly the 16 consecutive tokens the value product needs
+//   from it: the probabilities never move between lanes.
+// * Online softmax per row in the log2 domain; the int32 value accumulators
+//   are flushed to float only when a row maximum or the value-norm reference
+//   grows (rare after the first tiles).
+#include "combine.h"
+
+namespace tq {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kTile = 64;             // tokens per wave iteration
+constexpr int kWaves = 8;            // 512-thread workgroups, one per compute unit
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxChunks = 128;       // merge weights kept in LDS
+constexpr int kRow = kD + 16;         // LDS bytes per token row of value selectors
+constexpr int kSelLds = kTile * kRow;             // value selectors of the tile
+constexpr int kNormLds = 2 * kTile * 4;            // key and value norms of the tile
+constexpr int kAccLds = 16 * kD * 4;               // float output accumulator [row][coord]
+constexpr int kWaveLds = kSelLds + kNormLds + kAccLds;
+constexpr int kMergeLds = (kD * kD + 16 * kD + 16 * kMaxChunks + 16) * 4;
+constexpr int kLds = kWaves * kWaveLds > kMergeLds ? kWaves * kWaveLds : kMergeLds;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kQMax = 8355711.f;    // three-digit operand bound (32639 * 256 + 127)
+constexpr float kDigitBias = 8421504.f;  // 0x808080: biased digits are the bytes of q + bias
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// The eight selector dwords (quads 0..7, byte k = coordinate 4*quad + k) of a
+// 32-coordinate group stored in the 3-bit byte-lane layout (words X, Y, Z).
+__device__ __forceinline__ void selectors3(uint32_t X, uint32_t Y, uint32_t Z, uint32_t* s) {
+  const uint32_t m3 = 0x07070707u, m2 = 0x03030303u, m4 = 0x04040404u;
+  s[0] = X & m3;
+  s[1] = (X >> 3) & m3;
+  s[2] = ((X >> 6) & m2) | ((Z >> 4) & m4);
+  s[3] = Y & m3;
+  s[4] = (Y >> 3) & m3;
+  s[5] = ((Y >> 6) & m2) | ((Z >> 5) & m4);
+  s[6] = Z & m3;
+  s[7] = (Z >> 3) & m3;
+}
+
+// int8 pieces of sixteen codes (four selector dwords) from an 8-entry table.
+__device__ __forceinline__ v4i lookup(const uint32_t* s, uint32_t t_hi, uint32_t t_lo) {
+  v4i r;
+  r.x = (int)perm(t_hi, t_lo, s[0]);
+  r.y = (int)perm(t_hi, t_lo, s[1]);
+  r.z = (int)perm(t_hi, t_lo, s[2]);
+  r.w = (int)perm(t_hi, t_lo, s[3]);
+  return r;
+}
+
+__device__ __forceinline__ v2i read_tr8(const uint8_t* a) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(a));
+}
+
+// (2^24 t24 + 2^16 t16 + 2^8 t8) / 256 in float: the digit accumulators of a
+// value product in units of 256 (the kappa factor carries the rest)
+__device__ __forceinline__ float flushed(int t24, int t16, int t8) {
+  return fmaf(fmaf((float)t24, 256.f, (float)t16), 256.f, (float)t8);
+}
+
+__device__ __forceinline__ float rowmax4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+
+// ---- prologue: rotated queries as int8 operand pieces ----------------------
+//
+// Operand order (matches the key selectors): K-step ks, digit (0 = most
+// significant), lane l (row l%16, group h = l/16), byte s of the 16-byte
+// fragment = coordinate 32h + 16ks + s.  Q = 65536 a + 256 b + c with
+// balanced digits a, b, c in [-128, 127].
+__global__ __launch_bounds__(256) void qprep_fast_kernel(DecodeParams p) {
+  __shared__ float s_pit[kD * kD];   // Pi^T staged once (64 KB)
+  __shared__ float s_in[16 * kD];    // the group's query rows
+  __shared__ float s_q[16 * kD];     // rotated rows
+  __shared__ float s_sc[16];
+  const int bg = blockIdx.x;
+  const int b = bg / p.hkv, g = bg % p.hkv;
+  const int tid = threadIdx.x;
+  if (tid == 0) p.counters[bg] = 0u;
+  {
+    const v4f* src = reinterpret_cast<const v4f*>(p.k_pit);
+    v4f* dst = reinterpret_cast<v4f*>(s_pit);
+#pragma unroll
+    for (int k = 0; k < kD * kD / 4 / 256; ++k) dst[tid + 256 * k] = src[tid + 256 * k];
+  }
+  for (int e = tid; e < 16 * kD; e += 256) {
+    const int r = e / kD, j = e % kD;
+    float qj = 0.f;
+    if (r < p.rows) {
+      const int h = g * p.group + r / p.q_len, qi = r % p.q_len;
+      const int64_t off = (((int64_t)b * p.hq + h) * p.q_len + qi) * kD + j;
+      qj = p.q_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(p.q)[off] << 16)
+                    : static_cast<const float*>(p.q)[off];
+    }
+    s_in[e] = qj;
+  }
+  __syncthreads();
+  {
+    // thread: coordinate i, rows 8*half .. 8*half+7
+    const int i = tid & (kD - 1), half = tid >> 7;
+    float acc[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = 0.f;
+    for (int j = 0; j < kD; ++j) {
+      const float pij = s_pit[j * kD + i];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[r] = fmaf(pij, s_in[(8 * half + r) * kD + j], acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) s_q[(8 * half + r) * kD + i] = acc[r];
+  }
+  __syncthreads();
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = 4 * wave + rr;
+      float a = fmaxf(fabsf(s_q[r * kD + lane]), fabsf(s_q[r * kD + 64 + lane]));
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+      if (lane == 0) s_sc[r] = a > 0.f ? kQMax / a : 0.f;
+    }
+  }
+  __syncthreads();
+  uint32_t* qop = p.qop + (size_t)bg * 1536;
+  for (int e = tid; e < 1536; e += 256) {
+    const int dw = e & 3, ln = (e >> 2) & 63, digit = (e >> 8) % 3, ks = (e >> 8) / 3;
+    const int n = ln & 15, h = ln >> 4;
+    uint32_t word = 0;
+    for (int k = 0; k < 4; ++k) {
+      const int coord = 32 * h + 16 * ks + 4 * dw + k;
+      // the product may round one past the bound: clamp so the top digit fits int8
+      const int qv = (int)fminf(fmaxf(rintf(s_q[n * kD + coord] * s_sc[n]), -kQMax), kQMax);
+      const int q1 = (qv + 128) >> 8;   // floor((q + 128) / 256)
+      const int c = qv - 256 * q1;
+      const int a = (q1 + 128) >> 8;
+      const int bb = q1 - 256 * a;
+      const int dig = digit == 0 ? a : (digit == 1 ? bb : c);
+      word |= ((uint32_t)dig & 0xffu) << (8 * k);
+    }
+    qop[e] = word;
+  }
+  if (tid < 16) {
+    const float sc = s_sc[tid];
+    // score = sum_j Q_j C_j / (sigma 2^E) = 256 * [(256 t24 + t16) 256 + t8] / (sigma 2^E)
+    p.qconst[bg * 16 + tid] =
+        (tid < p.rows && sc > 0.f) ? 256.f * p.scale * kLog2e * exp2f(-(float)p.kgrid) / sc : 0.f;
+  }
+}
+
+// ---- main kernel -------------------------------------------------------------
+typedef uint32_t v3u __attribute__((ext_vector_type(3)));
+
+constexpr int kBufWord3 = 0x00020000;     // raw buffer resource, gfx9 data format
+constexpr float kFlushGap = 4.f;          // log2 headroom: p may reach 2^4 between flushes
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+
+// One 64-token tile of this wave: the three key and value words of one token
+// and 32-coordinate group per score tile st (token order 16(m/4) + 4st + m%4),
+// and one key and one value norm per lane (token T0 + lane).  Offsets are
+// per-lane so that the buffer range check covers every token: reads past the
+// cache return zeros.
+struct Tile {
+  v3u kw[4], vw[4];
+  float kn, vn;
+};
+
+__device__ __forceinline__ void load_tile(Tile& t, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          __amdgpu_buffer_rsrc_t rkn, __amdgpu_buffer_rsrc_t rvn,
+                                          const uint32_t* lw, uint32_t ln4, uint32_t T0) {
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    t.kw[st] = __builtin_amdgcn_raw_buffer_load_b96(rk, lw[st] + T0 * 48u, 0, 0);
+    t.vw[st] = __builtin_amdgcn_raw_buffer_load_b96(rv, lw[st] + T0 * 48u, 0, 0);
+  }
+  t.kn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rkn, ln4 + T0 * 4u, 0, 0));
+  t.vn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvn, ln4 + T0 * 4u, 0, 0));
+}
+
+// Cross-chunk merge by the last workgroup of (b, g): row maxima and weights
+// from every chunk's (m, l), then each thread accumulates one float4 of the
+// 16 x 128 output over all chunks with every load issued before any is used,
+// and the single inverse rotation runs against Pi_v staged in LDS.
+__device__ __forceinline__ void merge_fast(const DecodeParams& p, int b, int g, float* lds) {
+  float* s_pi = lds;                         // [kD][kD] Pi_v, row-major
+  float* s_o = s_pi + kD * kD;               // [16][kD] merged rotated rows
+  float* s_w = s_o + 16 * kD;                // [16][n_chunks] chunk weights / L
+  const int rows = p.rows, nch = p.n_chunks, tid = threadIdx.x;
+  const int bg = b * p.hkv + g;
+  const float* pml0 = p.part_ml + (size_t)bg * nch * rows * 2;
+  const float* po0 = p.part_o + (size_t)bg * nch * rows * kD;
+  // Pi_v: 8 float4 per thread, all in flight
+  {
+    const v4f* src = reinterpret_cast<const v4f*>(p.v_pi);
+    v4f buf[kD * kD / 4 / kThreads];
+#pragma unroll
+    for (int k = 0; k < kD * kD / 4 / kThreads; ++k) buf[k] = src[tid + kThreads * k];
+#pragma unroll
+    for (int k = 0; k < kD * kD / 4 / kThreads; ++k) reinterpret_cast<v4f*>(s_pi)[tid + kThreads * k] = buf[k];
+  }
+  // weights: 32 lanes per row
+  {
+    const int r = tid >> 5, cl = tid & 31;
+    float M = -INFINITY;
+    if (r < rows)
+      for (int c = cl; c < nch; c += 32) M = fmaxf(M, pml0[((size_t)c * rows + r) * 2]);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 32));
+    float L = 0.f;
+    if (r < rows)
+      for (int c = cl; c < nch; c += 32) {
+        const float mc = pml0[((size_t)c * rows + r) * 2];
+        const float w = (M == -INFINITY || mc == -INFINITY) ? 0.f : exp2f(mc - M);
+        s_w[r * nch + c] = w;
+        L = fmaf(w, pml0[((size_t)c * rows + r) * 2 + 1], L);
+      }
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) L += __shfl_xor(L, o, 32);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    __syncthreads();
+    if (r < rows)
+      for (int c = cl; c < nch; c += 32) s_w[r * nch + c] *= inv;
+  }
+  __syncthreads();
+  // one float4 of the output per thread (512 threads x 4 = 16 rows x 128)
+  {
+    const int e = 4 * tid, r = e / kD;
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    if (r < rows) {
+      const v4f* src = reinterpret_cast<const v4f*>(po0 + e);
+      const size_t stride = (size_t)rows * kD / 4;
+      int c = 0;
+      for (; c + 16 <= nch; c += 16) {
+        v4f v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = src[(size_t)(c + k) * stride];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) acc += v[k] * s_w[r * nch + c + k];
+      }
+      for (; c < nch; ++c) acc += src[(size_t)c * stride] * s_w[r * nch + c];
+    }
+    reinterpret_cast<v4f*>(s_o)[tid] = acc;
+  }
+  __syncthreads();
+  // out = o Pi_v (row-vector form of Pi_v^T o): thread -> column j, 4 rows
+  {
+    const int j = tid & (kD - 1), r0 = 4 * (tid >> 7);
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kD; ++i) {
+      const float pij = s_pi[i * kD + j];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a[k] = fmaf(s_o[(r0 + k) * kD + i], pij, a[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = r0 + k;
+      if (r < rows) {
+        const int h = g * p.group + r / p.q_len, qi = r % p.q_len;
+        p.out[(((int64_t)b * p.hq + h) * p.q_len + qi) * kD + j] = a[k];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[kLds];
+  __shared__ int s_last;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, h = lane >> 4;  // query row, lane group
+  const int chunk_id = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int bg = b * p.hkv + g;
+  const int rows = p.rows;
+  int64_t len64 = p.len[b];
+  len64 = len64 < 0 ? 0 : (len64 > p.cap ? p.cap : len64);
+  const int len = (int)len64;
+  const int c0 = chunk_id * p.chunk;
+  const int c1 = c0 + p.chunk < len ? c0 + p.chunk : len;
+  const int lim = len - p.q_len + (n % p.q_len) + 1;  // row n sees tokens < lim
+  const int lim_all = len - p.q_len + 1;             // tokens every row sees
+
+  const uint32_t* qo = p.qop + (size_t)bg * 1536 + lane * 4;
+  const v4i qa0 = *reinterpret_cast<const v4i*>(qo);
+  const v4i qb0 = *reinterpret_cast<const v4i*>(qo + 256);
+  const v4i qc0 = *reinterpret_cast<const v4i*>(qo + 512);
+  const v4i qa1 = *reinterpret_cast<const v4i*>(qo + 768);
+  const v4i qb1 = *reinterpret_cast<const v4i*>(qo + 1024);
+  const v4i qc1 = *reinterpret_cast<const v4i*>(qo + 1280);
+  const float rowc = p.qconst[bg * 16 + n];
+  const uint32_t kh1 = p.klut[1], kh0 = p.klut[0], kl1 = p.klut[3], kl0 = p.klut[2];
+  const uint32_t vh1 = p.vlut[1], vh0 = p.vlut[0], vl1 = p.vlut[3], vl0 = p.vlut[2];
+  const float kappa = 256.f * exp2f(-(float)p.vgrid);
+
+  const size_t base = (size_t)bg * (size_t)p.cap;
+  const uint32_t cap = (uint32_t)p.cap;
+  const __amdgpu_buffer_rsrc_t rk = rsrc(p.k_idx + base * 12, cap * 48u);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(p.v_idx + base * 12, cap * 48u);
+  const __amdgpu_buffer_rsrc_t rkn = rsrc(p.k_norm + base, cap * 4u);
+  const __amdgpu_buffer_rsrc_t rvn = rsrc(p.v_norm + base, cap * 4u);
+  uint32_t lw[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) lw[st] = (uint32_t)(16 * (n >> 2) + 4 * st + (n & 3)) * 48u + 12u * h;
+  const uint32_t ln4 = (uint32_t)lane * 4u;
+
+  uint8_t* sb = s_buf + wave * kWaveLds;
+  float* sn = reinterpret_cast<float*>(sb + kSelLds);            // [2][64] norms of the tile
+  v4f* so = reinterpret_cast<v4f*>(sb + kSelLds + kNormLds);     // [16 rows][32] x 4 coords
+  // float output of row n, coordinates 16u + 4h .. +3, lives in LDS: it is
+  // touched only when the int32 accumulators are flushed
+  auto oref = [&](int u) -> v4f& { return so[n * 32 + 4 * u + h]; };
+#pragma unroll
+  for (int u = 0; u < 8; ++u) oref(u) = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // Value-norm reference of this wave's tokens: the probability scale is fixed
+  // for the whole chunk, p * n_v * sig <= 2^4 * kQMax / 2^4.
+  const int t_first = c0 + wave * kTile;
+  float nmax = 0.f;
+  for (int T0 = t_first; T0 < c1; T0 += 8 * kWaves * kTile) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      v[k] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rvn, ln4 + (uint32_t)(T0 + k * kWaves * kTile) * 4u, 0, 0));
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (T0 + k * kWaves * kTile + lane < c1) nmax = fmaxf(nmax, v[k]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, o, 64));
+  // 0.1% margin: p n_v sig stays below kQMax through exp2 and product rounding
+  const float sig = nmax > 0.f ? kQMax / (nmax * 16.016f) : 0.f;
+  const float kflush = sig > 0.f ? kappa / sig : 0.f;
+
+  // running maximum of the row (log2 domain); a finite "minus infinity" so that
+  // masked scores (-inf) give exp2 = 0 and an empty row never forms inf - inf
+  float m_ref = -1e30f, l_run = 0.f;
+  v4i ahh[8], ax[8], all[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    ahh[u] = v4i{0, 0, 0, 0};
+    ax[u] = v4i{0, 0, 0, 0};
+    all[u] = v4i{0, 0, 0, 0};
+  }
+
+  auto process = [&](const Tile& cur, const int T0) {
+
+    // ---- scores on the matrix cores
+    float sc[16];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint32_t s8[8];
+      selectors3(cur.kw[st].x, cur.kw[st].y, cur.kw[st].z, s8);
+      const v4i ah0 = lookup(s8, kh1, kh0), al0 = lookup(s8, kl1, kl0);
+      const v4i ah1 = lookup(s8 + 4, kh1, kh0), al1 = lookup(s8 + 4, kl1, kl0);
+      // Q C = 2^24 a Ch + 2^16 (a Cl + b Ch) + 2^8 (b Cl + c Ch) [+ c Cl, below
+      // 2^-23 of the product]
+      v4i t24 = v4i{0, 0, 0, 0}, t16 = v4i{0, 0, 0, 0}, t8 = v4i{0, 0, 0, 0};
+      t24 = mfma(ah0, qa0, t24);
+      t16 = mfma(al0, qa0, t16);
+      t16 = mfma(ah0, qb0, t16);
+      t8 = mfma(al0, qb0, t8);
+      t8 = mfma(ah0, qc0, t8);
+      t24 = mfma(ah1, qa1, t24);
+      t16 = mfma(al1, qa1, t16);
+      t16 = mfma(ah1, qb1, t16);
+      t8 = mfma(al1, qb1, t8);
+      t8 = mfma(ah1, qc1, t8);
+      // 256 t24 + t16 is exact in int32; then one float rounding (2^-24)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[4 * st + i] = fmaf((float)(t24[i] * 256 + t16[i]), 256.f, (float)t8[i]);
+    }
+
+    // ---- value selectors and the tile's norms to LDS
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint32_t s8[8];
+      selectors3(cur.vw[st].x, cur.vw[st].y, cur.vw[st].z, s8);
+      const int tt = 16 * (n >> 2) + 4 * st + (n & 3);
+      v4u* dst = reinterpret_cast<v4u*>(sb + tt * kRow + 32 * h);
+      dst[0] = v4u{s8[0], s8[1], s8[2], s8[3]};
+      dst[1] = v4u{s8[4], s8[5], s8[6], s8[7]};
+    }
+    sn[lane] = cur.kn;
+    sn[kTile + lane] = cur.vn * sig;  // per-token weight of p in the probability digits
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- online softmax for row n over tokens tb .. tb+15 held by this lane
+    const int tb = T0 + 16 * h;
+    const v4f* snk = reinterpret_cast<const v4f*>(sn + 16 * h);
+    const v4f* snv = reinterpret_cast<const v4f*>(sn + kTile + 16 * h);
+    float s[16], wv[16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const v4f nk4 = snk[c], nv4 = snv[c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[4 * c + i] = sc[4 * c + i] * (rowc * nk4[i]);
+        wv[4 * c + i] = nv4[i];
+      }
+    }
+    const bool full = T0 + kTile <= c1 && T0 + kTile <= lim_all;  // no token of the tile is masked
+    if (!full) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int tok = tb + j;
+        if (!(tok < c1 && tok < lim)) s[j] = -INFINITY;
+      }
+    }
+    float tmax = s[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, s[j]);
+    tmax = rowmax4(tmax);
+    const bool grow = tmax > m_ref + kFlushGap;
+    if (__ballot(grow) != 0) {
+      const float m_new = grow ? tmax : m_ref;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        v4f o = oref(u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = fmaf(flushed(ahh[u][i], ax[u][i], all[u][i]), kflush, o[i]) * alpha;
+        oref(u) = o;
+        ahh[u] = v4i{0, 0, 0, 0};
+        ax[u] = v4i{0, 0, 0, 0};
+        all[u] = v4i{0, 0, 0, 0};
+      }
+      l_run *= alpha;
+      m_ref = m_new;
+    }
+    float psum = 0.f;
+    uint32_t qv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float pr = __builtin_amdgcn_exp2f(s[j] - m_ref);
+      psum += pr;
+      // q + 0x808080 with q = rint(p n_v sig) in [0, 8355711]: its bytes are
+      // the balanced digits of q plus 128
+      qv[j] = (uint32_t)fmaf(pr, wv[j], kDigitBias);
+    }
+    l_run += psum;
+    v4i ba, bb, bc;  // digits of 2^16, 2^8 and 1
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t a01 = perm(qv[4 * c + 1], qv[4 * c], 0x05010400u);  // q0.b0 q1.b0 q0.b1 q1.b1
+      const uint32_t a23 = perm(qv[4 * c + 3], qv[4 * c + 2], 0x05010400u);
+      const uint32_t b01 = perm(qv[4 * c + 1], qv[4 * c], 0x0c0c0602u);  // q0.b2 q1.b2 0 0
+      const uint32_t b23 = perm(qv[4 * c + 3], qv[4 * c + 2], 0x0c0c0602u);
+      bc[c] = (int)(perm(a23, a01, 0x05040100u) ^ 0x80808080u);
+      bb[c] = (int)(perm(a23, a01, 0x07060302u) ^ 0x80808080u);
+      ba[c] = (int)(perm(b23, b01, 0x05040100u) ^ 0x80808080u);
+    }
+
+    // ---- values on the matrix cores: coordinates 16u + n of tokens tb..tb+15
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint8_t* a0 = sb + (16 * h + (n >> 1)) * kRow + 16 * u + 8 * (n & 1);
+      const v2i r0 = read_tr8(a0);
+      const v2i r1 = read_tr8(a0 + 8 * kRow);
+      const uint32_t sv[4] = {(uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r1.x, (uint32_t)r1.y};
+      const v4i vh = lookup(sv, vh1, vh0), vl = lookup(sv, vl1, vl0);
+      // P' V = 2^24 a Vh + 2^16 (a Vl + b Vh) + 2^8 (b Vl + c Vh) [+ c Vl]
+      ahh[u] = mfma(vh, ba, ahh[u]);
+      ax[u] = mfma(vl, ba, ax[u]);
+      ax[u] = mfma(vh, bb, ax[u]);
+      all[u] = mfma(vl, bb, all[u]);
+      all[u] = mfma(vh, bc, all[u]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // two tile buffers in turn: the next tile's loads are in flight while the
+  // current one is processed.  The loads are unconditional (a tile past the
+  // chunk reads masked tokens, or zeros past the cache) so that the number of
+  // loads in flight is the same on every path and the waits stay partial.
+  Tile ta, tb;
+  load_tile(ta, rk, rv, rkn, rvn, lw, ln4, (uint32_t)t_first);
+  constexpr int kStep = kWaves * kTile;
+  for (int T0 = t_first; T0 < c1; T0 += 2 * kStep) {
+    load_tile(tb, rk, rv, rkn, rvn, lw, ln4, (uint32_t)(T0 + kStep));
+    process(ta, T0);
+    if (T0 + kStep >= c1) break;
+    load_tile(ta, rk, rv, rkn, rvn, lw, ln4, (uint32_t)(T0 + 2 * kStep));
+    process(tb, T0 + kStep);
+  }
+
+  v4f of[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    of[u] = oref(u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) of[u][i] = fmaf(flushed(ahh[u][i], ax[u][i], all[u][i]), kflush, of[u][i]);
+  }
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+
+  // ---- merge the four waves' partials of this chunk in LDS
+  __syncthreads();
+  float* cw = reinterpret_cast<float*>(s_buf);
+  {
+    float* mo = cw + wave * (16 * kD + 32);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mo[n * kD + 16 * u + 4 * h + i] = of[u][i];
+    if (h == 0) {
+      mo[16 * kD + n] = m_ref;
+      mo[16 * kD + 16 + n] = l_run;
+    }
+  }
+  __syncthreads();
+  float* po = p.part_o + ((size_t)bg * p.n_chunks + chunk_id) * rows * kD;
+  float* pml = p.part_ml + ((size_t)bg * p.n_chunks + chunk_id) * rows * 2;
+  for (int e = threadIdx.x; e < rows * kD; e += kThreads) {
+    const int r = e / kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cw[w * (16 * kD + 32) + 16 * kD + r]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* mo = cw + w * (16 * kD + 32);
+        const float mw = mo[16 * kD + r];
+        const float wt = mw == -INFINITY ? 0.f : exp2f(mw - M);
+        L = fmaf(wt, mo[16 * kD + 16 + r], L);
+        O = fmaf(wt, mo[e], O);
+      }
+    }
+    po[e] = O;
+    if ((e % kD) == 0) {
+      pml[2 * r] = M;
+      pml[2 * r + 1] = L;
+    }
+  }
+  // publish; the last workgroup of (b, g) to arrive merges every chunk
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(p.counters + bg, 1u) == (unsigned)(p.n_chunks - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  merge_fast(p, b, g, reinterpret_cast<float*>(s_buf));
+  if (threadIdx.x == 0) p.counters[bg] = 0u;
+}
+
+}  // namespace
+
+bool fast_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
+  return d == kD && kmode == TQ_MODE_MSE && kbits == 3 && vmode == TQ_MODE_MSE && vbits == 3 && rows <= 16;
+}
+
+hipError_t launch_decode_fast(const DecodeParams& p, hipStream_t stream) {
+  if (p.n_chunks > 65535 || p.hkv > 65535 || p.batch > 65535 || p.d != kD) return hipErrorInvalidValue;
+  qprep_fast_kernel<<<dim3(p.batch * p.hkv), dim3(256), 0, stream>>>(p);
+  if (p.n_chunks > kMaxChunks) return hipErrorInvalidValue;
+  decode_fast_kernel<<<dim3(p.n_chunks, p.hkv, p.batch), dim3(kThreads), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace tq

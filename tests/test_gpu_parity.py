@@ -134,7 +134,19 @@ DEC_CASES = [
     ("d96_mse4_group3_q3", 96, (4, 0), (3, 2), 2, 2, 4, 3, [513, 257], 600, True, False),
     ("d224_prod5_group4", 224, (5, 1), (4, 2), 1, 1, 8, 1, [999], 1000, True, False),
     ("d192_prod2_mse1", 192, (2, 1), (1, 0), 1, 3, 6, 2, [1300], 1300, False, False),
+    # head_dim 128 with 3-bit MSE keys and values and <= 16 rows per KV head run
+    # on the matrix-core kernel; these exercise its tails, chunking and flushes
+    ("fast_ragged_mse3", 128, (3, 0), (3, 0), 4, 2, 16, 1, [0, 63, 64, 5000], 5000, True, False),
+    ("fast_mtp2_many_chunks", 128, (3, 0), (3, 0), 1, 8, 64, 2, [20000], 20001, True, True),
+    ("fast_rows4", 128, (3, 0), (3, 0), 2, 2, 4, 2, [777, 1500], 1600, False, False),
+    ("fast_sharp_softmax", 128, (3, 0), (3, 0), 1, 2, 16, 1, [3000], 3000, False, False),
+    ("fast_growing_value_norms", 128, (3, 0), (3, 0), 1, 2, 32, 1, [4100], 4100, True, False),
 ]
+
+# query scale per case (default 0.02, like the keys); larger scales make the
+# softmax sharp and stress the score precision
+Q_STD = {"fast_sharp_softmax": 200.0, "d32_mse1_mse2": 1.0, "d96_mse4_group3_q3": 1.0,
+         "d224_prod5_group4": 1.0, "d192_prod2_mse1": 1.0}
 
 
 def _oracle_states(name, d, kspec, vspec, B, Hkv, N, bf16, outliers, seed=0):
@@ -145,6 +157,8 @@ def _oracle_states(name, d, kspec, vspec, B, Hkv, N, bf16, outliers, seed=0):
         from quantized_decode_attention_04_amd.workloads import outlier_scales
         k *= outlier_scales(1, 0, Hkv, d, 0)[None, :, None, :]
         v *= outlier_scales(1, 0, Hkv, d, 1)[None, :, None, :]
+    if name == "fast_growing_value_norms":
+        v *= np.linspace(0.5, 8.0, N, dtype=np.float32)[None, None, :, None]
     if bf16:
         from quantized_decode_attention_04_amd.workloads import round_bf16
         k, v = round_bf16(k), round_bf16(v)
@@ -172,7 +186,7 @@ def test_decode_parity_on_oracle_state(case):
     N = max(lens)
     k, v, kc, vc, ks, vs = _oracle_states(name, d, kspec, vspec, B, Hkv, N, bf16, outl)
     rng = np.random.default_rng(5)
-    q = rng.standard_normal((B, Hq, q_len, d)).astype(np.float32) * np.float32(0.02 if not name.startswith("d") else 1.0)
+    q = rng.standard_normal((B, Hq, q_len, d)).astype(np.float32) * np.float32(Q_STD.get(name, 0.02))
     if bf16:
         from quantized_decode_attention_04_amd.workloads import round_bf16
         q = round_bf16(q)
