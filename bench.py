@@ -37,7 +37,27 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=262144)
     ap.add_argument("--layers", type=int, default=0, help="override the number of layer buffers")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB mebibytes three times (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain float32 device-to-device copy of known size: its FETCH_SIZE and
+    WRITE_SIZE readings per dispatch give the factor by which those counters
+    over- or under-count HBM bytes."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "read_bytes_per_copy": n * 4, "write_bytes_per_copy": n * 4,
+                      "copies": 3}), flush=True)
 
 
 def cpu_baseline(w, sample_tokens: int) -> dict:
@@ -81,6 +101,9 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a single GPU)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
 
@@ -134,7 +157,7 @@ def main():
     pos_new = torch.tensor(lens_h - append, dtype=torch.int32, device=dev)
     lens = torch.tensor(lens_h, dtype=torch.int32, device=dev)
     ws_bytes = tq.tq_decode_workspace_size(kc, vc, B, hq, hkv, qlen, max_len)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((B, hq, qlen, d), dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(d)
 

@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     Codec,
     TQError,
     allocate_cache,
+    allocate_workspace,
     lib_path,
     tq_codec_create,
     tq_codec_destroy,

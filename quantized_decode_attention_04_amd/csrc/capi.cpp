@@ -157,10 +157,6 @@ DecodePlan plan_decode_fast(int batch, int hkv, int rows, int d, int64_t max_len
   size_t off = 0;
   p.off_counters = off;
   off = align256(off + bg * sizeof(uint32_t));
-  p.off_qop = off;
-  off = align256(off + bg * 6144);
-  p.off_qconst = off;
-  off = align256(off + bg * 16 * sizeof(float));
   p.off_part_o = off;
   off = align256(off + bg * p.n_chunks * rows * d * sizeof(float));
   p.off_part_ml = off;
@@ -411,6 +407,7 @@ tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void
   p.kwords = idx_words(kc->h);
   p.ksign_words = sign_words(kc->h);
   p.k_pit = kt->pit;
+  p.k_pi = kt->pi;
   p.k_st = kt->st;
   p.k_cent = kt->cent;
   p.k_idx = k->idx;
@@ -437,8 +434,6 @@ tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void
   p.out = out;
   hipError_t e;
   if (fast) {
-    p.qop = reinterpret_cast<uint32_t*>(w + plan.off_qop);
-    p.qconst = reinterpret_cast<float*>(w + plan.off_qconst);
     piece_tables(kc->h, p.klut);
     piece_tables(vc->h, p.vlut);
     p.kgrid = kc->h.grid_exp;

@@ -30,8 +30,12 @@
 //   from it: the probabilities never move between lanes.
 // * Online softmax per row in the log2 domain; the int32 value accumulators
 //   are flushed to float only when a row maximum or the value-norm reference
-//   grows (rare after the first tiles).
-#include "combine.h"
+//   grows (rare after the first tile of a wave).
+// * The query is rotated once per workgroup inside the kernel (fp32 matrix
+//   cores) while the first two tiles of every wave are already in flight, and
+//   each workgroup's buffer resources end at its chunk, so no byte outside the
+//   chunk is fetched.
+#include "tq_internal.h"
 
 namespace tq {
 namespace {
@@ -39,23 +43,40 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v3u __attribute__((ext_vector_type(3)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
-constexpr int kTile = 64;             // tokens per wave iteration
-constexpr int kWaves = 8;            // 512-thread workgroups, one per compute unit
+constexpr int kTile = 64;              // tokens per wave iteration
+constexpr int kWaves = 8;              // 512-thread workgroups, one per compute unit
 constexpr int kThreads = kWaves * 64;
-constexpr int kMaxChunks = 128;       // merge weights kept in LDS
-constexpr int kRow = kD + 16;         // LDS bytes per token row of value selectors
-constexpr int kSelLds = kTile * kRow;             // value selectors of the tile
+constexpr int kStep = kWaves * kTile;  // tokens per workgroup iteration
+constexpr int kMaxChunks = 128;        // merge weights kept in LDS
+constexpr int kRow = kD + 16;          // LDS bytes per token row of value selectors
+constexpr int kSelLds = kTile * kRow + 448;       // value selectors of the tile (+ row-group offsets)
 constexpr int kNormLds = 2 * kTile * 4;            // key and value norms of the tile
 constexpr int kAccLds = 16 * kD * 4;               // float output accumulator [row][coord]
 constexpr int kWaveLds = kSelLds + kNormLds + kAccLds;
 constexpr int kMergeLds = (kD * kD + 16 * kD + 16 * kMaxChunks + 16) * 4;
 constexpr int kLds = kWaves * kWaveLds > kMergeLds ? kWaves * kWaveLds : kMergeLds;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kQMax = 8355711.f;    // three-digit operand bound (32639 * 256 + 127)
-constexpr float kDigitBias = 8421504.f;  // 0x808080: biased digits are the bytes of q + bias
+constexpr float kQMax = 8355711.f;    // three-digit operand bound (2^23 - 0x8081)
+// 0x808080 = 2^23 + 0x8080: for 0 <= q <= kQMax the float q + 0x808080 lies in
+// [2^23, 2^24), where floats are the integers, and its mantissa is q + 0x8080:
+// byte 2 is the top digit a >= 0, bytes 1 and 0 are the balanced digits + 128
+constexpr float kDigitBias = 8421504.f;
+constexpr int kBufWord3 = 0x00020000;     // raw buffer resource, gfx9 data format
+constexpr float kFlushGap = 4.f;          // log2 headroom: p may reach 2^4 between flushes
+constexpr float kNormHeadroom = 1.125f;   // value-norm reference above the largest norm seen
+
+// Byte offset of row group q (rows 16q .. 16q+15) of a wave's value-selector
+// tile.  LDS has 64 four-byte banks (bank = byte address / 4 mod 64) and
+// serves a 16-byte store for 16 lanes at a time; offsets of 0, 128, 64 and 192
+// bytes mod 256 make the sixteen rows one store touches (4 per group) fill
+// all 64 banks, and put the two 16-lane halves of a transposing 8-byte read
+// 32 banks apart.  The offsets grow with q (+256 where needed) so that no
+// group overlaps the next.
+__device__ __forceinline__ int sel_group_offset(int q) { return 128 * (q & 1) + 320 * (q >> 1); }
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
@@ -99,111 +120,136 @@ __device__ __forceinline__ float flushed(int t24, int t16, int t8) {
   return fmaf(fmaf((float)t24, 256.f, (float)t16), 256.f, (float)t8);
 }
 
+// maximum over the four 16-lane rows (lanes n, n+16, n+32, n+48): the two
+// lane-swap instructions exchange whole rows, so the union of their two
+// results always holds both rows of each pair
 __device__ __forceinline__ float rowmax4(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
-// ---- prologue: rotated queries as int8 operand pieces ----------------------
-//
-// Operand order (matches the key selectors): K-step ks, digit (0 = most
-// significant), lane l (row l%16, group h = l/16), byte s of the 16-byte
-// fragment = coordinate 32h + 16ks + s.  Q = 65536 a + 256 b + c with
-// balanced digits a, b, c in [-128, 127].
-__global__ __launch_bounds__(256) void qprep_fast_kernel(DecodeParams p) {
-  __shared__ float s_pit[kD * kD];   // Pi^T staged once (64 KB)
-  __shared__ float s_in[16 * kD];    // the group's query rows
-  __shared__ float s_q[16 * kD];     // rotated rows
-  __shared__ float s_sc[16];
-  const int bg = blockIdx.x;
-  const int b = bg / p.hkv, g = bg % p.hkv;
-  const int tid = threadIdx.x;
-  if (tid == 0) p.counters[bg] = 0u;
-  {
-    const v4f* src = reinterpret_cast<const v4f*>(p.k_pit);
-    v4f* dst = reinterpret_cast<v4f*>(s_pit);
+__device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-    for (int k = 0; k < kD * kD / 4 / 256; ++k) dst[tid + 256 * k] = src[tid + 256 * k];
-  }
-  for (int e = tid; e < 16 * kD; e += 256) {
-    const int r = e / kD, j = e % kD;
-    float qj = 0.f;
-    if (r < p.rows) {
-      const int h = g * p.group + r / p.q_len, qi = r % p.q_len;
-      const int64_t off = (((int64_t)b * p.hq + h) * p.q_len + qi) * kD + j;
-      qj = p.q_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(p.q)[off] << 16)
-                    : static_cast<const float*>(p.q)[off];
-    }
-    s_in[e] = qj;
-  }
-  __syncthreads();
-  {
-    // thread: coordinate i, rows 8*half .. 8*half+7
-    const int i = tid & (kD - 1), half = tid >> 7;
-    float acc[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) acc[r] = 0.f;
-    for (int j = 0; j < kD; ++j) {
-      const float pij = s_pit[j * kD + i];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) acc[r] = fmaf(pij, s_in[(8 * half + r) * kD + j], acc[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) s_q[(8 * half + r) * kD + i] = acc[r];
-  }
-  __syncthreads();
-  {
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int rr = 0; rr < 4; ++rr) {
-      const int r = 4 * wave + rr;
-      float a = fmaxf(fabsf(s_q[r * kD + lane]), fabsf(s_q[r * kD + 64 + lane]));
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-      if (lane == 0) s_sc[r] = a > 0.f ? kQMax / a : 0.f;
-    }
-  }
-  __syncthreads();
-  uint32_t* qop = p.qop + (size_t)bg * 1536;
-  for (int e = tid; e < 1536; e += 256) {
-    const int dw = e & 3, ln = (e >> 2) & 63, digit = (e >> 8) % 3, ks = (e >> 8) / 3;
-    const int n = ln & 15, h = ln >> 4;
-    uint32_t word = 0;
-    for (int k = 0; k < 4; ++k) {
-      const int coord = 32 * h + 16 * ks + 4 * dw + k;
-      // the product may round one past the bound: clamp so the top digit fits int8
-      const int qv = (int)fminf(fmaxf(rintf(s_q[n * kD + coord] * s_sc[n]), -kQMax), kQMax);
-      const int q1 = (qv + 128) >> 8;   // floor((q + 128) / 256)
-      const int c = qv - 256 * q1;
-      const int a = (q1 + 128) >> 8;
-      const int bb = q1 - 256 * a;
-      const int dig = digit == 0 ? a : (digit == 1 ? bb : c);
-      word |= ((uint32_t)dig & 0xffu) << (8 * k);
-    }
-    qop[e] = word;
-  }
-  if (tid < 16) {
-    const float sc = s_sc[tid];
-    // score = sum_j Q_j C_j / (sigma 2^E) = 256 * [(256 t24 + t16) 256 + t8] / (sigma 2^E)
-    p.qconst[bg * 16 + tid] =
-        (tid < p.rows && sc > 0.f) ? 256.f * p.scale * kLog2e * exp2f(-(float)p.kgrid) / sc : 0.f;
-  }
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
 }
-
-// ---- main kernel -------------------------------------------------------------
-typedef uint32_t v3u __attribute__((ext_vector_type(3)));
-
-constexpr int kBufWord3 = 0x00020000;     // raw buffer resource, gfx9 data format
-constexpr float kFlushGap = 4.f;          // log2 headroom: p may reach 2^4 between flushes
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+
+// ---- query prologue ----------------------------------------------------------
+//
+// The rotated query rows of (b, g) as int8 operand digits, computed by the
+// whole workgroup.  Operand order (matches the key selectors): K-step ks,
+// digit (0 = most significant), lane l (row l%16, group h = l/16), byte s of
+// the 16-byte fragment = coordinate 32h + 16ks + s.  Q = 65536 a + 256 b + c
+// with balanced digits a, b, c in [-128, 127].
+struct QueryOps {
+  v4i a0, b0, c0, a1, b1, c1;
+  float rowc;  // score (log2 units) per unit of the digit product, >= 1e-30
+};
+
+// Operands of q_rot^T = Pi_k q^T on v_mfma_f32_16x16x4f32, wave w computing
+// output coordinates 16w .. 16w+15.  The contraction index is permuted so that
+// every lane reads contiguous runs: in K-step s (0..31) lane l supplies the
+// term j = 32 (l/16) + s, i.e. A = Pi[16w + l%16][32 (l/16) + s] and
+// B = q[row l%16][32 (l/16) + s].  Each lane loads 128 bytes of a Pi row and
+// 128 bytes from the start of its query run (a bf16 run uses the first 64),
+// eight 16-byte loads each, issued before the tiles so that waiting for them
+// leaves the tile loads in flight.
+struct QueryLoads {
+  v4f pi[8];
+  v4u qw[8];
+};
+
+__device__ __forceinline__ void query_loads(const DecodeParams& p, int b, int g, QueryLoads& ql) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, kq = lane >> 4;
+  const int rr = r < p.rows ? r : 0;
+  const int hh = g * p.group + rr / p.q_len, qi = rr % p.q_len;
+  const uint32_t esize = p.q_bf16 ? 2u : 4u;
+  const uint32_t q_bytes = (uint32_t)((int64_t)p.batch * p.hq * p.q_len * kD * esize);
+  const uint32_t qoff = (uint32_t)(((((int64_t)b * p.hq + hh) * p.q_len + qi) * kD + 32 * kq) * esize);
+  // reads past the query tensor (the tail of a bf16 run) return zeros
+  const __amdgpu_buffer_rsrc_t rq = rsrc(p.q, q_bytes);
+  const v4f* pi = reinterpret_cast<const v4f*>(p.k_pi + (16 * wave + r) * kD + 32 * kq);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ql.pi[i] = pi[i];
+    ql.qw[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 16u * i, 0, 0));
+  }
+}
+
+// Query element s of this lane's run from its loaded dwords.
+__device__ __forceinline__ float query_element(const DecodeParams& p, const QueryLoads& ql, int s) {
+  const uint32_t wf = ql.qw[s >> 2][s & 3];             // float run: dword s
+  const uint32_t wb = ql.qw[s >> 3][(s >> 1) & 3];      // bf16 run: half s&1 of dword s/2
+  const uint32_t bits = p.q_bf16 ? ((s & 1) ? (wb & 0xffff0000u) : (wb << 16)) : wf;
+  return (int)(threadIdx.x & 15) < p.rows ? __uint_as_float(bits) : 0.f;
+}
+
+// s_max: [8 waves][16 rows] partial row maxima; s_op: [2 ks][3 digits][64
+// lanes][4 dwords] operand dwords.  Neither is touched after the prologue.
+__device__ __forceinline__ void query_operands(const DecodeParams& p, const QueryLoads& ql, float* s_max,
+                                               uint32_t* s_op, QueryOps& qo) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, kq = lane >> 4;
+  // lane l ends with q_rot[row r][16 wave + 4 kq + i], i = 0..3 (four
+  // independent accumulation chains)
+  v4f part[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) part[c] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 32; ++s)
+    part[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(ql.pi[s >> 2][s & 3], query_element(p, ql, s), part[s & 3],
+                                                       0, 0, 0);
+  const v4f acc = (part[0] + part[1]) + (part[2] + part[3]);
+  const float m4 = rowmax4(fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])), fmaxf(fabsf(acc[2]), fabsf(acc[3]))));
+  if (kq == 0) s_max[wave * 16 + r] = m4;
+  __syncthreads();
+  float mx = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_max[w * 16 + r]);
+  const float sc = mx > 0.f ? kQMax / mx : 0.f;
+  // coordinates 16 wave + 4 kq + i are operand K-step wave & 1, lane
+  // r + 16 (wave >> 1), dword kq
+  uint32_t u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // the product may round one past the bound: clamp so the top digit fits int8
+    const float x = fminf(fmaxf(rintf(acc[i] * sc), -kQMax), kQMax);
+    u[i] = (uint32_t)((int)x + 0x808080);  // bytes: a+128, b+128, c+128
+  }
+  const uint32_t lo01 = perm(u[1], u[0], 0x05010400u);  // u0.b0 u1.b0 u0.b1 u1.b1
+  const uint32_t lo23 = perm(u[3], u[2], 0x05010400u);
+  const uint32_t hi01 = perm(u[1], u[0], 0x0c0c0602u);  // u0.b2 u1.b2 0 0
+  const uint32_t hi23 = perm(u[3], u[2], 0x0c0c0602u);
+  uint32_t* o = s_op + ((wave & 1) * 3 * 64 + r + 16 * (wave >> 1)) * 4 + kq;
+  o[0] = perm(hi23, hi01, 0x05040100u) ^ 0x80808080u;
+  o[64 * 4] = perm(lo23, lo01, 0x07060302u) ^ 0x80808080u;
+  o[128 * 4] = perm(lo23, lo01, 0x05040100u) ^ 0x80808080u;
+  __syncthreads();
+  const v4i* op = reinterpret_cast<const v4i*>(s_op) + lane;
+  qo.a0 = op[0];
+  qo.b0 = op[64];
+  qo.c0 = op[128];
+  qo.a1 = op[192];
+  qo.b1 = op[256];
+  qo.c1 = op[320];
+  // this lane's operand row is r as well
+  // score = sum_j Q_j C_j / (sc 2^E) = 256 [(256 t24 + t16) 256 + t8] / (sc 2^E)
+  qo.rowc = sc > 0.f ? 256.f * p.scale * kLog2e * exp2f(-(float)p.kgrid) / sc : 0.f;
+  qo.rowc = fmaxf(qo.rowc, 1e-30f);  // keeps -inf * rowc = -inf for a zero query row
 }
 
 // One 64-token tile of this wave: the three key and value words of one token
 // and 32-coordinate group per score tile st (token order 16(m/4) + 4st + m%4),
 // and one key and one value norm per lane (token T0 + lane).  Offsets are
 // per-lane so that the buffer range check covers every token: reads past the
-// cache return zeros.
+// chunk return zeros and fetch nothing.
 struct Tile {
   v3u kw[4], vw[4];
   float kn, vn;
@@ -308,6 +354,8 @@ __device__ __forceinline__ void merge_fast(const DecodeParams& p, int b, int g, 
 
 __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[kLds];
+  __shared__ __attribute__((aligned(16))) uint32_t s_op[2 * 3 * 64 * 4];
+  __shared__ float s_max[kWaves * 16];
   __shared__ int s_last;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -318,33 +366,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
   int64_t len64 = p.len[b];
   len64 = len64 < 0 ? 0 : (len64 > p.cap ? p.cap : len64);
   const int len = (int)len64;
+  // this workgroup's tokens c0 .. c0 + ntok - 1; token indices below are
+  // relative to c0
   const int c0 = chunk_id * p.chunk;
   const int c1 = c0 + p.chunk < len ? c0 + p.chunk : len;
-  const int lim = len - p.q_len + (n % p.q_len) + 1;  // row n sees tokens < lim
-  const int lim_all = len - p.q_len + 1;             // tokens every row sees
+  const uint32_t ntok = c1 > c0 ? (uint32_t)(c1 - c0) : 0u;
+  const int lim = len - p.q_len + (n % p.q_len) + 1 - c0;  // row n sees tokens < lim
+  const int lim_all = len - p.q_len + 1 - c0;              // tokens every row sees
 
-  const uint32_t* qo = p.qop + (size_t)bg * 1536 + lane * 4;
-  const v4i qa0 = *reinterpret_cast<const v4i*>(qo);
-  const v4i qb0 = *reinterpret_cast<const v4i*>(qo + 256);
-  const v4i qc0 = *reinterpret_cast<const v4i*>(qo + 512);
-  const v4i qa1 = *reinterpret_cast<const v4i*>(qo + 768);
-  const v4i qb1 = *reinterpret_cast<const v4i*>(qo + 1024);
-  const v4i qc1 = *reinterpret_cast<const v4i*>(qo + 1280);
-  const float rowc = p.qconst[bg * 16 + n];
-  const uint32_t kh1 = p.klut[1], kh0 = p.klut[0], kl1 = p.klut[3], kl0 = p.klut[2];
-  const uint32_t vh1 = p.vlut[1], vh0 = p.vlut[0], vl1 = p.vlut[3], vl0 = p.vlut[2];
-  const float kappa = 256.f * exp2f(-(float)p.vgrid);
-
-  const size_t base = (size_t)bg * (size_t)p.cap;
-  const uint32_t cap = (uint32_t)p.cap;
-  const __amdgpu_buffer_rsrc_t rk = rsrc(p.k_idx + base * 12, cap * 48u);
-  const __amdgpu_buffer_rsrc_t rv = rsrc(p.v_idx + base * 12, cap * 48u);
-  const __amdgpu_buffer_rsrc_t rkn = rsrc(p.k_norm + base, cap * 4u);
-  const __amdgpu_buffer_rsrc_t rvn = rsrc(p.v_norm + base, cap * 4u);
+  // ---- loads: the query prologue's first, then the first two tiles
+  QueryLoads ql;
+  query_loads(p, b, g, ql);
+  const size_t base = (size_t)bg * (size_t)p.cap + (size_t)(ntok > 0 ? c0 : 0);
+  const __amdgpu_buffer_rsrc_t rk = rsrc(p.k_idx + base * 12, ntok * 48u);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(p.v_idx + base * 12, ntok * 48u);
+  const __amdgpu_buffer_rsrc_t rkn = rsrc(p.k_norm + base, ntok * 4u);
+  const __amdgpu_buffer_rsrc_t rvn = rsrc(p.v_norm + base, ntok * 4u);
   uint32_t lw[4];
 #pragma unroll
   for (int st = 0; st < 4; ++st) lw[st] = (uint32_t)(16 * (n >> 2) + 4 * st + (n & 3)) * 48u + 12u * h;
   const uint32_t ln4 = (uint32_t)lane * 4u;
+  const uint32_t t_first = (uint32_t)(wave * kTile);
+  Tile ta, tb;
+  // issue order matters: the loop waits on the first tile's loads with the
+  // second tile's still in flight, which the wait counter can express only if
+  // every load of the first tile precedes every load of the second
+  load_tile(ta, rk, rv, rkn, rvn, lw, ln4, t_first);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(tb, rk, rv, rkn, rvn, lw, ln4, t_first + kStep);
+  // nothing that waits for the query loads may move above the tile loads
+  __builtin_amdgcn_sched_barrier(0);
+
+  QueryOps qo;
+  query_operands(p, ql, s_max, s_op, qo);
+  const float rowc = qo.rowc;
+  const uint32_t kh1 = p.klut[1], kh0 = p.klut[0], kl1 = p.klut[3], kl0 = p.klut[2];
+  const uint32_t vh1 = p.vlut[1], vh0 = p.vlut[0], vl1 = p.vlut[3], vl0 = p.vlut[2];
+  const float kappa = 256.f * exp2f(-(float)p.vgrid);
 
   uint8_t* sb = s_buf + wave * kWaveLds;
   float* sn = reinterpret_cast<float*>(sb + kSelLds);            // [2][64] norms of the tile
@@ -355,29 +413,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
 #pragma unroll
   for (int u = 0; u < 8; ++u) oref(u) = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // Value-norm reference of this wave's tokens: the probability scale is fixed
-  // for the whole chunk, p * n_v * sig <= 2^4 * kQMax / 2^4.
-  const int t_first = c0 + wave * kTile;
-  float nmax = 0.f;
-  for (int T0 = t_first; T0 < c1; T0 += 8 * kWaves * kTile) {
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      v[k] = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(rvn, ln4 + (uint32_t)(T0 + k * kWaves * kTile) * 4u, 0, 0));
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (T0 + k * kWaves * kTile + lane < c1) nmax = fmaxf(nmax, v[k]);
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, o, 64));
-  // 0.1% margin: p n_v sig stays below kQMax through exp2 and product rounding
-  const float sig = nmax > 0.f ? kQMax / (nmax * 16.016f) : 0.f;
-  const float kflush = sig > 0.f ? kappa / sig : 0.f;
-
   // running maximum of the row (log2 domain); a finite "minus infinity" so that
   // masked scores (-inf) give exp2 = 0 and an empty row never forms inf - inf
   float m_ref = -1e30f, l_run = 0.f;
+  // value-norm reference: probabilities enter the digits as p n_v sig with
+  // sig = kQMax / (16.016 nref), so p n_v sig <= kQMax while n_v <= nref;
+  // lsig = log2 sig is folded into the exponent, kflush = kappa / sig
+  float nref = 0.f, lsig = 0.f, isig = 1.f, kflush = kappa;
   v4i ahh[8], ax[8], all[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
@@ -386,8 +428,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
     all[u] = v4i{0, 0, 0, 0};
   }
 
-  auto process = [&](const Tile& cur, const int T0) {
-
+  auto process = [&](const Tile& cur, const uint32_t T0) {
     // ---- scores on the matrix cores
     float sc[16];
 #pragma unroll
@@ -399,16 +440,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
       // Q C = 2^24 a Ch + 2^16 (a Cl + b Ch) + 2^8 (b Cl + c Ch) [+ c Cl, below
       // 2^-23 of the product]
       v4i t24 = v4i{0, 0, 0, 0}, t16 = v4i{0, 0, 0, 0}, t8 = v4i{0, 0, 0, 0};
-      t24 = mfma(ah0, qa0, t24);
-      t16 = mfma(al0, qa0, t16);
-      t16 = mfma(ah0, qb0, t16);
-      t8 = mfma(al0, qb0, t8);
-      t8 = mfma(ah0, qc0, t8);
-      t24 = mfma(ah1, qa1, t24);
-      t16 = mfma(al1, qa1, t16);
-      t16 = mfma(ah1, qb1, t16);
-      t8 = mfma(al1, qb1, t8);
-      t8 = mfma(ah1, qc1, t8);
+      t24 = mfma(ah0, qo.a0, t24);
+      t16 = mfma(al0, qo.a0, t16);
+      t16 = mfma(ah0, qo.b0, t16);
+      t8 = mfma(al0, qo.b0, t8);
+      t8 = mfma(ah0, qo.c0, t8);
+      t24 = mfma(ah1, qo.a1, t24);
+      t16 = mfma(al1, qo.a1, t16);
+      t16 = mfma(ah1, qo.b1, t16);
+      t8 = mfma(al1, qo.b1, t8);
+      t8 = mfma(ah1, qo.c1, t8);
       // 256 t24 + t16 is exact in int32; then one float rounding (2^-24)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[4 * st + i] = fmaf((float)(t24[i] * 256 + t16[i]), 256.f, (float)t8[i]);
@@ -420,18 +461,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
       uint32_t s8[8];
       selectors3(cur.vw[st].x, cur.vw[st].y, cur.vw[st].z, s8);
       const int tt = 16 * (n >> 2) + 4 * st + (n & 3);
-      v4u* dst = reinterpret_cast<v4u*>(sb + tt * kRow + 32 * h);
+      v4u* dst = reinterpret_cast<v4u*>(sb + tt * kRow + sel_group_offset(n >> 2) + 32 * h);
       dst[0] = v4u{s8[0], s8[1], s8[2], s8[3]};
       dst[1] = v4u{s8[4], s8[5], s8[6], s8[7]};
     }
     sn[lane] = cur.kn;
-    sn[kTile + lane] = cur.vn * sig;  // per-token weight of p in the probability digits
+    sn[kTile + lane] = cur.vn;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- online softmax for row n over tokens tb .. tb+15 held by this lane
-    const int tb = T0 + 16 * h;
+    const int tb = (int)T0 + 16 * h;
     const v4f* snk = reinterpret_cast<const v4f*>(sn + 16 * h);
     const v4f* snv = reinterpret_cast<const v4f*>(sn + kTile + 16 * h);
     float s[16], wv[16];
@@ -440,24 +481,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
       const v4f nk4 = snk[c], nv4 = snv[c];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[4 * c + i] = sc[4 * c + i] * (rowc * nk4[i]);
+        s[4 * c + i] = sc[4 * c + i] * nk4[i];  // score / rowc
         wv[4 * c + i] = nv4[i];
       }
     }
-    const bool full = T0 + kTile <= c1 && T0 + kTile <= lim_all;  // no token of the tile is masked
+    const bool full = T0 + kTile <= ntok && (int)T0 + kTile <= lim_all;  // no token of the tile is masked
     if (!full) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int tok = tb + j;
-        if (!(tok < c1 && tok < lim)) s[j] = -INFINITY;
+        if (!(tok < (int)ntok && tok < lim)) s[j] = -INFINITY;
       }
     }
-    float tmax = s[0];
+    float tmax = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-    for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, s[j]);
-    tmax = rowmax4(tmax);
+    for (int j = 3; j < 15; j += 2) tmax = fmaxf(fmaxf(tmax, s[j]), s[j + 1]);
+    tmax = fmaxf(tmax, s[15]);
+    tmax = rowmax4(tmax) * rowc;
     const bool grow = tmax > m_ref + kFlushGap;
-    if (__ballot(grow) != 0) {
+    const bool vgrow = cur.vn > nref;
+    if (__ballot(grow || vgrow) != 0) {
+      const float nnew = __ballot(vgrow) != 0 ? kNormHeadroom * wave_max(cur.vn) : nref;
       const float m_new = grow ? tmax : m_ref;
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
 #pragma unroll
@@ -472,18 +516,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
       }
       l_run *= alpha;
       m_ref = m_new;
+      if (nnew > nref) {
+        nref = nnew;
+        const float sig = kQMax / (nref * 16.016f);
+        lsig = __log2f(sig);
+        isig = 1.f / sig;
+        kflush = kappa * isig;
+      }
     }
+    // p sig = exp2(s - m_ref + lsig); the digits carry p n_v sig
+    const float off = lsig - m_ref;
     float psum = 0.f;
     uint32_t qv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float pr = __builtin_amdgcn_exp2f(s[j] - m_ref);
+      const float pr = __builtin_amdgcn_exp2f(fmaf(s[j], rowc, off));
       psum += pr;
-      // q + 0x808080 with q = rint(p n_v sig) in [0, 8355711]: its bytes are
-      // the balanced digits of q plus 128
-      qv[j] = (uint32_t)fmaf(pr, wv[j], kDigitBias);
+      qv[j] = __float_as_uint(fmaf(pr, wv[j], kDigitBias));
     }
-    l_run += psum;
+    l_run = fmaf(psum, isig, l_run);
     v4i ba, bb, bc;  // digits of 2^16, 2^8 and 1
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -493,13 +544,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
       const uint32_t b23 = perm(qv[4 * c + 3], qv[4 * c + 2], 0x0c0c0602u);
       bc[c] = (int)(perm(a23, a01, 0x05040100u) ^ 0x80808080u);
       bb[c] = (int)(perm(a23, a01, 0x07060302u) ^ 0x80808080u);
-      ba[c] = (int)(perm(b23, b01, 0x05040100u) ^ 0x80808080u);
+      ba[c] = (int)perm(b23, b01, 0x05040100u);
     }
 
     // ---- values on the matrix cores: coordinates 16u + n of tokens tb..tb+15
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const uint8_t* a0 = sb + (16 * h + (n >> 1)) * kRow + 16 * u + 8 * (n & 1);
+      const uint8_t* a0 = sb + (16 * h + (n >> 1)) * kRow + sel_group_offset(h) + 16 * u + 8 * (n & 1);
       const v2i r0 = read_tr8(a0);
       const v2i r1 = read_tr8(a0 + 8 * kRow);
       const uint32_t sv[4] = {(uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r1.x, (uint32_t)r1.y};
@@ -516,19 +567,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // two tile buffers in turn: the next tile's loads are in flight while the
-  // current one is processed.  The loads are unconditional (a tile past the
-  // chunk reads masked tokens, or zeros past the cache) so that the number of
-  // loads in flight is the same on every path and the waits stay partial.
-  Tile ta, tb;
-  load_tile(ta, rk, rv, rkn, rvn, lw, ln4, (uint32_t)t_first);
-  constexpr int kStep = kWaves * kTile;
-  for (int T0 = t_first; T0 < c1; T0 += 2 * kStep) {
-    load_tile(tb, rk, rv, rkn, rvn, lw, ln4, (uint32_t)(T0 + kStep));
+  // two tile buffers in turn: a tile's successor is in flight while it is
+  // processed.  The loads are unconditional: past the chunk they read zeros
+  // without touching memory, so the number of loads in flight is the same
+  // on every path and the waits stay partial.
+  for (uint32_t T0 = t_first; T0 < ntok; T0 += 2 * kStep) {
     process(ta, T0);
-    if (T0 + kStep >= c1) break;
-    load_tile(ta, rk, rv, rkn, rvn, lw, ln4, (uint32_t)(T0 + 2 * kStep));
+    if (T0 + kStep >= ntok) break;
+    load_tile(ta, rk, rv, rkn, rvn, lw, ln4, T0 + 2 * kStep);
     process(tb, T0 + kStep);
+    load_tile(tb, rk, rv, rkn, rvn, lw, ln4, T0 + 3 * kStep);
   }
 
   v4f of[8];
@@ -541,7 +589,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
 
-  // ---- merge the four waves' partials of this chunk in LDS
+  // ---- merge the waves' partials of this chunk in LDS
   __syncthreads();
   float* cw = reinterpret_cast<float*>(s_buf);
   {
@@ -580,7 +628,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
       pml[2 * r + 1] = L;
     }
   }
-  // publish; the last workgroup of (b, g) to arrive merges every chunk
+  // publish; the last workgroup of (b, g) to arrive merges every chunk and
+  // leaves the arrival counter at zero for the next call
   __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) s_last = atomicAdd(p.counters + bg, 1u) == (unsigned)(p.n_chunks - 1);
@@ -598,9 +647,9 @@ bool fast_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, in
 }
 
 hipError_t launch_decode_fast(const DecodeParams& p, hipStream_t stream) {
-  if (p.n_chunks > 65535 || p.hkv > 65535 || p.batch > 65535 || p.d != kD) return hipErrorInvalidValue;
-  qprep_fast_kernel<<<dim3(p.batch * p.hkv), dim3(256), 0, stream>>>(p);
-  if (p.n_chunks > kMaxChunks) return hipErrorInvalidValue;
+  if (p.n_chunks < 1 || p.n_chunks > kMaxChunks || p.hkv > 65535 || p.batch > 65535 || p.d != kD ||
+      p.rows > 16 || (int64_t)p.chunk * 48 > 0xffffffffLL)
+    return hipErrorInvalidValue;
   decode_fast_kernel<<<dim3(p.n_chunks, p.hkv, p.batch), dim3(kThreads), 0, stream>>>(p);
   return hipGetLastError();
 }

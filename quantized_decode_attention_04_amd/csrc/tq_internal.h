@@ -85,6 +85,7 @@ struct DecodeParams {
   // key codec / cache
   int kmode, kbits, kwords, ksign_words;
   const float* k_pit;   // Pi_k^T
+  const float* k_pi;    // Pi_k row-major
   const float* k_st;    // S^T
   const float* k_cent;
   const uint32_t* k_idx;
@@ -110,10 +111,7 @@ struct DecodeParams {
   float* part_o;       // [batch*hkv][n_chunks][rows][d]
   float* part_ml;      // [batch*hkv][n_chunks][rows][2]
   float* out;          // [batch][hq][q_len][d]
-  // MFMA path: int8 query operands and per-row constants written by its
-  // prologue, and the byte look-up tables of the two codebooks
-  uint32_t* qop;       // [batch*hkv][d/64][3 digits][64 lanes][4 dwords]
-  float* qconst;       // [batch*hkv][16]
+  // MFMA path: the byte look-up tables of the two codebooks
   uint32_t klut[4];    // key centroid pieces: hi bytes 0-3, 4-7, lo bytes 0-3, 4-7
   uint32_t vlut[4];    // value centroid pieces
   int kgrid, vgrid;    // grid exponents E (centroid = integer * 2^-E)
@@ -122,7 +120,7 @@ struct DecodeParams {
 // Chunk length of the token split and the workspace layout for it.
 struct DecodePlan {
   int rows, chunk, n_chunks;
-  size_t off_counters, off_qrot, off_qs, off_part_o, off_part_ml, off_qop, off_qconst, total;
+  size_t off_counters, off_qrot, off_qs, off_part_o, off_part_ml, total;
   bool fast;
 };
 DecodePlan plan_decode(int batch, int hkv, int rows, int d, int64_t max_len, bool prod);

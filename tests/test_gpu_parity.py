@@ -171,7 +171,7 @@ def _gpu_decode(gk, gv, kcache, vcache, q, lens, max_len, scale, bf16):
     B, Hq, q_len, d = q.shape
     out = torch.zeros((B, Hq, q_len, d), dtype=torch.float32, device="cuda")
     nbytes = tq.tq_decode_workspace_size(gk, gv, B, Hq, kcache.heads, q_len, max_len)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     qd = to_device_f(q, bf16)
     ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
     tq.tq_decode_attention(gk, gv, qd, kcache, vcache, ld, max_len, scale, out, ws)
