@@ -157,9 +157,8 @@ tq_status tq_quantize_append(const tq_codec* codec, const void* x, int32_t x_dty
                              int32_t n_new, const int64_t* x_strides, const tq_cache* dst, const int32_t* d_pos,
                              void* stream);
 
-/* Bytes of device workspace tq_decode_attention needs for these sizes.  The
- * workspace holds per-call partial results and one arrival counter per
- * (sequence, KV head); see tq_decode_attention for its zero-fill rule. */
+/* Bytes of device workspace tq_decode_attention needs for these sizes (the
+ * per-chunk partial results of the split over the token axis). */
 tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t n_q_heads,
                                    int32_t n_kv_heads, int32_t q_len, int64_t max_len, size_t* bytes);
 
@@ -176,9 +175,7 @@ tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32
  *   scale    softmax scale (1/sqrt(head_dim) in [val])
  *   out      device float [batch][n_q_heads][q_len][head_dim]
  *   ws       device workspace of ws_bytes >= tq_decode_workspace_size(...),
- *            caller-owned and zero-filled before the first call that uses
- *            it; every call that runs to completion leaves its counters at
- *            zero again, so it needs no clearing between calls.  Calls that
+ *            caller-owned; its contents need no initialisation.  Calls that
  *            share a workspace must not run concurrently.
  * Query head h reads KV head h / (n_q_heads / n_kv_heads); row i of q_len
  * sees tokens t <= N_b - q_len + i ([omlx] make_mask: causal for new tokens).

@@ -252,8 +252,7 @@ def tq_decode_workspace_size(kc: Codec, vc: Codec, batch: int, n_q_heads: int, n
 
 def allocate_workspace(kc: Codec, vc: Codec, batch: int, n_q_heads: int, n_kv_heads: int, q_len: int,
                        max_len: int, device="cuda"):
-    """A zero-filled device workspace for tq_decode_attention with these sizes
-    (the library requires it zeroed before its first use)."""
+    """A device workspace for tq_decode_attention with these sizes."""
     import torch
     return torch.zeros(tq_decode_workspace_size(kc, vc, batch, n_q_heads, n_kv_heads, q_len, max_len),
                        dtype=torch.uint8, device=device)
@@ -264,8 +263,7 @@ def tq_decode_attention(kc: Codec, vc: Codec, q, kcache: Cache, vcache: Cache, l
     """out[b, h, i, :] = attention of q[b, h, i] over the compressed cache.
     q: [batch, n_q_heads, q_len, head_dim] contiguous f32/bf16; lens: int32
     device [batch]; out: float32 contiguous like q; ws: device byte tensor of at
-    least tq_decode_workspace_size(...) bytes, zero-filled before its first use
-    (allocate_workspace)."""
+    least tq_decode_workspace_size(...) bytes (allocate_workspace)."""
     import torch
     _on_device(q, lens, out, ws, *kcache.arrays().values(), *vcache.arrays().values())
     if q.dim() != 4 or not q.is_contiguous():

@@ -155,9 +155,7 @@ DecodePlan plan_decode_fast(int batch, int hkv, int rows, int d, int64_t max_len
   p.n_chunks = (int)((max_len + chunk - 1) / chunk);
   const size_t bg = (size_t)batch * hkv;
   size_t off = 0;
-  p.off_counters = off;
-  off = align256(off + bg * sizeof(uint32_t));
-  p.off_part_o = off;
+  p.off_part_o = off;  // the merge is a second kernel: no arrival counters
   off = align256(off + bg * p.n_chunks * rows * d * sizeof(float));
   p.off_part_ml = off;
   off = align256(off + bg * p.n_chunks * rows * 2 * sizeof(float));

@@ -2,9 +2,11 @@
 //
 // Covers head_dim 128 with 3-bit MSE keys and values and up to 16 query rows
 // per KV head (the 256k-context MTP-verify workload: 8 query heads per KV head
-// x 2 new tokens).  Same split over the token axis and the same cross-chunk
-// merge as the general kernel; the per-token work is reorganised so that both
-// products run as exact int8 matrix-core operations:
+// x 2 new tokens).  Same split over the token axis as the general kernel, with
+// the cross-chunk merge as a second, stream-ordered kernel (a device-wide fence
+// per workgroup would write back and invalidate the L2 of every XCD); the
+// per-token work is reorganised so that both products run as exact int8
+// matrix-core operations:
 //
 //   scores  S^T[token][row] = C_k[token][coord] . Q^T[coord][row]
 //   values  O^T[coord][row] = V^T[coord][token] . P'^T[token][row]
@@ -57,8 +59,7 @@ constexpr int kSelLds = kTile * kRow + 448;       // value selectors of the tile
 constexpr int kNormLds = 2 * kTile * 4;            // key and value norms of the tile
 constexpr int kAccLds = 16 * kD * 4;               // float output accumulator [row][coord]
 constexpr int kWaveLds = kSelLds + kNormLds + kAccLds;
-constexpr int kMergeLds = (kD * kD + 16 * kD + 16 * kMaxChunks + 16) * 4;
-constexpr int kLds = kWaves * kWaveLds > kMergeLds ? kWaves * kWaveLds : kMergeLds;
+constexpr int kLds = kWaves * kWaveLds;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kQMax = 8355711.f;    // three-digit operand bound (2^23 - 0x8081)
 // 0x808080 = 2^23 + 0x8080: for 0 <= q <= kQMax the float q + 0x808080 lies in
@@ -267,96 +268,10 @@ __device__ __forceinline__ void load_tile(Tile& t, __amdgpu_buffer_rsrc_t rk, __
   t.vn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvn, ln4 + T0 * 4u, 0, 0));
 }
 
-// Cross-chunk merge by the last workgroup of (b, g): row maxima and weights
-// from every chunk's (m, l), then each thread accumulates one float4 of the
-// 16 x 128 output over all chunks with every load issued before any is used,
-// and the single inverse rotation runs against Pi_v staged in LDS.
-__device__ __forceinline__ void merge_fast(const DecodeParams& p, int b, int g, float* lds) {
-  float* s_pi = lds;                         // [kD][kD] Pi_v, row-major
-  float* s_o = s_pi + kD * kD;               // [16][kD] merged rotated rows
-  float* s_w = s_o + 16 * kD;                // [16][n_chunks] chunk weights / L
-  const int rows = p.rows, nch = p.n_chunks, tid = threadIdx.x;
-  const int bg = b * p.hkv + g;
-  const float* pml0 = p.part_ml + (size_t)bg * nch * rows * 2;
-  const float* po0 = p.part_o + (size_t)bg * nch * rows * kD;
-  // Pi_v: 8 float4 per thread, all in flight
-  {
-    const v4f* src = reinterpret_cast<const v4f*>(p.v_pi);
-    v4f buf[kD * kD / 4 / kThreads];
-#pragma unroll
-    for (int k = 0; k < kD * kD / 4 / kThreads; ++k) buf[k] = src[tid + kThreads * k];
-#pragma unroll
-    for (int k = 0; k < kD * kD / 4 / kThreads; ++k) reinterpret_cast<v4f*>(s_pi)[tid + kThreads * k] = buf[k];
-  }
-  // weights: 32 lanes per row
-  {
-    const int r = tid >> 5, cl = tid & 31;
-    float M = -INFINITY;
-    if (r < rows)
-      for (int c = cl; c < nch; c += 32) M = fmaxf(M, pml0[((size_t)c * rows + r) * 2]);
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 32));
-    float L = 0.f;
-    if (r < rows)
-      for (int c = cl; c < nch; c += 32) {
-        const float mc = pml0[((size_t)c * rows + r) * 2];
-        const float w = (M == -INFINITY || mc == -INFINITY) ? 0.f : exp2f(mc - M);
-        s_w[r * nch + c] = w;
-        L = fmaf(w, pml0[((size_t)c * rows + r) * 2 + 1], L);
-      }
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) L += __shfl_xor(L, o, 32);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    __syncthreads();
-    if (r < rows)
-      for (int c = cl; c < nch; c += 32) s_w[r * nch + c] *= inv;
-  }
-  __syncthreads();
-  // one float4 of the output per thread (512 threads x 4 = 16 rows x 128)
-  {
-    const int e = 4 * tid, r = e / kD;
-    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-    if (r < rows) {
-      const v4f* src = reinterpret_cast<const v4f*>(po0 + e);
-      const size_t stride = (size_t)rows * kD / 4;
-      int c = 0;
-      for (; c + 16 <= nch; c += 16) {
-        v4f v[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = src[(size_t)(c + k) * stride];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) acc += v[k] * s_w[r * nch + c + k];
-      }
-      for (; c < nch; ++c) acc += src[(size_t)c * stride] * s_w[r * nch + c];
-    }
-    reinterpret_cast<v4f*>(s_o)[tid] = acc;
-  }
-  __syncthreads();
-  // out = o Pi_v (row-vector form of Pi_v^T o): thread -> column j, 4 rows
-  {
-    const int j = tid & (kD - 1), r0 = 4 * (tid >> 7);
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < kD; ++i) {
-      const float pij = s_pi[i * kD + j];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) a[k] = fmaf(s_o[(r0 + k) * kD + i], pij, a[k]);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int r = r0 + k;
-      if (r < rows) {
-        const int h = g * p.group + r / p.q_len, qi = r % p.q_len;
-        p.out[(((int64_t)b * p.hq + h) * p.q_len + qi) * kD + j] = a[k];
-      }
-    }
-  }
-}
-
 __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[kLds];
   __shared__ __attribute__((aligned(16))) uint32_t s_op[2 * 3 * 64 * 4];
   __shared__ float s_max[kWaves * 16];
-  __shared__ int s_last;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, h = lane >> 4;  // query row, lane group
@@ -628,16 +543,60 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
       pml[2 * r + 1] = L;
     }
   }
-  // publish; the last workgroup of (b, g) to arrive merges every chunk and
-  // leaves the arrival counter at zero for the next call
-  __threadfence();
+}
+
+// Cross-chunk merge, one workgroup of kD threads per (query row, KV head,
+// sequence), stream-ordered after the decode kernel: weights 2^(m_c - M) / L
+// from every chunk's (m, l), the merged rotated row o = sum_c w_c o_c (thread
+// j -> coordinate j), and the single inverse rotation out = Pi_v^T o, in row
+// form out_j = sum_i o_i Pi_v[i][j].
+__global__ __launch_bounds__(kD) void merge_fast_kernel(DecodeParams p) {
+  __shared__ float s_w[kMaxChunks];
+  __shared__ float s_o[kD];
+  __shared__ float s_red[4];
+  const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int bg = b * p.hkv + g, j = threadIdx.x, lane = j & 63, wave = j >> 6;
+  const int nch = p.n_chunks, rows = p.rows;
+  // column j of Pi_v: issued first, used last
+  float pv[kD];
+#pragma unroll
+  for (int i = 0; i < kD; ++i) pv[i] = p.v_pi[i * kD + j];
+  const float* pml = p.part_ml + (size_t)bg * nch * rows * 2;
+  const float* po = p.part_o + (size_t)bg * nch * rows * kD;
+  float mc = -INFINITY, lc = 0.f;
+  if (j < nch) {
+    mc = pml[((size_t)j * rows + r) * 2];
+    lc = pml[((size_t)j * rows + r) * 2 + 1];
+  }
+  float M = wave_max(mc);
+  if (lane == 0) s_red[wave] = M;
   __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(p.counters + bg, 1u) == (unsigned)(p.n_chunks - 1);
+  M = fmaxf(s_red[0], s_red[1]);
+  const float w = (j < nch && M != -INFINITY && mc != -INFINITY) ? exp2f(mc - M) : 0.f;
+  float L = w * lc;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+  if (lane == 0) s_red[2 + wave] = L;
+  if (j < kMaxChunks) s_w[j] = w;
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  merge_fast(p, b, g, reinterpret_cast<float*>(s_buf));
-  if (threadIdx.x == 0) p.counters[bg] = 0u;
+  L = s_red[2] + s_red[3];
+  float o = 0.f;
+  int c = 0;
+  for (; c + 16 <= nch; c += 16) {
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = po[((size_t)(c + k) * rows + r) * kD + j];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) o = fmaf(s_w[c + k], v[k], o);
+  }
+  for (; c < nch; ++c) o = fmaf(s_w[c], po[((size_t)c * rows + r) * kD + j], o);
+  s_o[j] = L > 0.f ? o / L : 0.f;
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < kD; ++i) acc = fmaf(s_o[i], pv[i], acc);
+  const int h = g * p.group + r / p.q_len, qi = r % p.q_len;
+  p.out[(((int64_t)b * p.hq + h) * p.q_len + qi) * kD + j] = acc;
 }
 
 }  // namespace
@@ -651,6 +610,7 @@ hipError_t launch_decode_fast(const DecodeParams& p, hipStream_t stream) {
       p.rows > 16 || (int64_t)p.chunk * 48 > 0xffffffffLL)
     return hipErrorInvalidValue;
   decode_fast_kernel<<<dim3(p.n_chunks, p.hkv, p.batch), dim3(kThreads), 0, stream>>>(p);
+  merge_fast_kernel<<<dim3(p.rows, p.hkv, p.batch), dim3(kD), 0, stream>>>(p);
   return hipGetLastError();
 }
 
