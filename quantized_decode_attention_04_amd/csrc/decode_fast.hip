@@ -68,7 +68,7 @@ constexpr float kQMax = 8355711.f;    // three-digit operand bound (2^23 - 0x808
 constexpr float kDigitBias = 8421504.f;
 constexpr int kBufWord3 = 0x00020000;     // raw buffer resource, gfx9 data format
 constexpr float kFlushGap = 4.f;          // log2 headroom: p may reach 2^4 between flushes
-constexpr float kNormHeadroom = 1.125f;   // value-norm reference above the largest norm seen
+constexpr float kNormHeadroom = 2.f;      // value-norm reference: twice the largest norm seen
 
 // Byte offset of row group q (rows 16q .. 16q+15) of a wave's value-selector
 // tile.  LDS has 64 four-byte banks (bank = byte address / 4 mod 64) and
@@ -335,6 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
   // sig = kQMax / (16.016 nref), so p n_v sig <= kQMax while n_v <= nref;
   // lsig = log2 sig is folded into the exponent, kflush = kappa / sig
   float nref = 0.f, lsig = 0.f, isig = 1.f, kflush = kappa;
+  bool empty = true;  // accumulators untouched so far (wave-uniform)
   v4i ahh[8], ax[8], all[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
@@ -419,15 +420,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
       const float nnew = __ballot(vgrow) != 0 ? kNormHeadroom * wave_max(cur.vn) : nref;
       const float m_new = grow ? tmax : m_ref;
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+      if (!empty) {  // nothing to move before the wave's first tile
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        v4f o = oref(u);
+        for (int u = 0; u < 8; ++u) {
+          v4f o = oref(u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = fmaf(flushed(ahh[u][i], ax[u][i], all[u][i]), kflush, o[i]) * alpha;
-        oref(u) = o;
-        ahh[u] = v4i{0, 0, 0, 0};
-        ax[u] = v4i{0, 0, 0, 0};
-        all[u] = v4i{0, 0, 0, 0};
+          for (int i = 0; i < 4; ++i) o[i] = fmaf(flushed(ahh[u][i], ax[u][i], all[u][i]), kflush, o[i]) * alpha;
+          oref(u) = o;
+          ahh[u] = v4i{0, 0, 0, 0};
+          ax[u] = v4i{0, 0, 0, 0};
+          all[u] = v4i{0, 0, 0, 0};
+        }
       }
       l_run *= alpha;
       m_ref = m_new;
@@ -450,6 +453,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
       qv[j] = __float_as_uint(fmaf(pr, wv[j], kDigitBias));
     }
     l_run = fmaf(psum, isig, l_run);
+    empty = false;
     v4i ba, bb, bc;  // digits of 2^16, 2^8 and 1
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
