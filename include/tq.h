@@ -157,6 +157,16 @@ tq_status tq_quantize_append(const tq_codec* codec, const void* x, int32_t x_dty
                              int32_t n_new, const int64_t* x_strides, const tq_cache* dst, const int32_t* d_pos,
                              void* stream);
 
+/* Quantise the new keys and values of one decode step in one launch ([omlx]
+ * update_and_fetch appends keys and values together).  Same semantics and
+ * errors as two tq_quantize_append calls, one with (kc, k, k_strides, kdst)
+ * and one with (vc, v, v_strides, vdst), sharing dtype, sizes and d_pos;
+ * kc and vc must have the same head_dim (else CONFIG_MISMATCH). */
+tq_status tq_quantize_append_kv(const tq_codec* kc, const tq_codec* vc, const void* k, const void* v,
+                                int32_t x_dtype, int32_t batch, int32_t heads, int32_t n_new,
+                                const int64_t* k_strides, const int64_t* v_strides, const tq_cache* kdst,
+                                const tq_cache* vdst, const int32_t* d_pos, void* stream);
+
 /* Bytes of device workspace tq_decode_attention needs for these sizes (the
  * per-chunk partial results of the split over the token axis). */
 tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t n_q_heads,

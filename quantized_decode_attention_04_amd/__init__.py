@@ -27,5 +27,6 @@ from ._binding import (  # noqa: F401
     tq_decode_workspace_size,
     tq_last_error,
     tq_quantize_append,
+    tq_quantize_append_kv,
     tq_status_string,
 )

@@ -60,6 +60,8 @@ def _load() -> ctypes.CDLL:
         "tq_codec_export": (I32, [P, P, P, P, P]),
         "tq_codec_upload": (I32, [P]),
         "tq_quantize_append": (I32, [P, P, I32, I32, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(_Cache), P, P]),
+        "tq_quantize_append_kv": (I32, [P, P, P, P, I32, I32, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                        ctypes.POINTER(_Cache), ctypes.POINTER(_Cache), P, P]),
         "tq_decode_workspace_size": (I32, [P, P, I32, I32, I32, I32, I64, ctypes.POINTER(SZ)]),
         "tq_decode_attention": (I32, [P, P, P, I32, I32, I32, I32, I32, ctypes.POINTER(_Cache),
                                       ctypes.POINTER(_Cache), P, I64, ctypes.c_float, P, P, SZ, P]),
@@ -77,7 +79,7 @@ _lib = _load()
 
 EXPORTED = (
     "tq_codec_create", "tq_codec_destroy", "tq_codec_get_info", "tq_codec_export", "tq_codec_upload",
-    "tq_quantize_append", "tq_decode_workspace_size", "tq_decode_attention", "tq_last_error",
+    "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_workspace_size", "tq_decode_attention", "tq_last_error",
     "tq_status_string",
 )
 
@@ -240,6 +242,29 @@ def tq_quantize_append(codec: Codec, x, cache: Cache, pos, stream=None) -> None:
     _check(_lib.tq_quantize_append(codec.handle, ctypes.c_void_p(x.data_ptr()), _dtype_code(x), int(x.shape[0]),
                                    int(x.shape[1]), int(x.shape[2]), strides, ctypes.byref(st),
                                    ctypes.c_void_p(pos.data_ptr()), _stream(stream)))
+
+
+def tq_quantize_append_kv(kc: Codec, vc: Codec, k, v, kcache: Cache, vcache: Cache, pos, stream=None) -> None:
+    """Quantise the new keys k and values v [batch, heads, n_new, head_dim]
+    (same dtype and sizes) into their caches at positions pos[b] + t, in one
+    launch."""
+    import torch
+    _on_device(k, v, pos, *kcache.arrays().values(), *vcache.arrays().values())
+    for x in (k, v):
+        if x.dim() != 4 or x.stride(3) != 1:
+            raise ValueError("k and v must be [batch, heads, n_new, head_dim] with unit coordinate stride")
+    if tuple(k.shape) != tuple(v.shape) or k.dtype != v.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    if k.shape[3] != kc.info["head_dim"]:
+        raise ValueError("head_dim of k does not match the key codec")
+    if pos.dtype != torch.int32 or pos.numel() != k.shape[0] or not pos.is_contiguous():
+        raise ValueError("pos must be a contiguous int32 tensor of length batch")
+    ks_, vs_ = (ctypes.c_int64 * 4)(*k.stride()), (ctypes.c_int64 * 4)(*v.stride())
+    kst, vst = kcache.as_struct(), vcache.as_struct()
+    _check(_lib.tq_quantize_append_kv(kc.handle, vc.handle, ctypes.c_void_p(k.data_ptr()),
+                                      ctypes.c_void_p(v.data_ptr()), _dtype_code(k), int(k.shape[0]),
+                                      int(k.shape[1]), int(k.shape[2]), ks_, vs_, ctypes.byref(kst),
+                                      ctypes.byref(vst), ctypes.c_void_p(pos.data_ptr()), _stream(stream)))
 
 
 def tq_decode_workspace_size(kc: Codec, vc: Codec, batch: int, n_q_heads: int, n_kv_heads: int, q_len: int,

@@ -260,37 +260,43 @@ tq_status tq_codec_upload(const tq_codec* c) {
   return ensure_tables(c, &t);
 }
 
-tq_status tq_quantize_append(const tq_codec* c, const void* x, int32_t x_dtype, int32_t batch, int32_t heads,
-                             int32_t n_new, const int64_t* x_strides, const tq_cache* dst, const int32_t* d_pos,
-                             void* stream) {
-  if (!c || !x || !dst || !d_pos) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: NULL argument");
-  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: bad x_dtype");
+}  // extern "C"
+
+// Checks one append and fills its kernel parameters; *empty is set when
+// n_new == 0 (nothing to launch).
+static tq_status prepare_append(const char* who, const tq_codec* c, const void* x, int32_t x_dtype, int32_t batch,
+                                int32_t heads, int32_t n_new, const int64_t* x_strides, const tq_cache* dst,
+                                const int32_t* d_pos, tq::QuantizeParams* out, bool* empty) {
+  const std::string w(who);
+  if (!c || !x || !dst || !d_pos) return fail(TQ_ERR_INVALID_ARG, w + ": NULL argument");
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, w + ": bad x_dtype");
   if (batch <= 0 || heads <= 0 || n_new < 0)
-    return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: batch and heads must be positive, n_new >= 0");
+    return fail(TQ_ERR_INVALID_ARG, w + ": batch and heads must be positive, n_new >= 0");
   const tq::HostCodec& h = c->h;
   std::string why;
-  if (!cache_ok(dst, h, &why)) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: " + why);
+  if (!cache_ok(dst, h, &why)) return fail(TQ_ERR_INVALID_ARG, w + ": " + why);
   if (dst->batch != batch || dst->heads != heads)
-    return fail(TQ_ERR_CONFIG_MISMATCH, "tq_quantize_append: cache batch/heads differ from the input's");
+    return fail(TQ_ERR_CONFIG_MISMATCH, w + ": cache batch/heads differ from the input's");
   int64_t s0, s1, s2;
   if (x_strides) {
-    if (x_strides[3] != 1) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: coordinate stride must be 1");
+    if (x_strides[3] != 1) return fail(TQ_ERR_INVALID_ARG, w + ": coordinate stride must be 1");
     s0 = x_strides[0];
     s1 = x_strides[1];
     s2 = x_strides[2];
-    if (s0 < 0 || s1 < 0 || s2 < 0) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: negative stride");
+    if (s0 < 0 || s1 < 0 || s2 < 0) return fail(TQ_ERR_INVALID_ARG, w + ": negative stride");
   } else {
     s2 = h.d;
     s1 = (int64_t)n_new * h.d;
     s0 = (int64_t)heads * s1;
   }
-  if (n_new == 0) return TQ_OK;
+  *empty = n_new == 0;
   tq::DevTables* t = nullptr;
-  if (h.mode != TQ_MODE_GROUP) {
+  if (!*empty && h.mode != TQ_MODE_GROUP) {
     tq_status st = ensure_tables(c, &t);
     if (st != TQ_OK) return st;
   }
-  tq::QuantizeParams p{};
+  tq::QuantizeParams& p = *out;
+  p = tq::QuantizeParams{};
   p.x = x;
   p.x_bf16 = x_dtype == TQ_BF16;
   p.s0 = s0;
@@ -321,8 +327,42 @@ tq_status tq_quantize_append(const tq_codec* c, const void* x, int32_t x_dtype, 
   p.gmin = dst->gmin;
   p.cap = dst->cap;
   p.pos = d_pos;
-  hipError_t e = tq::launch_quantize(p, static_cast<hipStream_t>(stream));
+  return TQ_OK;
+}
+
+extern "C" {
+
+tq_status tq_quantize_append(const tq_codec* c, const void* x, int32_t x_dtype, int32_t batch, int32_t heads,
+                             int32_t n_new, const int64_t* x_strides, const tq_cache* dst, const int32_t* d_pos,
+                             void* stream) {
+  tq::QuantizeSets sets{};
+  bool empty = false;
+  tq_status st = prepare_append("tq_quantize_append", c, x, x_dtype, batch, heads, n_new, x_strides, dst, d_pos,
+                                &sets.s[0], &empty);
+  if (st != TQ_OK) return st;
+  if (empty) return TQ_OK;
+  hipError_t e = tq::launch_quantize(sets, 1, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tq_quantize_append launch");
+  return TQ_OK;
+}
+
+tq_status tq_quantize_append_kv(const tq_codec* kc, const tq_codec* vc, const void* k, const void* v,
+                                int32_t x_dtype, int32_t batch, int32_t heads, int32_t n_new,
+                                const int64_t* k_strides, const int64_t* v_strides, const tq_cache* kdst,
+                                const tq_cache* vdst, const int32_t* d_pos, void* stream) {
+  tq::QuantizeSets sets{};
+  bool empty_k = false, empty_v = false;
+  tq_status st = prepare_append("tq_quantize_append_kv (keys)", kc, k, x_dtype, batch, heads, n_new, k_strides, kdst,
+                                d_pos, &sets.s[0], &empty_k);
+  if (st != TQ_OK) return st;
+  st = prepare_append("tq_quantize_append_kv (values)", vc, v, x_dtype, batch, heads, n_new, v_strides, vdst, d_pos,
+                      &sets.s[1], &empty_v);
+  if (st != TQ_OK) return st;
+  if (kc->h.d != vc->h.d)
+    return fail(TQ_ERR_CONFIG_MISMATCH, "tq_quantize_append_kv: key and value codecs have different head_dim");
+  if (empty_k) return TQ_OK;
+  hipError_t e = tq::launch_quantize(sets, 2, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tq_quantize_append_kv launch");
   return TQ_OK;
 }
 

@@ -73,7 +73,16 @@ struct QuantizeParams {
   const int32_t* pos;
 };
 
-hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);
+// One or two parameter blocks (a key and a value append) in one launch;
+// blockIdx.y selects the block.
+struct QuantizeSets {
+  QuantizeParams s[2];
+};
+
+// Appends of at most this many vectors per set use one workgroup per vector.
+constexpr int64_t kSmallAppend = 4096;
+
+hipError_t launch_quantize(const QuantizeSets& sets, int n_sets, hipStream_t stream);
 
 struct DecodeParams {
   // query

@@ -55,19 +55,21 @@ def _compare_indices(gw, ora, bits, d, tag):
 
 
 QUANT_CASES = [
-    # d, bits, mode, bf16
-    (128, 3, 0, False), (128, 3, 0, True), (128, 4, 0, True), (128, 2, 0, False), (128, 1, 0, False),
-    (128, 3, 1, True), (256, 3, 1, True), (64, 5, 1, False), (32, 2, 1, True),
-    (256, 2, 2, True), (128, 4, 2, False), (96, 3, 2, True), (160, 1, 2, False),
-    (96, 3, 0, True), (224, 4, 1, True),
+    # d, bits, mode, bf16, heads, n_new: 2*3*37 vectors take the one-workgroup-per-vector
+    # kernel (d 32/64/128, MSE and Prod); 2*8*300 > 4096 take the one-wave-per-vector kernel
+    (128, 3, 0, False, 3, 37), (128, 3, 0, True, 3, 37), (128, 4, 0, True, 3, 37), (128, 2, 0, False, 3, 37),
+    (128, 1, 0, False, 3, 37), (128, 3, 1, True, 3, 37), (256, 3, 1, True, 3, 37), (64, 5, 1, False, 3, 37),
+    (32, 2, 1, True, 3, 37), (256, 2, 2, True, 3, 37), (128, 4, 2, False, 3, 37), (96, 3, 2, True, 3, 37),
+    (160, 1, 2, False, 3, 37), (96, 3, 0, True, 3, 37), (224, 4, 1, True, 3, 37),
+    (128, 3, 0, True, 8, 300), (128, 3, 1, True, 8, 300), (64, 4, 1, False, 8, 300),
 ]
 
 
-@pytest.mark.parametrize("d,bits,mode,bf16", QUANT_CASES)
-def test_quantize_append_parity(d, bits, mode, bf16):
-    tag = f"quantize d={d} bits={bits} mode={mode} bf16={bf16}"
+@pytest.mark.parametrize("d,bits,mode,bf16,H,n_new", QUANT_CASES)
+def test_quantize_append_parity(d, bits, mode, bf16, H, n_new):
+    tag = f"quantize d={d} bits={bits} mode={mode} bf16={bf16} heads={H} n_new={n_new}"
     _say(tag)
-    B, H, n_new, cap = 2, 3, 37, 50
+    B, cap = 2, n_new + 13
     rng = np.random.default_rng(d * 10 + bits + 100 * mode)
     x = (rng.standard_normal((B, H, n_new, d)).astype(np.float32) * np.float32(0.02))
     x[0, 0, 0] = 0.0                      # a zero vector
@@ -86,7 +88,7 @@ def test_quantize_append_parity(d, bits, mode, bf16):
     torch.cuda.synchronize()
     got = download(cache)
     ora = oquant.quantize(x.astype(np.float64), oc)
-    # slots written: b=0 -> 40..49 (t < 10), b=1 -> 0..36
+    # slots written: b=0 -> cap-10 .. cap-1 (t < 10), b=1 -> 0 .. n_new-1
     sel = [(0, slice(cap - 10, cap), slice(0, 10)), (1, slice(0, n_new), slice(0, n_new))]
     written = np.zeros((B, H, cap), dtype=bool)
     for b, ss, ts in sel:
@@ -120,6 +122,48 @@ def test_quantize_append_parity(d, bits, mode, bf16):
             assert not bad.any(), f"{tag}: {bad.sum()} QJL sign mismatches outside the window"
             nwin += int((zwin & ok[..., None]).sum())
     _say(f"  window coordinates: {nwin}")
+
+
+@pytest.mark.parametrize("kspec,vspec,H,n_new", [((128, 3, 1), (128, 3, 0), 8, 2), ((128, 3, 0), (128, 4, 0), 8, 2),
+                                                   ((64, 4, 1), (64, 2, 2), 3, 5), ((128, 3, 1), (128, 4, 0), 8, 300)])
+def test_quantize_append_kv_matches_two_appends(kspec, vspec, H, n_new):
+    """One K+V launch writes exactly what two single appends write, and the
+    keys match the oracle (bit-exact outside the window)."""
+    tag = f"append_kv k={kspec} v={vspec} heads={H} n_new={n_new}"
+    _say(tag)
+    B, cap = 2, n_new + 9
+    rng = np.random.default_rng(zlib.crc32(tag.encode()))
+    from quantized_decode_attention_04_amd.workloads import round_bf16
+    k = round_bf16(rng.standard_normal((B, H, n_new, kspec[0])).astype(np.float32) * np.float32(0.02))
+    v = round_bf16(rng.standard_normal((B, H, n_new, vspec[0])).astype(np.float32) * np.float32(0.02))
+    gk, ok_ = _pair(kspec[0], kspec[1], 3, kspec[2])
+    gv, ov_ = _pair(vspec[0], vspec[1], 4, vspec[2])
+    pos = torch.tensor([cap - n_new, 1], dtype=torch.int32, device="cuda")
+    kd, vd = to_device_f(k, True), to_device_f(v, True)
+    K1, V1 = tq.allocate_cache(gk, B, H, cap), tq.allocate_cache(gv, B, H, cap)
+    K2, V2 = tq.allocate_cache(gk, B, H, cap), tq.allocate_cache(gv, B, H, cap)
+    tq.tq_quantize_append_kv(gk, gv, kd, vd, K1, V1, pos)
+    tq.tq_quantize_append(gk, kd, K2, pos)
+    tq.tq_quantize_append(gv, vd, V2, pos)
+    torch.cuda.synchronize()
+    for a, bb in ((download(K1), download(K2)), (download(V1), download(V2))):
+        for name in a:
+            assert np.array_equal(a[name], bb[name]), f"{tag}: {name} differs from the single append"
+    got = download(K1)
+    ora = oquant.quantize(k.astype(np.float64), ok_)
+    g = got["idx"][1][:, 1:1 + n_new]
+    _compare_indices(g, {"idx": ora["idx"][1], "margin": ora["margin"][1], "words": ora["words"][1]},
+                     ok_.mse_bits, kspec[0], tag)
+    np.testing.assert_allclose(got["norm"][1][:, 1:1 + n_new], ora["norm"][1], rtol=1e-6, atol=0)
+
+
+def test_quantize_append_kv_rejects_mismatched_head_dim():
+    gk, gv = tq.tq_codec_create(128, 3, 0, 0), tq.tq_codec_create(64, 3, 1, 0)
+    K, V = tq.allocate_cache(gk, 1, 2, 8), tq.allocate_cache(gv, 1, 2, 8)
+    k = torch.zeros((1, 2, 1, 128), dtype=torch.bfloat16, device="cuda")
+    pos = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises((tq.TQError, ValueError)):
+        tq.tq_quantize_append_kv(gk, gv, k, k, K, V, pos)
 
 
 DEC_CASES = [
