@@ -112,8 +112,6 @@ DecodePlan plan_decode(int batch, int hkv, int rows, int d, int64_t max_len, boo
   p.n_chunks = (int)((max_len + chunk - 1) / chunk);
   const size_t bg = (size_t)batch * hkv;
   size_t off = 0;
-  p.off_counters = off;
-  off = align256(off + bg * sizeof(uint32_t));
   p.off_qrot = off;
   off = align256(off + bg * rows * d * sizeof(float));
   p.off_qs = off;
@@ -155,7 +153,7 @@ DecodePlan plan_decode_fast(int batch, int hkv, int rows, int d, int64_t max_len
   p.n_chunks = (int)((max_len + chunk - 1) / chunk);
   const size_t bg = (size_t)batch * hkv;
   size_t off = 0;
-  p.off_part_o = off;  // the merge is a second kernel: no arrival counters
+  p.off_part_o = off;
   off = align256(off + bg * p.n_chunks * rows * d * sizeof(float));
   p.off_part_ml = off;
   off = align256(off + bg * p.n_chunks * rows * 2 * sizeof(float));
@@ -466,7 +464,6 @@ tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void
   p.len = d_len;
   p.chunk = plan.chunk;
   p.n_chunks = plan.n_chunks;
-  p.counters = reinterpret_cast<uint32_t*>(w + plan.off_counters);
   p.part_o = reinterpret_cast<float*>(w + plan.off_part_o);
   p.part_ml = reinterpret_cast<float*>(w + plan.off_part_ml);
   p.out = out;

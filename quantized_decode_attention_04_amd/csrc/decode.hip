@@ -13,16 +13,18 @@
 // group values in the original domain, o = sum_t p_t (q_t s_g + mn_g).
 //
 // Structure (the token axis is split across workgroups, "split-K"):
-//   qprep_kernel   one workgroup per (b, g): q_rot = Pi_k q (and S q_rot),
-//                  and clears the (b, g) arrival counter;
+//   qprep_kernel   one workgroup per (row, b, g): q_rot = Pi_k q (and S q_rot);
 //   decode_kernel  one workgroup per (chunk, g, b): tiles of 256 tokens;
 //                  phase A scores one token per thread against the rotated
 //                  queries in LDS (centroid look-up table in LDS), phase B
 //                  runs the online softmax per row, phase C accumulates the
 //                  values with one thread per coordinate; the partial
-//                  (m, l, o) of the chunk goes to the workspace; the last
-//                  workgroup of (b, g) to arrive merges all chunks and applies
-//                  the single inverse rotation Pi_v^T.
+//                  (m, l, o) of the chunk goes to the workspace;
+//   merge_kernel   one workgroup per (row, g, b): merges the chunks and applies
+//                  the single inverse rotation Pi_v^T (a stream-ordered second
+//                  kernel: a last-arriving-workgroup merge would need a
+//                  device-scope fence per workgroup, which writes back and
+//                  invalidates the L2 of every XCD).
 // Scores are kept in the log2 domain (multiplied by log2 e) so that the
 // softmax uses exp2.
 #include "tq_internal.h"
@@ -31,6 +33,7 @@ namespace tq {
 namespace {
 
 constexpr int kTile = 256;
+constexpr int kMaxMergeChunks = 4096;  // merge weights kept in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float load_q(const void* q, int64_t off, int bf16) {
@@ -86,30 +89,40 @@ __device__ __forceinline__ uint32_t token_field(const uint32_t* tokw, int j) {
   }
 }
 
+// q_rot = Pi_k q (and S q_rot for Prod keys) for one query row: one
+// workgroup of D threads per (row, sequence x KV head); thread i forms
+// coordinate i with its D terms loaded in batches (coalesced across i).
 template <int D>
-__global__ __launch_bounds__(256) void qprep_kernel(DecodeParams p) {
-  __shared__ float s_qr[2048];
-  const int bg = blockIdx.x;
-  const int b = bg / p.hkv, g = bg % p.hkv;
-  if (threadIdx.x == 0) p.counters[bg] = 0u;
-  const int n = p.rows * D;
-  for (int e = threadIdx.x; e < n; e += 256) {
-    const int r = e / D, i = e % D;
-    const int h = g * p.group + r / p.q_len, qi = r % p.q_len;
-    const int64_t qoff = (((int64_t)b * p.hq + h) * p.q_len + qi) * D;
-    float acc = 0.f;
-    for (int j = 0; j < D; ++j) acc = fmaf(p.k_pit[(size_t)j * D + i], load_q(p.q, qoff + j, p.q_bf16), acc);
-    s_qr[e] = acc;
-    p.qrot[(size_t)bg * n + e] = acc;
-  }
-  if (p.kmode != TQ_MODE_PROD) return;
+__global__ __launch_bounds__(D) void qprep_kernel(DecodeParams p) {
+  __shared__ float s_in[D], s_qr[D];
+  const int r = blockIdx.x, bg = blockIdx.y;
+  const int b = bg / p.hkv, g = bg % p.hkv, i = threadIdx.x;
+  const int h = g * p.group + r / p.q_len, qi = r % p.q_len;
+  const int64_t qoff = (((int64_t)b * p.hq + h) * p.q_len + qi) * D;
+  s_in[i] = load_q(p.q, qoff + i, p.q_bf16);
   __syncthreads();
-  for (int e = threadIdx.x; e < n; e += 256) {
-    const int r = e / D, i = e % D;
-    float acc = 0.f;
-    for (int j = 0; j < D; ++j) acc = fmaf(p.k_st[(size_t)j * D + i], s_qr[r * D + j], acc);
-    p.qs[(size_t)bg * n + e] = acc;
+  float acc = 0.f;
+  for (int j0 = 0; j0 < D; j0 += 32) {
+    float pv[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) pv[k] = p.k_pit[(size_t)(j0 + k) * D + i];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) acc = fmaf(pv[k], s_in[j0 + k], acc);
   }
+  const size_t e = ((size_t)bg * p.rows + r) * D + i;
+  p.qrot[e] = acc;
+  if (p.kmode != TQ_MODE_PROD) return;
+  s_qr[i] = acc;
+  __syncthreads();
+  float acs = 0.f;
+  for (int j0 = 0; j0 < D; j0 += 32) {
+    float sv[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) sv[k] = p.k_st[(size_t)(j0 + k) * D + i];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) acs = fmaf(sv[k], s_qr[j0 + k], acs);
+  }
+  p.qs[e] = acs;
 }
 
 // Scores of one token against all rows (rows beyond p.rows read zeros).
@@ -199,7 +212,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   __shared__ float s_nv[kTile];
   __shared__ float s_m[RMAX], s_l[RMAX], s_alpha[RMAX];
   __shared__ float s_kc[16], s_vc[16];
-  __shared__ int s_last;
 
   const int chunk_id = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.hkv + g;
@@ -313,51 +325,74 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     pml[2 * tid] = s_m[tid];
     pml[2 * tid + 1] = s_l[tid];
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(p.counters + bg, 1u) == (unsigned)(p.n_chunks - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
 
-  // last workgroup of (b, g): merge the chunks, then one inverse rotation
-  float* s_o = s_p;
-  const float* pml0 = p.part_ml + (size_t)bg * p.n_chunks * rows * 2;
-  const float* po0 = p.part_o + (size_t)bg * p.n_chunks * rows * D;
-  for (int e = tid; e < rows * D; e += 256) {
-    const int r = e / D;
-    float M = -INFINITY;
-    for (int c = 0; c < p.n_chunks; ++c) M = fmaxf(M, pml0[(size_t)c * rows * 2 + 2 * r]);
-    float L = 0.f, acc = 0.f;
-    if (M != -INFINITY) {
-      for (int c = 0; c < p.n_chunks; ++c) {
-        const float mc = pml0[(size_t)c * rows * 2 + 2 * r];
-        const float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
-        L = fmaf(w, pml0[(size_t)c * rows * 2 + 2 * r + 1], L);
-        acc = fmaf(w, po0[(size_t)c * rows * D + e], acc);
-      }
-    }
-    s_o[e] = L > 0.f ? acc / L : 0.f;
-  }
+// Cross-chunk merge, one workgroup of D threads per (query row, KV head,
+// sequence), stream-ordered after the decode kernel: weights 2^(m_c - M) / L
+// from every chunk's (m, l), the merged row o = sum_c w_c o_c (thread j ->
+// coordinate j), then the single inverse rotation out = Pi_v^T o for MSE
+// values (group values are already in the original domain).
+template <int D>
+__global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
+  constexpr int NW = (D + 63) / 64;
+  __shared__ float s_o[D];
+  __shared__ float s_red[2 * NW];
+  __shared__ float s_w[kMaxMergeChunks];
+  const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int bg = b * p.hkv + g, j = threadIdx.x, lane = j & 63, wave = j >> 6;
+  const int nch = p.n_chunks, rows = p.rows;
+  const float* pml = p.part_ml + (size_t)bg * nch * rows * 2;
+  const float* po = p.part_o + (size_t)bg * nch * rows * D;
+  float M = -INFINITY;
+  for (int c = j; c < nch; c += D) M = fmaxf(M, pml[((size_t)c * rows + r) * 2]);
+  M = wave_max(M);
+  if (lane == 0) s_red[wave] = M;
   __syncthreads();
-  for (int e = tid; e < rows * D; e += 256) {
-    const int r = e / D, jj = e % D;
-    float res;
-    if (vgroup) {
-      res = s_o[e];
-    } else {
-      res = 0.f;
-      for (int i = 0; i < D; ++i) res = fmaf(p.v_pi[(size_t)i * D + jj], s_o[r * D + i], res);
-    }
-    const int h = g * p.group + r / p.q_len, qi = r % p.q_len;
-    p.out[(((int64_t)b * p.hq + h) * p.q_len + qi) * D + jj] = res;
+  M = s_red[0];
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[w]);
+  float L = 0.f;
+  for (int c = j; c < nch; c += D) {
+    const float mc = pml[((size_t)c * rows + r) * 2];
+    const float w = (M == -INFINITY || mc == -INFINITY) ? 0.f : exp2f(mc - M);
+    s_w[c] = w;
+    L = fmaf(w, pml[((size_t)c * rows + r) * 2 + 1], L);
   }
-  if (tid == 0) p.counters[bg] = 0u;
+  L = wave_sum(L);
+  if (lane == 0) s_red[NW + wave] = L;
+  __syncthreads();
+  L = 0.f;
+  for (int w = 0; w < NW; ++w) L += s_red[NW + w];
+  float o = 0.f;
+  int c = 0;
+  for (; c + 8 <= nch; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = po[((size_t)(c + k) * rows + r) * D + j];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o = fmaf(s_w[c + k], v[k], o);
+  }
+  for (; c < nch; ++c) o = fmaf(s_w[c], po[((size_t)c * rows + r) * D + j], o);
+  o = L > 0.f ? o / L : 0.f;
+  float res = o;
+  if (p.vmode != TQ_MODE_GROUP) {
+    s_o[j] = o;
+    __syncthreads();
+    res = 0.f;
+    for (int i0 = 0; i0 < D; i0 += 32) {
+      float pv[32];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) pv[k] = p.v_pi[(size_t)(i0 + k) * D + j];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) res = fmaf(s_o[i0 + k], pv[k], res);
+    }
+  }
+  const int h = g * p.group + r / p.q_len, qi = r % p.q_len;
+  p.out[(((int64_t)b * p.hq + h) * p.q_len + qi) * D + j] = res;
 }
 
 template <int D>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
-  qprep_kernel<D><<<dim3(p.batch * p.hkv), dim3(256), 0, stream>>>(p);
+  qprep_kernel<D><<<dim3(p.rows, p.batch * p.hkv), dim3(D), 0, stream>>>(p);
   const dim3 grid(p.n_chunks, p.hkv, p.batch);
   if (p.rows <= 4) {
     decode_kernel<D, 4><<<grid, dim3(256), 0, stream>>>(p);
@@ -366,13 +401,14 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   } else {
     decode_kernel<D, 8><<<grid, dim3(256), 0, stream>>>(p);
   }
+  merge_kernel<D><<<dim3(p.rows, p.hkv, p.batch), dim3(D), 0, stream>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  if (p.n_chunks > 65535 || p.hkv > 65535 || p.batch > 65535) return hipErrorInvalidValue;
+  if (p.n_chunks > kMaxMergeChunks || p.hkv > 65535 || p.batch > 65535 || p.rows > 16) return hipErrorInvalidValue;
   switch (p.d) {
     case 32: return launch_d<32>(p, stream);
     case 64: return launch_d<64>(p, stream);

@@ -68,6 +68,9 @@ constexpr float kQMax = 8355711.f;    // three-digit operand bound (2^23 - 0x808
 constexpr float kDigitBias = 8421504.f;
 constexpr int kBufWord3 = 0x00020000;     // raw buffer resource, gfx9 data format
 constexpr float kFlushGap = 4.f;          // log2 headroom: p may reach 2^4 between flushes
+// p n_v sig <= 2^kFlushGap * 1.001 * nref * sig = kQMax: the 0.1% margin covers
+// exp2 and product rounding
+constexpr float kProbBound = 16.f * 1.001f;
 constexpr float kNormHeadroom = 2.f;      // value-norm reference: twice the largest norm seen
 
 // Byte offset of row group q (rows 16q .. 16q+15) of a wave's value-selector
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
   // masked scores (-inf) give exp2 = 0 and an empty row never forms inf - inf
   float m_ref = -1e30f, l_run = 0.f;
   // value-norm reference: probabilities enter the digits as p n_v sig with
-  // sig = kQMax / (16.016 nref), so p n_v sig <= kQMax while n_v <= nref;
+  // sig = kQMax / (kProbBound nref), so p n_v sig <= kQMax while n_v <= nref;
   // lsig = log2 sig is folded into the exponent, kflush = kappa / sig
   float nref = 0.f, lsig = 0.f, isig = 1.f, kflush = kappa;
   bool empty = true;  // accumulators untouched so far (wave-uniform)
@@ -436,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
       m_ref = m_new;
       if (nnew > nref) {
         nref = nnew;
-        const float sig = kQMax / (nref * 16.016f);
+        const float sig = kQMax / (nref * kProbBound);
         lsig = __log2f(sig);
         isig = 1.f / sig;
         kflush = kappa * isig;
@@ -561,17 +564,21 @@ __global__ __launch_bounds__(kD) void merge_fast_kernel(DecodeParams p) {
   const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.hkv + g, j = threadIdx.x, lane = j & 63, wave = j >> 6;
   const int nch = p.n_chunks, rows = p.rows;
-  // column j of Pi_v: issued first, used last
-  float pv[kD];
-#pragma unroll
-  for (int i = 0; i < kD; ++i) pv[i] = p.v_pi[i * kD + j];
   const float* pml = p.part_ml + (size_t)bg * nch * rows * 2;
   const float* po = p.part_o + (size_t)bg * nch * rows * kD;
+  // every load is independent of the weights: (m, l), the first 32 partial
+  // rows and column j of Pi_v are all in flight before any is used
   float mc = -INFINITY, lc = 0.f;
   if (j < nch) {
     mc = pml[((size_t)j * rows + r) * 2];
     lc = pml[((size_t)j * rows + r) * 2 + 1];
   }
+  float v[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) v[k] = k < nch ? po[((size_t)k * rows + r) * kD + j] : 0.f;
+  float pv[kD];
+#pragma unroll
+  for (int i = 0; i < kD; ++i) pv[i] = p.v_pi[i * kD + j];
   float M = wave_max(mc);
   if (lane == 0) s_red[wave] = M;
   __syncthreads();
@@ -585,15 +592,9 @@ __global__ __launch_bounds__(kD) void merge_fast_kernel(DecodeParams p) {
   __syncthreads();
   L = s_red[2] + s_red[3];
   float o = 0.f;
-  int c = 0;
-  for (; c + 16 <= nch; c += 16) {
-    float v[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = po[((size_t)(c + k) * rows + r) * kD + j];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) o = fmaf(s_w[c + k], v[k], o);
-  }
-  for (; c < nch; ++c) o = fmaf(s_w[c], po[((size_t)c * rows + r) * kD + j], o);
+  for (int k = 0; k < 32; ++k) o = fmaf(s_w[k], v[k], o);  // s_w is 0 past the last chunk
+  for (int c = 32; c < nch; ++c) o = fmaf(s_w[c], po[((size_t)c * rows + r) * kD + j], o);
   s_o[j] = L > 0.f ? o / L : 0.f;
   __syncthreads();
   float acc = 0.f;

@@ -114,7 +114,6 @@ struct DecodeParams {
   // split over the token axis
   int chunk, n_chunks;
   // workspace pieces
-  uint32_t* counters;  // [batch*hkv]
   float* qrot;         // [batch*hkv][rows][d]
   float* qs;           // [batch*hkv][rows][d] (Prod)
   float* part_o;       // [batch*hkv][n_chunks][rows][d]
@@ -129,7 +128,7 @@ struct DecodeParams {
 // Chunk length of the token split and the workspace layout for it.
 struct DecodePlan {
   int rows, chunk, n_chunks;
-  size_t off_counters, off_qrot, off_qs, off_part_o, off_part_ml, total;
+  size_t off_qrot, off_qs, off_part_o, off_part_ml, total;
   bool fast;
 };
 DecodePlan plan_decode(int batch, int hkv, int rows, int d, int64_t max_len, bool prod);
