@@ -174,26 +174,49 @@ __device__ __forceinline__ void score_dispatch(const DecodeParams& p, int64_t sl
   }
 }
 
-// Value of coordinate j of one token (MSE: c_v[idx]; the norm is folded into
-// the softmax weight.  Group: q s_g + mn_g).
-template <int VB, bool GROUP>
-__device__ __forceinline__ float value_coord(const DecodeParams& p, int64_t slot, int j, const float* s_vc) {
-  const uint32_t f = token_field<VB>(p.v_idx + slot * (int64_t)p.vwords, j);
+// Value of coordinate j of token t of the tile staged in LDS (MSE: c_v[idx];
+// the norm is folded into the softmax weight.  Group: q s_g + mn_g).
+template <int D, int VB, bool GROUP>
+__device__ __forceinline__ float value_coord(const uint32_t* s_vw, const float* s_vs, int t, int j,
+                                             const float* s_vc) {
+  constexpr int VW = D * VB / 32;
+  const uint32_t f = token_field<VB>(s_vw + t * VW, j);
   if constexpr (GROUP) {
-    const int64_t gidx = slot * p.vgroups + (j >> 5);
-    return fmaf((float)f, p.v_scale[gidx], p.v_gmin[gidx]);
+    const int gi = t * (D / 32) + (j >> 5);
+    return fmaf((float)f, s_vs[2 * gi], s_vs[2 * gi + 1]);
   } else {
     return s_vc[f];
   }
 }
 
+// Stage the value words (and group scales / minima) of the tile's tokens in
+// LDS with coalesced loads, so that the per-coordinate loop reads LDS.
+template <int D, int VB, bool GROUP>
+__device__ __forceinline__ void stage_values(const DecodeParams& p, int64_t slot0, int cnt, uint32_t* s_vw,
+                                             float* s_vs) {
+  constexpr int VW = D * VB / 32;
+  const uint32_t* src = p.v_idx + slot0 * VW;
+  for (int e = threadIdx.x; e < cnt * VW; e += 256) s_vw[e] = src[e];
+  if constexpr (GROUP) {
+    constexpr int NG = D / 32;
+    for (int e = threadIdx.x; e < cnt * NG; e += 256) {
+      s_vs[2 * e] = p.v_scale[slot0 * NG + e];
+      s_vs[2 * e + 1] = p.v_gmin[slot0 * NG + e];
+    }
+  }
+}
+
 template <int D, int RMAX, int VB, bool GROUP>
 __device__ __forceinline__ void accumulate_values(const DecodeParams& p, int64_t slot0, int cnt, int j, int rg,
-                                                  const float* s_p, const float* s_vc, float* o) {
+                                                  const float* s_p, const float* s_vc, float* o, uint32_t* s_vw,
+                                                  float* s_vs) {
   constexpr int NRG = 256 / D;
   constexpr int RPT = (RMAX + NRG - 1) / NRG;
+  stage_values<D, VB, GROUP>(p, slot0, cnt, s_vw, s_vs);
+  __syncthreads();
+  if (rg >= NRG) return;
   for (int t = 0; t < cnt; ++t) {
-    const float cv = value_coord<VB, GROUP>(p, slot0 + t, j, s_vc);
+    const float cv = value_coord<D, VB, GROUP>(s_vw, s_vs, t, j, s_vc);
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int r = rg + NRG * k;
@@ -212,6 +235,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   __shared__ float s_nv[kTile];
   __shared__ float s_m[RMAX], s_l[RMAX], s_alpha[RMAX];
   __shared__ float s_kc[16], s_vc[16];
+  __shared__ uint32_t s_vw[kTile * D * 4 / 32];  // the tile's value words (up to 4 bits)
+  __shared__ float s_vs[kTile * (D / 32) * 2];   // group scale and minimum pairs
 
   const int chunk_id = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.hkv + g;
@@ -290,22 +315,24 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     }
     __syncthreads();
     // phase C: values, one coordinate per thread
-    if (rg < NRG) {
+    {
+      if (rg < NRG) {
 #pragma unroll
-      for (int k = 0; k < RPT; ++k) {
-        const int r = rg + NRG * k;
-        if (r < rows) o[k] *= s_alpha[r];
+        for (int k = 0; k < RPT; ++k) {
+          const int r = rg + NRG * k;
+          if (r < rows) o[k] *= s_alpha[r];
+        }
       }
       const int64_t slot0 = base + t0;
       switch (p.vbits * 2 + (vgroup ? 1 : 0)) {
-        case 2: accumulate_values<D, RMAX, 1, false>(p, slot0, cnt, j, rg, s_p, s_vc, o); break;
-        case 3: accumulate_values<D, RMAX, 1, true>(p, slot0, cnt, j, rg, s_p, s_vc, o); break;
-        case 4: accumulate_values<D, RMAX, 2, false>(p, slot0, cnt, j, rg, s_p, s_vc, o); break;
-        case 5: accumulate_values<D, RMAX, 2, true>(p, slot0, cnt, j, rg, s_p, s_vc, o); break;
-        case 6: accumulate_values<D, RMAX, 3, false>(p, slot0, cnt, j, rg, s_p, s_vc, o); break;
-        case 7: accumulate_values<D, RMAX, 3, true>(p, slot0, cnt, j, rg, s_p, s_vc, o); break;
-        case 8: accumulate_values<D, RMAX, 4, false>(p, slot0, cnt, j, rg, s_p, s_vc, o); break;
-        default: accumulate_values<D, RMAX, 4, true>(p, slot0, cnt, j, rg, s_p, s_vc, o); break;
+        case 2: accumulate_values<D, RMAX, 1, false>(p, slot0, cnt, j, rg, s_p, s_vc, o, s_vw, s_vs); break;
+        case 3: accumulate_values<D, RMAX, 1, true>(p, slot0, cnt, j, rg, s_p, s_vc, o, s_vw, s_vs); break;
+        case 4: accumulate_values<D, RMAX, 2, false>(p, slot0, cnt, j, rg, s_p, s_vc, o, s_vw, s_vs); break;
+        case 5: accumulate_values<D, RMAX, 2, true>(p, slot0, cnt, j, rg, s_p, s_vc, o, s_vw, s_vs); break;
+        case 6: accumulate_values<D, RMAX, 3, false>(p, slot0, cnt, j, rg, s_p, s_vc, o, s_vw, s_vs); break;
+        case 7: accumulate_values<D, RMAX, 3, true>(p, slot0, cnt, j, rg, s_p, s_vc, o, s_vw, s_vs); break;
+        case 8: accumulate_values<D, RMAX, 4, false>(p, slot0, cnt, j, rg, s_p, s_vc, o, s_vw, s_vs); break;
+        default: accumulate_values<D, RMAX, 4, true>(p, slot0, cnt, j, rg, s_p, s_vc, o, s_vw, s_vs); break;
       }
     }
     __syncthreads();
@@ -396,10 +423,12 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.n_chunks, p.hkv, p.batch);
   if (p.rows <= 4) {
     decode_kernel<D, 4><<<grid, dim3(256), 0, stream>>>(p);
+  } else if (p.rows <= 8) {
+    decode_kernel<D, 8><<<grid, dim3(256), 0, stream>>>(p);
   } else if constexpr (D <= 128) {
     decode_kernel<D, 16><<<grid, dim3(256), 0, stream>>>(p);
   } else {
-    decode_kernel<D, 8><<<grid, dim3(256), 0, stream>>>(p);
+    return hipErrorInvalidValue;  // more than 8 rows at head_dim > 128 is refused on the host
   }
   merge_kernel<D><<<dim3(p.rows, p.hkv, p.batch), dim3(D), 0, stream>>>(p);
   return hipGetLastError();
