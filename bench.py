@@ -5,7 +5,10 @@ A step is one pass of the whole hot path over every layer of the workload:
 for each layer, quantise-on-append of the q_len new K and V tokens per
 sequence in one launch (the MTP-verify tokens of the 256k workload), then decode attention
 of the layer's queries over the compressed cache.  Inputs and compressed
-caches are resident in HBM before timing starts.
+caches are resident in HBM before timing starts.  The timed steps replay the
+whole step as one HIP graph (--no-graph: eager launches); the decode-call
+time behind roofline.achieved comes from HIP events around every call of an
+eager pass over the same layers.
 
 Default workload: 64 layers x 8 KV / 64 query heads, head_dim 128, 262144
 cached tokens, q_len 2, K and V 3-bit MSE, bf16 inputs with per-channel
@@ -35,6 +38,7 @@ def _args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="l64_d128_n256k_mse3_mtp2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager steps instead of a HIP graph of the step")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--layers", type=int, default=0, help="override the number of layer buffers")
@@ -199,34 +203,39 @@ def main():
 
     # ---- pre-marshalled C calls (the same entry points the binding wraps)
     lib = _binding._lib
-    stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
     dt_code = tq.TQ_BF16 if w.bf16 else tq.TQ_F32
-    calls = []
-    for l in range(layers):
-        ks_, vs_ = kcs[l].as_struct(), vcs[l].as_struct()
-        kstr = (ctypes.c_int64 * 4)(*kn[l].stride())
-        vstr = (ctypes.c_int64 * 4)(*vn[l].stride())
-        calls.append((ks_, vs_, kstr, vstr,
-                      (kc.handle, vc.handle, ctypes.c_void_p(kn[l].data_ptr()), ctypes.c_void_p(vn[l].data_ptr()),
-                       dt_code, B, hkv, append, kstr, vstr, ctypes.byref(ks_), ctypes.byref(vs_),
-                       ctypes.c_void_p(pos_new.data_ptr()), sp),
-                      None,
-                      (kc.handle, vc.handle, ctypes.c_void_p(qs[l].data_ptr()), dt_code, B, hq, hkv, qlen,
-                       ctypes.byref(ks_), ctypes.byref(vs_), ctypes.c_void_p(lens.data_ptr()), max_len,
-                       ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
-                       ws_bytes, sp)))
+    keep = []
+
+    def make_calls(stream_handle):
+        sp = ctypes.c_void_p(stream_handle)
+        calls = []
+        for l in range(layers):
+            ks_, vs_ = kcs[l].as_struct(), vcs[l].as_struct()
+            kstr = (ctypes.c_int64 * 4)(*kn[l].stride())
+            vstr = (ctypes.c_int64 * 4)(*vn[l].stride())
+            keep.append((ks_, vs_, kstr, vstr))
+            calls.append(((kc.handle, vc.handle, ctypes.c_void_p(kn[l].data_ptr()), ctypes.c_void_p(vn[l].data_ptr()),
+                           dt_code, B, hkv, append, kstr, vstr, ctypes.byref(ks_), ctypes.byref(vs_),
+                           ctypes.c_void_p(pos_new.data_ptr()), sp),
+                          (kc.handle, vc.handle, ctypes.c_void_p(qs[l].data_ptr()), dt_code, B, hq, hkv, qlen,
+                           ctypes.byref(ks_), ctypes.byref(vs_), ctypes.c_void_p(lens.data_ptr()), max_len,
+                           ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                           ws_bytes, sp)))
+        return calls
 
     def check(st):
         if st != 0:
             raise RuntimeError(tq.tq_last_error())
 
+    stream = torch.cuda.current_stream()
+    calls = make_calls(stream.cuda_stream)
+
     def step(events=None):
         for i, c in enumerate(calls):
-            check(lib.tq_quantize_append_kv(*c[4]))
+            check(lib.tq_quantize_append_kv(*c[0]))
             if events is not None:
                 events[i][0].record(stream)
-            check(lib.tq_decode_attention(*c[6]))
+            check(lib.tq_decode_attention(*c[1]))
             if events is not None:
                 events[i][1].record(stream)
 
@@ -234,17 +243,39 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # decode-call time: HIP events on the launch stream around every call of
+    # an eager pass (the dominant kernels; roofline.achieved)
     events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(events[s])
+    for s_ in range(args.steps):
+        step(events[s_])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    ms_per_step_eager = (t1 - t0) * 1000.0 / args.steps
     dec_ms = [e0.elapsed_time(e1) for row in events for (e0, e1) in row]
     dec_ms_avg = float(np.mean(dec_ms))
+
+    # the step as one HIP graph (the per-layer kernels without launch gaps):
+    # value and ms_per_step
+    ms_per_step = ms_per_step_eager
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        with torch.cuda.graph(graph, stream=cap):
+            for c in make_calls(torch.cuda.current_stream().cuda_stream):
+                check(lib.tq_quantize_append_kv(*c[0]))
+                check(lib.tq_decode_attention(*c[1]))
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_per_step = (t1 - t0) * 1000.0 / args.steps
 
     tokens_per_step = float(lens_h.sum()) * layers
     value = tokens_per_step / (ms_per_step / 1000.0)
@@ -299,6 +330,9 @@ def main():
                            "on the launch stream around each call",
             "traffic_source": traffic_src,
             "decode_call_us": dec_ms_avg * 1000.0,
+            "step": "one HIP graph of the 64 per-layer (append K+V, decode) calls" if not args.no_graph
+                    else "eager launches",
+            "ms_per_step_eager": ms_per_step_eager,
             "decode_alg_bytes_per_call": alg_bytes,
             "state_bytes_per_step": layer_state_bytes * layers,
             "step_gbps_state": layer_state_bytes * layers / (ms_per_step / 1000.0) / 1e9,
