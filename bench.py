@@ -135,6 +135,38 @@ def traffic_from_profile(kernel_source: str) -> tuple:
     return float(fields["traffic_bytes_per_call"]), path
 
 
+def bulk_prefill(tq, wl, w, kc, vc, dev, stream, warmup: int, reps: int, tokens: int = 8192) -> dict:
+    """Bulk quantise-on-append of ``tokens`` new tokens for every KV head of one
+    sequence (keys and values in one tq_quantize_append_kv call), timed with
+    HIP events on the launch stream: microseconds per call, the bytes it moves
+    (bf16/fp32 inputs read + packed state written) per second, and the
+    rotation FLOPs (Pi for keys and MSE values, S as well for Prod keys) per
+    second."""
+    import torch
+    K = tq.allocate_cache(kc, 1, w.hkv, tokens, dev)
+    V = tq.allocate_cache(vc, 1, w.hkv, tokens, dev)
+    kx = wl.device_normal((1, w.hkv, tokens, w.d), 0, 0, 900, w.bf16, dev)
+    vx = wl.device_normal((1, w.hkv, tokens, w.d), 0, 0, 901, w.bf16, dev)
+    pos = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(max(1, warmup)):
+        tq.tq_quantize_append_kv(kc, vc, kx, vx, K, V, pos)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(stream)
+        tq.tq_quantize_append_kv(kc, vc, kx, vx, K, V, pos)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1000.0
+    vectors = w.hkv * tokens
+    in_bytes = 2 * vectors * w.d * (2 if w.bf16 else 4)
+    out_bytes = vectors * (kc.info["bytes_per_token"] + vc.info["bytes_per_token"])
+    rot = 2 * w.d * w.d * vectors
+    flops = rot * ((2 if w.kmode == 1 else 1) + (1 if w.vmode != 2 else 0))
+    return {"tokens": tokens, "kv_heads": w.hkv, "us": us, "gbps": (in_bytes + out_bytes) / (us * 1e-6) / 1e9,
+            "gflops": flops / (us * 1e-6) / 1e9, "bytes": in_bytes + out_bytes, "flop": flops}
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -277,6 +309,8 @@ def main():
         t1 = time.perf_counter()
         ms_per_step = (t1 - t0) * 1000.0 / args.steps
 
+    prefill = bulk_prefill(tq, wl, w, kc, vc, dev, stream, args.warmup, max(args.steps, 5))
+
     tokens_per_step = float(lens_h.sum()) * layers
     value = tokens_per_step / (ms_per_step / 1000.0)
     # algorithmic bytes of one decode call: the packed state of every attended
@@ -286,6 +320,11 @@ def main():
     table_bytes = 2 * d * d * 4 + (d * d * 4 if w.kmode == 1 else 0)
     alg_bytes = layer_state_bytes + q_bytes + out_bytes + table_bytes
     achieved = alg_bytes / (dec_ms_avg / 1000.0) / 1e9
+    # the library takes the matrix-core path for d 128 with 3-bit MSE keys and
+    # values and at most 16 query rows per KV head (a label only)
+    fast = d == 128 and (w.kmode, w.kbits, w.vmode, w.vbits) == (0, 3, 0, 3) and (hq // hkv) * qlen <= 16
+    kernels = ("decode_fast_kernel + merge_fast_kernel" if fast
+               else "qprep_kernel + decode_kernel + merge_kernel")
     traffic, traffic_src = None, "counters taken on l64_d128_n256k_mse3_mtp2 only"
     if w.name == "l64_d128_n256k_mse3_mtp2":
         src = os.path.join(os.path.dirname(os.path.abspath(tq.__file__)), "csrc", "decode_fast.hip")
@@ -326,17 +365,19 @@ def main():
             "traffic": traffic,
         },
         "detail": {
-            "decode_call": "tq_decode_attention = decode_fast_kernel + merge_fast_kernel, timed with HIP events "
-                           "on the launch stream around each call",
+            "decode_call": f"tq_decode_attention = {kernels}, timed with HIP events on the launch stream "
+                           "around each call",
             "traffic_source": traffic_src,
             "decode_call_us": dec_ms_avg * 1000.0,
-            "step": "one HIP graph of the 64 per-layer (append K+V, decode) calls" if not args.no_graph
+            "decode_call_us_p10_p50_p90": [float(np.percentile(dec_ms, q)) * 1000.0 for q in (10, 50, 90)],
+            "step": f"one HIP graph of the {layers} per-layer (append K+V, decode) calls" if not args.no_graph
                     else "eager launches",
             "ms_per_step_eager": ms_per_step_eager,
             "decode_alg_bytes_per_call": alg_bytes,
             "state_bytes_per_step": layer_state_bytes * layers,
             "step_gbps_state": layer_state_bytes * layers / (ms_per_step / 1000.0) / 1e9,
             "ws_bytes": ws_bytes,
+            "bulk_prefill": prefill,
         },
     }
     if not args.no_cpu_baseline:

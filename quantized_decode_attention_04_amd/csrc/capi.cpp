@@ -50,7 +50,7 @@ tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out) {
   if (!c->uploaded[dev] && c->h.mode != TQ_MODE_GROUP) {
     const int d = c->h.d;
     const size_t dd = (size_t)d * d;
-    const size_t nfl = 3 * dd + 32;
+    const size_t nfl = 4 * dd + 32;
     void* block = nullptr;
     e = hipMalloc(&block, nfl * sizeof(float));
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(codec tables)");
@@ -58,13 +58,17 @@ tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out) {
     float* pit = host.data();
     float* pi = pit + dd;
     float* st = pi + dd;
-    float* cent = st + dd;
+    float* sk = st + dd;
+    float* cent = sk + dd;
     float* bnd = cent + 16;
     for (int i = 0; i < d; ++i)
       for (int j = 0; j < d; ++j) {
         pit[(size_t)j * d + i] = c->h.rot[(size_t)i * d + j];
         pi[(size_t)i * d + j] = c->h.rot[(size_t)i * d + j];
-        if (!c->h.sketch.empty()) st[(size_t)j * d + i] = c->h.sketch[(size_t)i * d + j];
+        if (!c->h.sketch.empty()) {
+          st[(size_t)j * d + i] = c->h.sketch[(size_t)i * d + j];
+          sk[(size_t)i * d + j] = c->h.sketch[(size_t)i * d + j];
+        }
       }
     for (int k = 0; k < c->h.levels; ++k) cent[k] = c->h.centroids[k];
     for (int k = 0; k + 1 < c->h.levels; ++k) bnd[k] = c->h.boundaries[k];
@@ -78,8 +82,9 @@ tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out) {
     t.pit = base;
     t.pi = base + dd;
     t.st = base + 2 * dd;
-    t.cent = base + 3 * dd;
-    t.bnd = base + 3 * dd + 16;
+    t.s = base + 3 * dd;
+    t.cent = base + 4 * dd;
+    t.bnd = base + 4 * dd + 16;
     c->uploaded[dev] = true;
   }
   *out = &t;
@@ -311,9 +316,17 @@ static tq_status prepare_append(const char* who, const tq_codec* c, const void* 
   p.sign_words = sign_words(h);
   p.groups = group_count(h);
   p.gbits = h.mode == TQ_MODE_GROUP ? h.bits : 0;
+  {
+    // 16-byte row loads need a 16-byte aligned base and strides
+    const int64_t es = p.x_bf16 ? 2 : 4;
+    p.x_vec16 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (s0 * es) % 16 == 0 && (s1 * es) % 16 == 0 &&
+                (s2 * es) % 16 == 0;
+  }
   if (t) {
     p.pit = t->pit;
+    p.pi = t->pi;
     p.st = t->st;
+    p.s = t->s;
     p.cent = t->cent;
     p.bnd = t->bnd;
   }

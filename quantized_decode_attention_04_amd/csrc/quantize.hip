@@ -1,15 +1,17 @@
 // Quantise-on-append for gfx950 ("omlx turboquant_kv.py", update_and_fetch:
 // only the new tokens are quantised and written at the written end).
 //
-// Bulk appends: one wave64 per head vector; lane l owns coordinates l, l+64,
-// ...  Steps:
-// load (bf16 or f32) -> wave-reduced norm -> y = Pi x with x broadcast from
-// LDS and Pi^T read row by row (coalesced across lanes, L2-resident) ->
-// nearest centroid by counting boundaries below u = y/n -> pack the indices
-// into the word layout with LDS atomic OR -> vector stores.  Prod keys then
-// form the rotated residual rho = y - n c[idx], its norm, z = S rho, and
-// write sign(z) as 64-lane ballots.  Group values skip the rotation and
-// quantise 32-coordinate groups (one half-wave each) by min/max.
+// For every head vector x: n = |x|, u = Pi x / n, the index of each rotated
+// coordinate counts the codebook boundaries below it, and the indices are
+// packed into the word layout; Prod keys add the rotated residual
+// rho = Pi x - n c[idx], its norm and the signs of S rho; group values
+// quantise 32-coordinate groups of the unrotated vector by their min and max.
+//
+// Two kernels, chosen by the size of the append only (so that keys and values
+// appended together or one by one take the same kernel and write the same
+// bits): bulk appends tile 64 vectors per workgroup and run the rotations on
+// the fp32 matrix cores; small appends (the decode step) give each vector a
+// whole workgroup so that its rotation's loads are all in flight at once.
 #include "tq_internal.h"
 
 namespace tq {
@@ -54,172 +56,274 @@ __device__ __forceinline__ void pack_field(uint32_t* w, int j, int b, uint32_t v
   }
 }
 
+// ---- bulk appends on the matrix cores --------------------------------------
+//
+// One 256-thread workgroup per tile of kMV = 64 vectors.  The tile is staged
+// in LDS as fp32 rows; the rotation of every vector, Y = X Pi^T, runs on
+// v_mfma_f32_16x16x4f32 (wave w computes the output columns 16c .. 16c+15,
+// c = w, w+4, ...; four row tiles of 16 vectors each).  The contraction index
+// is permuted so that each lane reads contiguous runs: in k-step s lane l
+// supplies the term j = (l/16) (D/4) + s, i.e. A = X[v][j] from LDS and
+// B = Pi[16c + l%16][j] from the row-major rotation.  Lane l then holds
+// Y[16r + 4(l/16) + e][16c + l%16], e = 0..3, and quantises those elements in
+// registers: u = y / n, the index counts the boundaries below u, and the
+// index bytes go to LDS, from where one thread per (vector, word) packs the
+// words.  Prod keys write the rotated residual rho = y - n c[idx] over the
+// tile, take its norm per vector and run Z = rho S^T the same way for the
+// sign bits.  Group values need no rotation: one thread per (vector, group)
+// quantises from the tile.
+constexpr int kMV = 64;
+
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
 template <int D>
-__global__ __launch_bounds__(256) void quantize_kernel(QuantizeSets sets) {
-  constexpr int NC = (D + 63) / 64;
-  const QuantizeParams& p = sets.s[blockIdx.y];
-  __shared__ float xs[4][D];
-  __shared__ uint32_t wbuf[4][32];
+struct __attribute__((aligned(16))) BulkLds {
+  float xs[kMV][D + 4];   // x tile, then the rotated residual (Prod); +4 spreads rows over banks
+  uint8_t codes[kMV][D];  // per-coordinate index, sign or group code
+  float nrm[kMV];
+  int64_t src[kMV];       // element offset of each vector's row in x, -1 past the end
+  int64_t slot[kMV];      // cache slot, -1 when the vector is not written
+};
 
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int64_t total = (int64_t)p.batch * p.heads * p.n_new;
-  const int64_t vec = (int64_t)blockIdx.x * 4 + wave;
-
-  bool active = vec < total;
-  int b = 0, h = 0, t = 0;
-  int64_t pos = 0;
-  if (active) {
-    t = (int)(vec % p.n_new);
-    const int64_t bh = vec / p.n_new;
-    h = (int)(bh % p.heads);
-    b = (int)(bh / p.heads);
-    pos = (int64_t)p.pos[b] + t;
-    active = pos >= 0 && pos < p.cap;
+// Word w of one vector from its per-coordinate codes (the packed layout:
+// LSB-first for 1, 2, 4 bits; byte lanes X, Y, Z per 32 coordinates for 3).
+__device__ __forceinline__ uint32_t pack_word(const uint8_t* codes, int w, int b) {
+  if (b == 3) {
+    const uint32_t* c = reinterpret_cast<const uint32_t*>(codes + 32 * (w / 3));
+    switch (w % 3) {
+      case 0: return c[0] | (c[1] << 3) | ((c[2] & 0x03030303u) << 6);
+      case 1: return c[3] | (c[4] << 3) | ((c[5] & 0x03030303u) << 6);
+      default:
+        return c[6] | (c[7] << 3) | (((c[2] >> 2) & 0x01010101u) << 6) | (((c[5] >> 2) & 0x01010101u) << 7);
+    }
   }
-  const int64_t tok = ((int64_t)b * p.heads + h) * p.cap + pos;  // token-head slot in the cache
-
-  float x[NC];
-  float ss = 0.f;
+  const int per = 32 / b;
+  const uint32_t* c = reinterpret_cast<const uint32_t*>(codes + per * w);
+  uint32_t word = 0;
+  for (int q = 0; q < per / 4; ++q) {
+    const uint32_t cw = c[q];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int i = lane + 64 * c;
-    x[c] = (active && i < D) ? load_x(p.x, (int64_t)b * p.s0 + (int64_t)h * p.s1 + (int64_t)t * p.s2 + i, p.x_bf16) : 0.f;
-    ss += x[c] * x[c];
+    for (int k = 0; k < 4; ++k) word |= ((cw >> (8 * k)) & 0xffu) << (b * (4 * q + k));
   }
-  if (lane < 32) wbuf[wave][lane] = 0u;
+  return word;
+}
+
+// Y = A B^T for the tile (A = L.xs, B = `mat` row-major [D][D]); calls
+// f(v, coord, y) for every element this lane holds.
+template <int D, typename F>
+__device__ __forceinline__ void tile_gemm(const BulkLds<D>& L, const float* __restrict__ mat, F&& f) {
+  constexpr int KS = D / 4;  // contraction terms per lane
+  constexpr int NCT = D / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int cc = 0; cc < (NCT + 3) / 4; ++cc) {
+    const int c = wave + 4 * cc;
+    if (c >= NCT) break;
+    v4f_t bq[KS / 4];
+    const v4f_t* brow = reinterpret_cast<const v4f_t*>(mat + (size_t)(16 * c + r16) * D + g4 * KS);
+#pragma unroll
+    for (int q = 0; q < KS / 4; ++q) bq[q] = brow[q];
+    v4f_t acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = v4f_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < KS / 4; ++q) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const v4f_t a = *reinterpret_cast<const v4f_t*>(&L.xs[16 * r + r16][g4 * KS + 4 * q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], bq[q][e], acc[r], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f(cc, r, e, 16 * r + 4 * g4 + e, 16 * c + r16, acc[r][e]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void quantize_bulk_kernel(QuantizeSets sets) {
+  constexpr int NCT = D / 16;
+  constexpr int NCC = (NCT + 3) / 4;  // column tiles per wave
+  const QuantizeParams& p = sets.s[blockIdx.y];
+  __shared__ BulkLds<D> L;
+  const int tid = threadIdx.x;
+  const int64_t total = (int64_t)p.batch * p.heads * p.n_new;
+  const int64_t v0 = (int64_t)blockIdx.x * kMV;
+
+  if (tid < kMV) {
+    const int64_t vec = v0 + tid;
+    int64_t src = -1, slot = -1;
+    if (vec < total) {
+      const int t = (int)(vec % p.n_new);
+      const int64_t bh = vec / p.n_new;
+      const int h = (int)(bh % p.heads), b = (int)(bh / p.heads);
+      src = (int64_t)b * p.s0 + (int64_t)h * p.s1 + (int64_t)t * p.s2;
+      const int64_t pos = (int64_t)p.pos[b] + t;
+      if (pos >= 0 && pos < p.cap) slot = ((int64_t)b * p.heads + h) * p.cap + pos;
+    }
+    L.src[tid] = src;
+    L.slot[tid] = slot;
+  }
+  __syncthreads();
+
+  // ---- the x tile (zeros for rows past the end)
+  if (p.x_vec16) {
+    constexpr int PER = 8;  // bf16 elements per 16 bytes; f32 uses 4
+    if (p.x_bf16) {
+      for (int e = tid; e < kMV * D / PER; e += 256) {
+        const int v = e / (D / PER), q = e % (D / PER);
+        const int64_t src = L.src[v];
+        uint4 w = {0u, 0u, 0u, 0u};
+        if (src >= 0) w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + src + PER * q);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          L.xs[v][PER * q + 2 * k] = __uint_as_float(ww[k] << 16);
+          L.xs[v][PER * q + 2 * k + 1] = __uint_as_float(ww[k] & 0xffff0000u);
+        }
+      }
+    } else {
+      for (int e = tid; e < kMV * D / 4; e += 256) {
+        const int v = e / (D / 4), q = e % (D / 4);
+        const int64_t src = L.src[v];
+        v4f_t w = v4f_t{0.f, 0.f, 0.f, 0.f};
+        if (src >= 0) w = *reinterpret_cast<const v4f_t*>(static_cast<const float*>(p.x) + src + 4 * q);
+        *reinterpret_cast<v4f_t*>(&L.xs[v][4 * q]) = w;
+      }
+    }
+  } else {
+    for (int e = tid; e < kMV * D; e += 256) {
+      const int v = e / D, j = e % D;
+      const int64_t src = L.src[v];
+      L.xs[v][j] = src >= 0 ? load_x(p.x, src + j, p.x_bf16) : 0.f;
+    }
+  }
+  __syncthreads();
 
   if (p.mode == TQ_MODE_GROUP) {
-    // groups of 32 coordinates = half-waves; min/max stay inside a half-wave
+    // asymmetric min/max per 32 coordinates of the unrotated vector
     const int top = (1 << p.gbits) - 1;
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int i = lane + 64 * c;
-      const bool valid = i < D;
-      float mn = valid ? x[c] : INFINITY;
-      float mx = valid ? x[c] : -INFINITY;
-#pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) {
-        mn = fminf(mn, __shfl_xor(mn, o, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    for (int e = tid; e < kMV * (D / 32); e += 256) {
+      const int v = e / (D / 32), g = e % (D / 32);
+      const float* xv = &L.xs[v][32 * g];
+      float mn = xv[0], mx = xv[0];
+      for (int r = 1; r < 32; ++r) {
+        mn = fminf(mn, xv[r]);
+        mx = fmaxf(mx, xv[r]);
       }
       const float rng = mx - mn;
-      uint32_t q = 0;
-      if (valid && rng > 0.f) {
-        const float tq = (x[c] - mn) * (float)top / rng;
-        q = (uint32_t)fminf(fmaxf(rintf(tq), 0.f), (float)top);
+      for (int r = 0; r < 32; ++r) {
+        uint32_t q = 0;
+        if (rng > 0.f) q = (uint32_t)fminf(fmaxf(rintf((xv[r] - mn) * (float)top / rng), 0.f), (float)top);
+        L.codes[v][32 * g + r] = (uint8_t)q;
       }
-      if (active && valid) {
-        pack_field(wbuf[wave], i, p.gbits, q);
-        if ((i & 31) == 0) {
-          p.scale[tok * p.groups + (i >> 5)] = rng / (float)top;
-          p.gmin[tok * p.groups + (i >> 5)] = mn;
-        }
+      const int64_t slot = L.slot[v];
+      if (slot >= 0) {
+        p.scale[slot * p.groups + g] = rng / (float)top;
+        p.gmin[slot * p.groups + g] = mn;
       }
     }
     __syncthreads();
-    if (active && lane < p.words) p.idx[tok * p.words + lane] = wbuf[wave][lane];
+    for (int e = tid; e < kMV * p.words; e += 256) {
+      const int v = e / p.words, w = e % p.words;
+      const int64_t slot = L.slot[v];
+      if (slot >= 0) p.idx[slot * p.words + w] = pack_word(L.codes[v], w, p.gbits);
+    }
     return;
   }
 
-  const float n = sqrtf(wave_sum(ss));
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int i = lane + 64 * c;
-    if (i < D) xs[wave][i] = x[c];
+  // ---- norms: four threads per vector
+  {
+    const int v = tid >> 2, part = tid & 3;
+    float ss = 0.f;
+    for (int j = part * (D / 4); j < (part + 1) * (D / 4); ++j) ss = fmaf(L.xs[v][j], L.xs[v][j], ss);
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    if (part == 0) L.nrm[v] = sqrtf(ss);
   }
   __syncthreads();
 
-  // y = Pi x, with Pi^T[j][i] = Pi[i][j] read along i (coalesced)
-  float y[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) y[c] = 0.f;
-  for (int j = 0; j < D; ++j) {
-    const float xj = xs[wave][j];
-    const float* row = p.pit + (size_t)j * D;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int i = lane + 64 * c;
-      if (i < D) y[c] = fmaf(row[i], xj, y[c]);
-    }
-  }
-
-  const float inv = n > 0.f ? 1.f / n : 0.f;
-  uint32_t idx[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const float u = y[c] * inv;
+  // ---- y = Pi x on the matrix cores, nearest centroid per element
+  const bool prod = p.mode == TQ_MODE_PROD;
+  float rho[NCC][4][4];
+  tile_gemm<D>(L, p.pi, [&](int cc, int r, int e, int v, int coord, float y) {
+    const float n = L.nrm[v];
+    const float inv = n > 0.f ? 1.f / n : 0.f;
+    const float u = y * inv;
     uint32_t k = 0;
     for (int m = 0; m < p.levels - 1; ++m) k += u > p.bnd[m] ? 1u : 0u;
-    idx[c] = k;
-    const int i = lane + 64 * c;
-    if (active && i < D) pack_field(wbuf[wave], i, p.mse_bits, k);
+    L.codes[v][coord] = (uint8_t)k;
+    rho[cc][r][e] = prod ? y - n * p.cent[k] : 0.f;
+  });
+  __syncthreads();  // every read of the x tile and write of the codes is done
+  for (int e = tid; e < kMV * p.words; e += 256) {
+    const int v = e / p.words, w = e % p.words;
+    const int64_t slot = L.slot[v];
+    if (slot >= 0) p.idx[slot * p.words + w] = pack_word(L.codes[v], w, p.mse_bits);
   }
-  __syncthreads();
-  if (active) {
-    if (lane < p.words) p.idx[tok * p.words + lane] = wbuf[wave][lane];
-    if (lane == 0) p.norm[tok] = n;
-  }
-  if (p.mode != TQ_MODE_PROD) return;
+  if (tid < kMV && L.slot[tid] >= 0) p.norm[L.slot[tid]] = L.nrm[tid];
+  if (!prod) return;
 
-  // Prod: rotated residual, its norm, z = S rho, sign bits
-  float rho[NC];
-  float rs = 0.f;
+  // ---- Prod: the rotated residual over the tile, its norm, z = S rho
+  {
+    const int lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int i = lane + 64 * c;
-    rho[c] = i < D ? y[c] - n * p.cent[idx[c]] : 0.f;
-    rs += rho[c] * rho[c];
-  }
-  const float gamma = sqrtf(wave_sum(rs));
+    for (int cc = 0; cc < NCC; ++cc) {
+      const int c = wave + 4 * cc;
+      if (c >= NCT) break;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int i = lane + 64 * c;
-    if (i < D) xs[wave][i] = rho[c];
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) L.xs[16 * r + 4 * g4 + e][16 * c + r16] = rho[cc][r][e];
+    }
   }
+  __syncthreads();  // the residual is complete; the index packing has read the codes
+  float gam = 0.f;
+  {
+    const int v = tid >> 2, part = tid & 3;
+    float ss = 0.f;
+    for (int j = part * (D / 4); j < (part + 1) * (D / 4); ++j) ss = fmaf(L.xs[v][j], L.xs[v][j], ss);
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    gam = sqrtf(ss);
+  }
+  tile_gemm<D>(L, p.s, [&](int, int, int, int v, int coord, float z) { L.codes[v][coord] = z >= 0.f ? 1 : 0; });
   __syncthreads();
-  float z[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) z[c] = 0.f;
-  for (int j = 0; j < D; ++j) {
-    const float rj = xs[wave][j];
-    const float* row = p.st + (size_t)j * D;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int i = lane + 64 * c;
-      if (i < D) z[c] = fmaf(row[i], rj, z[c]);
-    }
+  for (int e = tid; e < kMV * p.sign_words; e += 256) {
+    const int v = e / p.sign_words, w = e % p.sign_words;
+    const int64_t slot = L.slot[v];
+    if (slot >= 0) p.sign[slot * p.sign_words + w] = pack_word(L.codes[v], w, 1);
   }
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int i = lane + 64 * c;
-    const uint64_t m = __ballot(i < D && z[c] >= 0.f);
-    if (active) {
-      if (lane == 0) p.sign[tok * p.sign_words + 2 * c] = (uint32_t)m;
-      if (lane == 1 && 2 * c + 1 < p.sign_words) p.sign[tok * p.sign_words + 2 * c + 1] = (uint32_t)(m >> 32);
-    }
-  }
-  if (active && lane == 0) p.rnorm[tok] = gamma;
+  if ((tid & 3) == 0 && L.slot[tid >> 2] >= 0) p.rnorm[L.slot[tid >> 2]] = gam;
 }
 
 // Small appends (a few tokens per sequence and head, the decode-step case):
-// one 256-thread workgroup per vector, so that the rotation's loads are all
-// in flight at once instead of one wave streaming Pi^T through L2 in many
-// round trips.  Thread t owns coordinate i = t % D and the slice of the
-// contraction j in [part*JN, (part+1)*JN), part = t / D; the rotation and
-// sketch rows it needs are loaded before x arrives.  Every mode (group mode
-// needs no rotation), head_dim 32, 64 and 128.
+// one workgroup per vector (256 threads, 1024 at head_dim 256), so that the
+// rotation's loads are all in flight at once instead of one wave streaming
+// Pi^T through L2 in many round trips.  Thread t owns coordinate i = t % D
+// and the slice of the contraction j in [part*JN, (part+1)*JN), part = t / D;
+// the rotation rows it needs (and the sketch rows, up to head_dim 128) are
+// loaded before x arrives.  Every mode (group mode needs no rotation),
+// head_dim 32, 64, 128 and 256.
 template <int D>
-__global__ __launch_bounds__(256) void quantize_small_kernel(QuantizeSets sets) {
-  constexpr int PARTS = 256 / D;
+constexpr int small_threads() { return D <= 128 ? 256 : 1024; }
+
+template <int D>
+__global__ __launch_bounds__(small_threads<D>()) void quantize_small_kernel(QuantizeSets sets) {
+  constexpr int T = small_threads<D>();
+  constexpr int NW = T / 64;
+  constexpr int PARTS = T / D;
   constexpr int JN = D / PARTS;
-  static_assert(PARTS * D == 256 && JN <= 64, "one to eight slices of at most 64 terms");
+  constexpr bool kEarlySketch = D <= 128;  // at 1024 threads the sketch rows wait for the registers
+  static_assert(PARTS * D == T && JN <= 64, "one to eight slices of at most 64 terms");
   const QuantizeParams& p = sets.s[blockIdx.y];
   __shared__ float xs[D];
   __shared__ float part_sum[PARTS][D];
   __shared__ uint32_t wbuf[32];
-  __shared__ float red[4];
+  __shared__ float red[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = tid % D, part = tid / D, j0 = part * JN;
@@ -262,13 +366,28 @@ __global__ __launch_bounds__(256) void quantize_small_kernel(QuantizeSets sets) 
   }
 
   // rotation (and sketch) slices first, then x
+  // row slice j0 .. j0+JN-1 of row i: from the transposed table (coalesced
+  // across threads), or at 1024 threads as 16-byte loads of the row-major one
+  // (one address instead of JN)
+  auto load_slice = [&](const float* t, const float* rowmajor, float (&r)[JN]) {
+    if constexpr (kEarlySketch) {
+#pragma unroll
+      for (int k = 0; k < JN; ++k) r[k] = t[(size_t)(j0 + k) * D + i];
+    } else {
+      const float4* src = reinterpret_cast<const float4*>(rowmajor + (size_t)i * D + j0);
+#pragma unroll
+      for (int k = 0; k < JN / 4; ++k) {
+        const float4 v = src[k];
+        r[4 * k] = v.x;
+        r[4 * k + 1] = v.y;
+        r[4 * k + 2] = v.z;
+        r[4 * k + 3] = v.w;
+      }
+    }
+  };
   float pr[JN], sr[JN];
-#pragma unroll
-  for (int k = 0; k < JN; ++k) pr[k] = p.pit[(size_t)(j0 + k) * D + i];
-  if (prod) {
-#pragma unroll
-    for (int k = 0; k < JN; ++k) sr[k] = p.st[(size_t)(j0 + k) * D + i];
-  }
+  load_slice(p.pit, p.pi, pr);
+  if (kEarlySketch && prod) load_slice(p.st, p.s, sr);
   float xv = 0.f;
   if (tid < D) xv = load_x(p.x, (int64_t)b * p.s0 + (int64_t)h * p.s1 + (int64_t)t * p.s2 + tid, p.x_bf16);
   if (tid < 32) wbuf[tid] = 0u;
@@ -276,7 +395,10 @@ __global__ __launch_bounds__(256) void quantize_small_kernel(QuantizeSets sets) 
   float sq = wave_sum(xv * xv);
   if (lane == 0) red[wave] = sq;
   __syncthreads();
-  const float n = sqrtf(red[0] + red[1] + red[2] + red[3]);
+  float n2 = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) n2 += red[w];
+  const float n = sqrtf(n2);
 
   // y = Pi x
   float acc = 0.f;
@@ -304,8 +426,12 @@ __global__ __launch_bounds__(256) void quantize_small_kernel(QuantizeSets sets) 
   __syncthreads();  // every read of xs, part_sum and red above is done
   if (tid < D) xs[tid] = rho;
   if (lane == 0) red[wave] = rs;
+  if (!kEarlySketch) load_slice(p.st, p.s, sr);
   __syncthreads();
-  const float gamma = sqrtf(red[0] + red[1] + red[2] + red[3]);
+  float g2 = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) g2 += red[w];
+  const float gamma = sqrtf(g2);
   acc = 0.f;
 #pragma unroll
   for (int k = 0; k < JN; ++k) acc = fmaf(sr[k], xs[j0 + k], acc);
@@ -338,28 +464,29 @@ hipError_t launch_quantize(const QuantizeSets& sets, int n_sets, hipStream_t str
   const int d = sets.s[0].d;
   // the choice depends only on the sizes, so a key and a value append made
   // together or one by one take the same kernel and write the same bits
-  const bool small = total <= kSmallAppend && (d == 32 || d == 64 || d == 128);
+  const bool small = total <= kSmallAppend && (d == 32 || d == 64 || d == 128 || d == 256);
   if (small) {
-    const dim3 grid((unsigned)total, (unsigned)n_sets), block(256);
+    const dim3 grid((unsigned)total, (unsigned)n_sets);
     switch (d) {
-      case 32: quantize_small_kernel<32><<<grid, block, 0, stream>>>(sets); break;
-      case 64: quantize_small_kernel<64><<<grid, block, 0, stream>>>(sets); break;
-      default: quantize_small_kernel<128><<<grid, block, 0, stream>>>(sets); break;
+      case 32: quantize_small_kernel<32><<<grid, small_threads<32>(), 0, stream>>>(sets); break;
+      case 64: quantize_small_kernel<64><<<grid, small_threads<64>(), 0, stream>>>(sets); break;
+      case 128: quantize_small_kernel<128><<<grid, small_threads<128>(), 0, stream>>>(sets); break;
+      default: quantize_small_kernel<256><<<grid, small_threads<256>(), 0, stream>>>(sets); break;
     }
     return hipGetLastError();
   }
-  const int64_t blocks = (total + 3) / 4;
+  const int64_t blocks = (total + kMV - 1) / kMV;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks, (unsigned)n_sets), block(256);
   switch (d) {
-    case 32: quantize_kernel<32><<<grid, block, 0, stream>>>(sets); break;
-    case 64: quantize_kernel<64><<<grid, block, 0, stream>>>(sets); break;
-    case 96: quantize_kernel<96><<<grid, block, 0, stream>>>(sets); break;
-    case 128: quantize_kernel<128><<<grid, block, 0, stream>>>(sets); break;
-    case 160: quantize_kernel<160><<<grid, block, 0, stream>>>(sets); break;
-    case 192: quantize_kernel<192><<<grid, block, 0, stream>>>(sets); break;
-    case 224: quantize_kernel<224><<<grid, block, 0, stream>>>(sets); break;
-    case 256: quantize_kernel<256><<<grid, block, 0, stream>>>(sets); break;
+    case 32: quantize_bulk_kernel<32><<<grid, block, 0, stream>>>(sets); break;
+    case 64: quantize_bulk_kernel<64><<<grid, block, 0, stream>>>(sets); break;
+    case 96: quantize_bulk_kernel<96><<<grid, block, 0, stream>>>(sets); break;
+    case 128: quantize_bulk_kernel<128><<<grid, block, 0, stream>>>(sets); break;
+    case 160: quantize_bulk_kernel<160><<<grid, block, 0, stream>>>(sets); break;
+    case 192: quantize_bulk_kernel<192><<<grid, block, 0, stream>>>(sets); break;
+    case 224: quantize_bulk_kernel<224><<<grid, block, 0, stream>>>(sets); break;
+    case 256: quantize_bulk_kernel<256><<<grid, block, 0, stream>>>(sets); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -35,6 +35,7 @@ struct DevTables {
   float* pit = nullptr;   // Pi^T [d][d]: pit[j*d + i] = Pi[i][j]
   float* pi = nullptr;    // Pi   [d][d] row-major
   float* st = nullptr;    // S^T  [d][d]: st[j*d + i] = S[i][j] (Prod)
+  float* s = nullptr;     // S    [d][d] row-major (Prod)
   float* cent = nullptr;  // centroids [16]
   float* bnd = nullptr;   // boundaries [16]
   void* block = nullptr;  // single allocation holding all of the above
@@ -59,8 +60,11 @@ struct QuantizeParams {
   int64_t s0, s1, s2;  // element strides of batch, head, token (coordinate stride 1)
   int batch, heads, n_new;
   int d, mode, mse_bits, levels, words, sign_words, groups, gbits;
+  int x_vec16;        // x, its strides and element size allow 16-byte loads
   const float* pit;   // Pi^T
+  const float* pi;    // Pi (row-major)
   const float* st;    // S^T (Prod)
+  const float* s;     // S (row-major, Prod)
   const float* cent;  // centroids
   const float* bnd;   // boundaries
   uint32_t* idx;

@@ -56,7 +56,7 @@ def _compare_indices(gw, ora, bits, d, tag):
 
 QUANT_CASES = [
     # d, bits, mode, bf16, heads, n_new: 2*3*37 vectors take the one-workgroup-per-vector
-    # kernel (d 32/64/128, MSE and Prod); 2*8*300 > 4096 take the one-wave-per-vector kernel
+    # kernel (d 32/64/128); 2*8*300 > 4096 take the bulk (matrix-core) kernel
     (128, 3, 0, False, 3, 37), (128, 3, 0, True, 3, 37), (128, 4, 0, True, 3, 37), (128, 2, 0, False, 3, 37),
     (128, 1, 0, False, 3, 37), (128, 3, 1, True, 3, 37), (256, 3, 1, True, 3, 37), (64, 5, 1, False, 3, 37),
     (32, 2, 1, True, 3, 37), (256, 2, 2, True, 3, 37), (128, 4, 2, False, 3, 37), (96, 3, 2, True, 3, 37),
@@ -65,9 +65,29 @@ QUANT_CASES = [
 ]
 
 
+# bulk appends (2*8*300 vectors > 4096: 64-vector tiles on the matrix cores);
+# the last field offsets the input view by that many elements, which makes
+# rows unaligned for 16-byte loads and takes the element-wise load path
+BULK_CASES = [
+    (128, 3, 0, True, 8, 300, 0), (128, 3, 1, True, 8, 300, 1), (64, 4, 1, False, 8, 300, 0),
+    (256, 3, 1, True, 8, 300, 0), (256, 2, 2, True, 8, 300, 0), (128, 4, 0, True, 8, 300, 0),
+    (32, 2, 0, False, 8, 300, 3), (96, 3, 2, True, 8, 300, 0), (160, 1, 0, False, 8, 300, 0),
+    (224, 5, 1, True, 8, 300, 0), (192, 2, 1, False, 8, 300, 1), (128, 4, 2, False, 8, 300, 2),
+]
+
+
 @pytest.mark.parametrize("d,bits,mode,bf16,H,n_new", QUANT_CASES)
 def test_quantize_append_parity(d, bits, mode, bf16, H, n_new):
-    tag = f"quantize d={d} bits={bits} mode={mode} bf16={bf16} heads={H} n_new={n_new}"
+    _check_append(d, bits, mode, bf16, H, n_new, 0)
+
+
+@pytest.mark.parametrize("d,bits,mode,bf16,H,n_new,off", BULK_CASES)
+def test_quantize_bulk_append_parity(d, bits, mode, bf16, H, n_new, off):
+    _check_append(d, bits, mode, bf16, H, n_new, off)
+
+
+def _check_append(d, bits, mode, bf16, H, n_new, off):
+    tag = f"quantize d={d} bits={bits} mode={mode} bf16={bf16} heads={H} n_new={n_new} offset={off}"
     _say(tag)
     B, cap = 2, n_new + 13
     rng = np.random.default_rng(d * 10 + bits + 100 * mode)
@@ -81,8 +101,8 @@ def test_quantize_append_parity(d, bits, mode, bf16, H, n_new):
     cache = tq.allocate_cache(gc, B, H, cap)
     # a strided (non-contiguous) input: a view into a wider buffer
     wide = torch.zeros((B, H, n_new, d + 32), dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
-    wide[..., :d] = to_device_f(x, bf16)
-    xd = wide[..., :d]
+    wide[..., off:off + d] = to_device_f(x, bf16)
+    xd = wide[..., off:off + d]
     pos = torch.tensor([cap - 10, 0], dtype=torch.int32, device="cuda")   # b=0 runs past cap: skipped
     tq.tq_quantize_append(gc, xd, cache, pos)
     torch.cuda.synchronize()
