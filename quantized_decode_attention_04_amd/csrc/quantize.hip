@@ -143,10 +143,83 @@ __device__ __forceinline__ void tile_gemm(const BulkLds<D>& L, const float* __re
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void quantize_bulk_kernel(QuantizeSets sets) {
+// The rotated modes after the norms: y = Pi x on the matrix cores, the
+// nearest centroid of every element (NB = levels - 1 boundaries, unrolled),
+// the packed indices and norms; for Prod keys the residual, its norm and the
+// sign bits of z = S rho.
+template <int D, int NB, bool PROD>
+__device__ __forceinline__ void quantize_rotated(const QuantizeParams& p, BulkLds<D>& L) {
   constexpr int NCT = D / 16;
   constexpr int NCC = (NCT + 3) / 4;  // column tiles per wave
+  constexpr bool prod = PROD;
+  const int tid = threadIdx.x;
+  float bnd[NB], cent[NB + 1];  // uniform: scalar registers
+#pragma unroll
+  for (int m = 0; m < NB; ++m) bnd[m] = p.bnd[m];
+#pragma unroll
+  for (int m = 0; m <= NB; ++m) cent[m] = PROD ? p.cent[m] : 0.f;
+  float rho[NCC][4][4];
+  tile_gemm<D>(L, p.pi, [&](int cc, int r, int e, int v, int coord, float y) {
+    const float n = L.nrm[v];
+    const float inv = n > 0.f ? 1.f / n : 0.f;
+    const float u = y * inv;
+    // the boundaries are sorted: the last one below u names the centroid
+    uint32_t k = 0;
+    float c = cent[0];
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+      const bool above = u > bnd[m];
+      k += above ? 1u : 0u;
+      if (PROD) c = above ? cent[m + 1] : c;
+    }
+    L.codes[v][coord] = (uint8_t)k;
+    rho[cc][r][e] = PROD ? y - n * c : 0.f;
+  });
+  __syncthreads();  // every read of the x tile and write of the codes is done
+  for (int e = tid; e < kMV * p.words; e += 256) {
+    const int v = e / p.words, w = e % p.words;
+    const int64_t slot = L.slot[v];
+    if (slot >= 0) p.idx[slot * p.words + w] = pack_word(L.codes[v], w, p.mse_bits);
+  }
+  if (tid < kMV && L.slot[tid] >= 0) p.norm[L.slot[tid]] = L.nrm[tid];
+  if (!prod) return;
+
+  // ---- Prod: the rotated residual over the tile, its norm, z = S rho
+  {
+    const int lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+      const int c = wave + 4 * cc;
+      if (c >= NCT) break;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) L.xs[16 * r + 4 * g4 + e][16 * c + r16] = rho[cc][r][e];
+    }
+  }
+  __syncthreads();  // the residual is complete; the index packing has read the codes
+  float gam = 0.f;
+  {
+    const int v = tid >> 2, part = tid & 3;
+    float ss = 0.f;
+    for (int j = part * (D / 4); j < (part + 1) * (D / 4); ++j) ss = fmaf(L.xs[v][j], L.xs[v][j], ss);
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    gam = sqrtf(ss);
+  }
+  tile_gemm<D>(L, p.s, [&](int, int, int, int v, int coord, float z) { L.codes[v][coord] = z >= 0.f ? 1 : 0; });
+  __syncthreads();
+  for (int e = tid; e < kMV * p.sign_words; e += 256) {
+    const int v = e / p.sign_words, w = e % p.sign_words;
+    const int64_t slot = L.slot[v];
+    if (slot >= 0) p.sign[slot * p.sign_words + w] = pack_word(L.codes[v], w, 1);
+  }
+  if ((tid & 3) == 0 && L.slot[tid >> 2] >= 0) p.rnorm[L.slot[tid >> 2]] = gam;
+}
+
+// two waves per SIMD where the registers allow it (head_dim up to 128)
+template <int D>
+__global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void quantize_bulk_kernel(QuantizeSets sets) {
   const QuantizeParams& p = sets.s[blockIdx.y];
   __shared__ BulkLds<D> L;
   const int tid = threadIdx.x;
@@ -246,58 +319,13 @@ __global__ __launch_bounds__(256) void quantize_bulk_kernel(QuantizeSets sets) {
   }
   __syncthreads();
 
-  // ---- y = Pi x on the matrix cores, nearest centroid per element
   const bool prod = p.mode == TQ_MODE_PROD;
-  float rho[NCC][4][4];
-  tile_gemm<D>(L, p.pi, [&](int cc, int r, int e, int v, int coord, float y) {
-    const float n = L.nrm[v];
-    const float inv = n > 0.f ? 1.f / n : 0.f;
-    const float u = y * inv;
-    uint32_t k = 0;
-    for (int m = 0; m < p.levels - 1; ++m) k += u > p.bnd[m] ? 1u : 0u;
-    L.codes[v][coord] = (uint8_t)k;
-    rho[cc][r][e] = prod ? y - n * p.cent[k] : 0.f;
-  });
-  __syncthreads();  // every read of the x tile and write of the codes is done
-  for (int e = tid; e < kMV * p.words; e += 256) {
-    const int v = e / p.words, w = e % p.words;
-    const int64_t slot = L.slot[v];
-    if (slot >= 0) p.idx[slot * p.words + w] = pack_word(L.codes[v], w, p.mse_bits);
+  switch (p.levels) {
+    case 2: prod ? quantize_rotated<D, 1, true>(p, L) : quantize_rotated<D, 1, false>(p, L); break;
+    case 4: prod ? quantize_rotated<D, 3, true>(p, L) : quantize_rotated<D, 3, false>(p, L); break;
+    case 8: prod ? quantize_rotated<D, 7, true>(p, L) : quantize_rotated<D, 7, false>(p, L); break;
+    default: prod ? quantize_rotated<D, 15, true>(p, L) : quantize_rotated<D, 15, false>(p, L); break;
   }
-  if (tid < kMV && L.slot[tid] >= 0) p.norm[L.slot[tid]] = L.nrm[tid];
-  if (!prod) return;
-
-  // ---- Prod: the rotated residual over the tile, its norm, z = S rho
-  {
-    const int lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
-#pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) {
-      const int c = wave + 4 * cc;
-      if (c >= NCT) break;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) L.xs[16 * r + 4 * g4 + e][16 * c + r16] = rho[cc][r][e];
-    }
-  }
-  __syncthreads();  // the residual is complete; the index packing has read the codes
-  float gam = 0.f;
-  {
-    const int v = tid >> 2, part = tid & 3;
-    float ss = 0.f;
-    for (int j = part * (D / 4); j < (part + 1) * (D / 4); ++j) ss = fmaf(L.xs[v][j], L.xs[v][j], ss);
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    gam = sqrtf(ss);
-  }
-  tile_gemm<D>(L, p.s, [&](int, int, int, int v, int coord, float z) { L.codes[v][coord] = z >= 0.f ? 1 : 0; });
-  __syncthreads();
-  for (int e = tid; e < kMV * p.sign_words; e += 256) {
-    const int v = e / p.sign_words, w = e % p.sign_words;
-    const int64_t slot = L.slot[v];
-    if (slot >= 0) p.sign[slot * p.sign_words + w] = pack_word(L.codes[v], w, 1);
-  }
-  if ((tid & 3) == 0 && L.slot[tid >> 2] >= 0) p.rnorm[L.slot[tid >> 2]] = gam;
 }
 
 // Small appends (a few tokens per sequence and head, the decode-step case):
