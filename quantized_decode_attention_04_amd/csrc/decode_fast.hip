@@ -259,6 +259,22 @@ struct Tile {
   float kn, vn;
 };
 
+__device__ __forceinline__ void load_keys(Tile& t, __amdgpu_buffer_rsrc_t rk, const uint32_t* lw, uint32_t T0) {
+#pragma unroll
+  for (int st = 0; st < 4; ++st) t.kw[st] = __builtin_amdgcn_raw_buffer_load_b96(rk, lw[st] + T0 * 48u, 0, 0);
+}
+
+__device__ __forceinline__ void load_values(Tile& t, __amdgpu_buffer_rsrc_t rv, const uint32_t* lw, uint32_t T0) {
+#pragma unroll
+  for (int st = 0; st < 4; ++st) t.vw[st] = __builtin_amdgcn_raw_buffer_load_b96(rv, lw[st] + T0 * 48u, 0, 0);
+}
+
+__device__ __forceinline__ void load_norms(Tile& t, __amdgpu_buffer_rsrc_t rkn, __amdgpu_buffer_rsrc_t rvn,
+                                           uint32_t ln4, uint32_t T0) {
+  t.kn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rkn, ln4 + T0 * 4u, 0, 0));
+  t.vn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvn, ln4 + T0 * 4u, 0, 0));
+}
+
 __device__ __forceinline__ void load_tile(Tile& t, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                           __amdgpu_buffer_rsrc_t rkn, __amdgpu_buffer_rsrc_t rvn,
                                           const uint32_t* lw, uint32_t ln4, uint32_t T0) {
@@ -276,7 +292,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
   __shared__ __attribute__((aligned(16))) uint32_t s_op[2 * 3 * 64 * 4];
   __shared__ float s_max[kWaves * 16];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform: a scalar register keeps the tile loop uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, h = lane >> 4;  // query row, lane group
   const int chunk_id = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.hkv + g;
@@ -347,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
     all[u] = v4i{0, 0, 0, 0};
   }
 
-  auto process = [&](const Tile& cur, const uint32_t T0) {
+  auto process = [&](Tile& cur, const uint32_t T0, const uint32_t Tn) {
     // ---- scores on the matrix cores
     float sc[16];
 #pragma unroll
@@ -374,6 +391,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
       for (int i = 0; i < 4; ++i) sc[4 * st + i] = fmaf((float)(t24[i] * 256 + t16[i]), 256.f, (float)t8[i]);
     }
 
+    // the key words are consumed: the next tile of this buffer is loaded now
+    load_keys(cur, rk, lw, Tn);
     // ---- value selectors and the tile's norms to LDS
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -386,6 +405,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
     }
     sn[lane] = cur.kn;
     sn[kTile + lane] = cur.vn;
+    load_values(cur, rv, lw, Tn);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -490,15 +510,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
   };
 
   // two tile buffers in turn: a tile's successor is in flight while it is
-  // processed.  The loads are unconditional: past the chunk they read zeros
-  // without touching memory, so the number of loads in flight is the same
-  // on every path and the waits stay partial.
+  // processed, and a buffer's next tile (two steps ahead) is requested as
+  // soon as its words are consumed: the key words after the scores, the value
+  // words once their selectors are in LDS, the norms after the tile.  The
+  // loads are unconditional: past the chunk they read zeros without touching
+  // memory, so the number of loads in flight is the same on every path and
+  // the waits stay partial.
   for (uint32_t T0 = t_first; T0 < ntok; T0 += 2 * kStep) {
-    process(ta, T0);
+    process(ta, T0, T0 + 2 * kStep);
     if (T0 + kStep >= ntok) break;
-    load_tile(ta, rk, rv, rkn, rvn, lw, ln4, T0 + 2 * kStep);
-    process(tb, T0 + kStep);
-    load_tile(tb, rk, rv, rkn, rvn, lw, ln4, T0 + 3 * kStep);
+    load_norms(ta, rkn, rvn, ln4, T0 + 2 * kStep);
+    process(tb, T0 + kStep, T0 + 3 * kStep);
+    load_norms(tb, rkn, rvn, ln4, T0 + 3 * kStep);
   }
 
   v4f of[8];
