@@ -190,12 +190,31 @@ tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32
  * Query head h reads KV head h / (n_q_heads / n_kv_heads); row i of q_len
  * sees tokens t <= N_b - q_len + i ([omlx] make_mask: causal for new tokens).
  * A row that sees no token gets zeros.
- * Errors: INVALID_ARG, UNSUPPORTED, CONFIG_MISMATCH, CAPACITY (max_len > cap),
- * WORKSPACE, HIP. */
+ * Errors: INVALID_ARG, UNSUPPORTED (more than 16 rows per KV head, 8 above
+ * head_dim 128: use tq_prefill_attention), CONFIG_MISMATCH, CAPACITY
+ * (max_len > cap), WORKSPACE, HIP. */
 tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void* q, int32_t q_dtype, int32_t batch,
                               int32_t n_q_heads, int32_t n_kv_heads, int32_t q_len, const tq_cache* k,
                               const tq_cache* v, const int32_t* d_len, int64_t max_len, float scale, float* out,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace tq_prefill_attention needs for these sizes (one
+ * block of rows at a time reuses it). */
+tq_status tq_prefill_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t n_q_heads,
+                                    int32_t n_kv_heads, int32_t q_len, int64_t max_len, size_t* bytes);
+
+/* Prefill attention over the compressed cache ([omlx] prefill_attention:
+ * many new tokens attend to the cache and, causally, to each other, as in
+ * make_mask).  Same arguments, layouts, masking, ownership and errors as
+ * tq_decode_attention, with any q_len >= 1: the (n_q_heads / n_kv_heads) *
+ * q_len rows of each KV head are processed in blocks of 16 (8 above
+ * head_dim 128), one block after the other on the stream, so the cost grows
+ * with the number of blocks.  ws must hold tq_prefill_workspace_size(...)
+ * bytes.  UNSUPPORTED above 2^30 rows per KV head. */
+tq_status tq_prefill_attention(const tq_codec* kc, const tq_codec* vc, const void* q, int32_t q_dtype, int32_t batch,
+                               int32_t n_q_heads, int32_t n_kv_heads, int32_t q_len, const tq_cache* k,
+                               const tq_cache* v, const int32_t* d_len, int64_t max_len, float scale, float* out,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* tq_last_error(void);

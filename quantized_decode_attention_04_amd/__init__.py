@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     Codec,
     TQError,
     allocate_cache,
+    allocate_prefill_workspace,
     allocate_workspace,
     lib_path,
     tq_codec_create,
@@ -26,6 +27,8 @@ from ._binding import (  # noqa: F401
     tq_decode_attention,
     tq_decode_workspace_size,
     tq_last_error,
+    tq_prefill_attention,
+    tq_prefill_workspace_size,
     tq_quantize_append,
     tq_quantize_append_kv,
     tq_status_string,

@@ -50,7 +50,7 @@ def _load() -> ctypes.CDLL:
     # of pulling a second copy into the process
     import torch  # noqa: F401
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is not built: run `python -m quantized_decode_attention_04_amd.build_lib`")
+        raise ImportError(f"{_LIB_PATH} is not built: run `python quantized_decode_attention_04_amd/build_lib.py`")
     lib = ctypes.CDLL(_LIB_PATH)
     P, I32, I64, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
     sigs = {
@@ -65,6 +65,9 @@ def _load() -> ctypes.CDLL:
         "tq_decode_workspace_size": (I32, [P, P, I32, I32, I32, I32, I64, ctypes.POINTER(SZ)]),
         "tq_decode_attention": (I32, [P, P, P, I32, I32, I32, I32, I32, ctypes.POINTER(_Cache),
                                       ctypes.POINTER(_Cache), P, I64, ctypes.c_float, P, P, SZ, P]),
+        "tq_prefill_workspace_size": (I32, [P, P, I32, I32, I32, I32, I64, ctypes.POINTER(SZ)]),
+        "tq_prefill_attention": (I32, [P, P, P, I32, I32, I32, I32, I32, ctypes.POINTER(_Cache),
+                                       ctypes.POINTER(_Cache), P, I64, ctypes.c_float, P, P, SZ, P]),
         "tq_last_error": (ctypes.c_char_p, []),
         "tq_status_string": (ctypes.c_char_p, [I32]),
     }
@@ -79,8 +82,8 @@ _lib = _load()
 
 EXPORTED = (
     "tq_codec_create", "tq_codec_destroy", "tq_codec_get_info", "tq_codec_export", "tq_codec_upload",
-    "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_workspace_size", "tq_decode_attention", "tq_last_error",
-    "tq_status_string",
+    "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_workspace_size", "tq_decode_attention",
+    "tq_prefill_workspace_size", "tq_prefill_attention", "tq_last_error", "tq_status_string",
 )
 
 
@@ -283,12 +286,8 @@ def allocate_workspace(kc: Codec, vc: Codec, batch: int, n_q_heads: int, n_kv_he
                        dtype=torch.uint8, device=device)
 
 
-def tq_decode_attention(kc: Codec, vc: Codec, q, kcache: Cache, vcache: Cache, lens, max_len: int, scale: float,
-                        out, ws, stream=None) -> None:
-    """out[b, h, i, :] = attention of q[b, h, i] over the compressed cache.
-    q: [batch, n_q_heads, q_len, head_dim] contiguous f32/bf16; lens: int32
-    device [batch]; out: float32 contiguous like q; ws: device byte tensor of at
-    least tq_decode_workspace_size(...) bytes (allocate_workspace)."""
+def _attention(fn, kc: Codec, vc: Codec, q, kcache: Cache, vcache: Cache, lens, max_len: int, scale: float, out, ws,
+               stream) -> None:
     import torch
     _on_device(q, lens, out, ws, *kcache.arrays().values(), *vcache.arrays().values())
     if q.dim() != 4 or not q.is_contiguous():
@@ -299,8 +298,40 @@ def tq_decode_attention(kc: Codec, vc: Codec, q, kcache: Cache, vcache: Cache, l
         raise ValueError("lens must be a contiguous int32 tensor of length batch")
     ks, vs = kcache.as_struct(), vcache.as_struct()
     nbytes = ws.numel() * ws.element_size()
-    _check(_lib.tq_decode_attention(kc.handle, vc.handle, ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
-                                    int(q.shape[0]), int(q.shape[1]), int(kcache.heads), int(q.shape[2]),
-                                    ctypes.byref(ks), ctypes.byref(vs), ctypes.c_void_p(lens.data_ptr()),
-                                    int(max_len), ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()),
-                                    ctypes.c_void_p(ws.data_ptr()), nbytes, _stream(stream)))
+    _check(fn(kc.handle, vc.handle, ctypes.c_void_p(q.data_ptr()), _dtype_code(q), int(q.shape[0]), int(q.shape[1]),
+              int(kcache.heads), int(q.shape[2]), ctypes.byref(ks), ctypes.byref(vs), ctypes.c_void_p(lens.data_ptr()),
+              int(max_len), ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+              nbytes, _stream(stream)))
+
+
+def tq_decode_attention(kc: Codec, vc: Codec, q, kcache: Cache, vcache: Cache, lens, max_len: int, scale: float,
+                        out, ws, stream=None) -> None:
+    """out[b, h, i, :] = attention of q[b, h, i] over the compressed cache.
+    q: [batch, n_q_heads, q_len, head_dim] contiguous f32/bf16; lens: int32
+    device [batch]; out: float32 contiguous like q; ws: device byte tensor of at
+    least tq_decode_workspace_size(...) bytes (allocate_workspace)."""
+    _attention(_lib.tq_decode_attention, kc, vc, q, kcache, vcache, lens, max_len, scale, out, ws, stream)
+
+
+def tq_prefill_workspace_size(kc: Codec, vc: Codec, batch: int, n_q_heads: int, n_kv_heads: int, q_len: int,
+                              max_len: int) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.tq_prefill_workspace_size(kc.handle, vc.handle, int(batch), int(n_q_heads), int(n_kv_heads),
+                                          int(q_len), int(max_len), ctypes.byref(n)))
+    return n.value
+
+
+def allocate_prefill_workspace(kc: Codec, vc: Codec, batch: int, n_q_heads: int, n_kv_heads: int, q_len: int,
+                               max_len: int, device="cuda"):
+    """A device workspace for tq_prefill_attention with these sizes."""
+    import torch
+    return torch.zeros(tq_prefill_workspace_size(kc, vc, batch, n_q_heads, n_kv_heads, q_len, max_len),
+                       dtype=torch.uint8, device=device)
+
+
+def tq_prefill_attention(kc: Codec, vc: Codec, q, kcache: Cache, vcache: Cache, lens, max_len: int, scale: float,
+                         out, ws, stream=None) -> None:
+    """Like tq_decode_attention for any q_len (the q_len new tokens attend to
+    the cache and causally to each other); ws: at least
+    tq_prefill_workspace_size(...) bytes (allocate_prefill_workspace)."""
+    _attention(_lib.tq_prefill_attention, kc, vc, q, kcache, vcache, lens, max_len, scale, out, ws, stream)

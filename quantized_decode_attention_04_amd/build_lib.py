@@ -1,6 +1,6 @@
 """Build libtq.so in-tree with hipcc for gfx950.
 
-    python -m quantized_decode_attention_04_amd.build_lib
+    python quantized_decode_attention_04_amd/build_lib.py
 
 Every source is compiled (no up-to-date check), objects go to ``_build/`` at
 the repository root, and the library is written next to this file.

@@ -377,8 +377,13 @@ tq_status tq_quantize_append_kv(const tq_codec* kc, const tq_codec* vc, const vo
   return TQ_OK;
 }
 
+// Rows per launch: 16 up to head_dim 128, 8 above (the general kernel's
+// register budget).  Decode takes one launch; prefill walks the rows of each
+// KV head in blocks of this size.
+static int row_block(const tq_codec* kc) { return kc->h.d <= 128 ? 16 : 8; }
+
 static tq_status check_decode_shapes(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
-                                     int32_t q_len, int64_t max_len) {
+                                     int32_t q_len, int64_t max_len, bool blocks = false) {
   if (!kc || !vc) return fail(TQ_ERR_INVALID_ARG, "decode: codec is NULL");
   if (kc->h.mode != TQ_MODE_MSE && kc->h.mode != TQ_MODE_PROD)
     return fail(TQ_ERR_UNSUPPORTED, "decode: the key codec must be MSE or Prod");
@@ -389,12 +394,23 @@ static tq_status check_decode_shapes(const tq_codec* kc, const tq_codec* vc, int
     return fail(TQ_ERR_INVALID_ARG, "decode: batch, heads and q_len must be positive");
   if (hq % hkv) return fail(TQ_ERR_INVALID_ARG, "decode: n_q_heads must be a multiple of n_kv_heads");
   if (max_len <= 0) return fail(TQ_ERR_INVALID_ARG, "decode: max_len must be positive");
-  const int rows = (hq / hkv) * q_len;
-  const int rmax = kc->h.d <= 128 ? 16 : 8;
+  const int64_t rows = (int64_t)(hq / hkv) * q_len;
+  const int rmax = row_block(kc);
+  if (blocks) {
+    if (rows > (int64_t)1 << 30) return fail(TQ_ERR_UNSUPPORTED, "prefill: more than 2^30 query rows per KV head");
+    return TQ_OK;
+  }
   if (rows > rmax)
     return fail(TQ_ERR_UNSUPPORTED, "decode: (n_q_heads/n_kv_heads)*q_len above " + std::to_string(rmax) +
                                         " for this head_dim");
   return TQ_OK;
+}
+
+static size_t attention_workspace(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
+                                  int32_t q_len, int64_t max_len) {
+  const int rows = (int)std::min<int64_t>((int64_t)(hq / hkv) * q_len, row_block(kc));
+  return use_fast(kc, vc, rows) ? tq::plan_decode_fast(batch, hkv, rows, kc->h.d, max_len).total
+                                : tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, kc->h.mode == TQ_MODE_PROD).total;
 }
 
 tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
@@ -402,35 +418,46 @@ tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32
   if (!bytes) return fail(TQ_ERR_INVALID_ARG, "tq_decode_workspace_size: bytes is NULL");
   tq_status st = check_decode_shapes(kc, vc, batch, hq, hkv, q_len, max_len);
   if (st != TQ_OK) return st;
-  const int rows = (hq / hkv) * q_len;
-  *bytes = use_fast(kc, vc, rows) ? tq::plan_decode_fast(batch, hkv, rows, kc->h.d, max_len).total
-                                  : tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, kc->h.mode == TQ_MODE_PROD).total;
+  *bytes = attention_workspace(kc, vc, batch, hq, hkv, q_len, max_len);
   return TQ_OK;
 }
 
-tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void* q, int32_t q_dtype, int32_t batch,
-                              int32_t hq, int32_t hkv, int32_t q_len, const tq_cache* k, const tq_cache* v,
-                              const int32_t* d_len, int64_t max_len, float scale, float* out, void* ws,
-                              size_t ws_bytes, void* stream) {
-  tq_status st = check_decode_shapes(kc, vc, batch, hq, hkv, q_len, max_len);
+tq_status tq_prefill_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
+                                    int32_t q_len, int64_t max_len, size_t* bytes) {
+  if (!bytes) return fail(TQ_ERR_INVALID_ARG, "tq_prefill_workspace_size: bytes is NULL");
+  tq_status st = check_decode_shapes(kc, vc, batch, hq, hkv, q_len, max_len, true);
   if (st != TQ_OK) return st;
-  if (!q || !k || !v || !d_len || !out) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: NULL argument");
-  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: bad q_dtype");
-  if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: scale is not finite");
+  *bytes = attention_workspace(kc, vc, batch, hq, hkv, q_len, max_len);
+  return TQ_OK;
+}
+
+static tq_status attention_impl(const char* name, bool blocks, const tq_codec* kc, const tq_codec* vc, const void* q,
+                                int32_t q_dtype, int32_t batch, int32_t hq, int32_t hkv, int32_t q_len,
+                                const tq_cache* k, const tq_cache* v, const int32_t* d_len, int64_t max_len,
+                                float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  const std::string fn(name);
+  tq_status st = check_decode_shapes(kc, vc, batch, hq, hkv, q_len, max_len, blocks);
+  if (st != TQ_OK) return st;
+  if (!q || !k || !v || !d_len || !out) return fail(TQ_ERR_INVALID_ARG, fn + ": NULL argument");
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, fn + ": bad q_dtype");
+  if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, fn + ": scale is not finite");
   std::string why;
-  if (!cache_ok(k, kc->h, &why)) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: key " + why);
-  if (!cache_ok(v, vc->h, &why)) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: value " + why);
+  if (!cache_ok(k, kc->h, &why)) return fail(TQ_ERR_INVALID_ARG, fn + ": key " + why);
+  if (!cache_ok(v, vc->h, &why)) return fail(TQ_ERR_INVALID_ARG, fn + ": value " + why);
   if (k->batch != batch || v->batch != batch || k->heads != hkv || v->heads != hkv)
-    return fail(TQ_ERR_CONFIG_MISMATCH, "tq_decode_attention: cache batch/heads differ from the call's");
-  if (k->cap != v->cap) return fail(TQ_ERR_CONFIG_MISMATCH, "tq_decode_attention: key and value caps differ");
-  if (max_len > k->cap) return fail(TQ_ERR_CAPACITY, "tq_decode_attention: max_len exceeds the cache capacity");
-  const int rows = (hq / hkv) * q_len;
+    return fail(TQ_ERR_CONFIG_MISMATCH, fn + ": cache batch/heads differ from the call's");
+  if (k->cap != v->cap) return fail(TQ_ERR_CONFIG_MISMATCH, fn + ": key and value caps differ");
+  if (max_len > k->cap) return fail(TQ_ERR_CAPACITY, fn + ": max_len exceeds the cache capacity");
+  const int64_t rows_total = (int64_t)(hq / hkv) * q_len;
+  const int rows = (int)std::min<int64_t>(rows_total, row_block(kc));  // rows per launch
   const bool prod = kc->h.mode == TQ_MODE_PROD;
-  const bool fast = use_fast(kc, vc, rows);
+  // the matrix-core kernel addresses the queries with 32-bit offsets
+  const int64_t q_bytes = (int64_t)batch * hq * q_len * kc->h.d * (q_dtype == TQ_BF16 ? 2 : 4);
+  const bool fast = use_fast(kc, vc, rows) && q_bytes < ((int64_t)1 << 32);
   const tq::DecodePlan plan = fast ? tq::plan_decode_fast(batch, hkv, rows, kc->h.d, max_len)
                                    : tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, prod);
   if (!ws || ws_bytes < plan.total)
-    return fail(TQ_ERR_WORKSPACE, "tq_decode_attention: workspace needs " + std::to_string(plan.total) + " bytes");
+    return fail(TQ_ERR_WORKSPACE, fn + ": workspace needs " + std::to_string(plan.total) + " bytes");
   tq::DevTables* kt = nullptr;
   tq::DevTables* vt = nullptr;
   st = ensure_tables(kc, &kt);
@@ -480,20 +507,40 @@ tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void
   p.part_o = reinterpret_cast<float*>(w + plan.off_part_o);
   p.part_ml = reinterpret_cast<float*>(w + plan.off_part_ml);
   p.out = out;
-  hipError_t e;
   if (fast) {
     piece_tables(kc->h, p.klut);
     piece_tables(vc->h, p.vlut);
     p.kgrid = kc->h.grid_exp;
     p.vgrid = vc->h.grid_exp;
-    e = tq::launch_decode_fast(p, static_cast<hipStream_t>(stream));
   } else {
     p.qrot = reinterpret_cast<float*>(w + plan.off_qrot);
     p.qs = prod ? reinterpret_cast<float*>(w + plan.off_qs) : nullptr;
-    e = tq::launch_decode(p, static_cast<hipStream_t>(stream));
   }
-  if (e != hipSuccess) return hip_fail(e, "tq_decode_attention launch");
+  // one launch per block of rows; the blocks reuse the workspace in stream order
+  for (int64_t r0 = 0; r0 < rows_total; r0 += rows) {
+    p.row0 = (int)r0;
+    p.rows = (int)std::min<int64_t>(rows, rows_total - r0);
+    const hipError_t e = fast ? tq::launch_decode_fast(p, static_cast<hipStream_t>(stream))
+                              : tq::launch_decode(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, (fn + " launch").c_str());
+  }
   return TQ_OK;
+}
+
+tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void* q, int32_t q_dtype, int32_t batch,
+                              int32_t hq, int32_t hkv, int32_t q_len, const tq_cache* k, const tq_cache* v,
+                              const int32_t* d_len, int64_t max_len, float scale, float* out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  return attention_impl("tq_decode_attention", false, kc, vc, q, q_dtype, batch, hq, hkv, q_len, k, v, d_len, max_len,
+                        scale, out, ws, ws_bytes, stream);
+}
+
+tq_status tq_prefill_attention(const tq_codec* kc, const tq_codec* vc, const void* q, int32_t q_dtype, int32_t batch,
+                               int32_t hq, int32_t hkv, int32_t q_len, const tq_cache* k, const tq_cache* v,
+                               const int32_t* d_len, int64_t max_len, float scale, float* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return attention_impl("tq_prefill_attention", true, kc, vc, q, q_dtype, batch, hq, hkv, q_len, k, v, d_len,
+                        max_len, scale, out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

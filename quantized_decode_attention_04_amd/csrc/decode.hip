@@ -97,7 +97,8 @@ __global__ __launch_bounds__(D) void qprep_kernel(DecodeParams p) {
   __shared__ float s_in[D], s_qr[D];
   const int r = blockIdx.x, bg = blockIdx.y;
   const int b = bg / p.hkv, g = bg % p.hkv, i = threadIdx.x;
-  const int h = g * p.group + r / p.q_len, qi = r % p.q_len;
+  const int R = p.row0 + r;  // row among the KV head's group * q_len rows
+  const int h = g * p.group + R / p.q_len, qi = R % p.q_len;
   const int64_t qoff = (((int64_t)b * p.hq + h) * p.q_len + qi) * D;
   s_in[i] = load_q(p.q, qoff + i, p.q_bf16);
   __syncthreads();
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       }
 #pragma unroll
       for (int r = 0; r < RMAX; ++r) {
-        const bool vis = tid < cnt && r < rows && tok < len - p.q_len + (r % p.q_len) + 1;
+        const bool vis = tid < cnt && r < rows && tok < len - p.q_len + ((p.row0 + r) % p.q_len) + 1;
         s_p[tid * (RMAX + 1) + r] = vis ? s[r] * sl2 : -INFINITY;
       }
     }
@@ -413,7 +414,8 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
       for (int k = 0; k < 32; ++k) res = fmaf(s_o[i0 + k], pv[k], res);
     }
   }
-  const int h = g * p.group + r / p.q_len, qi = r % p.q_len;
+  const int R = p.row0 + r;
+  const int h = g * p.group + R / p.q_len, qi = R % p.q_len;
   p.out[(((int64_t)b * p.hq + h) * p.q_len + qi) * D + j] = res;
 }
 

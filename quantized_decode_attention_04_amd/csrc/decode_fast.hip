@@ -173,7 +173,8 @@ __device__ __forceinline__ void query_loads(const DecodeParams& p, int b, int g,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, kq = lane >> 4;
   const int rr = r < p.rows ? r : 0;
-  const int hh = g * p.group + rr / p.q_len, qi = rr % p.q_len;
+  const int R = p.row0 + rr;  // row among the KV head's group * q_len rows
+  const int hh = g * p.group + R / p.q_len, qi = R % p.q_len;
   const uint32_t esize = p.q_bf16 ? 2u : 4u;
   const uint32_t q_bytes = (uint32_t)((int64_t)p.batch * p.hq * p.q_len * kD * esize);
   const uint32_t qoff = (uint32_t)(((((int64_t)b * p.hq + hh) * p.q_len + qi) * kD + 32 * kq) * esize);
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
   const int c0 = chunk_id * p.chunk;
   const int c1 = c0 + p.chunk < len ? c0 + p.chunk : len;
   const uint32_t ntok = c1 > c0 ? (uint32_t)(c1 - c0) : 0u;
-  const int lim = len - p.q_len + (n % p.q_len) + 1 - c0;  // row n sees tokens < lim
+  const int lim = len - p.q_len + ((p.row0 + n) % p.q_len) + 1 - c0;  // row n sees tokens < lim
   const int lim_all = len - p.q_len + 1 - c0;              // tokens every row sees
 
   // ---- loads: the query prologue's first, then the first two tiles
@@ -623,7 +624,8 @@ __global__ __launch_bounds__(kD) void merge_fast_kernel(DecodeParams p) {
   float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < kD; ++i) acc = fmaf(s_o[i], pv[i], acc);
-  const int h = g * p.group + r / p.q_len, qi = r % p.q_len;
+  const int R = p.row0 + r;
+  const int h = g * p.group + R / p.q_len, qi = R % p.q_len;
   p.out[(((int64_t)b * p.hq + h) * p.q_len + qi) * kD + j] = acc;
 }
 

@@ -92,7 +92,8 @@ struct DecodeParams {
   // query
   const void* q;
   int q_bf16;
-  int batch, hq, hkv, q_len, group, rows;  // rows = group * q_len
+  int batch, hq, hkv, q_len, group, rows;  // rows of this launch (<= 16)
+  int row0;  // first row of the launch among the group * q_len rows of a KV head
   int d;
   float scale;
   // key codec / cache

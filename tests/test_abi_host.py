@@ -126,6 +126,25 @@ def test_decode_shape_validation(no_gpu):
         assert e.value.status == status, args
 
 
+def test_prefill_workspace_is_one_row_block(no_gpu):
+    """Prefill takes any q_len and plans its workspace for one block of rows
+    (16 rows up to head_dim 128, 8 above), which the blocks reuse."""
+    kc = tq.tq_codec_create(128, 3, 0, tq.TQ_MODE_MSE)
+    vc = tq.tq_codec_create(128, 3, 1, tq.TQ_MODE_MSE)
+    kp = tq.tq_codec_create(256, 3, 0, tq.TQ_MODE_PROD)
+    vg = tq.tq_codec_create(256, 2, 1, tq.TQ_MODE_GROUP)
+    pre, dec = tq.tq_prefill_workspace_size, tq.tq_decode_workspace_size
+    assert pre(kc, vc, 1, 8, 1, 2, 5000) == dec(kc, vc, 1, 8, 1, 2, 5000)      # 16 rows: one block
+    assert pre(kc, vc, 1, 8, 1, 512, 5000) == dec(kc, vc, 1, 8, 1, 2, 5000)    # 4096 rows: 16-row blocks
+    assert pre(kp, vg, 1, 2, 1, 300, 5000) == dec(kp, vg, 1, 8, 1, 1, 5000)    # d 256: 8-row blocks
+    with pytest.raises(tq.TQError) as e:
+        dec(kc, vc, 1, 8, 1, 3, 5000)                                         # 24 rows: not a decode step
+    assert e.value.status == 2
+    with pytest.raises(tq.TQError) as e:
+        pre(kc, vc, 1, 8, 1, 0, 5000)
+    assert e.value.status == 1
+
+
 def _fake_cache(batch, heads, cap, mode):
     fake = 0x1000
     c = _binding._Cache(fake, fake, fake, fake, fake, fake, batch, heads, cap)
