@@ -167,6 +167,35 @@ def bulk_prefill(tq, wl, w, kc, vc, dev, stream, warmup: int, reps: int, tokens:
             "gflops": flops / (us * 1e-6) / 1e9, "bytes": in_bytes + out_bytes, "flop": flops}
 
 
+def prefill_timing(tq, wl, w, kc, vc, K, V, lens, max_len, dev, stream, reps: int, q_len: int = 64) -> dict:
+    """tq_prefill_attention of ``q_len`` new tokens per sequence over one
+    layer's cache (the rows of each KV head run in blocks of 16 through the
+    decode kernels, each block reading the layer's state once), timed with HIP
+    events on the launch stream: microseconds per call, query tokens per
+    second, and the state bytes the blocks read per second."""
+    import torch
+    q = wl.device_normal((w.batch, w.hq, q_len, w.d), 0, 0, 902, w.bf16, dev)
+    out = torch.empty((w.batch, w.hq, q_len, w.d), dtype=torch.float32, device=dev)
+    ws = tq.allocate_prefill_workspace(kc, vc, w.batch, w.hq, w.hkv, q_len, max_len, dev)
+    scale = 1.0 / math.sqrt(w.d)
+    tq.tq_prefill_attention(kc, vc, q, K, V, lens, max_len, scale, out, ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(stream)
+        tq.tq_prefill_attention(kc, vc, q, K, V, lens, max_len, scale, out, ws)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1000.0
+    rows = (w.hq // w.hkv) * q_len
+    block = 16 if w.d <= 128 else 8
+    blocks = -(-rows // block)
+    state = int(w.lens().sum()) * w.hkv * (kc.info["bytes_per_token"] + vc.info["bytes_per_token"])
+    return {"q_len": q_len, "rows_per_kv_head": rows, "row_blocks": blocks, "us": us,
+            "query_tokens_per_s": w.batch * q_len / (us * 1e-6),
+            "state_read_gbps": blocks * state / (us * 1e-6) / 1e9}
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -310,6 +339,8 @@ def main():
         ms_per_step = (t1 - t0) * 1000.0 / args.steps
 
     prefill = bulk_prefill(tq, wl, w, kc, vc, dev, stream, args.warmup, max(args.steps, 5))
+    prefill_attn = prefill_timing(tq, wl, w, kc, vc, kcs[0], vcs[0], lens, max_len, dev, stream,
+                                  max(3, args.steps // 2))
 
     tokens_per_step = float(lens_h.sum()) * layers
     value = tokens_per_step / (ms_per_step / 1000.0)
@@ -378,6 +409,7 @@ def main():
             "step_gbps_state": layer_state_bytes * layers / (ms_per_step / 1000.0) / 1e9,
             "ws_bytes": ws_bytes,
             "bulk_prefill": prefill,
+            "prefill_attention": prefill_attn,
         },
     }
     if not args.no_cpu_baseline:
