@@ -196,6 +196,36 @@ def prefill_timing(tq, wl, w, kc, vc, K, V, lens, max_len, dev, stream, reps: in
             "state_read_gbps": blocks * state / (us * 1e-6) / 1e9}
 
 
+def gather_timing(tq, w, kc, vc, K, V, dev, stream, reps: int) -> dict:
+    """tq_cache_gather of one layer's K and V records into fresh caches (the
+    first half of the sequences, or the only one), timed with HIP events on the
+    launch stream; bytes = records read + written."""
+    import torch
+    lens = [int(x) for x in w.lens()]
+    keep = list(range(max(1, w.batch // 2)))
+    cap = max(lens[i] for i in keep)
+    Kd, Vd = tq.allocate_cache(kc, len(keep), w.hkv, cap, dev), tq.allocate_cache(vc, len(keep), w.hkv, cap, dev)
+    starts, counts = [0] * len(keep), [lens[i] for i in keep]
+
+    def run():
+        tq.tq_cache_gather(kc, K, kc, Kd, keep, starts, counts)
+        tq.tq_cache_gather(vc, V, vc, Vd, keep, starts, counts)
+
+    run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1000.0
+    nbytes = 2 * sum(counts) * w.hkv * (kc.info["bytes_per_token"] + vc.info["bytes_per_token"])
+    del Kd, Vd
+    return {"sequences": len(keep), "tokens": sum(counts), "us": us, "bytes": nbytes,
+            "gbps": nbytes / (us * 1e-6) / 1e9}
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -339,6 +369,7 @@ def main():
         ms_per_step = (t1 - t0) * 1000.0 / args.steps
 
     prefill = bulk_prefill(tq, wl, w, kc, vc, dev, stream, args.warmup, max(args.steps, 5))
+    gather = gather_timing(tq, w, kc, vc, kcs[0], vcs[0], dev, stream, max(3, args.steps // 2))
     prefill_attn = prefill_timing(tq, wl, w, kc, vc, kcs[0], vcs[0], lens, max_len, dev, stream,
                                   max(3, args.steps // 2))
 
@@ -410,6 +441,7 @@ def main():
             "ws_bytes": ws_bytes,
             "bulk_prefill": prefill,
             "prefill_attention": prefill_attn,
+            "cache_gather": gather,
         },
     }
     if not args.no_cpu_baseline:

@@ -216,6 +216,30 @@ tq_status tq_prefill_attention(const tq_codec* kc, const tq_codec* vc, const voi
                                const tq_cache* v, const int32_t* d_len, int64_t max_len, float scale, float* out,
                                void* ws, size_t ws_bytes, void* stream);
 
+/* Copy token records between caches of one codec, for batch bookkeeping
+ * ([omlx] BatchTurboQuantKVCache filter, extract, extend and merge select,
+ * split off or join batch rows; merge refuses caches of different bits or
+ * seed).  For every destination sequence b < dst->batch with
+ * src_batch[b] >= 0, the records of tokens src_start[b] .. src_start[b] +
+ * count[b] - 1 of source sequence src_batch[b] (every head, every field of
+ * the codec's mode) are copied unchanged to slots 0 .. count[b] - 1 of
+ * destination sequence b; other slots, and rows with src_batch[b] < 0, are
+ * left as they are.  Lengths are the caller's (as for decode); trimming the
+ * last tokens of a sequence is a length change only.
+ *   src_codec, dst_codec  the codecs the caches were written with: head_dim,
+ *                         bits, mode and seed must agree (else
+ *                         CONFIG_MISMATCH, like [omlx] merge)
+ *   src, dst              caches with equal head counts; the copied ranges
+ *                         must not overlap (distinct allocations)
+ *   src_batch, src_start, count  host int32 arrays of dst->batch entries
+ * At most 256 destination sequences per call (UNSUPPORTED above).
+ * Errors: INVALID_ARG (NULL, index out of range, negative start or count),
+ * CONFIG_MISMATCH, CAPACITY (src_start + count > src->cap, count >
+ * dst->cap), UNSUPPORTED, HIP. */
+tq_status tq_cache_gather(const tq_codec* src_codec, const tq_cache* src, const tq_codec* dst_codec,
+                          const tq_cache* dst, const int32_t* src_batch, const int32_t* src_start,
+                          const int32_t* count, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* tq_last_error(void);
 

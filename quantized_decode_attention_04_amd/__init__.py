@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     allocate_prefill_workspace,
     allocate_workspace,
     lib_path,
+    tq_cache_gather,
     tq_codec_create,
     tq_codec_destroy,
     tq_codec_export,

@@ -66,6 +66,8 @@ def _load() -> ctypes.CDLL:
         "tq_decode_attention": (I32, [P, P, P, I32, I32, I32, I32, I32, ctypes.POINTER(_Cache),
                                       ctypes.POINTER(_Cache), P, I64, ctypes.c_float, P, P, SZ, P]),
         "tq_prefill_workspace_size": (I32, [P, P, I32, I32, I32, I32, I64, ctypes.POINTER(SZ)]),
+        "tq_cache_gather": (I32, [P, ctypes.POINTER(_Cache), P, ctypes.POINTER(_Cache), ctypes.POINTER(I32),
+                                  ctypes.POINTER(I32), ctypes.POINTER(I32), P]),
         "tq_prefill_attention": (I32, [P, P, P, I32, I32, I32, I32, I32, ctypes.POINTER(_Cache),
                                        ctypes.POINTER(_Cache), P, I64, ctypes.c_float, P, P, SZ, P]),
         "tq_last_error": (ctypes.c_char_p, []),
@@ -83,7 +85,7 @@ _lib = _load()
 EXPORTED = (
     "tq_codec_create", "tq_codec_destroy", "tq_codec_get_info", "tq_codec_export", "tq_codec_upload",
     "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_workspace_size", "tq_decode_attention",
-    "tq_prefill_workspace_size", "tq_prefill_attention", "tq_last_error", "tq_status_string",
+    "tq_prefill_workspace_size", "tq_prefill_attention", "tq_cache_gather", "tq_last_error", "tq_status_string",
 )
 
 
@@ -335,3 +337,19 @@ def tq_prefill_attention(kc: Codec, vc: Codec, q, kcache: Cache, vcache: Cache, 
     the cache and causally to each other); ws: at least
     tq_prefill_workspace_size(...) bytes (allocate_prefill_workspace)."""
     _attention(_lib.tq_prefill_attention, kc, vc, q, kcache, vcache, lens, max_len, scale, out, ws, stream)
+
+
+def tq_cache_gather(src_codec: Codec, src: Cache, dst_codec: Codec, dst: Cache, src_batch, src_start, count,
+                    stream=None) -> None:
+    """Copy token records: destination sequence b gets tokens src_start[b] ..
+    src_start[b]+count[b]-1 of source sequence src_batch[b] (skipped when
+    src_batch[b] < 0) in slots 0 .. count[b]-1.  The three lists have
+    dst.batch entries (host integers)."""
+    _on_device(*src.arrays().values(), *dst.arrays().values())
+    n = int(dst.batch)
+    if not (len(src_batch) == len(src_start) == len(count) == n):
+        raise ValueError("src_batch, src_start and count need one entry per destination sequence")
+    arr = lambda xs: (ctypes.c_int32 * n)(*[int(x) for x in xs])
+    ss, ds = src.as_struct(), dst.as_struct()
+    _check(_lib.tq_cache_gather(src_codec.handle, ctypes.byref(ss), dst_codec.handle, ctypes.byref(ds),
+                                arr(src_batch), arr(src_start), arr(count), _stream(stream)))

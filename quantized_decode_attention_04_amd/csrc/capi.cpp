@@ -543,4 +543,64 @@ tq_status tq_prefill_attention(const tq_codec* kc, const tq_codec* vc, const voi
                         max_len, scale, out, ws, ws_bytes, stream);
 }
 
+tq_status tq_cache_gather(const tq_codec* src_codec, const tq_cache* src, const tq_codec* dst_codec,
+                          const tq_cache* dst, const int32_t* src_batch, const int32_t* src_start,
+                          const int32_t* count, void* stream) {
+  if (!src_codec || !dst_codec || !src || !dst || !src_batch || !src_start || !count)
+    return fail(TQ_ERR_INVALID_ARG, "tq_cache_gather: NULL argument");
+  const tq::HostCodec& a = src_codec->h;
+  const tq::HostCodec& c = dst_codec->h;
+  if (a.d != c.d || a.bits != c.bits || a.mode != c.mode || a.seed != c.seed)
+    return fail(TQ_ERR_CONFIG_MISMATCH, "tq_cache_gather: the caches belong to codecs of different head_dim, bits, "
+                                        "mode or seed");
+  std::string why;
+  if (!cache_ok(src, a, &why)) return fail(TQ_ERR_INVALID_ARG, "tq_cache_gather: source " + why);
+  if (!cache_ok(dst, c, &why)) return fail(TQ_ERR_INVALID_ARG, "tq_cache_gather: destination " + why);
+  if (src->heads != dst->heads) return fail(TQ_ERR_CONFIG_MISMATCH, "tq_cache_gather: head counts differ");
+  if (dst->batch > tq::kMaxGatherBatch)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_cache_gather: more than " + std::to_string(tq::kMaxGatherBatch) +
+                                        " destination sequences in one call");
+  tq::CacheGather g{};
+  int64_t max_count = 0;
+  for (int b = 0; b < dst->batch; ++b) {
+    const int32_t sb = src_batch[b], s0 = src_start[b], n = count[b];
+    g.src_batch[b] = sb;
+    g.src_start[b] = s0;
+    g.count[b] = n;
+    if (sb < 0) {
+      g.src_batch[b] = -1;
+      continue;
+    }
+    if (sb >= src->batch) return fail(TQ_ERR_INVALID_ARG, "tq_cache_gather: source sequence index out of range");
+    if (s0 < 0 || n < 0) return fail(TQ_ERR_INVALID_ARG, "tq_cache_gather: negative start or count");
+    if ((int64_t)s0 + n > src->cap) return fail(TQ_ERR_CAPACITY, "tq_cache_gather: range past the source capacity");
+    if (n > dst->cap) return fail(TQ_ERR_CAPACITY, "tq_cache_gather: count above the destination capacity");
+    max_count = std::max<int64_t>(max_count, n);
+  }
+  if (max_count == 0) return TQ_OK;
+  auto field = [&](const void* s, void* d, int w) {
+    g.src[g.n_fields] = static_cast<const uint32_t*>(s);
+    g.dst[g.n_fields] = static_cast<uint32_t*>(d);
+    g.width[g.n_fields] = w;
+    ++g.n_fields;
+  };
+  field(src->idx, dst->idx, idx_words(a));
+  if (a.mode != TQ_MODE_GROUP) field(src->norm, dst->norm, 1);
+  if (a.mode == TQ_MODE_PROD) {
+    field(src->rnorm, dst->rnorm, 1);
+    field(src->sign, dst->sign, sign_words(a));
+  }
+  if (a.mode == TQ_MODE_GROUP) {
+    field(src->scale, dst->scale, group_count(a));
+    field(src->gmin, dst->gmin, group_count(a));
+  }
+  g.heads = dst->heads;
+  g.dst_batch = dst->batch;
+  g.src_cap = src->cap;
+  g.dst_cap = dst->cap;
+  const hipError_t e = tq::launch_cache_gather(g, max_count, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tq_cache_gather launch");
+  return TQ_OK;
+}
+
 }  // extern "C"

@@ -145,4 +145,23 @@ bool fast_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, in
 DecodePlan plan_decode_fast(int batch, int hkv, int rows, int d, int64_t max_len);
 hipError_t launch_decode_fast(const DecodeParams& p, hipStream_t stream);
 
+// ---- token-record copies between caches of one codec ----------------------
+
+constexpr int kMaxGatherBatch = 256;  // destination sequences per call
+constexpr int kMaxFields = 4;         // idx + norm (MSE); idx, norm, rnorm, sign (Prod); idx, scale, gmin (group)
+
+struct CacheGather {
+  const uint32_t* src[kMaxFields];
+  uint32_t* dst[kMaxFields];
+  int width[kMaxFields];  // 32-bit elements per token-head of each field
+  int n_fields;
+  int heads, dst_batch;
+  int64_t src_cap, dst_cap;
+  int32_t src_batch[kMaxGatherBatch];  // -1: destination sequence not written
+  int32_t src_start[kMaxGatherBatch];
+  int32_t count[kMaxGatherBatch];
+};
+
+hipError_t launch_cache_gather(const CacheGather& g, int64_t max_count, hipStream_t stream);
+
 }  // namespace tq

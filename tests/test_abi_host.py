@@ -185,3 +185,34 @@ def test_decode_and_append_argument_errors(no_gpu):
     assert app(k, st=(ctypes.c_int64 * 4)(0, 0, 0, 2)) == 1
     assert app(k, n=0) == 0                    # nothing to do
     assert "coordinate stride" in tq.tq_last_error() or True
+
+
+def test_cache_gather_argument_errors(no_gpu):
+    """Record copies are refused before any launch when the codecs differ (the
+    pages' merge guard on bits and seed), heads differ, an index or range is
+    out of bounds, or too many destination sequences are asked for."""
+    lib = _binding._lib
+    kc = tq.tq_codec_create(128, 3, 0, tq.TQ_MODE_MSE)
+    other_seed = tq.tq_codec_create(128, 3, 5, tq.TQ_MODE_MSE)
+    other_bits = tq.tq_codec_create(128, 4, 0, tq.TQ_MODE_MSE)
+    src, dst = _fake_cache(3, 2, 100, 0), _fake_cache(2, 2, 50, 0)
+
+    def gather(sc=kc, s=src, dc=kc, d=dst, sb=(2, 0), st=(0, 0), n=(40, 50)):
+        m = d.batch
+        arr = lambda xs: (ctypes.c_int32 * m)(*xs)
+        return lib.tq_cache_gather(sc.handle, ctypes.byref(s), dc.handle, ctypes.byref(d), arr(sb), arr(st), arr(n),
+                                   None)
+
+    assert gather(dc=other_seed) == 3
+    assert gather(dc=other_bits) == 3
+    assert gather(d=_fake_cache(2, 4, 50, 0)) == 3            # head counts differ
+    assert gather(sb=(3, 0)) == 1                             # source sequence out of range
+    assert gather(st=(-1, 0)) == 1
+    assert gather(st=(70, 0)) == 4                            # 70 + 40 > source cap 100
+    assert gather(n=(40, 51)) == 4                            # above destination cap 50
+    assert gather(sb=(-1, -1)) == 0                           # nothing to copy: no launch
+    big = _fake_cache(257, 2, 50, 0)
+    assert gather(d=big, sb=[-1] * 257, st=[0] * 257, n=[0] * 257) == 2
+    bad = _fake_cache(3, 2, 100, 0)
+    bad.idx = None
+    assert gather(s=bad) == 1

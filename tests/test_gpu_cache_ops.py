@@ -1,0 +1,123 @@
+"""Batch bookkeeping on the packed state with tq_cache_gather: filter,
+extract, extend and merge of sequences (after "omlx turboquant_kv.py",
+BatchTurboQuantKVCache) copy the token records bit for bit, leave every other
+slot alone, and decode over the result equals decode over the original rows."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from tests.gpu_util import download, to_device_f
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+import quantized_decode_attention_04_amd as tq  # noqa: E402
+from quantized_decode_attention_04_amd.workloads import round_bf16  # noqa: E402
+
+SPECS = [(128, 3, 0), (128, 3, 1), (64, 2, 2), (256, 4, 0)]  # head_dim, bits, mode
+
+
+def _filled(codec, d, B, H, cap, lens, seed):
+    rng = np.random.default_rng(seed)
+    cache = tq.allocate_cache(codec, B, H, cap)
+    x = round_bf16(rng.standard_normal((B, H, cap, d)).astype(np.float32) * np.float32(0.02))
+    tq.tq_quantize_append(codec, to_device_f(x, True), cache, torch.zeros(B, dtype=torch.int32, device="cuda"))
+    # slots past each sequence's length hold records too (written above); the
+    # lengths only say which ones are attended
+    torch.cuda.synchronize()
+    return cache
+
+
+def _sentinel(codec, B, H, cap):
+    c = tq.allocate_cache(codec, B, H, cap)
+    for a in c.arrays().values():
+        a.fill_(-7)  # 0xfffffff9 / -7.0 as int bits: any record copied over it shows
+    return c
+
+
+@pytest.mark.parametrize("d,bits,mode", SPECS, ids=[f"d{d}_b{b}_m{m}" for d, b, m in SPECS])
+def test_filter_extract_extend_merge_copy_records(d, bits, mode):
+    print(f"cache ops d={d} bits={bits} mode={mode}", flush=True)
+    sys.stdout.flush()
+    codec = tq.tq_codec_create(d, bits, 11, mode)
+    H, cap = 3, 96
+    lens = [37, 96, 5, 60]
+    src = _filled(codec, d, 4, H, cap, lens, 1)
+    S = download(src)
+
+    def check(dst, rows):
+        """rows: per destination sequence (src_seq, start, count) or None."""
+        D = download(dst)
+        for name, a in D.items():
+            ref = np.uint32(0xFFFFFFF9) if a.dtype == np.uint32 else np.float32(-7.0)  # the sentinel
+            for b, r in enumerate(rows):
+                if r is None:
+                    assert np.all(a[b] == ref), f"{name} row {b} was not to be written"
+                    continue
+                sb, s0, n = r
+                assert np.array_equal(a[b, :, :n], S[name][sb, :, s0:s0 + n]), f"{name} row {b}"
+                assert np.all(a[b, :, n:] == ref), f"{name} row {b}: slots past the copy were written"
+
+    # filter: keep sequences 3 and 1 (in that order)
+    f = _sentinel(codec, 2, H, cap)
+    tq.tq_cache_gather(codec, src, codec, f, [3, 1], [0, 0], [lens[3], lens[1]])
+    # extract: sequence 2 alone, and a window of sequence 1 (tokens 10..49)
+    e = _sentinel(codec, 1, H, 64)
+    tq.tq_cache_gather(codec, src, codec, e, [2], [0], [lens[2]])
+    w = _sentinel(codec, 1, H, 64)
+    tq.tq_cache_gather(codec, src, codec, w, [1], [10], [40])
+    # extend: a 2-sequence batch joined by the filtered one -> 4 rows
+    x = _sentinel(codec, 4, H, cap)
+    tq.tq_cache_gather(codec, src, codec, x, [0, 2, -1, -1], [0, 0, 0, 0], [lens[0], lens[2], 0, 0])
+    tq.tq_cache_gather(codec, f, codec, x, [-1, -1, 0, 1], [0, 0, 0, 0], [0, 0, lens[3], lens[1]])
+    torch.cuda.synchronize()
+    check(f, [(3, 0, lens[3]), (1, 0, lens[1])])
+    check(e, [(2, 0, lens[2])])
+    check(w, [(1, 10, 40)])
+    check(x, [(0, 0, lens[0]), (2, 0, lens[2]), (3, 0, lens[3]), (1, 0, lens[1])])
+
+    # merge: single-sequence caches into one batch (the extracted ones)
+    m = _sentinel(codec, 2, H, cap)
+    tq.tq_cache_gather(codec, e, codec, m, [0, -1], [0, 0], [lens[2], 0])
+    tq.tq_cache_gather(codec, w, codec, m, [-1, 0], [0, 0], [0, 40])
+    torch.cuda.synchronize()
+    check(m, [(2, 0, lens[2]), (1, 10, 40)])
+
+
+def test_decode_over_filtered_batch_matches_original_rows():
+    d, H, G, q_len, cap = 128, 2, 8, 2, 3000
+    kc, vc = tq.tq_codec_create(d, 3, 0, 0), tq.tq_codec_create(d, 3, 1, 0)
+    lens = [2500, 3000, 700]
+    K, V = _filled(kc, d, 3, H, cap, lens, 2), _filled(vc, d, 3, H, cap, lens, 3)
+    keep = [2, 0]
+    Kf, Vf = tq.allocate_cache(kc, 2, H, cap), tq.allocate_cache(vc, 2, H, cap)
+    for src, dst, c in ((K, Kf, kc), (V, Vf, vc)):
+        tq.tq_cache_gather(c, src, c, dst, keep, [0, 0], [lens[i] for i in keep])
+    rng = np.random.default_rng(4)
+    q = round_bf16(rng.standard_normal((3, H * G, q_len, d)).astype(np.float32) * np.float32(0.02))
+    scale = 1 / math.sqrt(d)
+
+    def run(Kc, Vc, qq, ll):
+        B = qq.shape[0]
+        out = torch.zeros((B, H * G, q_len, d), dtype=torch.float32, device="cuda")
+        ws = tq.allocate_workspace(kc, vc, B, H * G, H, q_len, max(ll))
+        tq.tq_decode_attention(kc, vc, to_device_f(qq, True), Kc, Vc,
+                               torch.tensor(ll, dtype=torch.int32, device="cuda"), max(ll), scale, out, ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64)
+
+    full = run(K, V, q, lens)
+    part = run(Kf, Vf, q[keep], [lens[i] for i in keep])
+    err = np.abs(part - full[keep]).max() / np.abs(full[keep]).max()
+    print(f"  filtered decode vs original rows: max rel diff {err:.2e}", flush=True)
+    assert err < 1e-5   # the split over the token axis differs with the batch, so the sums round differently
