@@ -143,6 +143,34 @@ static int device_cus() {
   return cached[dev];
 }
 
+DecodePlan plan_decode_mfma(int batch, int hkv, int rows, int d, int64_t max_len, bool prod) {
+  DecodePlan p{};
+  p.rows = rows;
+  const int64_t step = 256;  // four waves x 64-token tiles
+  const int64_t heads = (int64_t)batch * hkv;
+  // about two workgroups per compute unit; every wave writes a partial and
+  // the merge takes at most 4096 of them per row
+  const int64_t per_head = std::max<int64_t>(1, (2 * device_cus() + heads - 1) / heads);
+  int64_t chunk = (max_len + per_head - 1) / per_head;
+  chunk = std::max<int64_t>(step, ((chunk + step - 1) / step) * step);
+  chunk = std::max<int64_t>(chunk, ((max_len + 1023) / 1024 + step - 1) / step * step);  // <= 1024 chunks
+  p.chunk = (int)chunk;
+  p.n_chunks = (int)((max_len + chunk - 1) / chunk);
+  const size_t bg = (size_t)batch * hkv;
+  const size_t parts = (size_t)p.n_chunks * 4;
+  size_t off = 0;
+  p.off_qrot = off;
+  off = align256(off + bg * rows * d * sizeof(float));
+  p.off_qs = off;
+  if (prod) off = align256(off + bg * rows * d * sizeof(float));
+  p.off_part_o = off;
+  off = align256(off + bg * parts * rows * d * sizeof(float));
+  p.off_part_ml = off;
+  off = align256(off + bg * parts * rows * 2 * sizeof(float));
+  p.total = off;
+  return p;
+}
+
 DecodePlan plan_decode_fast(int batch, int hkv, int rows, int d, int64_t max_len) {
   DecodePlan p{};
   p.rows = rows;
@@ -185,6 +213,11 @@ void piece_tables(const tq::HostCodec& h, uint32_t* lut) {
 
 bool use_fast(const tq_codec* kc, const tq_codec* vc, int rows) {
   return tq::fast_decode_supported(kc->h.d, kc->h.mode, kc->h.mse_bits, vc->h.mode, vc->h.mse_bits, rows);
+}
+
+bool use_mfma(const tq_codec* kc, const tq_codec* vc, int rows) {
+  return !use_fast(kc, vc, rows) &&
+         tq::mfma_decode_preferred(kc->h.d, kc->h.mode, kc->h.mse_bits, vc->h.mode, vc->h.mse_bits, rows);
 }
 
 }  // namespace
@@ -409,8 +442,10 @@ static tq_status check_decode_shapes(const tq_codec* kc, const tq_codec* vc, int
 static size_t attention_workspace(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
                                   int32_t q_len, int64_t max_len) {
   const int rows = (int)std::min<int64_t>((int64_t)(hq / hkv) * q_len, row_block(kc));
-  return use_fast(kc, vc, rows) ? tq::plan_decode_fast(batch, hkv, rows, kc->h.d, max_len).total
-                                : tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, kc->h.mode == TQ_MODE_PROD).total;
+  const bool prod = kc->h.mode == TQ_MODE_PROD;
+  if (use_fast(kc, vc, rows)) return tq::plan_decode_fast(batch, hkv, rows, kc->h.d, max_len).total;
+  if (use_mfma(kc, vc, rows)) return tq::plan_decode_mfma(batch, hkv, rows, kc->h.d, max_len, prod).total;
+  return tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, prod).total;
 }
 
 tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
@@ -454,8 +489,10 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
   // the matrix-core kernel addresses the queries with 32-bit offsets
   const int64_t q_bytes = (int64_t)batch * hq * q_len * kc->h.d * (q_dtype == TQ_BF16 ? 2 : 4);
   const bool fast = use_fast(kc, vc, rows) && q_bytes < ((int64_t)1 << 32);
+  const bool mfma = !fast && use_mfma(kc, vc, rows);
   const tq::DecodePlan plan = fast ? tq::plan_decode_fast(batch, hkv, rows, kc->h.d, max_len)
-                                   : tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, prod);
+                              : mfma ? tq::plan_decode_mfma(batch, hkv, rows, kc->h.d, max_len, prod)
+                                     : tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, prod);
   if (!ws || ws_bytes < plan.total)
     return fail(TQ_ERR_WORKSPACE, fn + ": workspace needs " + std::to_string(plan.total) + " bytes");
   tq::DevTables* kt = nullptr;
@@ -520,8 +557,9 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
   for (int64_t r0 = 0; r0 < rows_total; r0 += rows) {
     p.row0 = (int)r0;
     p.rows = (int)std::min<int64_t>(rows, rows_total - r0);
-    const hipError_t e = fast ? tq::launch_decode_fast(p, static_cast<hipStream_t>(stream))
-                              : tq::launch_decode(p, static_cast<hipStream_t>(stream));
+    const hipError_t e = fast   ? tq::launch_decode_fast(p, static_cast<hipStream_t>(stream))
+                         : mfma ? tq::launch_decode_mfma(p, static_cast<hipStream_t>(stream))
+                                : tq::launch_decode(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, (fn + " launch").c_str());
   }
   return TQ_OK;

@@ -438,6 +438,25 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_qprep(const DecodeParams& p, hipStream_t stream) {
+  switch (p.d) {
+    case 128: qprep_kernel<128><<<dim3(p.rows, p.batch * p.hkv), dim3(128), 0, stream>>>(p); break;
+    case 256: qprep_kernel<256><<<dim3(p.rows, p.batch * p.hkv), dim3(256), 0, stream>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
+  if (p.n_chunks > kMaxMergeChunks) return hipErrorInvalidValue;
+  switch (p.d) {
+    case 128: merge_kernel<128><<<dim3(p.rows, p.hkv, p.batch), dim3(128), 0, stream>>>(p); break;
+    case 256: merge_kernel<256><<<dim3(p.rows, p.hkv, p.batch), dim3(256), 0, stream>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.n_chunks > kMaxMergeChunks || p.hkv > 65535 || p.batch > 65535 || p.rows > 16) return hipErrorInvalidValue;
   switch (p.d) {

@@ -1,0 +1,314 @@
+// Decode attention over the compressed cache on the fp32 matrix cores, for
+// the codec modes the int8 kernel does not cover: Prod keys (the QJL term
+// included), 1/2/4-bit MSE values, group values.  Taken at head_dim 128 when
+// a launch has more than 8 query rows per KV head (prefill blocks,
+// multi-token decode), where it halves the general kernel's time.
+//
+// What is computed is the general kernel's ("turboquant validate_moe_phase2.py",
+// Tests 1 and 5; "omlx turboquant_kv.py", make_mask):
+//     s_t = scale * ( n_t <q_rot, c_k[idx_t]> + gamma_t sqrt(pi/2)/d <S q_rot, sigma_t> )
+//     o_rot = sum_t p_t n^v_t c_v[idx^v_t]   (MSE values; out = Pi_v^T o_rot / l)
+//     o     = sum_t p_t (q_t s_g + mn_g)     (group values)
+// with both products on v_mfma_f32_16x16x4f32 over dequantised operands, so
+// the accumulation is plain fp32:
+//
+//   scores  S[token][row] = sum_j A[token][j] Q[j][row], A = n c[idx] (and,
+//           for Prod keys, gamma sqrt(pi/2)/d sigma against S q_rot, in the
+//           same accumulator).  The contraction index is permuted: in k-step
+//           s lane l supplies coordinate j = (l/16) (D/4) + s, so each lane
+//           decodes one contiguous run of its token's packed words.
+//   values  O^T[slot][row] = sum_t V[t][coord(slot)] P[row][t]: the k-step s
+//           of token group tg takes token 16 tg + 4 (l/16) + s from lane l,
+//           which is exactly a score the lane holds, so the probabilities
+//           never move between lanes; lane l%16 = m owns the coordinates
+//           m (D/16) .. m (D/16) + D/16 - 1, one contiguous bit run of the
+//           token's packed value words.
+//
+// One 256-thread workgroup per (chunk, KV head, sequence); wave w takes the
+// 64-token tiles w, w+4, ... of the chunk with its own online softmax and
+// writes its own partial (m, l, o) (4 per chunk), merged by the general
+// path's merge kernel.  The query rows (rotated by the general path's qprep
+// kernel) sit in LDS.
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kTile = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kFlushGap = 8.f;  // log2 headroom of the lazy softmax reference
+
+__device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// maximum over the four 16-lane groups (lanes n, n+16, n+32, n+48)
+__device__ __forceinline__ float rowmax4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+// Index of coordinate r (0..31) of a 32-coordinate group with words w[0..B-1]
+// (LSB-first for 1, 2, 4 bits; byte lanes X, Y, Z for 3 bits).
+template <int B>
+__device__ __forceinline__ uint32_t group_code(const uint32_t* w, int r) {
+  if constexpr (B == 3) {
+    const int a = r >> 2, s = 8 * (r & 3);
+    switch (a) {
+      case 0: return (w[0] >> s) & 7u;
+      case 1: return (w[0] >> (s + 3)) & 7u;
+      case 2: return ((w[0] >> (s + 6)) & 3u) | (((w[2] >> (s + 6)) & 1u) << 2);
+      case 3: return (w[1] >> s) & 7u;
+      case 4: return (w[1] >> (s + 3)) & 7u;
+      case 5: return ((w[1] >> (s + 6)) & 3u) | (((w[2] >> (s + 7)) & 1u) << 2);
+      case 6: return (w[2] >> s) & 7u;
+      default: return (w[2] >> (s + 3)) & 7u;
+    }
+  } else {
+    const int bit = r * B;
+    return (w[bit >> 5] >> (bit & 31)) & ((1u << B) - 1u);
+  }
+}
+
+template <int D, int KB, int VB>
+__global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(DecodeParams p) {
+  constexpr int KS = D / 4;          // contraction terms per lane (k-steps)
+  constexpr int KG = KS / 32;        // 32-coordinate groups in a lane's key slice
+  constexpr int KW = KB * KG;        // index words of the slice
+  constexpr int NU = D / 16;         // value coordinate tiles = coordinates per lane run
+  constexpr int VRB = NU * VB;       // bits of a lane's value run (8..64)
+  constexpr int VW = (VRB + 31) / 32;
+  constexpr int QSTR = D + 4;        // LDS row stride of the query tables
+  static_assert(KG >= 1 && VRB % 8 == 0, "head_dim 128 or 256");
+  __shared__ __attribute__((aligned(16))) float s_q[16 * QSTR];
+  __shared__ __attribute__((aligned(16))) float s_qs[16 * QSTR];
+  __shared__ float s_kc[16], s_vc[16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15, g = lane >> 4;  // token slot / query row, lane group
+  const int chunk_id = blockIdx.x, gh = blockIdx.y, b = blockIdx.z;
+  const int bg = b * p.hkv + gh;
+  const int rows = p.rows;
+  const bool prod = p.kmode == TQ_MODE_PROD;
+  const bool vgroup = p.vmode == TQ_MODE_GROUP;
+  int64_t len64 = p.len[b];
+  len64 = len64 < 0 ? 0 : (len64 > p.cap ? p.cap : len64);
+  const int len = (int)len64;
+  const int c0 = chunk_id * p.chunk;
+  const int ntok = (c0 + p.chunk < len ? c0 + p.chunk : len) - c0;  // may be <= 0
+  const int lim = len - p.q_len + ((p.row0 + m) % p.q_len) + 1 - c0;  // row m sees tokens < lim
+
+  for (int e = threadIdx.x; e < 16 * D; e += kWaves * 64) {
+    const int r = e / D, j = e % D;
+    const size_t src = ((size_t)bg * rows + r) * D + j;
+    s_q[r * QSTR + j] = r < rows ? p.qrot[src] : 0.f;
+    s_qs[r * QSTR + j] = (prod && r < rows) ? p.qs[src] : 0.f;
+  }
+  if (threadIdx.x < 16) {
+    const int t = threadIdx.x;
+    s_kc[t] = t < (1 << p.kbits) ? p.k_cent[t] : 0.f;
+    s_vc[t] = (!vgroup && t < (1 << p.vbits)) ? p.v_cent[t] : 0.f;
+  }
+  __syncthreads();
+
+  const float sl2 = p.scale * kLog2e;
+  const float qjl = kQjlConstNumer / (float)D;
+  const size_t base = (size_t)bg * (size_t)p.cap + (size_t)c0;  // slot of token 0 of the chunk
+  float m_ref = -1e30f, l_run = 0.f;
+  v4f acc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int T0 = wave * kTile; T0 < ntok; T0 += kWaves * kTile) {
+    // ---- key operands: token T0 + 16 tg + m, coordinates g*KS .. g*KS + KS - 1
+    uint32_t kw[4][KW], ksw[4][KG];
+    float kn[4], kq[4];
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+      const int tok = T0 + 16 * tg + m;
+      const bool ok = tok < ntok;
+      const size_t slot = base + (ok ? tok : 0);
+#pragma unroll
+      for (int w = 0; w < KW; ++w) kw[tg][w] = ok ? p.k_idx[slot * p.kwords + g * KW + w] : 0u;
+#pragma unroll
+      for (int w = 0; w < KG; ++w) ksw[tg][w] = (ok && prod) ? p.k_sign[slot * p.ksign_words + g * KG + w] : 0u;
+      kn[tg] = ok ? p.k_norm[slot] : 0.f;
+      kq[tg] = (ok && prod) ? p.k_rnorm[slot] * qjl : 0.f;
+    }
+    // ---- scores: sacc[tg][i] = score of token T0 + 16 tg + 4 g + i for row m
+    v4f sacc[4];
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) sacc[tg] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t4 = 0; t4 < KS / 4; ++t4) {
+      const v4f qv = *reinterpret_cast<const v4f*>(&s_q[m * QSTR + g * KS + 4 * t4]);
+      const v4f qsv = *reinterpret_cast<const v4f*>(&s_qs[m * QSTR + g * KS + 4 * t4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = 4 * t4 + e;
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg) {
+          const uint32_t code = group_code<KB>(&kw[tg][KB * (s >> 5)], s & 31);
+          sacc[tg] = mfma4(kn[tg] * s_kc[code], qv[e], sacc[tg]);
+          if (prod) {
+            const bool bit = (ksw[tg][s >> 5] >> (s & 31)) & 1u;
+            sacc[tg] = mfma4(bit ? kq[tg] : -kq[tg], qsv[e], sacc[tg]);
+          }
+        }
+      }
+    }
+
+    // ---- online softmax of row m over this lane's 16 tokens
+    float sc[16];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = T0 + 16 * tg + 4 * g + i;
+        const float v = (tok < ntok && tok < lim) ? sacc[tg][i] * sl2 : -INFINITY;
+        sc[4 * tg + i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = rowmax4(tmax);
+    if (__ballot(tmax > m_ref + kFlushGap) != 0) {
+      const float m_new = fmaxf(m_ref, tmax);
+      const float alpha = exp2f(m_ref - m_new);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) acc[u] *= alpha;
+      l_run *= alpha;
+      m_ref = m_new;
+    }
+    // value norms (MSE values) of the lane's tokens: four consecutive ones per group
+    float pv[16];
+    float psum = 0.f;
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+      const int t0 = T0 + 16 * tg + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pr = exp2f(sc[4 * tg + i] - m_ref);
+        psum += pr;
+        const float nv = (vgroup || t0 + i >= ntok) ? 1.f : p.v_norm[base + t0 + i];
+        pv[4 * tg + i] = pr * nv;
+      }
+    }
+    l_run += psum;
+
+    // ---- values: token 16 tg + 4 g + s, coordinates m*NU .. m*NU + NU - 1
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int tok = T0 + 16 * tg + 4 * g + s;
+        const bool ok = tok < ntok;
+        const size_t slot = base + (ok ? tok : 0);
+        const int bit0 = m * VRB;
+        uint32_t run[VW];
+#pragma unroll
+        for (int w = 0; w < VW; ++w) run[w] = ok ? p.v_idx[slot * p.vwords + (bit0 >> 5) + w] : 0u;
+        float gs = 0.f, gm = 0.f;
+        if (vgroup) {
+          const int grp = (m * NU) >> 5;
+          gs = ok ? p.v_scale[slot * p.vgroups + grp] : 0.f;
+          gm = ok ? p.v_gmin[slot * p.vgroups + grp] : 0.f;
+        }
+        const int sh = bit0 & 31;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int bit = u * VB;  // within the run
+          uint32_t code;
+          if constexpr (VW == 1) {
+            code = (run[0] >> (sh + bit)) & ((1u << VB) - 1u);
+          } else {
+            code = (run[bit >> 5] >> (bit & 31)) & ((1u << VB) - 1u);
+          }
+          const float a = vgroup ? fmaf((float)code, gs, gm) : s_vc[code];
+          acc[u] = mfma4(a, pv[4 * tg + s], acc[u]);
+        }
+      }
+    }
+  }
+
+  // ---- this wave's partial: o[row m][coord (4g + i) NU + u], m and l of row m
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  const int part = chunk_id * kWaves + wave;
+  const int n_parts = gridDim.x * kWaves;
+  if (m < rows) {
+    float* po = p.part_o + (((size_t)bg * n_parts + part) * rows + m) * D;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) po[(4 * g + i) * NU + u] = acc[u][i];
+    if (g == 0) {
+      float* pml = p.part_ml + (((size_t)bg * n_parts + part) * rows + m) * 2;
+      pml[0] = m_ref;
+      pml[1] = l_run;
+    }
+  }
+}
+
+template <int D, int KB>
+hipError_t launch_kb(const DecodeParams& p, const dim3 grid, hipStream_t stream) {
+  if (p.vbits == 2) {
+    decode_mfma_kernel<D, KB, 2><<<grid, dim3(kWaves * 64), 0, stream>>>(p);
+  } else if (p.vbits == 4) {
+    decode_mfma_kernel<D, KB, 4><<<grid, dim3(kWaves * 64), 0, stream>>>(p);
+  } else if (p.vbits == 1 && p.vmode == TQ_MODE_MSE) {
+    decode_mfma_kernel<D, KB, 1><<<grid, dim3(kWaves * 64), 0, stream>>>(p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dd(const DecodeParams& p, const dim3 grid, hipStream_t stream) {
+  switch (p.kbits) {
+    case 1: return launch_kb<D, 1>(p, grid, stream);
+    case 2: return launch_kb<D, 2>(p, grid, stream);
+    case 3: return launch_kb<D, 3>(p, grid, stream);
+    case 4: return launch_kb<D, 4>(p, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool mfma_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
+  const bool kok = (kmode == TQ_MODE_MSE || kmode == TQ_MODE_PROD) && kbits >= 1 && kbits <= 4;
+  const bool vok = (vmode == TQ_MODE_MSE && (vbits == 1 || vbits == 2 || vbits == 4)) ||
+                   (vmode == TQ_MODE_GROUP && (vbits == 2 || vbits == 4));
+  return (d == 128 || d == 256) && kok && vok && rows >= 1 && rows <= 16;
+}
+
+// Measured on MI355X: at head_dim 128 with more than 8 rows (prefill blocks,
+// multi-token decode) this kernel takes half the general kernel's time (whose
+// work grows with the rows); at 8 rows or fewer, and at head_dim 256, the
+// general kernel is as fast or faster.
+bool mfma_decode_preferred(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
+  return d == 128 && rows > 8 && mfma_decode_supported(d, kmode, kbits, vmode, vbits, rows);
+}
+
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
+  if (!mfma_decode_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits, p.rows) || p.hkv > 65535 ||
+      p.batch > 65535 || p.n_chunks < 1 || (int64_t)p.n_chunks * kWaves > 4096 || p.chunk % (kWaves * kTile))
+    return hipErrorInvalidValue;
+  hipError_t e = launch_qprep(p, stream);
+  if (e != hipSuccess) return e;
+  const dim3 grid(p.n_chunks, p.hkv, p.batch);
+  e = p.d == 128 ? launch_dd<128>(p, grid, stream) : launch_dd<256>(p, grid, stream);
+  if (e != hipSuccess) return e;
+  DecodeParams pm = p;
+  pm.n_chunks = p.n_chunks * kWaves;  // one partial per wave
+  return launch_merge(pm, stream);
+}
+
+}  // namespace tq

@@ -139,6 +139,20 @@ struct DecodePlan {
 DecodePlan plan_decode(int batch, int hkv, int rows, int d, int64_t max_len, bool prod);
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+// The general path's query rotation (qrot, qs) and cross-chunk merge, also
+// used by the fp32 matrix-core kernel (head_dim 128 and 256).
+hipError_t launch_qprep(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_merge(const DecodeParams& p, hipStream_t stream);
+
+// fp32 matrix-core decode for the modes the int8 kernel does not cover:
+// head_dim 128/256, MSE or Prod keys of 1-4 index bits, MSE values of 1, 2
+// or 4 bits or group values of 2 or 4 bits, up to 16 rows.  The plan splits
+// each sequence's tokens into chunks; every wave of a workgroup writes its own
+// partial, so the merge sees 4 partials per chunk.
+bool mfma_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows);
+bool mfma_decode_preferred(int d, int kmode, int kbits, int vmode, int vbits, int rows);
+DecodePlan plan_decode_mfma(int batch, int hkv, int rows, int d, int64_t max_len, bool prod);
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 
 // MFMA decode path: which shapes it covers, its plan and its launcher.
 bool fast_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows);

@@ -205,12 +205,18 @@ DEC_CASES = [
     ("fast_rows4", 128, (3, 0), (3, 0), 2, 2, 4, 2, [777, 1500], 1600, False, False),
     ("fast_sharp_softmax", 128, (3, 0), (3, 0), 1, 2, 16, 1, [3000], 3000, False, False),
     ("fast_growing_value_norms", 128, (3, 0), (3, 0), 1, 2, 32, 1, [4100], 4100, True, False),
+    # fp32 matrix-core path (head_dim 128, more than 8 rows): 3-bit byte-lane keys with
+    # 2-bit values (16 rows); 1-bit Prod keys (2 bits) with 4-bit group values (12 rows)
+    ("mfma_mse3_mse2", 128, (3, 0), (2, 0), 1, 2, 16, 2, [1500], 1600, True, False),
+    ("mfma_prod2_group4", 128, (2, 1), (4, 2), 1, 2, 8, 3, [777], 800, True, False),
+    # general path at head_dim 256: 4-bit keys, 1-bit values
+    ("d256_mse4_mse1", 256, (4, 0), (1, 0), 2, 1, 4, 2, [900, 40], 1000, False, False),
 ]
 
 # query scale per case (default 0.02, like the keys); larger scales make the
 # softmax sharp and stress the score precision
 Q_STD = {"fast_sharp_softmax": 200.0, "d32_mse1_mse2": 1.0, "d96_mse4_group3_q3": 1.0,
-         "d224_prod5_group4": 1.0, "d192_prod2_mse1": 1.0}
+         "d224_prod5_group4": 1.0, "d192_prod2_mse1": 1.0, "mfma_mse3_mse2": 20.0, "d256_mse4_mse1": 1.0}
 
 
 def _oracle_states(name, d, kspec, vspec, B, Hkv, N, bf16, outliers, seed=0):
