@@ -1,0 +1,110 @@
+"""Randomised GPU parity: each case draws a codec pair (head_dim 32..256, MSE or
+Prod keys of every width, MSE or group values), a batch with ragged lengths,
+a GQA group and q_len (prefill above the decode row limit), an input dtype and
+a query scale (up to sharp softmaxes), then checks
+* quantise-on-append in two appends (every kernel by size) against the oracle:
+  codes bit-exact outside the decision window, norms to 1e-6 relative;
+* decode / prefill of the oracle's state against the oracle's decode: relative
+  L2 per row <= 1e-4.
+Cases are seeded: a failing one is reproduced by its id."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import attention as oatt
+from oracle import codec as ocodec
+from oracle import packing
+from oracle import quant as oquant
+from tests.gpu_util import WINDOW, download, rel_l2_rows, to_device_f, upload_state
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+import quantized_decode_attention_04_amd as tq  # noqa: E402
+from quantized_decode_attention_04_amd.workloads import round_bf16  # noqa: E402
+
+
+def _draw(seed):
+    rng = np.random.default_rng(seed)
+    d = int(rng.choice([32, 64, 96, 128, 128, 128, 160, 192, 224, 256, 256]))
+    kmode = int(rng.choice([0, 1]))
+    kbits = int(rng.integers(1, 5)) if kmode == 0 else int(rng.integers(2, 6))
+    vmode = int(rng.choice([0, 0, 2]))
+    vbits = int(rng.integers(1, 5)) if vmode == 0 else int(rng.integers(2, 5))
+    if rng.random() < 0.25:
+        kmode, kbits, vmode, vbits, d = 0, 3, 0, 3, 128   # the int8 matrix-core path
+    return rng, dict(d=d, kmode=kmode, kbits=kbits, vmode=vmode, vbits=vbits,
+                     Hkv=int(rng.choice([1, 2, 3])), G=int(rng.choice([1, 2, 4, 8])),
+                     q_len=int(rng.choice([1, 2, 3, 5])), B=int(rng.choice([1, 2, 3])))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_case(seed):
+    rng, c = _draw(1000 + seed)
+    d, B, Hkv, G, q_len = c["d"], c["B"], c["Hkv"], c["G"], c["q_len"]
+    lens = [int(x) for x in rng.integers(1, 1500, B)]
+    N = max(lens)
+    cap = N + int(rng.integers(0, 50))
+    bf16 = bool(rng.random() < 0.6)
+    qstd = float(rng.choice([0.02, 0.5, 5.0, 50.0]))
+    print(f"random case {seed}: {c} lens={lens} bf16={bf16} qstd={qstd}", flush=True)
+    sys.stdout.flush()
+    kc = ocodec.make_codec(d, c["kbits"], 0, c["kmode"])
+    vc = ocodec.make_codec(d, c["vbits"], 1, c["vmode"])
+    gk = tq.tq_codec_create(d, c["kbits"], 0, c["kmode"])
+    gv = tq.tq_codec_create(d, c["vbits"], 1, c["vmode"])
+    k = rng.standard_normal((B, Hkv, N, d)).astype(np.float32) * np.float32(0.02)
+    v = rng.standard_normal((B, Hkv, N, d)).astype(np.float32) * np.float32(0.02)
+    q = rng.standard_normal((B, Hkv * G, q_len, d)).astype(np.float32) * np.float32(qstd)
+    if bf16:
+        k, v, q = round_bf16(k), round_bf16(v), round_bf16(q)
+    ks, vs = oquant.quantize(k.astype(np.float64), kc), oquant.quantize(v.astype(np.float64), vc)
+
+    K, V = tq.allocate_cache(gk, B, Hkv, cap), tq.allocate_cache(gv, B, Hkv, cap)
+    split = int(rng.integers(1, N + 1))
+    for s0, s1 in ((0, split), (split, N)):
+        if s1 > s0:
+            pos = torch.full((B,), s0, dtype=torch.int32, device="cuda")
+            tq.tq_quantize_append_kv(gk, gv, to_device_f(np.ascontiguousarray(k[:, :, s0:s1]), bf16),
+                                     to_device_f(np.ascontiguousarray(v[:, :, s0:s1]), bf16), K, V, pos)
+    torch.cuda.synchronize()
+    for cache, st, oc, name in ((K, ks, kc, "keys"), (V, vs, vc, "values")):
+        got = download(cache)
+        if oc.mode == 2:
+            codes = packing.unpack(got["idx"][:, :, :N], oc.bits, d)
+            win = st["margin"] < WINDOW * ((1 << oc.bits) - 1)
+            assert not ((codes != st["q"]) & ~win).any(), f"{name}: group codes differ outside the window"
+        else:
+            idx = packing.unpack(got["idx"][:, :, :N], oc.mse_bits, d)
+            win = st["margin"] < WINDOW
+            assert not ((idx != st["idx"]) & ~win).any(), f"{name}: indices differ outside the window"
+            np.testing.assert_allclose(got["norm"][:, :, :N], st["norm"], rtol=1e-6, atol=0)
+
+    K2, V2 = tq.allocate_cache(gk, B, Hkv, cap), tq.allocate_cache(gv, B, Hkv, cap)
+    upload_state(K2, ks, c["kmode"], N)
+    upload_state(V2, vs, c["vmode"], N)
+    out = torch.zeros((B, Hkv * G, q_len, d), dtype=torch.float32, device="cuda")
+    ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    scale = 1 / math.sqrt(d)
+    if G * q_len <= (16 if d <= 128 else 8):
+        ws = tq.allocate_workspace(gk, gv, B, Hkv * G, Hkv, q_len, N)
+        tq.tq_decode_attention(gk, gv, to_device_f(q, bf16), K2, V2, ld, N, scale, out, ws)
+    else:
+        ws = tq.allocate_prefill_workspace(gk, gv, B, Hkv * G, Hkv, q_len, N)
+        tq.tq_prefill_attention(gk, gv, to_device_f(q, bf16), K2, V2, ld, N, scale, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    want = oatt.decode_attention_rotated(q.astype(np.float64), ks, kc, vs, vc, np.array(lens), scale)
+    err = rel_l2_rows(got, want).max()
+    print(f"  max row rel L2 {err:.2e}", flush=True)
+    assert err <= 1e-4
