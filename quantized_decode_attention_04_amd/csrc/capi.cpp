@@ -108,7 +108,9 @@ DecodePlan plan_decode(int batch, int hkv, int rows, int d, int64_t max_len, boo
   DecodePlan p{};
   p.rows = rows;
   const int64_t tile = 256;
-  const int64_t target_items = 1024;
+  // about two 256-token tiles per workgroup: measured 6-7% faster than one
+  // (the query prologue is amortised) and than four (fewer workgroups)
+  const int64_t target_items = 512;
   const int64_t total = (int64_t)batch * hkv * max_len;
   int64_t chunk = (total + target_items - 1) / target_items;
   chunk = ((chunk + tile - 1) / tile) * tile;
