@@ -392,12 +392,12 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   for (int w = 0; w < NW; ++w) L += s_red[NW + w];
   float o = 0.f;
   int c = 0;
-  for (; c + 8 <= nch; c += 8) {
-    float v[8];
+  for (; c + 16 <= nch; c += 16) {  // sixteen loads in flight per thread
+    float v[16];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = po[((size_t)(c + k) * rows + r) * D + j];
+    for (int k = 0; k < 16; ++k) v[k] = po[((size_t)(c + k) * rows + r) * D + j];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) o = fmaf(s_w[c + k], v[k], o);
+    for (int k = 0; k < 16; ++k) o = fmaf(s_w[c + k], v[k], o);
   }
   for (; c < nch; ++c) o = fmaf(s_w[c], po[((size_t)c * rows + r) * D + j], o);
   o = L > 0.f ? o / L : 0.f;

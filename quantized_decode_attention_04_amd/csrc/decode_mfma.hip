@@ -45,6 +45,13 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// A value loaded from a valid address (the callers clamp it), or zero: the
+// load is unconditional so that the loads of a tile issue back to back.
+template <class T>
+__device__ __forceinline__ T pick(T v, bool ok) {
+  return ok ? v : T(0);
+}
+
 // maximum over the four 16-lane groups (lanes n, n+16, n+32, n+48)
 __device__ __forceinline__ float rowmax4(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -135,11 +142,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(DecodeParams p
       const bool ok = tok < ntok;
       const size_t slot = base + (ok ? tok : 0);
 #pragma unroll
-      for (int w = 0; w < KW; ++w) kw[tg][w] = ok ? p.k_idx[slot * p.kwords + g * KW + w] : 0u;
+      for (int w = 0; w < KW; ++w) kw[tg][w] = pick(p.k_idx[slot * p.kwords + g * KW + w], ok);
 #pragma unroll
-      for (int w = 0; w < KG; ++w) ksw[tg][w] = (ok && prod) ? p.k_sign[slot * p.ksign_words + g * KG + w] : 0u;
-      kn[tg] = ok ? p.k_norm[slot] : 0.f;
-      kq[tg] = (ok && prod) ? p.k_rnorm[slot] * qjl : 0.f;
+      for (int w = 0; w < KG; ++w) ksw[tg][w] = prod ? pick(p.k_sign[slot * p.ksign_words + g * KG + w], ok) : 0u;
+      kn[tg] = pick(p.k_norm[slot], ok);
+      kq[tg] = prod ? pick(p.k_rnorm[slot], ok) * qjl : 0.f;
     }
     // ---- scores: sacc[tg][i] = score of token T0 + 16 tg + 4 g + i for row m
     v4f sacc[4];
@@ -195,7 +202,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(DecodeParams p
       for (int i = 0; i < 4; ++i) {
         const float pr = exp2f(sc[4 * tg + i] - m_ref);
         psum += pr;
-        const float nv = (vgroup || t0 + i >= ntok) ? 1.f : p.v_norm[base + t0 + i];
+        const bool ok = t0 + i < ntok;
+        float nv = 1.f;
+        if (!vgroup) {
+          const float x = p.v_norm[base + (ok ? t0 + i : 0)];
+          nv = ok ? x : 1.f;
+        }
         pv[4 * tg + i] = pr * nv;
       }
     }
@@ -212,12 +224,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(DecodeParams p
         const int bit0 = m * VRB;
         uint32_t run[VW];
 #pragma unroll
-        for (int w = 0; w < VW; ++w) run[w] = ok ? p.v_idx[slot * p.vwords + (bit0 >> 5) + w] : 0u;
+        for (int w = 0; w < VW; ++w) run[w] = pick(p.v_idx[slot * p.vwords + (bit0 >> 5) + w], ok);
         float gs = 0.f, gm = 0.f;
         if (vgroup) {
           const int grp = (m * NU) >> 5;
-          gs = ok ? p.v_scale[slot * p.vgroups + grp] : 0.f;
-          gm = ok ? p.v_gmin[slot * p.vgroups + grp] : 0.f;
+          gs = pick(p.v_scale[slot * p.vgroups + grp], ok);
+          gm = pick(p.v_gmin[slot * p.vgroups + grp], ok);
         }
         const int sh = bit0 & 31;
 #pragma unroll
@@ -294,7 +306,8 @@ bool mfma_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, in
 // work grows with the rows); at 8 rows or fewer, and at head_dim 256, the
 // general kernel is as fast or faster.
 bool mfma_decode_preferred(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
-  return d == 128 && rows > 8 && mfma_decode_supported(d, kmode, kbits, vmode, vbits, rows);
+  return d == 128 && (rows > 8 || bf16_decode_supported(d, kmode, kbits, vmode, vbits, rows)) &&
+         mfma_decode_supported(d, kmode, kbits, vmode, vbits, rows);
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
@@ -304,10 +317,14 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   hipError_t e = launch_qprep(p, stream);
   if (e != hipSuccess) return e;
   const dim3 grid(p.n_chunks, p.hkv, p.batch);
-  e = p.d == 128 ? launch_dd<128>(p, grid, stream) : launch_dd<256>(p, grid, stream);
+  const bool bf16 = bf16_decode_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits, p.rows);
+  if (bf16)
+    e = launch_decode_bf16_kernel(p, grid, stream);
+  else
+    e = p.d == 128 ? launch_dd<128>(p, grid, stream) : launch_dd<256>(p, grid, stream);
   if (e != hipSuccess) return e;
   DecodeParams pm = p;
-  pm.n_chunks = p.n_chunks * kWaves;  // one partial per wave
+  if (!bf16) pm.n_chunks = p.n_chunks * kWaves;  // one partial per wave (per workgroup for bf16)
   return launch_merge(pm, stream);
 }
 
