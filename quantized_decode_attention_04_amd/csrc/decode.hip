@@ -90,40 +90,51 @@ __device__ __forceinline__ uint32_t token_field(const uint32_t* tokw, int j) {
 }
 
 // q_rot = Pi_k q (and S q_rot for Prod keys) for one query row: one
-// workgroup of D threads per (row, sequence x KV head); thread i forms
-// coordinate i with its D terms loaded in batches (coalesced across i).
+// workgroup of 4 D threads per (row, sequence x KV head); thread (i, k) sums
+// the quarter k of coordinate i's D terms with all of its loads in flight
+// (coalesced across i), and the quarters are added through LDS.
 template <int D>
-__global__ __launch_bounds__(D) void qprep_kernel(DecodeParams p) {
-  __shared__ float s_in[D], s_qr[D];
+__global__ __launch_bounds__(4 * D) void qprep_kernel(DecodeParams p) {
+  constexpr int Q = D / 4, QB = Q <= 32 ? Q : Q / 2;  // terms per thread, per batch of loads
+  static_assert(D % 4 == 0 && Q % QB == 0 && QB <= 32, "batches must tile a quarter");
+  __shared__ float s_in[D], s_qr[D], s_part[4][D];
   const int r = blockIdx.x, bg = blockIdx.y;
-  const int b = bg / p.hkv, g = bg % p.hkv, i = threadIdx.x;
+  const int b = bg / p.hkv, g = bg % p.hkv;
+  const int i = threadIdx.x % D, k = threadIdx.x / D;
   const int R = p.row0 + r;  // row among the KV head's group * q_len rows
   const int h = g * p.group + R / p.q_len, qi = R % p.q_len;
   const int64_t qoff = (((int64_t)b * p.hq + h) * p.q_len + qi) * D;
-  s_in[i] = load_q(p.q, qoff + i, p.q_bf16);
+  if (k == 0) s_in[i] = load_q(p.q, qoff + i, p.q_bf16);
   __syncthreads();
   float acc = 0.f;
-  for (int j0 = 0; j0 < D; j0 += 32) {
-    float pv[32];
+  for (int t0 = 0; t0 < Q; t0 += QB) {
+    float pv[QB];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) pv[k] = p.k_pit[(size_t)(j0 + k) * D + i];
+    for (int t = 0; t < QB; ++t) pv[t] = p.k_pit[(size_t)(k * Q + t0 + t) * D + i];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) acc = fmaf(pv[k], s_in[j0 + k], acc);
+    for (int t = 0; t < QB; ++t) acc = fmaf(pv[t], s_in[k * Q + t0 + t], acc);
   }
+  s_part[k][i] = acc;
+  __syncthreads();
   const size_t e = ((size_t)bg * p.rows + r) * D + i;
-  p.qrot[e] = acc;
+  if (k == 0) {
+    const float qr = (s_part[0][i] + s_part[1][i]) + (s_part[2][i] + s_part[3][i]);
+    p.qrot[e] = qr;
+    s_qr[i] = qr;
+  }
   if (p.kmode != TQ_MODE_PROD) return;
-  s_qr[i] = acc;
   __syncthreads();
   float acs = 0.f;
-  for (int j0 = 0; j0 < D; j0 += 32) {
-    float sv[32];
+  for (int t0 = 0; t0 < Q; t0 += QB) {
+    float sv[QB];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) sv[k] = p.k_st[(size_t)(j0 + k) * D + i];
+    for (int t = 0; t < QB; ++t) sv[t] = p.k_st[(size_t)(k * Q + t0 + t) * D + i];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) acs = fmaf(sv[k], s_qr[j0 + k], acs);
+    for (int t = 0; t < QB; ++t) acs = fmaf(sv[t], s_qr[k * Q + t0 + t], acs);
   }
-  p.qs[e] = acs;
+  s_part[k][i] = acs;
+  __syncthreads();
+  if (k == 0) p.qs[e] = (s_part[0][i] + s_part[1][i]) + (s_part[2][i] + s_part[3][i]);
 }
 
 // Scores of one token against all rows (rows beyond p.rows read zeros).
@@ -355,73 +366,89 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   }
 }
 
-// Cross-chunk merge, one workgroup of D threads per (query row, KV head,
+// Cross-chunk merge, one workgroup of 4 D threads per (query row, KV head,
 // sequence), stream-ordered after the decode kernel: weights 2^(m_c - M) / L
-// from every chunk's (m, l), the merged row o = sum_c w_c o_c (thread j ->
-// coordinate j), then the single inverse rotation out = Pi_v^T o for MSE
-// values (group values are already in the original domain).
+// from every chunk's (m, l), the merged row o = sum_c w_c o_c, then the
+// single inverse rotation out = Pi_v^T o for MSE values (group values are
+// already in the original domain).  Thread (j, k) takes coordinate j of the
+// chunks c = k (mod 4), sixteen at a time, and the quarter k of the rotation's
+// terms, whose loads it issues first; the quarters meet in LDS.
 template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
-  constexpr int NW = (D + 63) / 64;
+__global__ __launch_bounds__(4 * D) void merge_kernel(DecodeParams p) {
+  constexpr int NT = 4 * D, NW = NT / 64, Q = D / 4;
+  static_assert(D % 16 == 0, "whole waves");
   __shared__ float s_o[D];
-  __shared__ float s_red[2 * NW];
+  __shared__ float s_part[4][D];
+  __shared__ float s_red[2][NW];
   __shared__ float s_w[kMaxMergeChunks];
   const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int bg = b * p.hkv + g, j = threadIdx.x, lane = j & 63, wave = j >> 6;
+  const int bg = b * p.hkv + g, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = tid % D, k = tid / D;
   const int nch = p.n_chunks, rows = p.rows;
+  const bool rotate = p.vmode != TQ_MODE_GROUP;
   const float* pml = p.part_ml + (size_t)bg * nch * rows * 2;
   const float* po = p.part_o + (size_t)bg * nch * rows * D;
+  float pv[Q];
+  if (rotate) {
+#pragma unroll
+    for (int t = 0; t < Q; ++t) pv[t] = p.v_pi[(size_t)(k * Q + t) * D + j];
+  }
   float M = -INFINITY;
-  for (int c = j; c < nch; c += D) M = fmaxf(M, pml[((size_t)c * rows + r) * 2]);
+  for (int c = tid; c < nch; c += NT) M = fmaxf(M, pml[((size_t)c * rows + r) * 2]);
   M = wave_max(M);
-  if (lane == 0) s_red[wave] = M;
+  if (lane == 0) s_red[0][wave] = M;
   __syncthreads();
-  M = s_red[0];
-  for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[w]);
+  M = s_red[0][0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[0][w]);
   float L = 0.f;
-  for (int c = j; c < nch; c += D) {
+  for (int c = tid; c < nch; c += NT) {
     const float mc = pml[((size_t)c * rows + r) * 2];
     const float w = (M == -INFINITY || mc == -INFINITY) ? 0.f : exp2f(mc - M);
     s_w[c] = w;
     L = fmaf(w, pml[((size_t)c * rows + r) * 2 + 1], L);
   }
   L = wave_sum(L);
-  if (lane == 0) s_red[NW + wave] = L;
+  if (lane == 0) s_red[1][wave] = L;
   __syncthreads();
   L = 0.f;
-  for (int w = 0; w < NW; ++w) L += s_red[NW + w];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) L += s_red[1][w];
   float o = 0.f;
-  int c = 0;
-  for (; c + 16 <= nch; c += 16) {  // sixteen loads in flight per thread
+  int c = k;
+  for (; c + 4 * 15 < nch; c += 4 * 16) {  // sixteen loads in flight per thread
     float v[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = po[((size_t)(c + k) * rows + r) * D + j];
+    for (int t = 0; t < 16; ++t) v[t] = po[((size_t)(c + 4 * t) * rows + r) * D + j];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) o = fmaf(s_w[c + k], v[k], o);
+    for (int t = 0; t < 16; ++t) o = fmaf(s_w[c + 4 * t], v[t], o);
   }
-  for (; c < nch; ++c) o = fmaf(s_w[c], po[((size_t)c * rows + r) * D + j], o);
-  o = L > 0.f ? o / L : 0.f;
-  float res = o;
-  if (p.vmode != TQ_MODE_GROUP) {
-    s_o[j] = o;
-    __syncthreads();
-    res = 0.f;
-    for (int i0 = 0; i0 < D; i0 += 32) {
-      float pv[32];
-#pragma unroll
-      for (int k = 0; k < 32; ++k) pv[k] = p.v_pi[(size_t)(i0 + k) * D + j];
-#pragma unroll
-      for (int k = 0; k < 32; ++k) res = fmaf(s_o[i0 + k], pv[k], res);
-    }
+  for (; c < nch; c += 4) o = fmaf(s_w[c], po[((size_t)c * rows + r) * D + j], o);
+  s_part[k][j] = o;
+  __syncthreads();
+  if (k == 0) {
+    o = (s_part[0][j] + s_part[1][j]) + (s_part[2][j] + s_part[3][j]);
+    s_o[j] = L > 0.f ? o / L : 0.f;
   }
+  __syncthreads();
   const int R = p.row0 + r;
   const int h = g * p.group + R / p.q_len, qi = R % p.q_len;
-  p.out[(((int64_t)b * p.hq + h) * p.q_len + qi) * D + j] = res;
+  float* out = p.out + (((int64_t)b * p.hq + h) * p.q_len + qi) * D;
+  if (!rotate) {
+    if (k == 0) out[j] = s_o[j];
+    return;
+  }
+  float res = 0.f;
+#pragma unroll
+  for (int t = 0; t < Q; ++t) res = fmaf(s_o[k * Q + t], pv[t], res);
+  s_part[k][j] = res;
+  __syncthreads();
+  if (k == 0) out[j] = (s_part[0][j] + s_part[1][j]) + (s_part[2][j] + s_part[3][j]);
 }
 
 template <int D>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
-  qprep_kernel<D><<<dim3(p.rows, p.batch * p.hkv), dim3(D), 0, stream>>>(p);
+  qprep_kernel<D><<<dim3(p.rows, p.batch * p.hkv), dim3(4 * D), 0, stream>>>(p);
   const dim3 grid(p.n_chunks, p.hkv, p.batch);
   if (p.rows <= 4) {
     decode_kernel<D, 4><<<grid, dim3(256), 0, stream>>>(p);
@@ -432,7 +459,7 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   } else {
     return hipErrorInvalidValue;  // more than 8 rows at head_dim > 128 is refused on the host
   }
-  merge_kernel<D><<<dim3(p.rows, p.hkv, p.batch), dim3(D), 0, stream>>>(p);
+  merge_kernel<D><<<dim3(p.rows, p.hkv, p.batch), dim3(4 * D), 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -440,8 +467,8 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_qprep(const DecodeParams& p, hipStream_t stream) {
   switch (p.d) {
-    case 128: qprep_kernel<128><<<dim3(p.rows, p.batch * p.hkv), dim3(128), 0, stream>>>(p); break;
-    case 256: qprep_kernel<256><<<dim3(p.rows, p.batch * p.hkv), dim3(256), 0, stream>>>(p); break;
+    case 128: qprep_kernel<128><<<dim3(p.rows, p.batch * p.hkv), dim3(4 * 128), 0, stream>>>(p); break;
+    case 256: qprep_kernel<256><<<dim3(p.rows, p.batch * p.hkv), dim3(4 * 256), 0, stream>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -450,8 +477,8 @@ hipError_t launch_qprep(const DecodeParams& p, hipStream_t stream) {
 hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
   if (p.n_chunks > kMaxMergeChunks) return hipErrorInvalidValue;
   switch (p.d) {
-    case 128: merge_kernel<128><<<dim3(p.rows, p.hkv, p.batch), dim3(128), 0, stream>>>(p); break;
-    case 256: merge_kernel<256><<<dim3(p.rows, p.hkv, p.batch), dim3(256), 0, stream>>>(p); break;
+    case 128: merge_kernel<128><<<dim3(p.rows, p.hkv, p.batch), dim3(4 * 128), 0, stream>>>(p); break;
+    case 256: merge_kernel<256><<<dim3(p.rows, p.hkv, p.batch), dim3(4 * 256), 0, stream>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

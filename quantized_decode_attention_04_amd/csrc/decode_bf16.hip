@@ -65,11 +65,17 @@ __device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel)
   return __builtin_amdgcn_perm(s0, s1, sel);
 }
 
-// A value loaded from a valid address (the callers clamp it), or zero: the
-// load is unconditional so that the loads of a tile issue back to back.
+// A value loaded from a valid address (the caller clamps it), or zero; the
+// load itself is unconditional.
 template <class T>
 __device__ __forceinline__ T pick(T v, bool ok) {
   return ok ? v : T(0);
+}
+
+// The T at a byte offset from a base pointer.
+template <class T>
+__device__ __forceinline__ T ld(const char* base, uint32_t off) {
+  return *reinterpret_cast<const T*>(base + off);
 }
 
 // bf16 bits of x, rounded to nearest even (finite x)
@@ -201,38 +207,46 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
   const float sl2 = p.scale * kLog2e;
   const float qjl = kQjlConstNumer / (float)D;
   const size_t base = (size_t)bg * (size_t)p.cap + (size_t)c0;  // slot of token 0 of the chunk
-  const int vword = (m * VRB) >> 5, vshift = (m * VRB) & 31;
+  // the chunk's fields (uniform bases); a token index t < ntok (< 2^24)
+  // addresses them with 24-bit products and 32-bit byte offsets
+  const char* kidx = reinterpret_cast<const char*>(p.k_idx + base * p.kwords);
+  const char* ksgn = PROD ? reinterpret_cast<const char*>(p.k_sign + base * p.ksign_words) : nullptr;
+  const char* knrm = reinterpret_cast<const char*>(p.k_norm + base);
+  const char* krnm = PROD ? reinterpret_cast<const char*>(p.k_rnorm + base) : nullptr;
+  const char* vnrm = reinterpret_cast<const char*>(p.v_norm + base);
+  const char* vidx = reinterpret_cast<const char*>(p.v_idx + base * p.vwords);
+  const uint32_t kstride = 4u * p.kwords, sstride = 4u * p.ksign_words, vstride = 4u * p.vwords;
+  const uint32_t koff = 4u * g * KB, soff = 4u * g, voff = 4u * ((m * VRB) >> 5);
+  const int vshift = (m * VRB) & 31;
   float m_ref = -1e30f, l_run = 0.f;
   v4f acc[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
 
   for (int T0 = wave * kTile; T0 < ntok; T0 += kWaves * kTile) {
+    // Tokens past the chunk's end read the last token instead: every load is
+    // valid, and their scores are masked, so they weigh nothing.
     // ---- key words of token T0 + 16 tg + m, coordinates 32 g .. 32 g + 31
     uint32_t kw[4][KB], ksw[4];
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
-      const int tok = T0 + 16 * tg + m;
-      const bool ok = tok < ntok;
-      const size_t slot = base + (ok ? tok : 0);
+      const uint32_t t = (uint32_t)min(T0 + 16 * tg + m, ntok - 1);
 #pragma unroll
-      for (int w = 0; w < KB; ++w) kw[tg][w] = pick(p.k_idx[slot * p.kwords + g * KB + w], ok);
+      for (int w = 0; w < KB; ++w) kw[tg][w] = ld<uint32_t>(kidx, __umul24(t, kstride) + koff + 4u * w);
       ksw[tg] = 0u;
-      if constexpr (PROD) ksw[tg] = pick(p.k_sign[slot * p.ksign_words + g], ok);
+      if constexpr (PROD) ksw[tg] = ld<uint32_t>(ksgn, __umul24(t, sstride) + soff);
     }
     // ---- norms and value runs of the lane's tokens T0 + 16 tg + 4 g + r
     float kn[16], kq[16], vn[16];
     uint32_t vw[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int tok = T0 + 16 * (i >> 2) + 4 * g + (i & 3);
-      const bool ok = tok < ntok;
-      const size_t slot = base + (ok ? tok : 0);
-      kn[i] = pick(p.k_norm[slot], ok);
+      const uint32_t t = (uint32_t)min(T0 + 16 * (i >> 2) + 4 * g + (i & 3), ntok - 1);
+      kn[i] = ld<float>(knrm, 4u * t);
       kq[i] = 0.f;
-      if constexpr (PROD) kq[i] = pick(p.k_rnorm[slot], ok) * qjl;
-      vn[i] = pick(p.v_norm[slot], ok);
-      vw[i] = pick(p.v_idx[slot * p.vwords + vword], ok) >> vshift;
+      if constexpr (PROD) kq[i] = ld<float>(krnm, 4u * t) * qjl;
+      vn[i] = ld<float>(vnrm, 4u * t);
+      vw[i] = ld<uint32_t>(vidx, __umul24(t, vstride) + voff) >> vshift;
     }
 
     // ---- scores
@@ -309,13 +323,29 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
         const float rc = pv[8 * h + 2 * e + 1] - __uint_as_float(c & 0xffff0000u);
         bl[e] = perm(__float_as_uint(rc), __float_as_uint(ra), 0x07060302u);
       }
+      // LDS byte offsets of the value codes: byte k of va[i][t] is 4 x the
+      // code of coordinate (8/VB) k + t of token i
+      constexpr int TPB = 8 / VB;
+      uint32_t va[8][TPB];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int t = 0; t < TPB; ++t) {
+          const int sh = 2 - VB * t;
+          const uint32_t w = vw[8 * h + i];
+          va[i][t] = (sh >= 0 ? (w << sh) : (w >> -sh)) & (0x01010101u * (VMASK << 2));
+        }
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         v4u ah, al;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t ta = s_vt[(vw[8 * h + 2 * e] >> (VB * u)) & VMASK];
-          const uint32_t tc = s_vt[(vw[8 * h + 2 * e + 1] >> (VB * u)) & VMASK];
+          // byte u / TPB, zero-extended (selector 0x0c gives a zero byte)
+          const uint32_t bsel = 0x0c0c0c00u + (uint32_t)(u / TPB);
+          const uint32_t oa = perm(0u, va[2 * e][u % TPB], bsel);
+          const uint32_t oc = perm(0u, va[2 * e + 1][u % TPB], bsel);
+          const uint32_t ta = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(s_vt) + oa);
+          const uint32_t tc = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(s_vt) + oc);
           ah[e] = perm(tc, ta, 0x05040100u);
           al[e] = perm(tc, ta, 0x07060302u);
         }
