@@ -366,7 +366,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
   }
 
   auto process = [&](Tile& cur, const uint32_t T0, const uint32_t Tn) {
-    // ---- scores on the matrix cores
+    // ---- scores on the matrix cores, with the value selectors of the same
+    // score tile computed while its ten products run (the scheduling groups
+    // put two VALU instructions behind each MFMA)
     float sc[16];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -374,36 +376,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
       selectors3(cur.kw[st].x, cur.kw[st].y, cur.kw[st].z, s8);
       const v4i ah0 = lookup(s8, kh1, kh0), al0 = lookup(s8, kl1, kl0);
       const v4i ah1 = lookup(s8 + 4, kh1, kh0), al1 = lookup(s8 + 4, kl1, kl0);
+      __builtin_amdgcn_sched_barrier(0);
       // Q C = 2^24 a Ch + 2^16 (a Cl + b Ch) + 2^8 (b Cl + c Ch) [+ c Cl, below
       // 2^-23 of the product]
       v4i t24 = v4i{0, 0, 0, 0}, t16 = v4i{0, 0, 0, 0}, t8 = v4i{0, 0, 0, 0};
       t24 = mfma(ah0, qo.a0, t24);
       t16 = mfma(al0, qo.a0, t16);
-      t16 = mfma(ah0, qo.b0, t16);
       t8 = mfma(al0, qo.b0, t8);
+      t16 = mfma(ah0, qo.b0, t16);
       t8 = mfma(ah0, qo.c0, t8);
       t24 = mfma(ah1, qo.a1, t24);
       t16 = mfma(al1, qo.a1, t16);
-      t16 = mfma(ah1, qo.b1, t16);
       t8 = mfma(al1, qo.b1, t8);
+      t16 = mfma(ah1, qo.b1, t16);
       t8 = mfma(ah1, qo.c1, t8);
+      {
+        uint32_t v8[8];
+        selectors3(cur.vw[st].x, cur.vw[st].y, cur.vw[st].z, v8);
+        const int tt = 16 * (n >> 2) + 4 * st + (n & 3);
+        v4u* dst = reinterpret_cast<v4u*>(sb + tt * kRow + sel_group_offset(n >> 2) + 32 * h);
+        dst[0] = v4u{v8[0], v8[1], v8[2], v8[3]};
+        dst[1] = v4u{v8[4], v8[5], v8[6], v8[7]};
+      }
+#pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);    // the two LDS stores
       // 256 t24 + t16 is exact in int32; then one float rounding (2^-24)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[4 * st + i] = fmaf((float)(t24[i] * 256 + t16[i]), 256.f, (float)t8[i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // the key words are consumed: the next tile of this buffer is loaded now
     load_keys(cur, rk, lw, Tn);
-    // ---- value selectors and the tile's norms to LDS
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      uint32_t s8[8];
-      selectors3(cur.vw[st].x, cur.vw[st].y, cur.vw[st].z, s8);
-      const int tt = 16 * (n >> 2) + 4 * st + (n & 3);
-      v4u* dst = reinterpret_cast<v4u*>(sb + tt * kRow + sel_group_offset(n >> 2) + 32 * h);
-      dst[0] = v4u{s8[0], s8[1], s8[2], s8[3]};
-      dst[1] = v4u{s8[4], s8[5], s8[6], s8[7]};
-    }
     sn[lane] = cur.kn;
     sn[kTile + lane] = cur.vn;
     load_values(cur, rv, lw, Tn);
