@@ -478,6 +478,131 @@ __global__ __launch_bounds__(small_threads<D>()) void quantize_small_kernel(Quan
   if (tid == 0) p.rnorm[tok] = gamma;
 }
 
+// MSE appends of a decode step at head_dim <= 128: one wave per (vector,
+// 32-coordinate group), so that each workgroup streams 32 rows of Pi instead
+// of all of them and needs no workgroup barrier.  Lane (c, k) = (lane / 2, lane % 2) loads half
+// k of x and of row 32 g + c of Pi (16-byte loads, all in flight at once);
+// the two halves of ||x||^2 and of (Pi x)_{32 g + c} meet by one lane
+// exchange.  The group's b packed words (aligned in every layout: words
+// b g .. b g + b - 1) are written by the wave that owns them.  Every wave of
+// a vector computes the same norm; the group-0 one stores it.
+template <int D>
+__global__ __launch_bounds__(64) void quantize_mse_split_kernel(QuantizeSets sets) {
+  constexpr int NS = D / 32, JN = D / 2;
+  static_assert(D % 32 == 0 && JN % 8 == 0, "whole groups, 16-byte slices");
+  const QuantizeParams& p = sets.s[blockIdx.y];
+  __shared__ uint32_t wbuf[4];
+  const int lane = threadIdx.x, c = lane >> 1, part = lane & 1;
+  const int64_t total = (int64_t)p.batch * p.heads * p.n_new;
+  const int64_t vec = blockIdx.x / NS;
+  const int g = (int)(blockIdx.x % NS);
+  if (vec >= total) return;  // whole workgroup
+  const int t = (int)(vec % p.n_new);
+  const int64_t bh = vec / p.n_new;
+  const int h = (int)(bh % p.heads), b = (int)(bh / p.heads);
+  // the write position is needed only by the stores: its load is in flight
+  // with the others
+  const int32_t pos32 = p.pos[b];
+
+  float4 pr[JN / 4];
+  const float4* src = reinterpret_cast<const float4*>(p.pi + (size_t)(32 * g + c) * D + part * JN);
+#pragma unroll
+  for (int k = 0; k < JN / 4; ++k) pr[k] = src[k];
+  float xv[JN];
+  const int64_t x0 = (int64_t)b * p.s0 + (int64_t)h * p.s1 + (int64_t)t * p.s2 + part * JN;
+  if (p.x_vec16 && p.x_bf16) {  // eight bf16 per 16-byte load
+    const uint4* xs = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + x0);
+#pragma unroll
+    for (int k = 0; k < JN / 8; ++k) {
+      const uint4 w = xs[k];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xv[8 * k + 2 * e] = __uint_as_float(ww[e] << 16);
+        xv[8 * k + 2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
+      }
+    }
+  } else if (p.x_vec16) {  // four floats per 16-byte load
+    const float4* xs = reinterpret_cast<const float4*>(static_cast<const float*>(p.x) + x0);
+#pragma unroll
+    for (int k = 0; k < JN / 4; ++k) {
+      const float4 w = xs[k];
+      xv[4 * k] = w.x;
+      xv[4 * k + 1] = w.y;
+      xv[4 * k + 2] = w.z;
+      xv[4 * k + 3] = w.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < JN; ++k) xv[k] = load_x(p.x, x0 + k, p.x_bf16);
+  }
+  if (lane < 4) wbuf[lane] = 0u;
+  float sq0 = 0.f, sq1 = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int k = 0; k < JN / 4; ++k) {
+    sq0 = fmaf(xv[4 * k], xv[4 * k], sq0);
+    sq1 = fmaf(xv[4 * k + 1], xv[4 * k + 1], sq1);
+    sq0 = fmaf(xv[4 * k + 2], xv[4 * k + 2], sq0);
+    sq1 = fmaf(xv[4 * k + 3], xv[4 * k + 3], sq1);
+    a0 = fmaf(pr[k].x, xv[4 * k], a0);
+    a1 = fmaf(pr[k].y, xv[4 * k + 1], a1);
+    a0 = fmaf(pr[k].z, xv[4 * k + 2], a0);
+    a1 = fmaf(pr[k].w, xv[4 * k + 3], a1);
+  }
+  float sq = sq0 + sq1, acc = a0 + a1;
+  // lane pairs (2c, 2c + 1) hold the two halves; the half-0 sum goes first in
+  // both lanes so that every lane of the vector forms the same norm
+  const float sq_o = __shfl_xor(sq, 1, 64), acc_o = __shfl_xor(acc, 1, 64);
+  sq = part == 0 ? sq + sq_o : sq_o + sq;
+  acc = part == 0 ? acc + acc_o : acc_o + acc;
+  const float n = sqrtf(sq);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (part == 0) {
+    const float u = acc * (n > 0.f ? 1.f / n : 0.f);
+    uint32_t idx = 0;
+    for (int m = 0; m < p.levels - 1; ++m) idx += u > p.bnd[m] ? 1u : 0u;
+    pack_field(wbuf, c, p.mse_bits, idx);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int64_t pos = (int64_t)pos32 + t;
+  if (pos < 0 || pos >= p.cap) return;  // nothing is written for this vector
+  const int64_t tok = ((int64_t)b * p.heads + h) * p.cap + pos;
+  if (lane < p.mse_bits) p.idx[tok * p.words + g * p.mse_bits + lane] = wbuf[lane];
+  if (g == 0 && lane == 0) p.norm[tok] = n;
+}
+
+template <int D>
+void launch_small(const QuantizeSets& sets, int n_sets, int64_t total, hipStream_t stream) {
+  if constexpr (D > 128) {
+    quantize_small_kernel<D><<<dim3((unsigned)total, (unsigned)n_sets), small_threads<D>(), 0, stream>>>(sets);
+  } else {
+    // MSE sets take the split kernel, the others one workgroup per vector; a
+    // key and a value append of the same modes stay one launch
+    bool mse[2] = {false, false};
+    for (int k = 0; k < n_sets; ++k) mse[k] = sets.s[k].mode == TQ_MODE_MSE;
+    if (n_sets == 1 || mse[0] == mse[1]) {
+      if (mse[0])
+        quantize_mse_split_kernel<D><<<dim3((unsigned)(total * (D / 32)), (unsigned)n_sets), 64, 0, stream>>>(sets);
+      else
+        quantize_small_kernel<D><<<dim3((unsigned)total, (unsigned)n_sets), small_threads<D>(), 0, stream>>>(sets);
+      return;
+    }
+    for (int k = 0; k < 2; ++k) {
+      QuantizeSets one;
+      one.s[0] = sets.s[k];
+      one.s[1] = sets.s[k];
+      if (mse[k])
+        quantize_mse_split_kernel<D><<<dim3((unsigned)(total * (D / 32)), 1u), 64, 0, stream>>>(one);
+      else
+        quantize_small_kernel<D><<<dim3((unsigned)total, 1u), small_threads<D>(), 0, stream>>>(one);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const QuantizeSets& sets, int n_sets, hipStream_t stream) {
@@ -494,12 +619,11 @@ hipError_t launch_quantize(const QuantizeSets& sets, int n_sets, hipStream_t str
   // together or one by one take the same kernel and write the same bits
   const bool small = total <= kSmallAppend && (d == 32 || d == 64 || d == 128 || d == 256);
   if (small) {
-    const dim3 grid((unsigned)total, (unsigned)n_sets);
     switch (d) {
-      case 32: quantize_small_kernel<32><<<grid, small_threads<32>(), 0, stream>>>(sets); break;
-      case 64: quantize_small_kernel<64><<<grid, small_threads<64>(), 0, stream>>>(sets); break;
-      case 128: quantize_small_kernel<128><<<grid, small_threads<128>(), 0, stream>>>(sets); break;
-      default: quantize_small_kernel<256><<<grid, small_threads<256>(), 0, stream>>>(sets); break;
+      case 32: launch_small<32>(sets, n_sets, total, stream); break;
+      case 64: launch_small<64>(sets, n_sets, total, stream); break;
+      case 128: launch_small<128>(sets, n_sets, total, stream); break;
+      default: launch_small<256>(sets, n_sets, total, stream); break;
     }
     return hipGetLastError();
   }
