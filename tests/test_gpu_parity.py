@@ -86,6 +86,20 @@ def test_quantize_bulk_append_parity(d, bits, mode, bf16, H, n_new, off):
     _check_append(d, bits, mode, bf16, H, n_new, off)
 
 
+# decode-step appends whose rows are not 16-byte aligned: the per-group MSE
+# kernel (d <= 128) and the one-workgroup-per-vector kernel take their
+# element-wise load paths
+SMALL_UNALIGNED_CASES = [
+    (128, 3, 0, True, 3, 37, 1), (64, 2, 0, False, 3, 37, 3), (32, 4, 0, True, 3, 37, 5),
+    (128, 1, 0, False, 3, 37, 2), (128, 3, 1, True, 3, 37, 1),
+]
+
+
+@pytest.mark.parametrize("d,bits,mode,bf16,H,n_new,off", SMALL_UNALIGNED_CASES)
+def test_quantize_small_unaligned_parity(d, bits, mode, bf16, H, n_new, off):
+    _check_append(d, bits, mode, bf16, H, n_new, off)
+
+
 def _check_append(d, bits, mode, bf16, H, n_new, off):
     tag = f"quantize d={d} bits={bits} mode={mode} bf16={bf16} heads={H} n_new={n_new} offset={off}"
     _say(tag)
