@@ -226,6 +226,36 @@ def gather_timing(tq, w, kc, vc, K, V, dev, stream, reps: int) -> dict:
             "gbps": nbytes / (us * 1e-6) / 1e9}
 
 
+def layer_view(c, l: int):
+    """Layer l of a cache allocated with the layers as its batch: the same
+    arrays sliced to batch 1 (contiguous, so only the base pointers move)."""
+    import dataclasses
+    sl = lambda t: None if t is None else t[l:l + 1]
+    return dataclasses.replace(c, batch=1, idx=sl(c.idx), norm=sl(c.norm), rnorm=sl(c.rnorm), sign=sl(c.sign),
+                               scale=sl(c.scale), gmin=sl(c.gmin))
+
+
+def stream_read_reference(dev, reps: int = 10, gib: int = 2) -> dict:
+    """A streaming read of the same run: torch's float32 sum over `gib` GiB
+    (a plain library reduction, read-bound), timed with HIP events."""
+    import torch
+    n = gib * (1 << 30) // 4
+    buf = torch.ones(n, dtype=torch.float32, device=dev)
+    out = torch.empty((), dtype=torch.float32, device=dev)
+    torch.sum(buf, dim=0, out=out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        torch.sum(buf, dim=0, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    del buf
+    return {"kernel": f"torch.sum over {gib} GiB float32", "bytes": n * 4, "us": ms * 1000.0,
+            "gbps": n * 4 / (ms / 1000.0) / 1e9}
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -259,12 +289,23 @@ def main():
     if args.layers:
         layers = args.layers
 
-    # ---- set-up (not timed): per-layer compressed caches, queries, new tokens
+    # ---- set-up (not timed): per-layer compressed caches, queries, new tokens.
+    # With one sequence per layer the layers' caches and queries are slices of
+    # one allocation batched over the layers, so that one extra call can also
+    # read every layer at once (the labelled upper bound below).
+    stacked = B == 1 and layers > 1
+    if stacked:
+        K_all = tq.allocate_cache(kc, layers, hkv, max_len, dev)
+        V_all = tq.allocate_cache(vc, layers, hkv, max_len, dev)
+        q_all = torch.empty((layers, hq, qlen, d), dtype=torch.bfloat16 if w.bf16 else torch.float32, device=dev)
     kcs, vcs, qs, kn, vn = [], [], [], [], []
     pos0 = torch.zeros(B, dtype=torch.int32, device=dev)
     for l in range(layers):
-        K = tq.allocate_cache(kc, B, hkv, max_len, dev)
-        V = tq.allocate_cache(vc, B, hkv, max_len, dev)
+        if stacked:
+            K, V = layer_view(K_all, l), layer_view(V_all, l)
+        else:
+            K = tq.allocate_cache(kc, B, hkv, max_len, dev)
+            V = tq.allocate_cache(vc, B, hkv, max_len, dev)
         ksc = wl.outlier_scales(0, l, hkv, d, 0) if w.outliers else None
         vsc = wl.outlier_scales(0, l, hkv, d, 1) if w.outliers else None
         hist = max_len - append
@@ -280,6 +321,9 @@ def main():
         kcs.append(K)
         vcs.append(V)
         qs.append(wl.device_normal((B, hq, qlen, d), 0, l, wl.STREAM_Q, w.bf16, dev))
+        if stacked:
+            q_all[l:l + 1].copy_(qs[-1])
+            qs[-1] = q_all[l:l + 1]
         kn.append(wl.device_normal((B, hkv, append, d), 0, l, wl.STREAM_KNEW, w.bf16, dev, ksc))
         vn.append(wl.device_normal((B, hkv, append, d), 0, l, wl.STREAM_VNEW, w.bf16, dev, vsc))
     torch.cuda.synchronize()
@@ -373,6 +417,33 @@ def main():
     prefill_attn = prefill_timing(tq, wl, w, kc, vc, kcs[0], vcs[0], lens, max_len, dev, stream,
                                   max(3, args.steps // 2))
 
+    single = None
+    if stacked:
+        # upper bound, not the step: one call over every layer as a batch of
+        # `layers` sequences; a real decode step cannot do this, since each
+        # layer's query needs the previous layer's output
+        lens_all = torch.full((layers,), int(lens_h[0]), dtype=torch.int32, device=dev)
+        ws_all = torch.zeros(tq.tq_decode_workspace_size(kc, vc, layers, hq, hkv, qlen, max_len), dtype=torch.uint8,
+                             device=dev)
+        out_all = torch.empty((layers, hq, qlen, d), dtype=torch.float32, device=dev)
+        tq.tq_decode_attention(kc, vc, q_all, K_all, V_all, lens_all, max_len, scale, out_all, ws_all)
+        torch.cuda.synchronize()
+        reps = max(3, args.steps // 2)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b_ in ev:
+            a.record(stream)
+            tq.tq_decode_attention(kc, vc, q_all, K_all, V_all, lens_all, max_len, scale, out_all, ws_all)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        sms = float(np.median([a.elapsed_time(b_) for a, b_ in ev]))
+        sbytes = layer_state_bytes * layers
+        single = {"label": f"upper bound, not a decode step: one tq_decode_attention over all {layers} layers as a "
+                           f"batch of {layers} sequences",
+                  "us": sms * 1000.0, "state_bytes": sbytes, "gbps": sbytes / (sms / 1000.0) / 1e9,
+                  "frac": sbytes / (sms / 1000.0) / 1e9 / HBM_PEAK_GBPS}
+        del ws_all, out_all
+    stream_ref = stream_read_reference(dev)
+
     tokens_per_step = float(lens_h.sum()) * layers
     value = tokens_per_step / (ms_per_step / 1000.0)
     # algorithmic bytes of one decode call: the packed state of every attended
@@ -384,9 +455,15 @@ def main():
     achieved = alg_bytes / (dec_ms_avg / 1000.0) / 1e9
     # the library takes the matrix-core path for d 128 with 3-bit MSE keys and
     # values and at most 16 query rows per KV head (a label only)
-    fast = d == 128 and (w.kmode, w.kbits, w.vmode, w.vbits) == (0, 3, 0, 3) and (hq // hkv) * qlen <= 16
+    rows = (hq // hkv) * qlen
+    fast = d == 128 and (w.kmode, w.kbits, w.vmode, w.vbits) == (0, 3, 0, 3) and rows <= 16
+    kcode_bits = w.kbits - 1 if w.kmode == 1 else w.kbits
+    bf16_path = (not fast and d == 128 and w.kmode in (0, 1) and kcode_bits in (1, 2) and w.vmode == 0
+                 and w.vbits in (1, 2, 4) and rows <= 16)
     kernels = ("decode_fast_kernel + merge_fast_kernel" if fast
+               else "qprep_kernel + decode_bf16_kernel + merge_kernel" if bf16_path
                else "qprep_kernel + decode_kernel + merge_kernel")
+    dtype = "i8+f32" if fast else "bf16x2+f32" if bf16_path else "f32"
     traffic, traffic_src = None, "counters taken on l64_d128_n256k_mse3_mtp2 only"
     if w.name == "l64_d128_n256k_mse3_mtp2":
         src = os.path.join(os.path.dirname(os.path.abspath(tq.__file__)), "csrc", "decode_fast.hip")
@@ -403,7 +480,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8+f32",
+        "dtype": dtype,
         "data": "synthetic: seeded N(0,1)*0.02 bf16 K/V/q" + (" with per-channel outliers" if w.outliers else ""),
         "config": {
             "workload": w.name,
@@ -442,6 +519,9 @@ def main():
             "bulk_prefill": prefill,
             "prefill_attention": prefill_attn,
             "cache_gather": gather,
+            "stream_read_reference": stream_ref,
+            "achieved_vs_stream_read": achieved / stream_ref["gbps"],
+            "single_launch_all_layers": single,
         },
     }
     if not args.no_cpu_baseline:
