@@ -57,7 +57,8 @@ constexpr int kMaxChunks = 128;        // merge weights kept in LDS
 constexpr int kRow = kD + 16;          // LDS bytes per token row of value selectors
 constexpr int kSelLds = kTile * kRow + 448;       // value selectors of the tile (+ row-group offsets)
 constexpr int kNormLds = 2 * kTile * 4;            // key and value norms of the tile
-constexpr int kAccLds = 16 * kD * 4;               // float output accumulator [row][coord]
+constexpr int kAccRow = kD / 4 + 1;               // 16-byte slots per accumulator row (one of padding)
+constexpr int kAccLds = 16 * kAccRow * 16;         // float output accumulator [row][coord]
 constexpr int kWaveLds = kSelLds + kNormLds + kAccLds;
 constexpr int kLds = kWaves * kWaveLds;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -157,51 +158,59 @@ struct QueryOps {
 };
 
 // Operands of q_rot^T = Pi_k q^T on v_mfma_f32_16x16x4f32, wave w computing
-// output coordinates 16w .. 16w+15.  The contraction index is permuted so that
-// every lane reads contiguous runs: in K-step s (0..31) lane l supplies the
-// term j = 32 (l/16) + s, i.e. A = Pi[16w + l%16][32 (l/16) + s] and
-// B = q[row l%16][32 (l/16) + s].  Each lane loads 128 bytes of a Pi row and
-// 128 bytes from the start of its query run (a bf16 run uses the first 64),
-// eight 16-byte loads each, issued before the tiles so that waiting for them
-// leaves the tile loads in flight.
+// output coordinates 16w .. 16w+15.  In K-step s (0..31) lane l supplies the
+// term j = 32 (l/16) + s, i.e. A = Pi[16w + l%16][32 (l/16) + s], read from
+// the transposed table Pi^T[j][16w + l%16] (for each s the 64 lanes read four
+// 64-byte runs), and B = q[row l%16][32 (l/16) + s] from LDS.  The query rows
+// are staged once per workgroup: thread t loads four consecutive elements of
+// row t/32 (16-byte or 8-byte loads, coalesced).  All of these loads are
+// issued before the tiles, so that waiting for them leaves the tile loads in
+// flight.
+constexpr int kQRow = kD + 4;  // LDS floats per staged query row (16-byte reads without bank conflicts)
+
 struct QueryLoads {
-  v4f pi[8];
-  v4u qw[8];
+  float pit[32];
+  v4f qs;
 };
 
 __device__ __forceinline__ void query_loads(const DecodeParams& p, int b, int g, QueryLoads& ql) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, kq = lane >> 4;
-  const int rr = r < p.rows ? r : 0;
-  const int R = p.row0 + rr;  // row among the KV head's group * q_len rows
+  const float* pt = p.k_pit + (size_t)(32 * kq) * kD + 16 * wave + r;
+#pragma unroll
+  for (int s = 0; s < 32; ++s) ql.pit[s] = pt[(size_t)s * kD];
+  const int t = threadIdx.x, qr = t >> 5, qc = (t & 31) * 4;
+  const int R = p.row0 + (qr < p.rows ? qr : 0);  // row among the KV head's group * q_len rows
   const int hh = g * p.group + R / p.q_len, qi = R % p.q_len;
   const uint32_t esize = p.q_bf16 ? 2u : 4u;
   const uint32_t q_bytes = (uint32_t)((int64_t)p.batch * p.hq * p.q_len * kD * esize);
-  const uint32_t qoff = (uint32_t)(((((int64_t)b * p.hq + hh) * p.q_len + qi) * kD + 32 * kq) * esize);
-  // reads past the query tensor (the tail of a bf16 run) return zeros
+  const uint32_t qoff = (uint32_t)(((((int64_t)b * p.hq + hh) * p.q_len + qi) * kD + qc) * esize);
   const __amdgpu_buffer_rsrc_t rq = rsrc(p.q, q_bytes);
-  const v4f* pi = reinterpret_cast<const v4f*>(p.k_pi + (16 * wave + r) * kD + 32 * kq);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    ql.pi[i] = pi[i];
-    ql.qw[i] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 16u * i, 0, 0));
+  if (p.q_bf16) {
+    const v2i w = __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(rq, qoff, 0, 0));
+    ql.qs = v4f{__uint_as_float((uint32_t)w.x << 16), __uint_as_float((uint32_t)w.x & 0xffff0000u),
+                __uint_as_float((uint32_t)w.y << 16), __uint_as_float((uint32_t)w.y & 0xffff0000u)};
+  } else {
+    ql.qs = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff, 0, 0));
   }
+  if (qr >= p.rows) ql.qs = v4f{0.f, 0.f, 0.f, 0.f};
 }
 
-// Query element s of this lane's run from its loaded dwords.
-__device__ __forceinline__ float query_element(const DecodeParams& p, const QueryLoads& ql, int s) {
-  const uint32_t wf = ql.qw[s >> 2][s & 3];             // float run: dword s
-  const uint32_t wb = ql.qw[s >> 3][(s >> 1) & 3];      // bf16 run: half s&1 of dword s/2
-  const uint32_t bits = p.q_bf16 ? ((s & 1) ? (wb & 0xffff0000u) : (wb << 16)) : wf;
-  return (int)(threadIdx.x & 15) < p.rows ? __uint_as_float(bits) : 0.f;
-}
-
-// s_max: [8 waves][16 rows] partial row maxima; s_op: [2 ks][3 digits][64
-// lanes][4 dwords] operand dwords.  Neither is touched after the prologue.
-__device__ __forceinline__ void query_operands(const DecodeParams& p, const QueryLoads& ql, float* s_max,
-                                               uint32_t* s_op, QueryOps& qo) {
+// s_q: [16 rows][kQRow] staged query rows; s_max: [8 waves][16 rows] partial
+// row maxima; s_op: [2 ks][3 digits][64 lanes][4 dwords] operand dwords.  None
+// is touched after the prologue.
+__device__ __forceinline__ void query_operands(const DecodeParams& p, const QueryLoads& ql, float* s_q,
+                                               float* s_max, uint32_t* s_op, QueryOps& qo) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, kq = lane >> 4;
+  {
+    const int t = threadIdx.x;
+    *reinterpret_cast<v4f*>(s_q + (t >> 5) * kQRow + (t & 31) * 4) = ql.qs;
+  }
+  __syncthreads();
+  v4f qv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qv[i] = *reinterpret_cast<const v4f*>(s_q + r * kQRow + 32 * kq + 4 * i);
   // lane l ends with q_rot[row r][16 wave + 4 kq + i], i = 0..3 (four
   // independent accumulation chains)
   v4f part[4];
@@ -209,8 +218,7 @@ __device__ __forceinline__ void query_operands(const DecodeParams& p, const Quer
   for (int c = 0; c < 4; ++c) part[c] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 32; ++s)
-    part[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(ql.pi[s >> 2][s & 3], query_element(p, ql, s), part[s & 3],
-                                                       0, 0, 0);
+    part[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(ql.pit[s], qv[s >> 2][s & 3], part[s & 3], 0, 0, 0);
   const v4f acc = (part[0] + part[1]) + (part[2] + part[3]);
   const float m4 = rowmax4(fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])), fmaxf(fabsf(acc[2]), fabsf(acc[3]))));
   if (kq == 0) s_max[wave * 16 + r] = m4;
@@ -334,7 +342,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
   __builtin_amdgcn_sched_barrier(0);
 
   QueryOps qo;
-  query_operands(p, ql, s_max, s_op, qo);
+  // the staged query rows occupy the start of s_buf until the prologue's
+  // last barrier; the waves' tile areas are written only after it
+  query_operands(p, ql, reinterpret_cast<float*>(s_buf), s_max, s_op, qo);
   const float rowc = qo.rowc;
   const uint32_t kh1 = p.klut[1], kh0 = p.klut[0], kl1 = p.klut[3], kl0 = p.klut[2];
   const uint32_t vh1 = p.vlut[1], vh0 = p.vlut[0], vl1 = p.vlut[3], vl0 = p.vlut[2];
@@ -342,10 +352,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
 
   uint8_t* sb = s_buf + wave * kWaveLds;
   float* sn = reinterpret_cast<float*>(sb + kSelLds);            // [2][64] norms of the tile
-  v4f* so = reinterpret_cast<v4f*>(sb + kSelLds + kNormLds);     // [16 rows][32] x 4 coords
+  v4f* so = reinterpret_cast<v4f*>(sb + kSelLds + kNormLds);     // [16 rows][kAccRow] x 4 coords
   // float output of row n, coordinates 16u + 4h .. +3, lives in LDS: it is
   // touched only when the int32 accumulators are flushed
-  auto oref = [&](int u) -> v4f& { return so[n * 32 + 4 * u + h]; };
+  // (rows kAccRow slots apart: a 16-lane group's 16-byte accesses, one row
+  // each, cover all 64 banks)
+  auto oref = [&](int u) -> v4f& { return so[n * kAccRow + 4 * u + h]; };
 #pragma unroll
   for (int u = 0; u < 8; ++u) oref(u) = v4f{0.f, 0.f, 0.f, 0.f};
 
@@ -544,44 +556,53 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
 
-  // ---- merge the waves' partials of this chunk in LDS
+  // ---- merge the waves' partials of this chunk in LDS: each wave's block
+  // holds its 16 rows (padded to kMoRow floats, so that a 16-lane group of
+  // 16-byte stores covers all 64 banks) and its (m, l); the per-(wave, row)
+  // weights 2^(m_w - M) are formed once
+  constexpr int kMoRow = kD + 4, kMoBlock = 16 * kMoRow + 32;
   __syncthreads();
   float* cw = reinterpret_cast<float*>(s_buf);
+  float* s_wt = cw + kWaves * kMoBlock;  // [kWaves][16] weights, then [16] M, [16] L
   {
-    float* mo = cw + wave * (16 * kD + 32);
+    float* mo = cw + wave * kMoBlock;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mo[n * kD + 16 * u + 4 * h + i] = of[u][i];
+    for (int u = 0; u < 8; ++u) *reinterpret_cast<v4f*>(mo + n * kMoRow + 16 * u + 4 * h) = of[u];
     if (h == 0) {
-      mo[16 * kD + n] = m_ref;
-      mo[16 * kD + 16 + n] = l_run;
+      mo[16 * kMoRow + n] = m_ref;
+      mo[16 * kMoRow + 16 + n] = l_run;
     }
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int r = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cw[w * kMoBlock + 16 * kMoRow + r]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = cw[w * kMoBlock + 16 * kMoRow + r];
+      const float wt = (M == -INFINITY || mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      s_wt[w * 16 + r] = wt;
+      L = fmaf(wt, cw[w * kMoBlock + 16 * kMoRow + 16 + r], L);
+    }
+    s_wt[kWaves * 16 + r] = M;
+    s_wt[kWaves * 16 + 16 + r] = L;
   }
   __syncthreads();
   float* po = p.part_o + ((size_t)bg * p.n_chunks + chunk_id) * rows * kD;
   float* pml = p.part_ml + ((size_t)bg * p.n_chunks + chunk_id) * rows * 2;
   for (int e = threadIdx.x; e < rows * kD; e += kThreads) {
-    const int r = e / kD;
-    float M = -INFINITY;
+    const int r = e / kD, c = e % kD;
+    float O = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cw[w * (16 * kD + 32) + 16 * kD + r]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float* mo = cw + w * (16 * kD + 32);
-        const float mw = mo[16 * kD + r];
-        const float wt = mw == -INFINITY ? 0.f : exp2f(mw - M);
-        L = fmaf(wt, mo[16 * kD + 16 + r], L);
-        O = fmaf(wt, mo[e], O);
-      }
-    }
+    for (int w = 0; w < kWaves; ++w) O = fmaf(s_wt[w * 16 + r], cw[w * kMoBlock + r * kMoRow + c], O);
     po[e] = O;
-    if ((e % kD) == 0) {
-      pml[2 * r] = M;
-      pml[2 * r + 1] = L;
-    }
+  }
+  if (threadIdx.x < rows) {
+    pml[2 * threadIdx.x] = s_wt[kWaves * 16 + threadIdx.x];
+    pml[2 * threadIdx.x + 1] = s_wt[kWaves * 16 + 16 + threadIdx.x];
   }
 }
 
