@@ -42,6 +42,10 @@ def _args():
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--layers", type=int, default=0, help="override the number of layer buffers")
+    ap.add_argument("--all-layers-call", action="store_true",
+                    help="also time one tq_decode_attention over every layer at once (a labelled upper bound, kept "
+                         "out of the default run so that its dispatches do not mix with the per-layer calls in "
+                         "kernel traces)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes three times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -417,8 +421,8 @@ def main():
     prefill_attn = prefill_timing(tq, wl, w, kc, vc, kcs[0], vcs[0], lens, max_len, dev, stream,
                                   max(3, args.steps // 2))
 
-    single = None
-    if stacked:
+    single = "not run (bench.py --all-layers-call)" if stacked else None
+    if stacked and args.all_layers_call:
         # upper bound, not the step: one call over every layer as a batch of
         # `layers` sequences; a real decode step cannot do this, since each
         # layer's query needs the previous layer's output
