@@ -145,6 +145,9 @@ static int device_cus() {
   return cached[dev];
 }
 
+// Largest chunk of a batched launch on the matrix-core paths (tokens).
+constexpr int64_t kRaggedChunk = 8192;
+
 DecodePlan plan_decode_mfma(int batch, int hkv, int rows, int d, int64_t max_len, bool prod) {
   DecodePlan p{};
   p.rows = rows;
@@ -154,6 +157,10 @@ DecodePlan plan_decode_mfma(int batch, int hkv, int rows, int d, int64_t max_len
   // the merge takes at most 4096 of them per row
   const int64_t per_head = std::max<int64_t>(1, (2 * device_cus() + heads - 1) / heads);
   int64_t chunk = (max_len + per_head - 1) / per_head;
+  // a batch may be ragged: the host knows only the longest sequence, so the
+  // chunk is capped and a long sequence spreads over several workgroups
+  // (chunks past a sequence's end exit at once)
+  if (batch > 1) chunk = std::min<int64_t>(chunk, kRaggedChunk);
   chunk = std::max<int64_t>(step, ((chunk + step - 1) / step) * step);
   chunk = std::max<int64_t>(chunk, ((max_len + 1023) / 1024 + step - 1) / step * step);  // <= 1024 chunks
   p.chunk = (int)chunk;
@@ -181,6 +188,7 @@ DecodePlan plan_decode_fast(int batch, int hkv, int rows, int d, int64_t max_len
   const int64_t heads = (int64_t)batch * hkv;
   const int64_t per_head = std::max<int64_t>(1, (device_cus() + heads - 1) / heads);  // one workgroup per CU
   int64_t chunk = (max_len + per_head - 1) / per_head;
+  if (batch > 1) chunk = std::min<int64_t>(chunk, kRaggedChunk);  // as in plan_decode_mfma
   chunk = ((chunk + step - 1) / step) * step;
   chunk = std::max<int64_t>(step, chunk);
   chunk = std::max<int64_t>(chunk, ((max_len + 127) / 128 + step - 1) / step * step);  // <= 128 chunks
