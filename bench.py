@@ -369,8 +369,10 @@ def main():
     stream = torch.cuda.current_stream()
     calls = make_calls(stream.cuda_stream)
 
-    def step(events=None):
+    def step(events=None, app_events=None):
         for i, c in enumerate(calls):
+            if app_events is not None:
+                app_events[i].record(stream)
             check(lib.tq_quantize_append_kv(*c[0]))
             if events is not None:
                 events[i][0].record(stream)
@@ -386,14 +388,18 @@ def main():
     # an eager pass (the dominant kernels; roofline.achieved)
     events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
               for _ in range(args.steps)]
+    # the append call is bracketed by an event recorded before it and the
+    # decode call's start event
+    app_events = [[torch.cuda.Event(enable_timing=True) for _ in calls] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s_ in range(args.steps):
-        step(events[s_])
+        step(events[s_], app_events[s_])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step_eager = (t1 - t0) * 1000.0 / args.steps
     dec_ms = [e0.elapsed_time(e1) for row in events for (e0, e1) in row]
+    app_ms = [a.elapsed_time(ev[0]) for arow, erow in zip(app_events, events) for a, ev in zip(arow, erow)]
     dec_ms_avg = float(np.mean(dec_ms))
 
     # the step as one HIP graph (the per-layer kernels without launch gaps):
@@ -513,6 +519,9 @@ def main():
             "traffic_source": traffic_src,
             "decode_call_us": dec_ms_avg * 1000.0,
             "decode_call_us_p10_p50_p90": [float(np.percentile(dec_ms, q)) * 1000.0 for q in (10, 50, 90)],
+            "append_call": f"tq_quantize_append_kv of the {append} new K and V tokens of every sequence and KV head "
+                           "of a layer, timed with HIP events on the launch stream",
+            "append_call_us": float(np.mean(app_ms)) * 1000.0,
             "step": f"one HIP graph of the {layers} per-layer (append K+V, decode) calls" if not args.no_graph
                     else "eager launches",
             "ms_per_step_eager": ms_per_step_eager,
