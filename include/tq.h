@@ -157,8 +157,11 @@ tq_status tq_quantize_append(const tq_codec* codec, const void* x, int32_t x_dty
                              int32_t n_new, const int64_t* x_strides, const tq_cache* dst, const int32_t* d_pos,
                              void* stream);
 
-/* Quantise the new keys and values of one decode step in one launch ([omlx]
- * update_and_fetch appends keys and values together).  Same semantics and
+/* Quantise the new keys and values of one decode step in one call ([omlx]
+ * update_and_fetch appends keys and values together): one kernel launch when
+ * both codecs take the same append kernel, two when they differ (at head_dim
+ * <= 128 MSE caches take a per-group kernel, Prod and group caches a
+ * per-vector one).  Same semantics and
  * errors as two tq_quantize_append calls, one with (kc, k, k_strides, kdst)
  * and one with (vc, v, v_strides, vdst), sharing dtype, sizes and d_pos;
  * kc and vc must have the same head_dim (else CONFIG_MISMATCH). */
