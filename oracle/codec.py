@@ -30,7 +30,12 @@ Readings taken where the pages are silent
   the dyadic grid 2^-E, E the largest integer with max|c| 2^E <= 16256 (about
   14 significant bits; every stored value is an exact float32 and an exact
   15-bit integer multiple of 2^-E).  Boundaries are the exact midpoints of
-  the stored centroids.
+  the stored centroids.  The grid is a storage format of the codec (each
+  stored centroid is 256 hi + lo grid units with 8-bit pieces); the
+  unrounded float64 solution is kept in ``Codec.solution`` so that the cost
+  of the grid can be checked against it: with |stored - solution| <= 2^-(E+1)
+  the per-vector distortion d D grows by at most d 2^-(2E+2) (the centroid
+  condition makes the first-order term vanish).
 * QJL sketch: S has iid N(0, 1) entries (stream 1 of the codec seed) and acts
   on the rotated residual; stored as float32.
 """

@@ -136,6 +136,52 @@ def test_stored_codebook_grid(d, bits):
     assert np.all(cb.centroids.astype(np.float32).astype(np.float64) == cb.centroids)
 
 
+def _stored_cells(d, c, bnd):
+    """Distortion sum_k int_cell_k (y - c_k)^2 f_d(y) dy and the largest
+    |E[Y | cell_k] - c_k|, cells bounded by ``bnd``, by adaptive quadrature
+    (independent of the closed forms the solver uses)."""
+    f = lambda y: codec.coordinate_density(d, y)
+    edges = np.concatenate(([-1.0], bnd, [1.0]))
+    dist, resid = 0.0, 0.0
+    for k in range(len(c)):
+        lo, hi = edges[k], edges[k + 1]
+        q = lambda g: integrate.quad(g, lo, hi, epsabs=0, epsrel=1e-12, limit=200)[0]
+        dist += q(lambda y: (y - c[k]) ** 2 * f(y))
+        resid = max(resid, abs(q(lambda y: y * f(y)) / q(f) - c[k]))
+    return dist, resid
+
+
+# every (head_dim, index bits) a workload or a test of this repository uses
+GRID_COST_CASES = [(128, 1), (128, 2), (128, 3), (128, 4), (256, 1), (256, 2), (256, 3), (256, 4),
+                   (32, 1), (32, 2), (32, 4), (64, 2), (64, 3), (64, 4), (96, 3), (96, 4), (160, 1),
+                   (192, 1), (192, 2), (224, 4)]
+
+
+@pytest.mark.parametrize("d,bits", GRID_COST_CASES)
+def test_stored_codebook_distortion_cost(d, bits):
+    """Cost of storing the centroids on the 2^-E grid, pinned by the
+    mathematics of the Lloyd-Max conditions rather than by the solver.
+
+    Moving centroid k of an optimal quantiser by delta_k with its cell fixed
+    adds exactly P(cell_k) delta_k^2 to the distortion (the centroid is the
+    cell's conditional mean), and re-drawing the cells at the new midpoints
+    can only lower it (nearest-neighbour cells are optimal for given
+    centroids).  With |delta_k| <= 2^-(E+1) the stored codebook's per-vector
+    distortion d D therefore exceeds the optimum by at most d 2^-(2E+2).
+    Each stored centroid also stays within half a grid unit of the
+    conditional mean of its own (stored) cell."""
+    cb = codec.make_codec(d, bits, 0, codec.MODE_MSE)
+    e = cb.grid_exp
+    sol = cb.solution
+    d_opt, r_opt = _stored_cells(d, sol, 0.5 * (sol[:-1] + sol[1:]))
+    d_sto, r_sto = _stored_cells(d, cb.centroids, cb.boundaries)
+    assert r_opt < 1e-11                                  # the solution is a fixed point
+    excess = d * (d_sto - d_opt)
+    assert -1e-12 <= excess <= d * 2.0 ** (-2 * e - 2)
+    assert excess <= 1e-6 * d * d_opt                     # relative cost below one part in 10^6
+    assert r_sto <= 2.0 ** (-e - 1)
+
+
 def test_survey_derived_values():
     # sqrt(d) * c for d = 128, 3 bits (derived independently with scipy when
     # the build was planned; 5 decimals)
