@@ -150,12 +150,20 @@ tq_status tq_codec_upload(const tq_codec* codec);
  *            x_strides[0..3], s3 == 1 required), dtype x_dtype
  *   dst      the cache to write; dst->batch == batch, dst->heads == heads
  *   d_pos    device int32[batch]: token t of sequence b goes to position
- *            d_pos[b] + t.  Positions outside [0, cap) are skipped (nothing
- *            is written for them); validate positions on the host.
- * Errors: INVALID_ARG, CONFIG_MISMATCH (cache shape), HIP. */
+ *            d_pos[b] + t
+ *   pos_end  host bound on the written end after the append: the caller
+ *            guarantees d_pos[b] + n_new <= pos_end for every b (the
+ *            positions live on the device, so the library checks the bound,
+ *            not the positions).  pos_end > dst->cap is refused with
+ *            CAPACITY before anything is launched.  A device position that
+ *            breaks the caller's guarantee (d_pos[b] < 0, or a token at or
+ *            past cap) is never written out of bounds: such tokens are
+ *            dropped.
+ * Errors: INVALID_ARG (pos_end < n_new, ...), CONFIG_MISMATCH (cache shape),
+ * CAPACITY (pos_end > cap), HIP. */
 tq_status tq_quantize_append(const tq_codec* codec, const void* x, int32_t x_dtype, int32_t batch, int32_t heads,
                              int32_t n_new, const int64_t* x_strides, const tq_cache* dst, const int32_t* d_pos,
-                             void* stream);
+                             int64_t pos_end, void* stream);
 
 /* Quantise the new keys and values of one decode step in one call ([omlx]
  * update_and_fetch appends keys and values together): one kernel launch when
@@ -163,12 +171,13 @@ tq_status tq_quantize_append(const tq_codec* codec, const void* x, int32_t x_dty
  * <= 128 MSE caches take a per-group kernel, Prod and group caches a
  * per-vector one).  Same semantics and
  * errors as two tq_quantize_append calls, one with (kc, k, k_strides, kdst)
- * and one with (vc, v, v_strides, vdst), sharing dtype, sizes and d_pos;
- * kc and vc must have the same head_dim (else CONFIG_MISMATCH). */
+ * and one with (vc, v, v_strides, vdst), sharing dtype, sizes, d_pos and
+ * pos_end (CAPACITY if pos_end exceeds either cache's cap); kc and vc must
+ * have the same head_dim (else CONFIG_MISMATCH). */
 tq_status tq_quantize_append_kv(const tq_codec* kc, const tq_codec* vc, const void* k, const void* v,
                                 int32_t x_dtype, int32_t batch, int32_t heads, int32_t n_new,
                                 const int64_t* k_strides, const int64_t* v_strides, const tq_cache* kdst,
-                                const tq_cache* vdst, const int32_t* d_pos, void* stream);
+                                const tq_cache* vdst, const int32_t* d_pos, int64_t pos_end, void* stream);
 
 /* Bytes of device workspace tq_decode_attention needs for these sizes (the
  * per-chunk partial results of the split over the token axis). */
@@ -184,7 +193,9 @@ tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32
  *   d_len    device int32[batch]: attended length N_b of each sequence
  *            (after the q_len new tokens were appended); clamped to cap;
  *            every N_b must be <= max_len (tokens beyond max_len are ignored)
- *   max_len  host bound on the lengths, 1 <= max_len <= cap; sizes the grid
+ *   max_len  host bound on the lengths, 1 <= max_len <= cap and
+ *            max_len <= 2^26 (67,108,864 tokens per sequence; UNSUPPORTED
+ *            above); sizes the grid
  *   scale    softmax scale (1/sqrt(head_dim) in [val])
  *   out      device float [batch][n_q_heads][q_len][head_dim]
  *   ws       device workspace of ws_bytes >= tq_decode_workspace_size(...),
@@ -194,7 +205,7 @@ tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32
  * sees tokens t <= N_b - q_len + i ([omlx] make_mask: causal for new tokens).
  * A row that sees no token gets zeros.
  * Errors: INVALID_ARG, UNSUPPORTED (more than 16 rows per KV head, 8 above
- * head_dim 128: use tq_prefill_attention), CONFIG_MISMATCH, CAPACITY
+ * head_dim 128: use tq_prefill_attention; max_len above 2^26), CONFIG_MISMATCH, CAPACITY
  * (max_len > cap), WORKSPACE, HIP. */
 tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void* q, int32_t q_dtype, int32_t batch,
                               int32_t n_q_heads, int32_t n_kv_heads, int32_t q_len, const tq_cache* k,
@@ -242,6 +253,16 @@ tq_status tq_prefill_attention(const tq_codec* kc, const tq_codec* vc, const voi
 tq_status tq_cache_gather(const tq_codec* src_codec, const tq_cache* src, const tq_codec* dst_codec,
                           const tq_cache* dst, const int32_t* src_batch, const int32_t* src_start,
                           const int32_t* count, void* stream);
+
+/* Measurement: read `bytes` of device memory once, as a plain streaming read
+ * (16-byte loads, eight in flight per thread), the reference a decode
+ * kernel's HBM rate is compared with.  Nothing in the library's path uses it.
+ *   buf      device, 16-byte aligned; bytes a positive multiple of 16
+ *   sink     device uint32[blocks * 256] (caller-owned; written only in the
+ *            rare case that a thread's folded words equal one fixed value)
+ *   blocks   workgroups of 256 threads, 1..2^20
+ * Errors: INVALID_ARG, HIP. */
+tq_status tq_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, int32_t blocks, void* stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* tq_last_error(void);

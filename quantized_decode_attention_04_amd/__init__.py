@@ -33,4 +33,5 @@ from ._binding import (  # noqa: F401
     tq_quantize_append,
     tq_quantize_append_kv,
     tq_status_string,
+    tq_stream_read,
 )

@@ -59,9 +59,10 @@ def _load() -> ctypes.CDLL:
         "tq_codec_get_info": (I32, [P, ctypes.POINTER(_CodecInfo)]),
         "tq_codec_export": (I32, [P, P, P, P, P]),
         "tq_codec_upload": (I32, [P]),
-        "tq_quantize_append": (I32, [P, P, I32, I32, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(_Cache), P, P]),
+        "tq_quantize_append": (I32, [P, P, I32, I32, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(_Cache), P, I64,
+                                     P]),
         "tq_quantize_append_kv": (I32, [P, P, P, P, I32, I32, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(I64),
-                                        ctypes.POINTER(_Cache), ctypes.POINTER(_Cache), P, P]),
+                                        ctypes.POINTER(_Cache), ctypes.POINTER(_Cache), P, I64, P]),
         "tq_decode_workspace_size": (I32, [P, P, I32, I32, I32, I32, I64, ctypes.POINTER(SZ)]),
         "tq_decode_attention": (I32, [P, P, P, I32, I32, I32, I32, I32, ctypes.POINTER(_Cache),
                                       ctypes.POINTER(_Cache), P, I64, ctypes.c_float, P, P, SZ, P]),
@@ -70,6 +71,7 @@ def _load() -> ctypes.CDLL:
                                   ctypes.POINTER(I32), ctypes.POINTER(I32), P]),
         "tq_prefill_attention": (I32, [P, P, P, I32, I32, I32, I32, I32, ctypes.POINTER(_Cache),
                                        ctypes.POINTER(_Cache), P, I64, ctypes.c_float, P, P, SZ, P]),
+        "tq_stream_read": (I32, [P, U64, P, I32, P]),
         "tq_last_error": (ctypes.c_char_p, []),
         "tq_status_string": (ctypes.c_char_p, [I32]),
     }
@@ -85,7 +87,8 @@ _lib = _load()
 EXPORTED = (
     "tq_codec_create", "tq_codec_destroy", "tq_codec_get_info", "tq_codec_export", "tq_codec_upload",
     "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_workspace_size", "tq_decode_attention",
-    "tq_prefill_workspace_size", "tq_prefill_attention", "tq_cache_gather", "tq_last_error", "tq_status_string",
+    "tq_prefill_workspace_size", "tq_prefill_attention", "tq_cache_gather", "tq_stream_read", "tq_last_error",
+    "tq_status_string",
 )
 
 
@@ -233,9 +236,10 @@ def _on_device(*ts):
             raise ValueError("tensor must be on a HIP device")
 
 
-def tq_quantize_append(codec: Codec, x, cache: Cache, pos, stream=None) -> None:
+def tq_quantize_append(codec: Codec, x, cache: Cache, pos, pos_end: int, stream=None) -> None:
     """Quantise x [batch, heads, n_new, head_dim] into ``cache`` at positions
-    pos[b] + t (pos: int32 device tensor [batch])."""
+    pos[b] + t (pos: int32 device tensor [batch]); ``pos_end`` is the caller's
+    host bound on pos[b] + n_new (TQError CAPACITY above cache.cap)."""
     import torch
     _on_device(x, pos, *cache.arrays().values())
     if x.dim() != 4 or x.shape[3] != codec.info["head_dim"] or x.stride(3) != 1:
@@ -246,13 +250,14 @@ def tq_quantize_append(codec: Codec, x, cache: Cache, pos, stream=None) -> None:
     st = cache.as_struct()
     _check(_lib.tq_quantize_append(codec.handle, ctypes.c_void_p(x.data_ptr()), _dtype_code(x), int(x.shape[0]),
                                    int(x.shape[1]), int(x.shape[2]), strides, ctypes.byref(st),
-                                   ctypes.c_void_p(pos.data_ptr()), _stream(stream)))
+                                   ctypes.c_void_p(pos.data_ptr()), int(pos_end), _stream(stream)))
 
 
-def tq_quantize_append_kv(kc: Codec, vc: Codec, k, v, kcache: Cache, vcache: Cache, pos, stream=None) -> None:
+def tq_quantize_append_kv(kc: Codec, vc: Codec, k, v, kcache: Cache, vcache: Cache, pos, pos_end: int,
+                          stream=None) -> None:
     """Quantise the new keys k and values v [batch, heads, n_new, head_dim]
     (same dtype and sizes) into their caches at positions pos[b] + t, in one
-    launch."""
+    launch; ``pos_end`` bounds pos[b] + n_new as in tq_quantize_append."""
     import torch
     _on_device(k, v, pos, *kcache.arrays().values(), *vcache.arrays().values())
     for x in (k, v):
@@ -269,7 +274,8 @@ def tq_quantize_append_kv(kc: Codec, vc: Codec, k, v, kcache: Cache, vcache: Cac
     _check(_lib.tq_quantize_append_kv(kc.handle, vc.handle, ctypes.c_void_p(k.data_ptr()),
                                       ctypes.c_void_p(v.data_ptr()), _dtype_code(k), int(k.shape[0]),
                                       int(k.shape[1]), int(k.shape[2]), ks_, vs_, ctypes.byref(kst),
-                                      ctypes.byref(vst), ctypes.c_void_p(pos.data_ptr()), _stream(stream)))
+                                      ctypes.byref(vst), ctypes.c_void_p(pos.data_ptr()), int(pos_end),
+                                      _stream(stream)))
 
 
 def tq_decode_workspace_size(kc: Codec, vc: Codec, batch: int, n_q_heads: int, n_kv_heads: int, q_len: int,
@@ -353,3 +359,15 @@ def tq_cache_gather(src_codec: Codec, src: Cache, dst_codec: Codec, dst: Cache, 
     ss, ds = src.as_struct(), dst.as_struct()
     _check(_lib.tq_cache_gather(src_codec.handle, ctypes.byref(ss), dst_codec.handle, ctypes.byref(ds),
                                 arr(src_batch), arr(src_start), arr(count), _stream(stream)))
+
+
+def tq_stream_read(buf, sink, blocks: int, stream=None) -> None:
+    """Measurement: one streaming read of the device tensor ``buf`` (all its
+    bytes; 16-byte aligned, a multiple of 16 bytes); ``sink``: a device tensor
+    of at least blocks * 256 32-bit elements."""
+    _on_device(buf, sink)
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() * sink.element_size() < 4 * 256 * int(blocks):
+        raise ValueError("sink needs blocks * 256 32-bit elements")
+    _check(_lib.tq_stream_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_uint64(nbytes),
+                               ctypes.c_void_p(sink.data_ptr()), int(blocks), _stream(stream)))

@@ -102,109 +102,6 @@ bool cache_ok(const tq_cache* c, const tq::HostCodec& h, std::string* why) {
 
 }  // namespace
 
-namespace tq {
-
-DecodePlan plan_decode(int batch, int hkv, int rows, int d, int64_t max_len, bool prod) {
-  DecodePlan p{};
-  p.rows = rows;
-  const int64_t tile = 256;
-  // about two 256-token tiles per workgroup: measured 6-7% faster than one
-  // (the query prologue is amortised) and than four (fewer workgroups)
-  const int64_t target_items = 512;
-  const int64_t total = (int64_t)batch * hkv * max_len;
-  int64_t chunk = (total + target_items - 1) / target_items;
-  chunk = ((chunk + tile - 1) / tile) * tile;
-  chunk = std::max<int64_t>(tile, std::min<int64_t>(chunk, 16384));
-  p.chunk = (int)chunk;
-  p.n_chunks = (int)((max_len + chunk - 1) / chunk);
-  const size_t bg = (size_t)batch * hkv;
-  size_t off = 0;
-  p.off_qrot = off;
-  off = align256(off + bg * rows * d * sizeof(float));
-  p.off_qs = off;
-  if (prod) off = align256(off + bg * rows * d * sizeof(float));
-  p.off_part_o = off;
-  off = align256(off + bg * p.n_chunks * rows * d * sizeof(float));
-  p.off_part_ml = off;
-  off = align256(off + bg * p.n_chunks * rows * 2 * sizeof(float));
-  p.total = off;
-  return p;
-}
-
-// Compute units of the current device (256 on MI355X; the fallback when no
-// device answers keeps workspace sizing usable on hosts without a GPU).
-static int device_cus() {
-  static int cached[kMaxDevices] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  if (cached[dev] <= 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
-// Largest chunk of a batched launch on the matrix-core paths (tokens).
-constexpr int64_t kRaggedChunk = 8192;
-
-DecodePlan plan_decode_mfma(int batch, int hkv, int rows, int d, int64_t max_len, bool prod) {
-  DecodePlan p{};
-  p.rows = rows;
-  const int64_t step = 256;  // four waves x 64-token tiles
-  const int64_t heads = (int64_t)batch * hkv;
-  // about two workgroups per compute unit; every wave writes a partial and
-  // the merge takes at most 4096 of them per row
-  const int64_t per_head = std::max<int64_t>(1, (2 * device_cus() + heads - 1) / heads);
-  int64_t chunk = (max_len + per_head - 1) / per_head;
-  // a batch may be ragged: the host knows only the longest sequence, so the
-  // chunk is capped and a long sequence spreads over several workgroups
-  // (chunks past a sequence's end exit at once)
-  if (batch > 1) chunk = std::min<int64_t>(chunk, kRaggedChunk);
-  chunk = std::max<int64_t>(step, ((chunk + step - 1) / step) * step);
-  chunk = std::max<int64_t>(chunk, ((max_len + 1023) / 1024 + step - 1) / step * step);  // <= 1024 chunks
-  p.chunk = (int)chunk;
-  p.n_chunks = (int)((max_len + chunk - 1) / chunk);
-  const size_t bg = (size_t)batch * hkv;
-  const size_t parts = (size_t)p.n_chunks * 4;
-  size_t off = 0;
-  p.off_qrot = off;
-  off = align256(off + bg * rows * d * sizeof(float));
-  p.off_qs = off;
-  if (prod) off = align256(off + bg * rows * d * sizeof(float));
-  p.off_part_o = off;
-  off = align256(off + bg * parts * rows * d * sizeof(float));
-  p.off_part_ml = off;
-  off = align256(off + bg * parts * rows * 2 * sizeof(float));
-  p.total = off;
-  return p;
-}
-
-DecodePlan plan_decode_fast(int batch, int hkv, int rows, int d, int64_t max_len) {
-  DecodePlan p{};
-  p.rows = rows;
-  p.fast = true;
-  const int64_t step = 512;                 // eight waves x 64-token tiles
-  const int64_t heads = (int64_t)batch * hkv;
-  const int64_t per_head = std::max<int64_t>(1, (device_cus() + heads - 1) / heads);  // one workgroup per CU
-  int64_t chunk = (max_len + per_head - 1) / per_head;
-  if (batch > 1) chunk = std::min<int64_t>(chunk, kRaggedChunk);  // as in plan_decode_mfma
-  chunk = ((chunk + step - 1) / step) * step;
-  chunk = std::max<int64_t>(step, chunk);
-  chunk = std::max<int64_t>(chunk, ((max_len + 127) / 128 + step - 1) / step * step);  // <= 128 chunks
-  p.chunk = (int)chunk;
-  p.n_chunks = (int)((max_len + chunk - 1) / chunk);
-  const size_t bg = (size_t)batch * hkv;
-  size_t off = 0;
-  p.off_part_o = off;
-  off = align256(off + bg * p.n_chunks * rows * d * sizeof(float));
-  p.off_part_ml = off;
-  off = align256(off + bg * p.n_chunks * rows * 2 * sizeof(float));
-  p.total = off;
-  return p;
-}
-
-}  // namespace tq
 
 namespace {
 
@@ -312,7 +209,7 @@ tq_status tq_codec_upload(const tq_codec* c) {
 // n_new == 0 (nothing to launch).
 static tq_status prepare_append(const char* who, const tq_codec* c, const void* x, int32_t x_dtype, int32_t batch,
                                 int32_t heads, int32_t n_new, const int64_t* x_strides, const tq_cache* dst,
-                                const int32_t* d_pos, tq::QuantizeParams* out, bool* empty) {
+                                const int32_t* d_pos, int64_t pos_end, tq::QuantizeParams* out, bool* empty) {
   const std::string w(who);
   if (!c || !x || !dst || !d_pos) return fail(TQ_ERR_INVALID_ARG, w + ": NULL argument");
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, w + ": bad x_dtype");
@@ -323,6 +220,13 @@ static tq_status prepare_append(const char* who, const tq_codec* c, const void* 
   if (!cache_ok(dst, h, &why)) return fail(TQ_ERR_INVALID_ARG, w + ": " + why);
   if (dst->batch != batch || dst->heads != heads)
     return fail(TQ_ERR_CONFIG_MISMATCH, w + ": cache batch/heads differ from the input's");
+  // the written end after the append, bounded on the host ([omlx]
+  // update_and_fetch writes at the written end; a write past the allocated
+  // capacity must not be lost silently)
+  if (pos_end < n_new) return fail(TQ_ERR_INVALID_ARG, w + ": pos_end is below n_new");
+  if (pos_end > dst->cap)
+    return fail(TQ_ERR_CAPACITY, w + ": the append ends at " + std::to_string(pos_end) + ", past the cache capacity " +
+                                     std::to_string(dst->cap));
   int64_t s0, s1, s2;
   if (x_strides) {
     if (x_strides[3] != 1) return fail(TQ_ERR_INVALID_ARG, w + ": coordinate stride must be 1");
@@ -336,11 +240,6 @@ static tq_status prepare_append(const char* who, const tq_codec* c, const void* 
     s0 = (int64_t)heads * s1;
   }
   *empty = n_new == 0;
-  tq::DevTables* t = nullptr;
-  if (!*empty && h.mode != TQ_MODE_GROUP) {
-    tq_status st = ensure_tables(c, &t);
-    if (st != TQ_OK) return st;
-  }
   tq::QuantizeParams& p = *out;
   p = tq::QuantizeParams{};
   p.x = x;
@@ -365,14 +264,6 @@ static tq_status prepare_append(const char* who, const tq_codec* c, const void* 
     p.x_vec16 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (s0 * es) % 16 == 0 && (s1 * es) % 16 == 0 &&
                 (s2 * es) % 16 == 0;
   }
-  if (t) {
-    p.pit = t->pit;
-    p.pi = t->pi;
-    p.st = t->st;
-    p.s = t->s;
-    p.cent = t->cent;
-    p.bnd = t->bnd;
-  }
   p.idx = dst->idx;
   p.norm = dst->norm;
   p.rnorm = dst->rnorm;
@@ -384,17 +275,35 @@ static tq_status prepare_append(const char* who, const tq_codec* c, const void* 
   return TQ_OK;
 }
 
+// After every argument of a call has been checked: the codec's device tables
+// (uploaded on first use on this device) go into its parameter block.
+static tq_status bind_tables(const tq_codec* c, tq::QuantizeParams* p) {
+  if (c->h.mode == TQ_MODE_GROUP) return TQ_OK;
+  tq::DevTables* t = nullptr;
+  const tq_status st = ensure_tables(c, &t);
+  if (st != TQ_OK) return st;
+  p->pit = t->pit;
+  p->pi = t->pi;
+  p->st = t->st;
+  p->s = t->s;
+  p->cent = t->cent;
+  p->bnd = t->bnd;
+  return TQ_OK;
+}
+
 extern "C" {
 
 tq_status tq_quantize_append(const tq_codec* c, const void* x, int32_t x_dtype, int32_t batch, int32_t heads,
                              int32_t n_new, const int64_t* x_strides, const tq_cache* dst, const int32_t* d_pos,
-                             void* stream) {
+                             int64_t pos_end, void* stream) {
   tq::QuantizeSets sets{};
   bool empty = false;
   tq_status st = prepare_append("tq_quantize_append", c, x, x_dtype, batch, heads, n_new, x_strides, dst, d_pos,
-                                &sets.s[0], &empty);
+                                pos_end, &sets.s[0], &empty);
   if (st != TQ_OK) return st;
   if (empty) return TQ_OK;
+  st = bind_tables(c, &sets.s[0]);
+  if (st != TQ_OK) return st;
   hipError_t e = tq::launch_quantize(sets, 1, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tq_quantize_append launch");
   return TQ_OK;
@@ -403,18 +312,22 @@ tq_status tq_quantize_append(const tq_codec* c, const void* x, int32_t x_dtype, 
 tq_status tq_quantize_append_kv(const tq_codec* kc, const tq_codec* vc, const void* k, const void* v,
                                 int32_t x_dtype, int32_t batch, int32_t heads, int32_t n_new,
                                 const int64_t* k_strides, const int64_t* v_strides, const tq_cache* kdst,
-                                const tq_cache* vdst, const int32_t* d_pos, void* stream) {
+                                const tq_cache* vdst, const int32_t* d_pos, int64_t pos_end, void* stream) {
   tq::QuantizeSets sets{};
   bool empty_k = false, empty_v = false;
   tq_status st = prepare_append("tq_quantize_append_kv (keys)", kc, k, x_dtype, batch, heads, n_new, k_strides, kdst,
-                                d_pos, &sets.s[0], &empty_k);
+                                d_pos, pos_end, &sets.s[0], &empty_k);
   if (st != TQ_OK) return st;
   st = prepare_append("tq_quantize_append_kv (values)", vc, v, x_dtype, batch, heads, n_new, v_strides, vdst, d_pos,
-                      &sets.s[1], &empty_v);
+                      pos_end, &sets.s[1], &empty_v);
   if (st != TQ_OK) return st;
   if (kc->h.d != vc->h.d)
     return fail(TQ_ERR_CONFIG_MISMATCH, "tq_quantize_append_kv: key and value codecs have different head_dim");
   if (empty_k) return TQ_OK;
+  st = bind_tables(kc, &sets.s[0]);
+  if (st != TQ_OK) return st;
+  st = bind_tables(vc, &sets.s[1]);
+  if (st != TQ_OK) return st;
   hipError_t e = tq::launch_quantize(sets, 2, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tq_quantize_append_kv launch");
   return TQ_OK;
@@ -437,6 +350,8 @@ static tq_status check_decode_shapes(const tq_codec* kc, const tq_codec* vc, int
     return fail(TQ_ERR_INVALID_ARG, "decode: batch, heads and q_len must be positive");
   if (hq % hkv) return fail(TQ_ERR_INVALID_ARG, "decode: n_q_heads must be a multiple of n_kv_heads");
   if (max_len <= 0) return fail(TQ_ERR_INVALID_ARG, "decode: max_len must be positive");
+  if (max_len > tq::kMaxDecodeLen)
+    return fail(TQ_ERR_UNSUPPORTED, "decode: max_len above " + std::to_string(tq::kMaxDecodeLen) + " tokens");
   const int64_t rows = (int64_t)(hq / hkv) * q_len;
   const int rmax = row_block(kc);
   if (blocks) {
@@ -449,13 +364,31 @@ static tq_status check_decode_shapes(const tq_codec* kc, const tq_codec* vc, int
   return TQ_OK;
 }
 
-static size_t attention_workspace(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
-                                  int32_t q_len, int64_t max_len) {
+// The decode path and its plan for these sizes: one function for the
+// workspace size queries and the calls, so that a workspace sized through the
+// API always fits the call.
+enum class DecodePath { kFast, kMfma, kGeneral };
+
+static tq::DecodePlan choose_plan(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
+                                  int32_t q_len, int64_t max_len, DecodePath* path) {
   const int rows = (int)std::min<int64_t>((int64_t)(hq / hkv) * q_len, row_block(kc));
   const bool prod = kc->h.mode == TQ_MODE_PROD;
-  if (use_fast(kc, vc, rows)) return tq::plan_decode_fast(batch, hkv, rows, kc->h.d, max_len).total;
-  if (use_mfma(kc, vc, rows)) return tq::plan_decode_mfma(batch, hkv, rows, kc->h.d, max_len, prod).total;
-  return tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, prod).total;
+  if (use_fast(kc, vc, rows)) {
+    *path = DecodePath::kFast;
+    return tq::plan_decode_fast(batch, hkv, rows, kc->h.d, max_len);
+  }
+  if (use_mfma(kc, vc, rows)) {
+    *path = DecodePath::kMfma;
+    return tq::plan_decode_mfma(batch, hkv, rows, kc->h.d, max_len, prod);
+  }
+  *path = DecodePath::kGeneral;
+  return tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, prod);
+}
+
+static size_t attention_workspace(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
+                                  int32_t q_len, int64_t max_len) {
+  DecodePath path;
+  return choose_plan(kc, vc, batch, hq, hkv, q_len, max_len, &path).total;
 }
 
 tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
@@ -496,13 +429,10 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
   const int64_t rows_total = (int64_t)(hq / hkv) * q_len;
   const int rows = (int)std::min<int64_t>(rows_total, row_block(kc));  // rows per launch
   const bool prod = kc->h.mode == TQ_MODE_PROD;
-  // the matrix-core kernel addresses the queries with 32-bit offsets
-  const int64_t q_bytes = (int64_t)batch * hq * q_len * kc->h.d * (q_dtype == TQ_BF16 ? 2 : 4);
-  const bool fast = use_fast(kc, vc, rows) && q_bytes < ((int64_t)1 << 32);
-  const bool mfma = !fast && use_mfma(kc, vc, rows);
-  const tq::DecodePlan plan = fast ? tq::plan_decode_fast(batch, hkv, rows, kc->h.d, max_len)
-                              : mfma ? tq::plan_decode_mfma(batch, hkv, rows, kc->h.d, max_len, prod)
-                                     : tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, prod);
+  DecodePath path;
+  const tq::DecodePlan plan = choose_plan(kc, vc, batch, hq, hkv, q_len, max_len, &path);
+  const bool fast = path == DecodePath::kFast;
+  const bool mfma = path == DecodePath::kMfma;
   if (!ws || ws_bytes < plan.total)
     return fail(TQ_ERR_WORKSPACE, fn + ": workspace needs " + std::to_string(plan.total) + " bytes");
   tq::DevTables* kt = nullptr;
@@ -589,6 +519,16 @@ tq_status tq_prefill_attention(const tq_codec* kc, const tq_codec* vc, const voi
                                size_t ws_bytes, void* stream) {
   return attention_impl("tq_prefill_attention", true, kc, vc, q, q_dtype, batch, hq, hkv, q_len, k, v, d_len,
                         max_len, scale, out, ws, ws_bytes, stream);
+}
+
+tq_status tq_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, int32_t blocks, void* stream) {
+  if (!buf || !sink) return fail(TQ_ERR_INVALID_ARG, "tq_stream_read: NULL argument");
+  if (bytes == 0 || bytes % 16 || reinterpret_cast<uintptr_t>(buf) % 16)
+    return fail(TQ_ERR_INVALID_ARG, "tq_stream_read: bytes must be a positive multiple of 16, buf 16-byte aligned");
+  if (blocks < 1 || blocks > (1 << 20)) return fail(TQ_ERR_INVALID_ARG, "tq_stream_read: blocks out of range");
+  const hipError_t e = tq::launch_stream_read(buf, bytes, sink, blocks, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tq_stream_read launch");
+  return TQ_OK;
 }
 
 tq_status tq_cache_gather(const tq_codec* src_codec, const tq_cache* src, const tq_codec* dst_codec,

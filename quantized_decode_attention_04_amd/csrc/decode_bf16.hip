@@ -407,12 +407,6 @@ hipError_t launch_vb(const DecodeParams& p, const dim3 grid, hipStream_t stream)
 
 }  // namespace
 
-bool bf16_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
-  const bool kok = (kmode == TQ_MODE_MSE || kmode == TQ_MODE_PROD) && (kbits == 1 || kbits == 2);
-  const bool vok = vmode == TQ_MODE_MSE && (vbits == 1 || vbits == 2 || vbits == 4);
-  return d == kDim && kok && vok && rows >= 1 && rows <= 16;
-}
-
 // The decode kernel of this file for a launch that bf16_decode_supported
 // accepts; the query prologue and the merge are the caller's.
 hipError_t launch_decode_bf16_kernel(const DecodeParams& p, const dim3 grid, hipStream_t stream) {

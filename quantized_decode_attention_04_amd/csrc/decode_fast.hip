@@ -54,6 +54,7 @@ constexpr int kWaves = 8;              // 512-thread workgroups, one per compute
 constexpr int kThreads = kWaves * 64;
 constexpr int kStep = kWaves * kTile;  // tokens per workgroup iteration
 constexpr int kMaxChunks = 128;        // merge weights kept in LDS
+constexpr int kMaxChunk = 1 << 19;     // tokens per chunk (int32 accumulator bound, see the launcher)
 constexpr int kRow = kD + 16;          // LDS bytes per token row of value selectors
 constexpr int kSelLds = kTile * kRow + 448;       // value selectors of the tile (+ row-group offsets)
 constexpr int kNormLds = 2 * kTile * 4;            // key and value norms of the tile
@@ -180,12 +181,15 @@ __device__ __forceinline__ void query_loads(const DecodeParams& p, int b, int g,
 #pragma unroll
   for (int s = 0; s < 32; ++s) ql.pit[s] = pt[(size_t)s * kD];
   const int t = threadIdx.x, qr = t >> 5, qc = (t & 31) * 4;
-  const int R = p.row0 + (qr < p.rows ? qr : 0);  // row among the KV head's group * q_len rows
-  const int hh = g * p.group + R / p.q_len, qi = R % p.q_len;
+  // the rows of KV head g are contiguous in q (query heads g*group ..
+  // g*group+group-1, q_len rows each): the buffer starts at this launch's
+  // first row, so 32-bit offsets cover any query tensor
+  const int rr = qr < p.rows ? qr : 0;
   const uint32_t esize = p.q_bf16 ? 2u : 4u;
-  const uint32_t q_bytes = (uint32_t)((int64_t)p.batch * p.hq * p.q_len * kD * esize);
-  const uint32_t qoff = (uint32_t)(((((int64_t)b * p.hq + hh) * p.q_len + qi) * kD + qc) * esize);
-  const __amdgpu_buffer_rsrc_t rq = rsrc(p.q, q_bytes);
+  const char* qbase = static_cast<const char*>(p.q) +
+                      ((((int64_t)b * p.hq + (int64_t)g * p.group) * p.q_len + p.row0) * kD) * esize;
+  const uint32_t qoff = (uint32_t)((rr * kD + qc) * esize);
+  const __amdgpu_buffer_rsrc_t rq = rsrc(qbase, (uint32_t)(p.rows * kD) * esize);
   if (p.q_bf16) {
     const v2i w = __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(rq, qoff, 0, 0));
     ql.qs = v4f{__uint_as_float((uint32_t)w.x << 16), __uint_as_float((uint32_t)w.x & 0xffff0000u),
@@ -661,13 +665,12 @@ __global__ __launch_bounds__(kD) void merge_fast_kernel(DecodeParams p) {
 
 }  // namespace
 
-bool fast_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
-  return d == kD && kmode == TQ_MODE_MSE && kbits == 3 && vmode == TQ_MODE_MSE && vbits == 3 && rows <= 16;
-}
-
 hipError_t launch_decode_fast(const DecodeParams& p, hipStream_t stream) {
+  // each wave takes at most chunk / 512 tiles between flushes of its int32
+  // value accumulators; one tile adds at most 64 (128*127 + 64*128) < 2^21 to
+  // an element, so chunks of at most 2^19 tokens (1024 tiles) stay below 2^31
   if (p.n_chunks < 1 || p.n_chunks > kMaxChunks || p.hkv > 65535 || p.batch > 65535 || p.d != kD ||
-      p.rows > 16 || (int64_t)p.chunk * 48 > 0xffffffffLL)
+      p.rows > 16 || p.chunk > kMaxChunk)
     return hipErrorInvalidValue;
   decode_fast_kernel<<<dim3(p.n_chunks, p.hkv, p.batch), dim3(kThreads), 0, stream>>>(p);
   merge_fast_kernel<<<dim3(p.rows, p.hkv, p.batch), dim3(kD), 0, stream>>>(p);

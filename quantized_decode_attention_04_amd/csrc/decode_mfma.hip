@@ -294,22 +294,6 @@ hipError_t launch_dd(const DecodeParams& p, const dim3 grid, hipStream_t stream)
 
 }  // namespace
 
-bool mfma_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
-  const bool kok = (kmode == TQ_MODE_MSE || kmode == TQ_MODE_PROD) && kbits >= 1 && kbits <= 4;
-  const bool vok = (vmode == TQ_MODE_MSE && (vbits == 1 || vbits == 2 || vbits == 4)) ||
-                   (vmode == TQ_MODE_GROUP && (vbits == 2 || vbits == 4));
-  return (d == 128 || d == 256) && kok && vok && rows >= 1 && rows <= 16;
-}
-
-// Measured on MI355X: at head_dim 128 with more than 8 rows (prefill blocks,
-// multi-token decode) this kernel takes half the general kernel's time (whose
-// work grows with the rows); at 8 rows or fewer, and at head_dim 256, the
-// general kernel is as fast or faster.
-bool mfma_decode_preferred(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
-  return d == 128 && (rows > 8 || bf16_decode_supported(d, kmode, kbits, vmode, vbits, rows)) &&
-         mfma_decode_supported(d, kmode, kbits, vmode, vbits, rows);
-}
-
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   if (!mfma_decode_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits, p.rows) || p.hkv > 65535 ||
       p.batch > 65535 || p.n_chunks < 1 || (int64_t)p.n_chunks * kWaves > 4096 || p.chunk % (kWaves * kTile))

@@ -1,0 +1,155 @@
+// Which kernel takes a decode launch, and the chunk plan and workspace
+// layout of each decode path.  Host code only (no HIP kernels), so that it can
+// be built and checked on hosts without a GPU.
+#include <algorithm>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+// ---- which decode kernel covers which codecs ---------------------------------
+
+// int8 matrix-core kernel (decode_fast.hip): head_dim 128, 3-bit MSE keys and
+// values, up to 16 rows.
+bool fast_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
+  return d == 128 && kmode == TQ_MODE_MSE && kbits == 3 && vmode == TQ_MODE_MSE && vbits == 3 && rows <= 16;
+}
+
+// bf16 split-operand kernel (decode_bf16.hip): head_dim 128, key codes of 1
+// or 2 bits (MSE, or the MSE part of 2/3-bit Prod keys), MSE values of 1, 2
+// or 4 bits, up to 16 rows.
+bool bf16_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
+  const bool kok = (kmode == TQ_MODE_MSE || kmode == TQ_MODE_PROD) && (kbits == 1 || kbits == 2);
+  const bool vok = vmode == TQ_MODE_MSE && (vbits == 1 || vbits == 2 || vbits == 4);
+  return d == 128 && kok && vok && rows >= 1 && rows <= 16;
+}
+
+// fp32 matrix-core kernel (decode_mfma.hip).
+bool mfma_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
+  const bool kok = (kmode == TQ_MODE_MSE || kmode == TQ_MODE_PROD) && kbits >= 1 && kbits <= 4;
+  const bool vok = (vmode == TQ_MODE_MSE && (vbits == 1 || vbits == 2 || vbits == 4)) ||
+                   (vmode == TQ_MODE_GROUP && (vbits == 2 || vbits == 4));
+  return (d == 128 || d == 256) && kok && vok && rows >= 1 && rows <= 16;
+}
+
+// Measured on MI355X: at head_dim 128 with more than 8 rows (prefill blocks,
+// multi-token decode) the fp32 matrix-core kernel takes half the general
+// kernel's time (whose work grows with the rows); at 8 rows or fewer, and at
+// head_dim 256, the general kernel is as fast or faster.  Launches the bf16
+// kernel covers go through launch_decode_mfma as well.
+bool mfma_decode_preferred(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
+  return d == 128 && (rows > 8 || bf16_decode_supported(d, kmode, kbits, vmode, vbits, rows)) &&
+         mfma_decode_supported(d, kmode, kbits, vmode, vbits, rows);
+}
+
+// ---- chunk plans and workspace layouts ---------------------------------------
+
+DecodePlan plan_decode(int batch, int hkv, int rows, int d, int64_t max_len, bool prod) {
+  DecodePlan p{};
+  p.rows = rows;
+  const int64_t tile = 256;
+  // about two 256-token tiles per workgroup: measured 6-7% faster than one
+  // (the query prologue is amortised) and than four (fewer workgroups)
+  const int64_t target_items = 512;
+  const int64_t total = (int64_t)batch * hkv * max_len;
+  int64_t chunk = (total + target_items - 1) / target_items;
+  chunk = ((chunk + tile - 1) / tile) * tile;
+  chunk = std::max<int64_t>(tile, std::min<int64_t>(chunk, 16384));
+  p.chunk = (int)chunk;
+  p.n_chunks = (int)((max_len + chunk - 1) / chunk);
+  const size_t bg = (size_t)batch * hkv;
+  size_t off = 0;
+  p.off_qrot = off;
+  off = align256(off + bg * rows * d * sizeof(float));
+  p.off_qs = off;
+  if (prod) off = align256(off + bg * rows * d * sizeof(float));
+  p.off_part_o = off;
+  off = align256(off + bg * p.n_chunks * rows * d * sizeof(float));
+  p.off_part_ml = off;
+  off = align256(off + bg * p.n_chunks * rows * 2 * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+// Compute units of the current device (256 on MI355X; the fallback when no
+// device answers keeps workspace sizing usable on hosts without a GPU).
+static int device_cus() {
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Largest chunk of a batched launch on the matrix-core paths (tokens).
+constexpr int64_t kRaggedChunk = 8192;
+
+DecodePlan plan_decode_mfma(int batch, int hkv, int rows, int d, int64_t max_len, bool prod) {
+  DecodePlan p{};
+  p.rows = rows;
+  const int64_t step = 256;  // four waves x 64-token tiles
+  const int64_t heads = (int64_t)batch * hkv;
+  // about two workgroups per compute unit; every wave writes a partial and
+  // the merge takes at most 4096 of them per row
+  const int64_t per_head = std::max<int64_t>(1, (2 * device_cus() + heads - 1) / heads);
+  int64_t chunk = (max_len + per_head - 1) / per_head;
+  // a batch may be ragged: the host knows only the longest sequence, so the
+  // chunk is capped and a long sequence spreads over several workgroups
+  // (chunks past a sequence's end exit at once)
+  if (batch > 1) chunk = std::min<int64_t>(chunk, kRaggedChunk);
+  chunk = std::max<int64_t>(step, ((chunk + step - 1) / step) * step);
+  chunk = std::max<int64_t>(chunk, ((max_len + 1023) / 1024 + step - 1) / step * step);  // <= 1024 chunks
+  p.chunk = (int)chunk;
+  p.n_chunks = (int)((max_len + chunk - 1) / chunk);
+  const size_t bg = (size_t)batch * hkv;
+  const size_t parts = (size_t)p.n_chunks * 4;
+  size_t off = 0;
+  p.off_qrot = off;
+  off = align256(off + bg * rows * d * sizeof(float));
+  p.off_qs = off;
+  if (prod) off = align256(off + bg * rows * d * sizeof(float));
+  p.off_part_o = off;
+  off = align256(off + bg * parts * rows * d * sizeof(float));
+  p.off_part_ml = off;
+  off = align256(off + bg * parts * rows * 2 * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+DecodePlan plan_decode_fast(int batch, int hkv, int rows, int d, int64_t max_len) {
+  DecodePlan p{};
+  p.rows = rows;
+  p.fast = true;
+  const int64_t step = 512;                 // eight waves x 64-token tiles
+  const int64_t heads = (int64_t)batch * hkv;
+  const int64_t per_head = std::max<int64_t>(1, (device_cus() + heads - 1) / heads);  // one workgroup per CU
+  int64_t chunk = (max_len + per_head - 1) / per_head;
+  if (batch > 1) chunk = std::min<int64_t>(chunk, kRaggedChunk);  // as in plan_decode_mfma
+  chunk = ((chunk + step - 1) / step) * step;
+  chunk = std::max<int64_t>(step, chunk);
+  // at most 2^19 tokens per chunk (the kernel's int32 accumulator bound),
+  // which with max_len <= 2^26 still leaves <= 128 chunks
+  chunk = std::min<int64_t>(chunk, (int64_t)1 << 19);
+  chunk = std::max<int64_t>(chunk, ((max_len + 127) / 128 + step - 1) / step * step);  // <= 128 chunks
+  p.chunk = (int)chunk;
+  p.n_chunks = (int)((max_len + chunk - 1) / chunk);
+  const size_t bg = (size_t)batch * hkv;
+  size_t off = 0;
+  p.off_part_o = off;
+  off = align256(off + bg * p.n_chunks * rows * d * sizeof(float));
+  p.off_part_ml = off;
+  off = align256(off + bg * p.n_chunks * rows * 2 * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+}  // namespace tq

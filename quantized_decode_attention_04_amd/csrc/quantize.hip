@@ -25,7 +25,7 @@ __device__ __forceinline__ float load_x(const void* x, int64_t off, int bf16) {
   return static_cast<const float*>(x)[off];
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+__device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
@@ -143,6 +143,44 @@ __device__ __forceinline__ void tile_gemm(const BulkLds<D>& L, const float* __re
   }
 }
 
+// Same, in float64 on v_mfma_f64_16x16x4f64 (same lane layout as the fp32
+// instruction; the fp32 operands widen exactly, so every product is exact and
+// only the float64 accumulation rounds).  Used for the rotation of Prod keys,
+// whose residual y - n c[idx] is a difference of nearly equal terms.
+typedef double v4d_t __attribute__((ext_vector_type(4)));
+
+template <int D, typename F>
+__device__ __forceinline__ void tile_gemm_f64(const BulkLds<D>& L, const float* __restrict__ mat, F&& f) {
+  constexpr int KS = D / 4;
+  constexpr int NCT = D / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int cc = 0; cc < (NCT + 3) / 4; ++cc) {
+    const int c = wave + 4 * cc;
+    if (c >= NCT) break;
+    const v4f_t* brow = reinterpret_cast<const v4f_t*>(mat + (size_t)(16 * c + r16) * D + g4 * KS);
+    v4d_t acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = v4d_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+    for (int q = 0; q < KS / 4; ++q) {
+      const v4f_t bq = brow[q];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const v4f_t a = *reinterpret_cast<const v4f_t*>(&L.xs[16 * r + r16][g4 * KS + 4 * q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[r] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[e], (double)bq[e], acc[r], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f(cc, r, e, 16 * r + 4 * g4 + e, 16 * c + r16, acc[r][e]);
+  }
+}
+
 // The rotated modes after the norms: y = Pi x on the matrix cores, the
 // nearest centroid of every element (NB = levels - 1 boundaries, unrolled),
 // the packed indices and norms; for Prod keys the residual, its norm and the
@@ -159,22 +197,35 @@ __device__ __forceinline__ void quantize_rotated(const QuantizeParams& p, BulkLd
 #pragma unroll
   for (int m = 0; m <= NB; ++m) cent[m] = PROD ? p.cent[m] : 0.f;
   float rho[NCC][4][4];
-  tile_gemm<D>(L, p.pi, [&](int cc, int r, int e, int v, int coord, float y) {
-    const float n = L.nrm[v];
-    const float inv = n > 0.f ? 1.f / n : 0.f;
-    const float u = y * inv;
-    // the boundaries are sorted: the last one below u names the centroid
-    uint32_t k = 0;
-    float c = cent[0];
+  if constexpr (PROD) {
+    // float64 rotation: the residual keeps the accuracy of its own size
+    tile_gemm_f64<D>(L, p.pi, [&](int cc, int r, int e, int v, int coord, double y) {
+      const double n = (double)L.nrm[v];
+      const double u = n > 0.0 ? y / n : 0.0;
+      uint32_t k = 0;
+      float c = cent[0];
 #pragma unroll
-    for (int m = 0; m < NB; ++m) {
-      const bool above = u > bnd[m];
-      k += above ? 1u : 0u;
-      if (PROD) c = above ? cent[m + 1] : c;
-    }
-    L.codes[v][coord] = (uint8_t)k;
-    rho[cc][r][e] = PROD ? y - n * c : 0.f;
-  });
+      for (int m = 0; m < NB; ++m) {
+        const bool above = u > (double)bnd[m];
+        k += above ? 1u : 0u;
+        c = above ? cent[m + 1] : c;
+      }
+      L.codes[v][coord] = (uint8_t)k;
+      rho[cc][r][e] = (float)(y - n * (double)c);
+    });
+  } else {
+    tile_gemm<D>(L, p.pi, [&](int cc, int r, int e, int v, int coord, float y) {
+      const float n = L.nrm[v];
+      const float inv = n > 0.f ? 1.f / n : 0.f;
+      const float u = y * inv;
+      // the boundaries are sorted: the last one below u names the centroid
+      uint32_t k = 0;
+#pragma unroll
+      for (int m = 0; m < NB; ++m) k += u > bnd[m] ? 1u : 0u;
+      L.codes[v][coord] = (uint8_t)k;
+      rho[cc][r][e] = 0.f;
+    });
+  }
   __syncthreads();  // every read of the x tile and write of the codes is done
   for (int e = tid; e < kMV * p.words; e += 256) {
     const int v = e / p.words, w = e % p.words;
@@ -201,11 +252,11 @@ __device__ __forceinline__ void quantize_rotated(const QuantizeParams& p, BulkLd
   float gam = 0.f;
   {
     const int v = tid >> 2, part = tid & 3;
-    float ss = 0.f;
-    for (int j = part * (D / 4); j < (part + 1) * (D / 4); ++j) ss = fmaf(L.xs[v][j], L.xs[v][j], ss);
+    double ss = 0.0;
+    for (int j = part * (D / 4); j < (part + 1) * (D / 4); ++j) ss = fma((double)L.xs[v][j], (double)L.xs[v][j], ss);
     ss += __shfl_xor(ss, 1, 64);
     ss += __shfl_xor(ss, 2, 64);
-    gam = sqrtf(ss);
+    gam = (float)sqrt(ss);
   }
   tile_gemm<D>(L, p.s, [&](int, int, int, int v, int coord, float z) { L.codes[v][coord] = z >= 0.f ? 1 : 0; });
   __syncthreads();
@@ -308,14 +359,15 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void quantize_bulk_kernel(Qu
     return;
   }
 
-  // ---- norms: four threads per vector
+  // ---- norms: four threads per vector (float64 sum of squares, so that the
+  // stored float32 norm is the correctly rounded one)
   {
     const int v = tid >> 2, part = tid & 3;
-    float ss = 0.f;
-    for (int j = part * (D / 4); j < (part + 1) * (D / 4); ++j) ss = fmaf(L.xs[v][j], L.xs[v][j], ss);
+    double ss = 0.0;
+    for (int j = part * (D / 4); j < (part + 1) * (D / 4); ++j) ss = fma((double)L.xs[v][j], (double)L.xs[v][j], ss);
     ss += __shfl_xor(ss, 1, 64);
     ss += __shfl_xor(ss, 2, 64);
-    if (part == 0) L.nrm[v] = sqrtf(ss);
+    if (part == 0) L.nrm[v] = (float)sqrt(ss);
   }
   __syncthreads();
 
@@ -350,8 +402,9 @@ __global__ __launch_bounds__(small_threads<D>()) void quantize_small_kernel(Quan
   const QuantizeParams& p = sets.s[blockIdx.y];
   __shared__ float xs[D];
   __shared__ float part_sum[PARTS][D];
+  __shared__ double part_sum_d[PARTS][D];  // Prod: the rotation in float64
   __shared__ uint32_t wbuf[32];
-  __shared__ float red[NW];
+  __shared__ double red[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = tid % D, part = tid / D, j0 = part * JN;
@@ -420,27 +473,45 @@ __global__ __launch_bounds__(small_threads<D>()) void quantize_small_kernel(Quan
   if (tid < D) xv = load_x(p.x, (int64_t)b * p.s0 + (int64_t)h * p.s1 + (int64_t)t * p.s2 + tid, p.x_bf16);
   if (tid < 32) wbuf[tid] = 0u;
   if (tid < D) xs[tid] = xv;
-  float sq = wave_sum(xv * xv);
+  // the norm from a float64 sum of squares (the stored float32 norm is the
+  // correctly rounded one)
+  const double sq = wave_sum_d((double)xv * (double)xv);
   if (lane == 0) red[wave] = sq;
   __syncthreads();
-  float n2 = 0.f;
+  double n2 = 0.0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) n2 += red[w];
-  const float n = sqrtf(n2);
+  const float n = (float)sqrt(n2);
 
-  // y = Pi x
-  float acc = 0.f;
+  // y = Pi x (Prod keys in float64: their residual y - n c[idx] is a
+  // difference of nearly equal terms)
+  if (prod) {
+    double accd = 0.0;
 #pragma unroll
-  for (int k = 0; k < JN; ++k) acc = fmaf(pr[k], xs[j0 + k], acc);
-  part_sum[part][i] = acc;
+    for (int k = 0; k < JN; ++k) accd = fma((double)pr[k], (double)xs[j0 + k], accd);
+    part_sum_d[part][i] = accd;
+  } else {
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < JN; ++k) acc = fmaf(pr[k], xs[j0 + k], acc);
+    part_sum[part][i] = acc;
+  }
   __syncthreads();
-  float y = 0.f;
+  double yd = 0.0;
   uint32_t idx = 0;
   if (tid < D) {
+    if (prod) {
 #pragma unroll
-    for (int q = 0; q < PARTS; ++q) y += part_sum[q][tid];
-    const float u = y * (n > 0.f ? 1.f / n : 0.f);
-    for (int m = 0; m < p.levels - 1; ++m) idx += u > p.bnd[m] ? 1u : 0u;
+      for (int q = 0; q < PARTS; ++q) yd += part_sum_d[q][tid];
+      const double u = n > 0.f ? yd / (double)n : 0.0;
+      for (int m = 0; m < p.levels - 1; ++m) idx += u > (double)p.bnd[m] ? 1u : 0u;
+    } else {
+      float y = 0.f;
+#pragma unroll
+      for (int q = 0; q < PARTS; ++q) y += part_sum[q][tid];
+      const float u = y * (n > 0.f ? 1.f / n : 0.f);
+      for (int m = 0; m < p.levels - 1; ++m) idx += u > p.bnd[m] ? 1u : 0u;
+    }
     pack_field(wbuf, tid, p.mse_bits, idx);
   }
   __syncthreads();
@@ -448,19 +519,19 @@ __global__ __launch_bounds__(small_threads<D>()) void quantize_small_kernel(Quan
   if (tid == 0) p.norm[tok] = n;
   if (!prod) return;
 
-  // Prod: rotated residual, its norm, z = S rho, sign bits
-  const float rho = tid < D ? y - n * p.cent[idx] : 0.f;
-  const float rs = wave_sum(rho * rho);
+  // Prod: rotated residual (float64), its norm, z = S rho, sign bits
+  const double rho = tid < D ? yd - (double)n * (double)p.cent[idx] : 0.0;
+  const double rs = wave_sum_d(rho * rho);
   __syncthreads();  // every read of xs, part_sum and red above is done
-  if (tid < D) xs[tid] = rho;
+  if (tid < D) xs[tid] = (float)rho;
   if (lane == 0) red[wave] = rs;
   if (!kEarlySketch) load_slice(p.st, p.s, sr);
   __syncthreads();
-  float g2 = 0.f;
+  double g2 = 0.0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) g2 += red[w];
-  const float gamma = sqrtf(g2);
-  acc = 0.f;
+  const float gamma = (float)sqrt(g2);
+  float acc = 0.f;
 #pragma unroll
   for (int k = 0; k < JN; ++k) acc = fmaf(sr[k], xs[j0 + k], acc);
   part_sum[part][i] = acc;

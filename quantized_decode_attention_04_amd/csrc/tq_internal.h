@@ -14,6 +14,11 @@
 namespace tq {
 
 constexpr int kMaxDevices = 16;
+// Longest attended length a decode or prefill call takes (tokens per
+// sequence): the general path merges at most 4096 chunks of at most 16384
+// tokens, and the int8 matrix-core path keeps each wave's exact int32 value
+// accumulators below 2^31 with chunks of at most 2^19 tokens (128 chunks).
+constexpr int64_t kMaxDecodeLen = (int64_t)1 << 26;
 constexpr int kGridMax = 16256;  // 127 * 128: |centroid| * 2^E bound
 constexpr float kQjlConstNumer = 1.2533141373155003f;  // sqrt(pi/2)
 
@@ -181,5 +186,11 @@ struct CacheGather {
 };
 
 hipError_t launch_cache_gather(const CacheGather& g, int64_t max_count, hipStream_t stream);
+
+// ---- measurement ------------------------------------------------------------
+
+// Threads per workgroup of the streaming-read kernel.
+constexpr int kStreamThreads = 256;
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
 
 }  // namespace tq

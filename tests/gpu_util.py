@@ -45,3 +45,31 @@ def rel_l2_rows(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     num = np.linalg.norm(a - b, axis=-1)
     den = np.linalg.norm(b, axis=-1)
     return np.where(den > 0, num / np.where(den > 0, den, 1), num)
+
+
+def expected_window(codec, n_vectors: int) -> float:
+    """Expected number of decision values within WINDOW of their threshold for
+    n_vectors isotropic inputs: rotated coordinates follow the coordinate
+    density f_d near each codebook boundary; a QJL sign's z / gamma is N(0, 1)
+    (its window is |z| / (sqrt(d) gamma) < WINDOW); a group code's fractional
+    part is uniform (window |frac - 1/2| < WINDOW (2^b - 1)).  Used to bound
+    the window counts the parity tests report."""
+    import math
+    from oracle import codec as ocodec
+    d = codec.head_dim
+    if codec.mode == ocodec.MODE_GROUP:
+        top = (1 << codec.bits) - 1
+        return n_vectors * d * 2.0 * WINDOW * top
+    per = 2.0 * WINDOW * float(np.sum(ocodec.coordinate_density(d, codec.boundaries)))
+    lam = n_vectors * d * per
+    if codec.mode == ocodec.MODE_PROD:
+        lam += n_vectors * d * 2.0 * WINDOW * math.sqrt(d) / math.sqrt(2.0 * math.pi)
+    return lam
+
+
+def window_ceiling(lam: float) -> float:
+    """A count a Poisson(lam) variable exceeds with negligible probability
+    (lam + 6 sqrt(lam) + 6), with 50% slack for inputs that are only close to
+    isotropic (bf16 rounding, outlier channels)."""
+    import math
+    return 1.5 * (lam + 6.0 * math.sqrt(lam) + 6.0)

@@ -100,10 +100,14 @@ def test_create_rejects_bad_parameters():
 def no_gpu():
     import torch
     if torch.cuda.is_available():
+        # every call below is refused on the host before a launch, but the
+        # pointers are placeholders: if a check ever regressed, a GPU host
+        # would launch a kernel on them, so these run where no GPU is present
+        # (the CPU suite, every time)
         pytest.skip("argument-validation tests pass placeholder pointers; they run on hosts without a GPU")
 
 
-def test_decode_shape_validation(no_gpu):
+def test_decode_shape_validation():
     kc = tq.tq_codec_create(128, 3, 0, tq.TQ_MODE_MSE)
     vc = tq.tq_codec_create(128, 4, 1, tq.TQ_MODE_MSE)
     vg = tq.tq_codec_create(128, 2, 1, tq.TQ_MODE_GROUP)
@@ -126,7 +130,7 @@ def test_decode_shape_validation(no_gpu):
         assert e.value.status == status, args
 
 
-def test_prefill_workspace_is_one_row_block(no_gpu):
+def test_prefill_workspace_is_one_row_block():
     """Prefill takes any q_len and plans its workspace for one block of rows
     (16 rows up to head_dim 128, 8 above), which the blocks reuse."""
     kc = tq.tq_codec_create(128, 3, 0, tq.TQ_MODE_MSE)
@@ -169,6 +173,10 @@ def test_decode_and_append_argument_errors(no_gpu):
     assert dec(scale=float("nan")) == 1
     assert dec(ws_bytes=need - 1) == 5
     assert dec(max_len=101) == 4
+    # longest supported sequence: 2^26 tokens (int32 accumulator and merge bounds)
+    huge = _fake_cache(1, 8, (1 << 26) + 1, 0)
+    assert dec(kcache=huge, vcache=huge, max_len=(1 << 26) + 1) == 2
+    assert "max_len above" in tq.tq_last_error()
     assert dec(vcache=_fake_cache(1, 8, 99, 0), max_len=50) == 3
     assert dec(kcache=_fake_cache(1, 4, 100, 0)) == 3
     bad = _fake_cache(1, 8, 100, 0)
@@ -176,15 +184,25 @@ def test_decode_and_append_argument_errors(no_gpu):
     assert dec(kcache=bad) == 1
     # append
     strides = (ctypes.c_int64 * 4)(8 * 2 * 128, 2 * 128, 128, 1)
-    app = lambda cache, x=P, n=2, st=strides, dt=1: lib.tq_quantize_append(kc.handle, x, dt, 1, 8, n, st,
-                                                                           ctypes.byref(cache), P, None)
+    app = lambda cache, x=P, n=2, st=strides, dt=1, end=100: lib.tq_quantize_append(
+        kc.handle, x, dt, 1, 8, n, st, ctypes.byref(cache), P, end, None)
     assert app(k, x=None) == 1
     assert app(k, dt=5) == 1
     assert app(k, n=-1) == 1
     assert app(_fake_cache(2, 8, 100, 0)) == 3
     assert app(k, st=(ctypes.c_int64 * 4)(0, 0, 0, 2)) == 1
-    assert app(k, n=0) == 0                    # nothing to do
-    assert "coordinate stride" in tq.tq_last_error() or True
+    assert "coordinate stride" in tq.tq_last_error()
+    # the written end after the append is bounded on the host: past the
+    # capacity is CAPACITY, below n_new is INVALID_ARG
+    assert app(k, end=101) == 4
+    assert "capacity" in tq.tq_last_error()
+    assert app(k, end=1) == 1
+    assert app(k, n=0, end=0) == 0             # nothing to do
+    appkv = lambda end: lib.tq_quantize_append_kv(kc.handle, kc.handle, P, P, 1, 1, 8, 2, strides, strides,
+                                                   ctypes.byref(k), ctypes.byref(_fake_cache(1, 8, 50, 0)), P, end,
+                                                   None)
+    assert appkv(51) == 4                      # past the smaller (value) cache
+    assert appkv(1) == 1
 
 
 def test_cache_gather_argument_errors(no_gpu):

@@ -31,7 +31,7 @@ def _filled(codec, d, B, H, cap, lens, seed):
     rng = np.random.default_rng(seed)
     cache = tq.allocate_cache(codec, B, H, cap)
     x = round_bf16(rng.standard_normal((B, H, cap, d)).astype(np.float32) * np.float32(0.02))
-    tq.tq_quantize_append(codec, to_device_f(x, True), cache, torch.zeros(B, dtype=torch.int32, device="cuda"))
+    tq.tq_quantize_append(codec, to_device_f(x, True), cache, torch.zeros(B, dtype=torch.int32, device="cuda"), cap)
     # slots past each sequence's length hold records too (written above); the
     # lengths only say which ones are attended
     torch.cuda.synchronize()

@@ -37,7 +37,7 @@ def test_graph_replays_match_eager(kspec, vspec, n):
         pos0 = torch.zeros(B, dtype=torch.int32, device=dev)
         kx = wl.device_normal((B, hkv, n - qlen, d), 3, l, 100, True, dev)
         vx = wl.device_normal((B, hkv, n - qlen, d), 3, l, 101, True, dev)
-        tq.tq_quantize_append_kv(gk, gv, kx, vx, K, V, pos0)
+        tq.tq_quantize_append_kv(gk, gv, kx, vx, K, V, pos0, n - qlen)
         kn = wl.device_normal((B, hkv, qlen, d), 3, l, 102, True, dev)
         vn = wl.device_normal((B, hkv, qlen, d), 3, l, 103, True, dev)
         q = wl.device_normal((B, hq, qlen, d), 3, l, 104, True, dev)
@@ -50,7 +50,7 @@ def test_graph_replays_match_eager(kspec, vspec, n):
 
     def run(l):
         K, V, kn, vn, q = layers[l]
-        tq.tq_quantize_append_kv(gk, gv, kn, vn, K, V, pos)
+        tq.tq_quantize_append_kv(gk, gv, kn, vn, K, V, pos, n)
         tq.tq_decode_attention(gk, gv, q, K, V, lens, n, scale, outs[l], ws)
 
     # eager reference (warms the codec tables before capture)

@@ -19,7 +19,8 @@ from oracle import attention as oatt
 from oracle import codec as ocodec
 from oracle import packing
 from oracle import quant as oquant
-from tests.gpu_util import WINDOW, download, rel_l2_rows, to_device_f, upload_state
+from tests.gpu_util import (WINDOW, download, expected_window, rel_l2_rows, to_device_f, upload_state,
+                            window_ceiling)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,19 +118,23 @@ def _check_append(d, bits, mode, bf16, H, n_new, off):
     wide = torch.zeros((B, H, n_new, d + 32), dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
     wide[..., off:off + d] = to_device_f(x, bf16)
     xd = wide[..., off:off + d]
-    pos = torch.tensor([cap - 10, 0], dtype=torch.int32, device="cuda")   # b=0 runs past cap: skipped
-    tq.tq_quantize_append(gc, xd, cache, pos)
+    pos = torch.tensor([cap - n_new, 0], dtype=torch.int32, device="cuda")
+    # an append that would end past the capacity is refused before any launch
+    with pytest.raises(tq.TQError) as exc:
+        tq.tq_quantize_append(gc, xd, cache, pos, cap + 1)
+    assert exc.value.status == 4                                   # TQ_ERR_CAPACITY
+    tq.tq_quantize_append(gc, xd, cache, pos, cap)
     torch.cuda.synchronize()
     got = download(cache)
     ora = oquant.quantize(x.astype(np.float64), oc)
-    # slots written: b=0 -> cap-10 .. cap-1 (t < 10), b=1 -> 0 .. n_new-1
-    sel = [(0, slice(cap - 10, cap), slice(0, 10)), (1, slice(0, n_new), slice(0, n_new))]
+    # slots written: b=0 -> cap-n_new .. cap-1 (its last slot), b=1 -> 0 .. n_new-1
+    sel = [(0, slice(cap - n_new, cap), slice(0, n_new)), (1, slice(0, n_new), slice(0, n_new))]
     written = np.zeros((B, H, cap), dtype=bool)
     for b, ss, ts in sel:
         written[b, :, ss] = True
     for k, a in got.items():
         assert not np.any(a[~written]), f"{tag}: {k} written outside the appended slots"
-    nwin = 0
+    nwin = nmis = 0
     for b, ss, ts in sel:
         o = {k: v[b, :, ts] for k, v in ora.items() if isinstance(v, np.ndarray)}
         g = {k: v[b, :, ss] for k, v in got.items()}
@@ -140,22 +145,30 @@ def _check_append(d, bits, mode, bf16, H, n_new, off):
             bad = (qg != o["q"]) & ~inwin
             assert not bad.any(), f"{tag}: group codes differ outside the window"
             nwin += int(inwin.sum())
+            nmis += int((qg != o["q"]).sum())
             np.testing.assert_allclose(g["scale"], o["scale"], rtol=1e-6, atol=0)
             np.testing.assert_array_equal(g["gmin"], o["min"].astype(np.float32))
             continue
         w, allmatch = _compare_indices(g["idx"], {"idx": o["idx"], "margin": o["margin"], "words": o["words"]},
                                        oc.mse_bits, d, tag)
         nwin += w
+        nmis += int((packing.unpack(g["idx"], oc.mse_bits, d) != o["idx"]).sum())
         np.testing.assert_allclose(g["norm"], o["norm"], rtol=1e-6, atol=0)
         if mode == 1:
             ok = allmatch
-            np.testing.assert_allclose(g["rnorm"][ok], o["rnorm"][ok], rtol=1e-5, atol=1e-12)
+            np.testing.assert_allclose(g["rnorm"][ok], o["rnorm"][ok], rtol=1e-6, atol=0)
             gs = packing.unpack(g["sign"], 1, d)
             zwin = o["zmargin"] < WINDOW
             bad = (gs != o["sign_bits"]) & ~zwin & ok[..., None]
             assert not bad.any(), f"{tag}: {bad.sum()} QJL sign mismatches outside the window"
             nwin += int((zwin & ok[..., None]).sum())
-    _say(f"  window coordinates: {nwin}")
+            nmis += int(((gs != o["sign_bits"]) & ok[..., None]).sum())
+    # the window holds what the input distribution predicts, so the bit-exact
+    # comparison outside it covers all but a few coordinates
+    lam = expected_window(oc, 2 * H * n_new)
+    _say(f"  window coordinates: {nwin} (expected {lam:.2f}), GPU/oracle code differences inside it: {nmis}")
+    assert nwin <= window_ceiling(lam), f"{tag}: {nwin} window coordinates, expected about {lam:.2f}"
+    assert nmis <= nwin
 
 
 @pytest.mark.parametrize("kspec,vspec,H,n_new", [((128, 3, 1), (128, 3, 0), 8, 2), ((128, 3, 0), (128, 4, 0), 8, 2),
@@ -176,9 +189,9 @@ def test_quantize_append_kv_matches_two_appends(kspec, vspec, H, n_new):
     kd, vd = to_device_f(k, True), to_device_f(v, True)
     K1, V1 = tq.allocate_cache(gk, B, H, cap), tq.allocate_cache(gv, B, H, cap)
     K2, V2 = tq.allocate_cache(gk, B, H, cap), tq.allocate_cache(gv, B, H, cap)
-    tq.tq_quantize_append_kv(gk, gv, kd, vd, K1, V1, pos)
-    tq.tq_quantize_append(gk, kd, K2, pos)
-    tq.tq_quantize_append(gv, vd, V2, pos)
+    tq.tq_quantize_append_kv(gk, gv, kd, vd, K1, V1, pos, cap)
+    tq.tq_quantize_append(gk, kd, K2, pos, cap)
+    tq.tq_quantize_append(gv, vd, V2, pos, cap)
     torch.cuda.synchronize()
     for a, bb in ((download(K1), download(K2)), (download(V1), download(V2))):
         for name in a:
@@ -197,7 +210,7 @@ def test_quantize_append_kv_rejects_mismatched_head_dim():
     k = torch.zeros((1, 2, 1, 128), dtype=torch.bfloat16, device="cuda")
     pos = torch.zeros(1, dtype=torch.int32, device="cuda")
     with pytest.raises((tq.TQError, ValueError)):
-        tq.tq_quantize_append_kv(gk, gv, k, k, K, V, pos)
+        tq.tq_quantize_append_kv(gk, gv, k, k, K, V, pos, 1)
 
 
 DEC_CASES = [
@@ -332,11 +345,11 @@ def test_end_to_end_quantize_then_decode(case):
     # prefill in two appends (a bulk one and a short tail)
     cut = N - 3
     kd, vd = to_device_f(k, bf16), to_device_f(v, bf16)
-    tq.tq_quantize_append(gk, kd[:, :, :cut], kcache, pos)
-    tq.tq_quantize_append(gv, vd[:, :, :cut], vcache, pos)
+    tq.tq_quantize_append(gk, kd[:, :, :cut], kcache, pos, cut)
+    tq.tq_quantize_append(gv, vd[:, :, :cut], vcache, pos, cut)
     pos2 = torch.full((B,), cut, dtype=torch.int32, device="cuda")
-    tq.tq_quantize_append(gk, kd[:, :, cut:], kcache, pos2)
-    tq.tq_quantize_append(gv, vd[:, :, cut:], vcache, pos2)
+    tq.tq_quantize_append(gk, kd[:, :, cut:], kcache, pos2, N)
+    tq.tq_quantize_append(gv, vd[:, :, cut:], vcache, pos2, N)
     torch.cuda.synchronize()
     gks, gvs = download(kcache), download(vcache)
     assert np.array_equal(gks["idx"][:, :, :N], ks["words"])
@@ -359,3 +372,19 @@ def test_end_to_end_quantize_then_decode(case):
     live = np.linalg.norm(ref, axis=-1) > 0
     cos = np.sum(got * ref, -1)[live] / (np.linalg.norm(got, axis=-1) * np.linalg.norm(ref, axis=-1))[live]
     _say(f"  cos-sim to unquantised attention: mean {cos.mean():.6f} min {cos.min():.6f}")
+    # the oracle's own figures on these inputs, less a margin (the pages print
+    # no values for this metric: a regression floor, not a parity bar)
+    floor_mean, floor_min = QUALITY_FLOORS[name]
+    assert cos.mean() >= floor_mean and cos.min() >= floor_min
+
+
+# cos-sim to exact attention on the unquantised K and V ("turboquant
+# validate_moe_phase2.py", Test 1's metric): floors below what the oracle's
+# quantise + decode gives on the end-to-end inputs (mean / min: gqa8 0.9955 /
+# 0.9950, mtp2 0.9806 / 0.9668, moe 0.9342 / 0.9317, ragged 0.9959 / 0.9950)
+QUALITY_FLOORS = {
+    "gqa8_prod3_mse4": (0.99, 0.99),
+    "mtp2_mse3_outliers": (0.975, 0.96),
+    "moe_d256_prod3_group2": (0.925, 0.925),
+    "ragged_prod3_mse4": (0.99, 0.99),
+}

@@ -93,7 +93,7 @@ def test_prefill_matches_decode_for_a_decode_step():
     gk, gv = tq.tq_codec_create(d, 3, 0, 0), tq.tq_codec_create(d, 3, 1, 0)
     K, V = tq.allocate_cache(gk, B, Hkv, N), tq.allocate_cache(gv, B, Hkv, N)
     pos = torch.zeros(B, dtype=torch.int32, device="cuda")
-    tq.tq_quantize_append_kv(gk, gv, to_device_f(k, True), to_device_f(v, True), K, V, pos)
+    tq.tq_quantize_append_kv(gk, gv, to_device_f(k, True), to_device_f(v, True), K, V, pos, N)
     ld = torch.tensor([N], dtype=torch.int32, device="cuda")
     qd = to_device_f(q, True)
     o1 = torch.zeros((B, Hq, q_len, d), dtype=torch.float32, device="cuda")

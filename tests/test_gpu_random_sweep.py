@@ -76,7 +76,7 @@ def test_random_case(seed):
         if s1 > s0:
             pos = torch.full((B,), s0, dtype=torch.int32, device="cuda")
             tq.tq_quantize_append_kv(gk, gv, to_device_f(np.ascontiguousarray(k[:, :, s0:s1]), bf16),
-                                     to_device_f(np.ascontiguousarray(v[:, :, s0:s1]), bf16), K, V, pos)
+                                     to_device_f(np.ascontiguousarray(v[:, :, s0:s1]), bf16), K, V, pos, s1)
     torch.cuda.synchronize()
     for cache, st, oc, name in ((K, ks, kc, "keys"), (V, vs, vc, "values")):
         got = download(cache)
