@@ -143,10 +143,12 @@ __device__ __forceinline__ void tile_gemm(const BulkLds<D>& L, const float* __re
   }
 }
 
-// Same, in float64 on v_mfma_f64_16x16x4f64 (same lane layout as the fp32
-// instruction; the fp32 operands widen exactly, so every product is exact and
-// only the float64 accumulation rounds).  Used for the rotation of Prod keys,
-// whose residual y - n c[idx] is a difference of nearly equal terms.
+// Same, in float64 on v_mfma_f64_16x16x4f64 (the fp32 operands widen
+// exactly, so every product is exact and only the float64 accumulation
+// rounds).  Used for the rotation of Prod keys, whose residual y - n c[idx] is
+// a difference of nearly equal terms.  The operands sit in the lanes as for
+// the fp32 instruction, but register e of lane l holds output row l/16 + 4e
+// (measured on gfx950), not 4 (l/16) + e.
 typedef double v4d_t __attribute__((ext_vector_type(4)));
 
 template <int D, typename F>
@@ -177,7 +179,7 @@ __device__ __forceinline__ void tile_gemm_f64(const BulkLds<D>& L, const float* 
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) f(cc, r, e, 16 * r + 4 * g4 + e, 16 * c + r16, acc[r][e]);
+      for (int e = 0; e < 4; ++e) f(cc, r, e, 16 * r + g4 + 4 * e, 16 * c + r16, acc[r][e]);
   }
 }
 
@@ -245,7 +247,7 @@ __device__ __forceinline__ void quantize_rotated(const QuantizeParams& p, BulkLd
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) L.xs[16 * r + 4 * g4 + e][16 * c + r16] = rho[cc][r][e];
+        for (int e = 0; e < 4; ++e) L.xs[16 * r + g4 + 4 * e][16 * c + r16] = rho[cc][r][e];  // float64 layout
     }
   }
   __syncthreads();  // the residual is complete; the index packing has read the codes
