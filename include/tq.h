@@ -212,6 +212,25 @@ tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void
                               const tq_cache* v, const int32_t* d_len, int64_t max_len, float scale, float* out,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* tq_decode_attention for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc.  Same arguments, semantics and errors, without ws / ws_bytes:
+ * the per-chunk partial results go to a device array the library holds, 64
+ * MiB per device (every device the library runs on keeps it until the
+ * process ends).  The call allocates nothing -- no hipMalloc, hipFree or
+ * allocating library routine -- so both codecs' tables must already be on
+ * the current device (tq_codec_upload, or any earlier call that used them
+ * there), else INVALID_ARG.  Sizes whose workspace (tq_decode_workspace_size)
+ * exceeds 64 MiB are refused with WORKSPACE.  Every call on one device shares
+ * that device's array, which keeps the last call's contents (the decode
+ * writes every partial it reads, so nothing needs clearing): calls that
+ * overlap on one device -- on different streams or threads -- race, and must
+ * be ordered by the caller. */
+tq_status tq_decode_attention_noalloc(const tq_codec* kc, const tq_codec* vc, const void* q, int32_t q_dtype,
+                                      int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t q_len,
+                                      const tq_cache* k, const tq_cache* v, const int32_t* d_len, int64_t max_len,
+                                      float scale, float* out, void* stream);
+
 /* Bytes of device workspace tq_prefill_attention needs for these sizes (one
  * block of rows at a time reuses it). */
 tq_status tq_prefill_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t n_q_heads,

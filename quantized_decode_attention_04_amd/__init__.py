@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     tq_codec_get_info,
     tq_codec_upload,
     tq_decode_attention,
+    tq_decode_attention_noalloc,
     tq_decode_workspace_size,
     tq_last_error,
     tq_prefill_attention,

@@ -72,6 +72,8 @@ def _load() -> ctypes.CDLL:
         "tq_prefill_attention": (I32, [P, P, P, I32, I32, I32, I32, I32, ctypes.POINTER(_Cache),
                                        ctypes.POINTER(_Cache), P, I64, ctypes.c_float, P, P, SZ, P]),
         "tq_stream_read": (I32, [P, U64, P, I32, P]),
+        "tq_decode_attention_noalloc": (I32, [P, P, P, I32, I32, I32, I32, I32, ctypes.POINTER(_Cache),
+                                              ctypes.POINTER(_Cache), P, I64, ctypes.c_float, P, P]),
         "tq_last_error": (ctypes.c_char_p, []),
         "tq_status_string": (ctypes.c_char_p, [I32]),
     }
@@ -88,7 +90,7 @@ EXPORTED = (
     "tq_codec_create", "tq_codec_destroy", "tq_codec_get_info", "tq_codec_export", "tq_codec_upload",
     "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_workspace_size", "tq_decode_attention",
     "tq_prefill_workspace_size", "tq_prefill_attention", "tq_cache_gather", "tq_stream_read", "tq_last_error",
-    "tq_status_string",
+    "tq_status_string", "tq_decode_attention_noalloc",
 )
 
 
@@ -319,6 +321,27 @@ def tq_decode_attention(kc: Codec, vc: Codec, q, kcache: Cache, vcache: Cache, l
     device [batch]; out: float32 contiguous like q; ws: device byte tensor of at
     least tq_decode_workspace_size(...) bytes (allocate_workspace)."""
     _attention(_lib.tq_decode_attention, kc, vc, q, kcache, vcache, lens, max_len, scale, out, ws, stream)
+
+
+def tq_decode_attention_noalloc(kc: Codec, vc: Codec, q, kcache: Cache, vcache: Cache, lens, max_len: int,
+                                scale: float, out, stream=None) -> None:
+    """tq_decode_attention with the library's own device scratch instead of a
+    workspace (allocates nothing; the codecs' tables must be on the device
+    already, tq_codec_upload)."""
+    import torch
+    _on_device(q, lens, out, *kcache.arrays().values(), *vcache.arrays().values())
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [batch, n_q_heads, q_len, head_dim] tensor")
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must be a contiguous float32 tensor shaped like q")
+    if lens.dtype != torch.int32 or lens.numel() != q.shape[0] or not lens.is_contiguous():
+        raise ValueError("lens must be a contiguous int32 tensor of length batch")
+    ks, vs = kcache.as_struct(), vcache.as_struct()
+    _check(_lib.tq_decode_attention_noalloc(kc.handle, vc.handle, ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
+                                            int(q.shape[0]), int(q.shape[1]), int(kcache.heads), int(q.shape[2]),
+                                            ctypes.byref(ks), ctypes.byref(vs), ctypes.c_void_p(lens.data_ptr()),
+                                            int(max_len), ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()),
+                                            _stream(stream)))
 
 
 def tq_prefill_workspace_size(kc: Codec, vc: Codec, batch: int, n_q_heads: int, n_kv_heads: int, q_len: int,

@@ -38,8 +38,10 @@ uint64_t bytes_per_token(const tq::HostCodec& h) {
   return b;
 }
 
-// Upload the codec's tables to the current device (once per device).
-tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out) {
+// Upload the codec's tables to the current device (once per device).  With
+// may_upload false a codec whose tables are not on the device yet is refused
+// instead (the entry point that allocates nothing).
+tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out, bool may_upload = true) {
   tq_codec* c = const_cast<tq_codec*>(cc);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -47,6 +49,8 @@ tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out) {
   if (dev < 0 || dev >= tq::kMaxDevices) return fail(TQ_ERR_UNSUPPORTED, "device index above 15");
   std::lock_guard<std::mutex> lock(c->mu);
   tq::DevTables& t = c->dev[dev];
+  if (!c->uploaded[dev] && c->h.mode != TQ_MODE_GROUP && !may_upload)
+    return fail(TQ_ERR_INVALID_ARG, "codec tables are not on this device yet: call tq_codec_upload first");
   if (!c->uploaded[dev] && c->h.mode != TQ_MODE_GROUP) {
     const int d = c->h.d;
     const size_t dd = (size_t)d * d;
@@ -412,7 +416,8 @@ tq_status tq_prefill_workspace_size(const tq_codec* kc, const tq_codec* vc, int3
 static tq_status attention_impl(const char* name, bool blocks, const tq_codec* kc, const tq_codec* vc, const void* q,
                                 int32_t q_dtype, int32_t batch, int32_t hq, int32_t hkv, int32_t q_len,
                                 const tq_cache* k, const tq_cache* v, const int32_t* d_len, int64_t max_len,
-                                float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+                                float scale, float* out, void* ws, size_t ws_bytes, void* stream,
+                                bool may_upload = true) {
   const std::string fn(name);
   tq_status st = check_decode_shapes(kc, vc, batch, hq, hkv, q_len, max_len, blocks);
   if (st != TQ_OK) return st;
@@ -437,10 +442,10 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
     return fail(TQ_ERR_WORKSPACE, fn + ": workspace needs " + std::to_string(plan.total) + " bytes");
   tq::DevTables* kt = nullptr;
   tq::DevTables* vt = nullptr;
-  st = ensure_tables(kc, &kt);
+  st = ensure_tables(kc, &kt, may_upload);
   if (st != TQ_OK) return st;
   if (vc->h.mode != TQ_MODE_GROUP) {
-    st = ensure_tables(vc, &vt);
+    st = ensure_tables(vc, &vt, may_upload);
     if (st != TQ_OK) return st;
   }
   char* w = static_cast<char*>(ws);
@@ -504,6 +509,24 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
   }
   return TQ_OK;
 }
+
+}  // extern "C"
+
+namespace tq {
+
+tq_status decode_attention_in(const char* name, const tq_codec* kc, const tq_codec* vc, const void* q,
+                              int32_t q_dtype, int32_t batch, int32_t hq, int32_t hkv, int32_t q_len,
+                              const tq_cache* k, const tq_cache* v, const int32_t* d_len, int64_t max_len,
+                              float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  return attention_impl(name, false, kc, vc, q, q_dtype, batch, hq, hkv, q_len, k, v, d_len, max_len, scale, out, ws,
+                        ws_bytes, stream, false);
+}
+
+tq_status set_error(tq_status s, const std::string& msg) { return fail(s, msg); }
+
+}  // namespace tq
+
+extern "C" {
 
 tq_status tq_decode_attention(const tq_codec* kc, const tq_codec* vc, const void* q, int32_t q_dtype, int32_t batch,
                               int32_t hq, int32_t hkv, int32_t q_len, const tq_cache* k, const tq_cache* v,

@@ -187,6 +187,18 @@ struct CacheGather {
 
 hipError_t launch_cache_gather(const CacheGather& g, int64_t max_count, hipStream_t stream);
 
+// ---- the decode call behind the entry point that allocates nothing ------------
+
+// tq_decode_attention's checks, plan and launches with the given workspace,
+// refusing (instead of uploading) a codec whose tables are not on the current
+// device yet; name prefixes the error messages.
+tq_status decode_attention_in(const char* name, const tq_codec* kc, const tq_codec* vc, const void* q,
+                              int32_t q_dtype, int32_t batch, int32_t hq, int32_t hkv, int32_t q_len,
+                              const tq_cache* k, const tq_cache* v, const int32_t* d_len, int64_t max_len,
+                              float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+// Records msg as the thread's last error and returns s.
+tq_status set_error(tq_status s, const std::string& msg);
+
 // ---- measurement ------------------------------------------------------------
 
 // Threads per workgroup of the streaming-read kernel.
