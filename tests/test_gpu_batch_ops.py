@@ -1,0 +1,195 @@
+"""GPU batch bookkeeping against the oracle's definition (oracle.batch): the
+library's record copies (tq_cache_gather) for filter / extract / extend /
+merge, appends at each row's written end and length trims must leave the
+device caches holding exactly the oracle's batch, and decode over them must
+match the oracle's decode (relative L2 1e-4 per row).  Covers the regressions
+"omlx turboquant_kv.py" records: an append after a filter landing inside a
+survivor's live tokens (the _phys_end note), capacity slots being attended
+(the state note), and short rows next to long ones (the make_mask note)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import attention as oatt
+from oracle import batch as obatch
+from oracle import codec as ocodec
+from oracle import quant as oquant
+from tests.gpu_util import WINDOW, download, rel_l2_rows, to_device_f, words_i32
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+import quantized_decode_attention_04_amd as tq  # noqa: E402
+from quantized_decode_attention_04_amd.workloads import round_bf16  # noqa: E402
+
+H, D = 2, 128
+
+
+def _window_free(rng, shape, oc):
+    """bf16 draws N(0, 0.02^2) whose quantised state is unique (no decision
+    value inside the window), so that GPU and oracle codes must agree bit for
+    bit."""
+    x = round_bf16(rng.standard_normal(shape).astype(np.float32) * np.float32(0.02))
+    for _ in range(50):
+        st = oquant.quantize(x.astype(np.float64), oc)
+        m = st["margin"] < WINDOW * (((1 << oc.bits) - 1) if oc.mode == 2 else 1)
+        if oc.mode == 1:
+            m = m | (st["zmargin"] < WINDOW)
+        bad = m.any(-1)
+        if not bad.any():
+            return x
+        x = x.copy()
+        x[bad] = round_bf16(rng.standard_normal((int(bad.sum()), shape[-1])).astype(np.float32) * np.float32(0.02))
+    raise RuntimeError("no window-free draw")
+
+
+def _upload(cache, ob: obatch.Batch, cap):
+    """Write the oracle batch into a device cache; slots past each length get
+    large garbage records (never attended)."""
+    arrays, lens = obatch.padded(ob, cap)
+    rng = np.random.default_rng(99)
+    for name, t in cache.arrays().items():
+        key = {"idx": "words", "norm": "norm", "rnorm": "rnorm", "sign": "sign_words", "scale": "scale",
+               "gmin": "min"}[name]
+        a = np.array(arrays[key])
+        for b, n in enumerate(lens):
+            tail = a[b, :, n:]
+            if a.dtype.kind in "ui":
+                a[b, :, n:] = rng.integers(0, 2**32, tail.shape, dtype=np.uint64).astype(a.dtype)
+            else:
+                a[b, :, n:] = 1e4 * (1.0 + rng.random(tail.shape))
+        src = words_i32(a) if a.dtype.kind in "ui" else np.asarray(a, dtype=np.float32)
+        t.copy_(torch.from_numpy(np.ascontiguousarray(src)).to(t.device))
+
+
+def _check_state(cache, ob: obatch.Batch, tag):
+    """The attended slots of the device cache hold the oracle batch: packed
+    words and sign bits bit for bit, float side data to 1e-6 relative
+    (copied records are exact; an appended token's norm is the device's own
+    float32 arithmetic)."""
+    got = download(cache)
+    arrays, lens = obatch.padded(ob, cache.cap)
+    for name, a in got.items():
+        key = {"idx": "words", "norm": "norm", "rnorm": "rnorm", "sign": "sign_words", "scale": "scale",
+               "gmin": "min"}[name]
+        want = np.asarray(arrays[key])
+        for b, n in enumerate(lens):
+            if a.dtype.kind == "f":
+                np.testing.assert_allclose(a[b, :, :n], want[b, :, :n], rtol=1e-6, atol=0,
+                                           err_msg=f"{tag}: {name} of row {b}")
+            else:
+                assert np.array_equal(a[b, :, :n], want[b, :, :n].astype(np.uint32)), \
+                    f"{tag}: {name} of row {b} differs from the oracle"
+
+
+def _decode_check(gk, gv, kcache, vcache, kb, vb, q, tag):
+    B = len(kb.seqs)
+    lens = kb.lens
+    assert list(lens) == list(vb.lens)
+    max_len = int(max(1, lens.max()))
+    out = torch.zeros((B, q.shape[1], 1, D), dtype=torch.float32, device="cuda")
+    ws = tq.allocate_workspace(gk, gv, B, q.shape[1], H, 1, max_len)
+    tq.tq_decode_attention(gk, gv, to_device_f(q, True), kcache, vcache,
+                           torch.tensor(lens, dtype=torch.int32, device="cuda"), max_len, 1 / math.sqrt(D), out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ka, _ = obatch.padded(kb, max_len)
+    va, _ = obatch.padded(vb, max_len)
+    want = oatt.decode_attention_rotated(q.astype(np.float64), obatch.unpacked(ka, kb.codec), kb.codec,
+                                         obatch.unpacked(va, vb.codec), vb.codec, lens, 1 / math.sqrt(D))
+    err = rel_l2_rows(got, want)
+    print(f"  {tag}: decode max row rel L2 {err.max():.2e}", flush=True)
+    assert err.max() <= 1e-4, tag
+
+
+CODECS = [((3, 1), (4, 0)), ((3, 0), (3, 0))]   # (bits, mode) of K and V: general path, int8 path
+
+
+@pytest.mark.parametrize("kspec,vspec", CODECS, ids=["prod3_mse4", "mse3_mse3"])
+def test_batch_ops_match_the_oracle(kspec, vspec):
+    print(f"batch ops k={kspec} v={vspec}", flush=True)
+    sys.stdout.flush()
+    rng = np.random.default_rng(7)
+    okc, ovc = ocodec.make_codec(D, kspec[0], 0, kspec[1]), ocodec.make_codec(D, vspec[0], 1, vspec[1])
+    gk, gv = tq.tq_codec_create(D, kspec[0], 0, kspec[1]), tq.tq_codec_create(D, vspec[0], 1, vspec[1])
+    lens, cap = [37, 300, 5, 180], 320
+    xk = [round_bf16(rng.standard_normal((H, n, D)).astype(np.float32) * np.float32(0.02)) for n in lens]
+    xv = [round_bf16(rng.standard_normal((H, n, D)).astype(np.float32) * np.float32(0.02)) for n in lens]
+    K, V = obatch.from_inputs(xk, okc), obatch.from_inputs(xv, ovc)
+    Kd, Vd = tq.allocate_cache(gk, 4, H, cap), tq.allocate_cache(gv, 4, H, cap)
+    _upload(Kd, K, cap)
+    _upload(Vd, V, cap)
+    q4 = round_bf16(rng.standard_normal((4, 16, 1, D)).astype(np.float32) * np.float32(0.5))
+    _decode_check(gk, gv, Kd, Vd, K, V, q4, "source batch (garbage past every length)")
+
+    # filter: keep rows 3 and 1, in that order
+    keep = [3, 1]
+    Kf, Vf = tq.allocate_cache(gk, 2, H, cap), tq.allocate_cache(gv, 2, H, cap)
+    for g, src, dst in ((gk, Kd, Kf), (gv, Vd, Vf)):
+        tq.tq_cache_gather(g, src, g, dst, keep, [0, 0], [lens[i] for i in keep])
+    Kof, Vof = obatch.filter_rows(K, keep), obatch.filter_rows(V, keep)
+    torch.cuda.synchronize()
+    _check_state(Kf, Kof, "filter keys")
+    _check_state(Vf, Vof, "filter values")
+    before = {k: v.copy() for k, v in download(Kf).items()}
+
+    # append 2 tokens to each survivor at its own written end (the _phys_end
+    # regression: not at an offset taken from another row)
+    newk = [_window_free(rng, (H, 2, D), okc) for _ in keep]
+    newv = [_window_free(rng, (H, 2, D), ovc) for _ in keep]
+    ends = [lens[i] for i in keep]
+    pos = torch.tensor(ends, dtype=torch.int32, device="cuda")
+    nk = np.stack(newk)              # [2, H, 2, D]
+    nv = np.stack(newv)
+    tq.tq_quantize_append_kv(gk, gv, to_device_f(nk, True), to_device_f(nv, True), Kf, Vf, pos, max(ends) + 2)
+    Kof, Vof = obatch.append(Kof, newk), obatch.append(Vof, newv)
+    torch.cuda.synchronize()
+    _check_state(Kf, Kof, "append after filter, keys")
+    _check_state(Vf, Vof, "append after filter, values")
+    after = download(Kf)
+    for name in before:              # the survivors' live tokens are untouched
+        for b, n in enumerate(ends):
+            assert np.array_equal(after[name][b, :, :n], before[name][b, :, :n]), f"{name} row {b} overwritten"
+    _decode_check(gk, gv, Kf, Vf, Kof, Vof, q4[keep], "filtered + appended")
+
+    # extract a window of row 1 (tokens 10..49) and trim the filtered row 0
+    Ke, Ve = tq.allocate_cache(gk, 1, H, 64), tq.allocate_cache(gv, 1, H, 64)
+    for g, src, dst in ((gk, Kd, Ke), (gv, Vd, Ve)):
+        tq.tq_cache_gather(g, src, g, dst, [1], [10], [40])
+    Koe, Voe = obatch.extract(K, 1, 10, 40), obatch.extract(V, 1, 10, 40)
+    torch.cuda.synchronize()
+    _check_state(Ke, Koe, "extract")
+    _decode_check(gk, gv, Ke, Ve, Koe, Voe, q4[1:2], "extracted window")
+    _decode_check(gk, gv, Kf, Vf, obatch.trim(Kof, 0, 50), obatch.trim(Vof, 0, 50), q4[keep], "trimmed row")
+
+    # extend / merge: the filtered batch, then row 2 (5 tokens) and the window
+    Km, Vm = tq.allocate_cache(gk, 4, H, cap), tq.allocate_cache(gv, 4, H, cap)
+    fl = [int(x) for x in Kof.lens]
+    for g, srcs, dst in ((gk, (Kf, Kd, Ke), Km), (gv, (Vf, Vd, Ve), Vm)):
+        tq.tq_cache_gather(g, srcs[0], g, dst, [0, 1, -1, -1], [0, 0, 0, 0], [fl[0], fl[1], 0, 0])
+        tq.tq_cache_gather(g, srcs[1], g, dst, [-1, -1, 2, -1], [0, 0, 0, 0], [0, 0, lens[2], 0])
+        tq.tq_cache_gather(g, srcs[2], g, dst, [-1, -1, -1, 0], [0, 0, 0, 0], [0, 0, 0, 40])
+    Kom = obatch.merge(Kof, obatch.extract(K, 2, 0, lens[2]), Koe)
+    Vom = obatch.merge(Vof, obatch.extract(V, 2, 0, lens[2]), Voe)
+    torch.cuda.synchronize()
+    _check_state(Km, Kom, "merge keys")
+    _check_state(Vm, Vom, "merge values")
+    _decode_check(gk, gv, Km, Vm, Kom, Vom, q4[[3, 1, 2, 0]], "merged batch")
+
+    # the pages' merge guard: caches of codecs with different bits or seed
+    other = tq.tq_codec_create(D, kspec[0], 5, kspec[1])
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_cache_gather(gk, Kd, other, Km, [0, -1, -1, -1], [0, 0, 0, 0], [5, 0, 0, 0])
+    assert e.value.status == 3
+    with pytest.raises(ValueError):
+        obatch.merge(K, obatch.from_inputs(xk[:1], ocodec.make_codec(D, kspec[0], 5, kspec[1])))
