@@ -27,7 +27,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import quant
-from .codec import MODE_GROUP, MODE_MSE, MODE_PROD, Codec
+from .codec import MODE_GROUP, MODE_MSE, MODE_PROD, MODE_SPLIT, Codec
 
 
 def _visible(n_b: int, q_len: int, i: int) -> int:
@@ -68,6 +68,12 @@ def reference_attention(q, k, v, lens, scale: float) -> np.ndarray:
 
 def key_scores_rotated(qrow: np.ndarray, kstate: dict, kc: Codec, cnt: int) -> np.ndarray:
     """score(q, K_t) for t < cnt from the rotated query (no K reconstruction)."""
+    if kc.mode == MODE_SPLIT:
+        # the sum of the two parts' scores, each against its own rotated query
+        lo = {"idx": kstate["idx"][..., :kc.d_lo], "norm": kstate["norm"]}
+        hi = {"idx": kstate["idx"][..., kc.d_lo:], "norm": kstate["rnorm"]}
+        return (key_scores_rotated(qrow[:kc.d_lo], lo, kc.low, cnt) +
+                key_scores_rotated(qrow[kc.d_lo:], hi, kc.high, cnt))
     q_rot = kc.rot @ qrow                                  # Pi q
     cv = kc.centroids[kstate["idx"][:cnt]]                 # [cnt, d]
     s = np.asarray(kstate["norm"][:cnt], dtype=np.float64) * (cv @ q_rot)
@@ -82,6 +88,11 @@ def value_accumulate_rotated(p: np.ndarray, vstate: dict, vc: Codec, cnt: int) -
     """sum_t p_t V~_t, accumulated in the rotated domain for MSE values."""
     if vc.mode == MODE_GROUP:
         return p @ quant.dequantize_group(vstate["q"][:cnt], vstate["scale"][:cnt], vstate["min"][:cnt])
+    if vc.mode == MODE_SPLIT:
+        lo = {"idx": vstate["idx"][..., :vc.d_lo], "norm": vstate["norm"]}
+        hi = {"idx": vstate["idx"][..., vc.d_lo:], "norm": vstate["rnorm"]}
+        return np.concatenate([value_accumulate_rotated(p, lo, vc.low, cnt),
+                               value_accumulate_rotated(p, hi, vc.high, cnt)])
     assert vc.mode == MODE_MSE
     w = p * np.asarray(vstate["norm"][:cnt], dtype=np.float64)
     o_rot = w @ vc.centroids[vstate["idx"][:cnt]]          # rotated domain

@@ -38,7 +38,7 @@ from typing import List
 import numpy as np
 
 from . import quant
-from .codec import MODE_GROUP, MODE_MSE, MODE_PROD, Codec
+from .codec import MODE_GROUP, MODE_MSE, MODE_PROD, MODE_SPLIT, Codec
 
 # the fields a cache stores per token-head, by mode (packing.pack output and
 # float32 side data)
@@ -46,6 +46,7 @@ STORED = {
     MODE_MSE: ("words", "norm"),
     MODE_PROD: ("words", "norm", "rnorm", "sign_words"),
     MODE_GROUP: ("words", "scale", "min"),
+    MODE_SPLIT: ("words", "norm", "rnorm"),
 }
 
 
@@ -85,7 +86,7 @@ def extract(batch: Batch, b: int, start: int, count: int) -> Batch:
 
 
 def _same_codec(a: Codec, b: Codec) -> bool:
-    return (a.head_dim, a.bits, a.mode, a.seed) == (b.head_dim, b.bits, b.mode, b.seed)
+    return (a.head_dim, a.bits, a.mode, a.seed) == (b.head_dim, b.bits, b.mode, b.seed)   # split: bits is the width
 
 
 def merge(*batches: Batch) -> Batch:
@@ -125,6 +126,8 @@ def padded(batch: Batch, cap: int, fill=0):
 
 def unpacked(arrays: dict, codec: Codec) -> dict:
     """A padded state in the form the oracle's decode reads (unpacked codes)."""
+    if codec.mode == MODE_SPLIT:
+        return quant.state_from_words(codec, arrays["words"], norm=arrays["norm"], rnorm=arrays["rnorm"])
     if codec.mode == MODE_GROUP:
         return quant.state_from_words(codec, arrays["words"], scale=arrays["scale"], mn=arrays["min"])
     return quant.state_from_words(codec, arrays["words"], norm=arrays["norm"], rnorm=arrays.get("rnorm"),

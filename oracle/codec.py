@@ -53,6 +53,7 @@ from . import prng
 MODE_MSE = 0
 MODE_PROD = 1
 MODE_GROUP = 2
+MODE_SPLIT = 3
 
 GRID_MAX = 16256  # 127 * 128: largest stored centroid magnitude in grid units
 GROUP_SIZE = 32
@@ -132,9 +133,10 @@ def store_codebook(c: np.ndarray):
     return cs, bnd, e
 
 
-def rotation(d: int, seed: int) -> np.ndarray:
-    """Pi (float64): QR of the seed's stream-0 Gaussian with positive diag(R)."""
-    g = prng.gaussian_matrix(seed, prng.STREAM_ROTATION, d)
+def rotation(d: int, seed: int, stream: int = prng.STREAM_ROTATION) -> np.ndarray:
+    """Pi (float64): QR of the seed's Gaussian (stream 0 unless stated) with
+    positive diag(R)."""
+    g = prng.gaussian_matrix(seed, stream, d)
     q, r = np.linalg.qr(g)
     sgn = np.where(np.diag(r) < 0.0, -1.0, 1.0)
     return q * sgn[None, :]
@@ -164,7 +166,7 @@ class Codec:
         return 1 << self.mse_bits
 
 
-def make_codec(head_dim: int, bits: int, seed: int, mode: int) -> Codec:
+def make_codec(head_dim: int, bits: int, seed: int, mode: int, rot_stream: int = prng.STREAM_ROTATION) -> Codec:
     """Build a codec.  Prod spends bits-1 on the MSE stage and 1 on QJL signs
     ("omlx turboquant_kv.py", ``_infer_head_dim``: the Prod state's packed
     width uses bits - 1); group mode has no rotation or codebook."""
@@ -180,8 +182,81 @@ def make_codec(head_dim: int, bits: int, seed: int, mode: int) -> Codec:
         raise ValueError("unsupported (bits, mode)")
     sol = lloyd_max_solve(d, mse_bits)
     cs, bnd, e = store_codebook(sol)
-    rot = rotation(d, seed).astype(np.float32).astype(np.float64)
+    rot = rotation(d, seed, rot_stream).astype(np.float32).astype(np.float64)
     sk = None
     if mode == MODE_PROD:
         sk = sketch(d, seed).astype(np.float32).astype(np.float64)
     return Codec(d, bits, seed, mode, mse_bits, rot, cs, bnd, sk, e, sol)
+
+
+# ---- fractional bit-widths ---------------------------------------------------
+#
+# "omlx turboquant_kv.py", _rebuild_codecs: a bit-width is fractional when it
+# is not within 1e-6 of an integer; then the key codec takes floor(bits) and
+# the value codec ceil(bits) (both MSE, key on seed s, value on s + 1);
+# otherwise both take bits.  The same page's state helpers carry a
+# TurboQuantSplitState(low, high): two sub-states filtered and concatenated
+# together along the batch axis.  Reading taken for it (the plainest one the
+# rest supports): a split codec of fractional width b quantises the first
+# d_lo channels of a head vector with a floor(b)-bit MSE codec ("low") and the
+# last d_hi channels with a ceil(b)-bit one ("high"), each an independent
+# TurboQuant instance of its own dimension (own rotation, norm and Lloyd-Max
+# codebook), d_hi = round((b - floor b) d / 32) * 32 so that both parts are
+# whole 32-coordinate groups; the mean width is b whenever (b - floor b) d is
+# a multiple of 32 (2.5, 3.5, 3.25 and 3.75 bits at d = 128).  The low part's
+# rotation is stream 0 of the seed, the high part's stream 2.
+
+
+def is_fractional(bits: float) -> bool:
+    return not math.isclose(bits, round(bits), abs_tol=1e-6)
+
+
+def kv_bits(bits: float):
+    """(key bits, value bits) of the codec rebuild rule."""
+    if is_fractional(bits):
+        return int(math.floor(bits)), int(math.ceil(bits))
+    return int(round(bits)), int(round(bits))
+
+
+def kv_codecs(head_dim: int, bits: float, seed: int):
+    """The key and value MSE codecs a cache of width ``bits`` rebuilds."""
+    kb, vb = kv_bits(bits)
+    return make_codec(head_dim, kb, seed, MODE_MSE), make_codec(head_dim, vb, seed + 1, MODE_MSE)
+
+
+@dataclass
+class SplitCodec:
+    head_dim: int
+    bits: float
+    seed: int
+    low: Codec      # channels 0 .. d_lo - 1, floor(bits)
+    high: Codec     # channels d_lo .. d - 1, ceil(bits)
+    mode: int = MODE_SPLIT
+
+    @property
+    def d_lo(self) -> int:
+        return self.low.head_dim
+
+    @property
+    def d_hi(self) -> int:
+        return self.high.head_dim
+
+
+def split_shape(head_dim: int, bits: float):
+    """(d_lo, d_hi, low bits, high bits) of a split codec."""
+    if not is_fractional(bits):
+        raise ValueError("a split codec needs a fractional bit-width")
+    lo, hi = int(math.floor(bits)), int(math.ceil(bits))
+    d_hi = int(round((bits - lo) * head_dim / 32.0)) * 32
+    if lo < 1 or hi > 4 or not 32 <= d_hi <= head_dim - 32:
+        raise ValueError("unsupported split: each part needs 32..head_dim-32 channels and 1..4 bits")
+    return head_dim - d_hi, d_hi, lo, hi
+
+
+def make_split_codec(head_dim: int, bits: float, seed: int) -> SplitCodec:
+    d = int(head_dim)
+    if d <= 0 or d % 32 or d > 256:
+        raise ValueError("head_dim must be a positive multiple of 32, at most 256")
+    d_lo, d_hi, lo, hi = split_shape(d, bits)
+    return SplitCodec(d, float(bits), seed, make_codec(d_lo, lo, seed, MODE_MSE),
+                      make_codec(d_hi, hi, seed, MODE_MSE, rot_stream=prng.STREAM_SPLIT_HIGH))

@@ -34,6 +34,7 @@ MASK64 = (1 << 64) - 1
 
 STREAM_ROTATION = 0
 STREAM_SKETCH = 1
+STREAM_SPLIT_HIGH = 2   # rotation of the high part of a split codec
 
 
 def stream_start(seed: int, stream: int) -> int:

@@ -39,7 +39,7 @@ import math
 import numpy as np
 
 from . import packing
-from .codec import GROUP_SIZE, MODE_GROUP, MODE_MSE, MODE_PROD, Codec
+from .codec import GROUP_SIZE, MODE_GROUP, MODE_MSE, MODE_PROD, MODE_SPLIT, Codec
 
 
 def _f32(a) -> np.ndarray:
@@ -114,11 +114,31 @@ def group_quantize(v: np.ndarray, bits: int, group_size: int = GROUP_SIZE) -> di
     }
 
 
+def split_quantize(x: np.ndarray, codec) -> dict:
+    """Split codec: the low channels through the low MSE codec, the high
+    channels through the high one.  The stored layout is one token record: the
+    low part's packed words then the high part's, the low norm ("norm") and
+    the high norm ("rnorm"); margins and codes are the two parts' side by
+    side."""
+    x = np.asarray(x, dtype=np.float64)
+    lo = mse_quantize(x[..., :codec.d_lo], codec.low)
+    hi = mse_quantize(x[..., codec.d_lo:], codec.high)
+    return {
+        "low": lo, "high": hi,
+        "words": np.concatenate([lo["words"], hi["words"]], axis=-1),
+        "norm": lo["norm"], "rnorm": hi["norm"],
+        "idx": np.concatenate([lo["idx"], hi["idx"]], axis=-1),
+        "margin": np.concatenate([lo["margin"], hi["margin"]], axis=-1),
+    }
+
+
 def quantize(x: np.ndarray, codec: Codec) -> dict:
     if codec.mode == MODE_MSE:
         return mse_quantize(x, codec)
     if codec.mode == MODE_PROD:
         return prod_quantize(x, codec)
+    if codec.mode == MODE_SPLIT:
+        return split_quantize(x, codec)
     return group_quantize(x, codec.bits)
 
 
@@ -158,6 +178,10 @@ def dequantize_state(state: dict, codec: Codec) -> np.ndarray:
         return dequantize_mse(state["norm"], state["idx"], codec)
     if codec.mode == MODE_PROD:
         return dequantize_prod(state["norm"], state["idx"], state["rnorm"], state["sign_bits"], codec)
+    if codec.mode == MODE_SPLIT:
+        lo = dequantize_mse(state["norm"], state["idx"][..., :codec.d_lo], codec.low)
+        hi = dequantize_mse(state["rnorm"], state["idx"][..., codec.d_lo:], codec.high)
+        return np.concatenate([lo, hi], axis=-1)
     return dequantize_group(state["q"], state["scale"], state["min"])
 
 
@@ -167,6 +191,12 @@ def state_from_words(codec: Codec, words, norm=None, rnorm=None, sign_words=None
     d = codec.head_dim
     if codec.mode == MODE_GROUP:
         return {"q": packing.unpack(words, codec.bits, d), "scale": scale, "min": mn}
+    if codec.mode == MODE_SPLIT:
+        w_lo = codec.d_lo * codec.low.bits // 32
+        words = np.asarray(words)
+        idx = np.concatenate([packing.unpack(words[..., :w_lo], codec.low.bits, codec.d_lo),
+                              packing.unpack(words[..., w_lo:], codec.high.bits, codec.d_hi)], axis=-1)
+        return {"idx": idx, "norm": norm, "rnorm": rnorm}
     st = {"idx": packing.unpack(words, codec.mse_bits, d), "norm": norm}
     if codec.mode == MODE_PROD:
         st["rnorm"] = rnorm
