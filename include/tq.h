@@ -69,8 +69,14 @@ typedef enum {
  *          MSE + QJL).  bits 2..5.  Keys only.
  *   GROUP: asymmetric min-max quantisation of the unrotated vector in groups
  *          of 32 coordinates with float32 scale and minimum per group ([val]
- *          quantize_values).  bits 1..4.  Values only.                      */
-typedef enum { TQ_MODE_MSE = 0, TQ_MODE_PROD = 1, TQ_MODE_GROUP = 2 } tq_mode;
+ *          quantize_values).  bits 1..4.  Values only.
+ *   SPLIT: a fractional width b ([omlx] TurboQuantSplitState(low, high)):
+ *          the first d_lo channels through a floor(b)-bit MSE codec ("low"),
+ *          the last d_hi = round((b - floor b) * head_dim / 32) * 32 channels
+ *          through a ceil(b)-bit one ("high"), each with its own rotation,
+ *          norm and codebook.  Built by tq_codec_create_split only.  Keys or
+ *          values.                                                         */
+typedef enum { TQ_MODE_MSE = 0, TQ_MODE_PROD = 1, TQ_MODE_GROUP = 2, TQ_MODE_SPLIT = 3 } tq_mode;
 
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 
@@ -78,15 +84,17 @@ typedef struct tq_codec tq_codec; /* opaque, immutable after creation */
 
 typedef struct {
   int32_t head_dim;
-  int32_t bits;        /* bits per coordinate as requested (Prod includes the sign bit) */
+  int32_t bits;        /* bits per coordinate as requested (Prod includes the sign bit); SPLIT: floor(b) */
   int32_t mode;        /* tq_mode */
-  int32_t mse_bits;    /* bits of the packed index stream: bits (MSE, GROUP) or bits-1 (PROD) */
-  int32_t levels;      /* 2^mse_bits (MSE, PROD); 0 in GROUP mode */
-  int32_t idx_words;   /* W = head_dim*mse_bits/32 words per token-head ([omlx] _infer_head_dim) */
+  int32_t mse_bits;    /* bits of the packed index stream: bits (MSE, GROUP) or bits-1 (PROD); SPLIT: low part's */
+  int32_t levels;      /* 2^mse_bits (MSE, PROD, SPLIT low part); 0 in GROUP mode */
+  int32_t idx_words;   /* words per token-head of idx: head_dim*mse_bits/32 ([omlx] _infer_head_dim);
+                          SPLIT: the low part's words plus the high part's (= ceil(head_dim*b/32)
+                          when (b - floor b)*head_dim is a multiple of 32) */
   int32_t sign_words;  /* head_dim/32 in PROD mode, else 0 */
   int32_t groups;      /* head_dim/32 in GROUP mode, else 0 */
-  int32_t grid_exp;    /* E: every centroid is an integer multiple of 2^-E (|c| 2^E <= 16256) */
-  int32_t reserved;
+  int32_t grid_exp;    /* E: every centroid is an integer multiple of 2^-E (|c| 2^E <= 16256); SPLIT: low part's */
+  int32_t split_high_dim; /* SPLIT: d_hi, channels of the high part (the last ones); else 0 */
   uint64_t seed;
   uint64_t bytes_per_token; /* compressed bytes per token-head (state only) */
 } tq_codec_info;
@@ -100,6 +108,10 @@ typedef struct {
  *   sign   uint32 [..][cap][sign_words]  Prod: QJL sign bits, bit j = coordinate j
  *   scale  float  [..][cap][groups]      GROUP: (max-min)/(2^bits-1) per group
  *   gmin   float  [..][cap][groups]      GROUP: minimum per group ("zeros")
+ * A SPLIT cache holds both sub-states of [omlx] TurboQuantSplitState(low,
+ * high) in one token record: idx is the low part's packed words followed by
+ * the high part's (idx_words in all), norm the low part's norm and rnorm the
+ * high part's.
  * Packed layout of idx: see the codec section of the library's design notes;
  * for 1, 2 and 4 bits it is an LSB-first stream (index j at bits
  * [b*j, b*j+b) of the word stream); 3-bit indices use a byte-lane layout
@@ -123,6 +135,28 @@ typedef struct {
  * not a multiple of 32 in 32..256, bits out of range for the mode). */
 tq_status tq_codec_create(int32_t head_dim, int32_t bits, uint64_t seed, int32_t mode, tq_codec** out);
 
+/* The two codecs of a cache of width `bits` ([omlx] _rebuild_codecs): when
+ * bits is fractional (not within 1e-6 of an integer) the key codec takes
+ * floor(bits) and the value codec ceil(bits), else both take bits; both are
+ * MSE codecs, the key one on `seed` and the value one on seed + 1.  The
+ * caller owns both (tq_codec_destroy).  Errors: INVALID_ARG (NULL), UNSUPPORTED
+ * (a resulting width outside 1..4 bits, head_dim as for tq_codec_create). */
+tq_status tq_codec_create_kv(int32_t head_dim, double bits, uint64_t seed, tq_codec** key_out, tq_codec** value_out);
+
+/* A SPLIT codec of fractional width `bits` (see tq_mode): the low part is the
+ * MSE codec (d_lo, floor(bits), seed) with its rotation from stream 0 of the
+ * seed, the high part the MSE codec (d_hi, ceil(bits), seed) with its
+ * rotation from stream 2.  Errors: INVALID_ARG (out NULL), UNSUPPORTED
+ * (bits within 1e-6 of an integer, a part with fewer than 32 channels, a
+ * part outside 1..4 bits, head_dim not a multiple of 32 in 64..256). */
+tq_status tq_codec_create_split(int32_t head_dim, double bits, uint64_t seed, tq_codec** out);
+
+/* The low (which = 0) or high (which = 1) part of a SPLIT codec, as an MSE
+ * codec of the part's channels, owned by `codec` (valid until it is
+ * destroyed; never pass it to tq_codec_destroy).  Use it to export a part's
+ * tables.  Errors: INVALID_ARG (not a SPLIT codec, which not 0 or 1). */
+tq_status tq_codec_part(const tq_codec* codec, int32_t which, const tq_codec** out);
+
 /* Free a codec and its device tables.  NULL is a no-op.  The caller must make
  * sure no work using it is still queued on any stream. */
 void tq_codec_destroy(tq_codec* codec);
@@ -135,7 +169,10 @@ tq_status tq_codec_get_info(const tq_codec* codec, tq_codec_info* info);
  *   centroids  [levels] ascending
  *   boundaries [levels-1] midpoints of neighbouring centroids
  *   sketch     [head_dim][head_dim] S (PROD only; left untouched otherwise)
- * GROUP codecs have no tables (returns OK and writes nothing). */
+ * GROUP codecs have no tables (returns OK and writes nothing).  SPLIT codecs
+ * write the block-diagonal rotation (low part's rotation on channels 0..d_lo-1,
+ * the high part's on the rest) and the low part's centroids and boundaries
+ * (tq_codec_part exports either part's own tables). */
 tq_status tq_codec_export(const tq_codec* codec, float* rot, float* centroids, float* boundaries, float* sketch);
 
 /* Upload the codec's tables to the current device now (otherwise done on

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     TQ_MODE_GROUP,
     TQ_MODE_MSE,
     TQ_MODE_PROD,
+    TQ_MODE_SPLIT,
     Cache,
     Codec,
     TQError,
@@ -21,6 +22,9 @@ from ._binding import (  # noqa: F401
     lib_path,
     tq_cache_gather,
     tq_codec_create,
+    tq_codec_create_kv,
+    tq_codec_create_split,
+    tq_codec_part,
     tq_codec_destroy,
     tq_codec_export,
     tq_codec_get_info,

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtq.so")
 
 TQ_OK = 0
-TQ_MODE_MSE, TQ_MODE_PROD, TQ_MODE_GROUP = 0, 1, 2
+TQ_MODE_MSE, TQ_MODE_PROD, TQ_MODE_GROUP, TQ_MODE_SPLIT = 0, 1, 2, 3
 TQ_F32, TQ_BF16 = 0, 1
 
 
@@ -32,7 +32,7 @@ class _CodecInfo(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32), ("mode", ctypes.c_int32),
         ("mse_bits", ctypes.c_int32), ("levels", ctypes.c_int32), ("idx_words", ctypes.c_int32),
         ("sign_words", ctypes.c_int32), ("groups", ctypes.c_int32), ("grid_exp", ctypes.c_int32),
-        ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64), ("bytes_per_token", ctypes.c_uint64),
+        ("split_high_dim", ctypes.c_int32), ("seed", ctypes.c_uint64), ("bytes_per_token", ctypes.c_uint64),
     ]
 
 
@@ -56,6 +56,9 @@ def _load() -> ctypes.CDLL:
     sigs = {
         "tq_codec_create": (I32, [I32, I32, U64, I32, ctypes.POINTER(P)]),
         "tq_codec_destroy": (None, [P]),
+        "tq_codec_create_kv": (I32, [I32, ctypes.c_double, U64, ctypes.POINTER(P), ctypes.POINTER(P)]),
+        "tq_codec_create_split": (I32, [I32, ctypes.c_double, U64, ctypes.POINTER(P)]),
+        "tq_codec_part": (I32, [P, I32, ctypes.POINTER(P)]),
         "tq_codec_get_info": (I32, [P, ctypes.POINTER(_CodecInfo)]),
         "tq_codec_export": (I32, [P, P, P, P, P]),
         "tq_codec_upload": (I32, [P]),
@@ -90,7 +93,7 @@ EXPORTED = (
     "tq_codec_create", "tq_codec_destroy", "tq_codec_get_info", "tq_codec_export", "tq_codec_upload",
     "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_workspace_size", "tq_decode_attention",
     "tq_prefill_workspace_size", "tq_prefill_attention", "tq_cache_gather", "tq_stream_read", "tq_last_error",
-    "tq_status_string", "tq_decode_attention_noalloc",
+    "tq_status_string", "tq_decode_attention_noalloc", "tq_codec_create_kv", "tq_codec_create_split", "tq_codec_part",
 )
 
 
@@ -112,10 +115,13 @@ def _check(status: int) -> None:
 
 
 class Codec:
-    """Owner of a ``tq_codec*`` handle (destroyed with the object)."""
+    """Owner of a ``tq_codec*`` handle (destroyed with the object), or a
+    borrowed part of a split codec (``owner`` keeps the split codec alive and
+    the part is never destroyed on its own)."""
 
-    def __init__(self, handle: int):
+    def __init__(self, handle: int, owner: "Optional[Codec]" = None):
         self._h = ctypes.c_void_p(handle)
+        self._owner = owner
         self.info = tq_codec_get_info(self)
 
     @property
@@ -125,7 +131,7 @@ class Codec:
         return self._h
 
     def __del__(self):
-        if getattr(self, "_h", None) is not None:
+        if getattr(self, "_h", None) is not None and getattr(self, "_owner", None) is None:
             _lib.tq_codec_destroy(self._h)
             self._h = None
 
@@ -137,7 +143,32 @@ def tq_codec_create(head_dim: int, bits: int, seed: int, mode: int) -> Codec:
     return Codec(out.value)
 
 
+def tq_codec_create_kv(head_dim: int, bits: float, seed: int):
+    """(key codec, value codec) of a cache of width ``bits`` (floor / ceil
+    for a fractional width; see include/tq.h)."""
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    _check(_lib.tq_codec_create_kv(int(head_dim), float(bits), ctypes.c_uint64(int(seed) & (2**64 - 1)),
+                                   ctypes.byref(k), ctypes.byref(v)))
+    return Codec(k.value), Codec(v.value)
+
+
+def tq_codec_create_split(head_dim: int, bits: float, seed: int) -> Codec:
+    out = ctypes.c_void_p()
+    _check(_lib.tq_codec_create_split(int(head_dim), float(bits), ctypes.c_uint64(int(seed) & (2**64 - 1)),
+                                      ctypes.byref(out)))
+    return Codec(out.value)
+
+
+def tq_codec_part(codec: Codec, which: int) -> Codec:
+    """The low (0) or high (1) MSE part of a split codec (borrowed)."""
+    out = ctypes.c_void_p()
+    _check(_lib.tq_codec_part(codec.handle, int(which), ctypes.byref(out)))
+    return Codec(out.value, owner=codec)
+
+
 def tq_codec_destroy(codec: Codec) -> None:
+    if getattr(codec, "_owner", None) is not None:
+        raise ValueError("a part of a split codec is owned by the split codec")
     if codec._h is not None:
         _lib.tq_codec_destroy(codec._h)
         codec._h = None
@@ -210,6 +241,9 @@ def allocate_cache(codec: Codec, batch: int, heads: int, cap: int, device="cuda"
     if info["mode"] == TQ_MODE_PROD:
         c.rnorm = z()
         c.sign = z(info["sign_words"], dt=torch.int32)
+    if info["mode"] == TQ_MODE_SPLIT:
+        c.norm = z()          # the low part's norm
+        c.rnorm = z()         # the high part's norm
     if info["mode"] == TQ_MODE_GROUP:
         c.scale = z(info["groups"])
         c.gmin = z(info["groups"])

@@ -26,7 +26,12 @@ tq_status hip_fail(hipError_t e, const char* what) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int idx_words(const tq::HostCodec& h) { return h.d * h.mse_bits / 32; }
+// words of the low part of a split codec (its high part follows)
+int split_low_words(const tq::HostCodec& h) { return (h.d - h.split_dhi) * h.mse_bits / 32; }
+int idx_words(const tq::HostCodec& h) {
+  if (h.mode == TQ_MODE_SPLIT) return split_low_words(h) + h.split_dhi * (h.mse_bits + 1) / 32;
+  return h.d * h.mse_bits / 32;
+}
 int sign_words(const tq::HostCodec& h) { return h.mode == TQ_MODE_PROD ? h.d / 32 : 0; }
 int group_count(const tq::HostCodec& h) { return h.mode == TQ_MODE_GROUP ? h.d / 32 : 0; }
 
@@ -35,6 +40,7 @@ uint64_t bytes_per_token(const tq::HostCodec& h) {
   if (h.mode == TQ_MODE_MSE) b += 4;
   if (h.mode == TQ_MODE_PROD) b += 8 + 4ull * sign_words(h);
   if (h.mode == TQ_MODE_GROUP) b += 8ull * group_count(h);
+  if (h.mode == TQ_MODE_SPLIT) b += 8;  // the two parts' norms
   return b;
 }
 
@@ -54,7 +60,7 @@ tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out, bool may_upload
   if (!c->uploaded[dev] && c->h.mode != TQ_MODE_GROUP) {
     const int d = c->h.d;
     const size_t dd = (size_t)d * d;
-    const size_t nfl = 4 * dd + 32;
+    const size_t nfl = 4 * dd + 64;
     void* block = nullptr;
     e = hipMalloc(&block, nfl * sizeof(float));
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(codec tables)");
@@ -65,17 +71,36 @@ tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out, bool may_upload
     float* sk = st + dd;
     float* cent = sk + dd;
     float* bnd = cent + 16;
-    for (int i = 0; i < d; ++i)
-      for (int j = 0; j < d; ++j) {
-        pit[(size_t)j * d + i] = c->h.rot[(size_t)i * d + j];
-        pi[(size_t)i * d + j] = c->h.rot[(size_t)i * d + j];
-        if (!c->h.sketch.empty()) {
-          st[(size_t)j * d + i] = c->h.sketch[(size_t)i * d + j];
-          sk[(size_t)i * d + j] = c->h.sketch[(size_t)i * d + j];
+    float* cent2 = bnd + 16;
+    float* bnd2 = cent2 + 16;
+    // a split codec's rotation is block diagonal: each part rotates its own
+    // channels (the query rotation and the output's inverse rotation then act
+    // on the whole vector at once)
+    const tq::HostCodec* blk[2] = {&c->h, nullptr};
+    int off[2] = {0, 0};
+    if (c->h.mode == TQ_MODE_SPLIT) {
+      blk[0] = &c->part[0]->h;
+      blk[1] = &c->part[1]->h;
+      off[1] = blk[0]->d;
+    }
+    for (int q = 0; q < 2 && blk[q]; ++q) {
+      const tq::HostCodec& hb = *blk[q];
+      const int db = hb.d, o = off[q];
+      for (int i = 0; i < db; ++i)
+        for (int j = 0; j < db; ++j) {
+          const float r = hb.rot[(size_t)i * db + j];
+          pit[(size_t)(o + j) * d + o + i] = r;
+          pi[(size_t)(o + i) * d + o + j] = r;
+          if (!hb.sketch.empty()) {
+            st[(size_t)(o + j) * d + o + i] = hb.sketch[(size_t)i * db + j];
+            sk[(size_t)(o + i) * d + o + j] = hb.sketch[(size_t)i * db + j];
+          }
         }
-      }
-    for (int k = 0; k < c->h.levels; ++k) cent[k] = c->h.centroids[k];
-    for (int k = 0; k + 1 < c->h.levels; ++k) bnd[k] = c->h.boundaries[k];
+      float* ce = q == 0 ? cent : cent2;
+      float* bo = q == 0 ? bnd : bnd2;
+      for (int k = 0; k < hb.levels; ++k) ce[k] = hb.centroids[k];
+      for (int k = 0; k + 1 < hb.levels; ++k) bo[k] = hb.boundaries[k];
+    }
     e = hipMemcpy(block, host.data(), nfl * sizeof(float), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(block);
@@ -89,6 +114,8 @@ tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out, bool may_upload
     t.s = base + 3 * dd;
     t.cent = base + 4 * dd;
     t.bnd = base + 4 * dd + 16;
+    t.cent2 = base + 4 * dd + 32;
+    t.bnd2 = base + 4 * dd + 48;
     c->uploaded[dev] = true;
   }
   *out = &t;
@@ -99,6 +126,7 @@ bool cache_ok(const tq_cache* c, const tq::HostCodec& h, std::string* why) {
   if (!c->idx) { *why = "cache idx is NULL"; return false; }
   if (h.mode != TQ_MODE_GROUP && !c->norm) { *why = "cache norm is NULL"; return false; }
   if (h.mode == TQ_MODE_PROD && (!c->rnorm || !c->sign)) { *why = "Prod cache needs rnorm and sign"; return false; }
+  if (h.mode == TQ_MODE_SPLIT && !c->rnorm) { *why = "split cache needs rnorm (the high part's norm)"; return false; }
   if (h.mode == TQ_MODE_GROUP && (!c->scale || !c->gmin)) { *why = "group cache needs scale and gmin"; return false; }
   if (c->batch <= 0 || c->heads <= 0 || c->cap <= 0) { *why = "cache batch, heads and cap must be positive"; return false; }
   return true;
@@ -165,10 +193,97 @@ tq_status tq_codec_create(int32_t head_dim, int32_t bits, uint64_t seed, int32_t
   return TQ_OK;
 }
 
+tq_status tq_codec_create_kv(int32_t head_dim, double bits, uint64_t seed, tq_codec** key_out,
+                             tq_codec** value_out) {
+  if (!key_out || !value_out) return fail(TQ_ERR_INVALID_ARG, "tq_codec_create_kv: NULL argument");
+  *key_out = *value_out = nullptr;
+  if (!std::isfinite(bits) || bits < 0.5 || bits > 16.0)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_codec_create_kv: bits out of range");
+  // [omlx] _rebuild_codecs: fractional unless within 1e-6 of an integer;
+  // keys floor(bits), values ceil(bits)
+  const double r = std::nearbyint(bits);
+  const bool fractional = std::fabs(bits - r) > 1e-6;
+  const int kb = fractional ? (int)std::floor(bits) : (int)r;
+  const int vb = fractional ? (int)std::ceil(bits) : (int)r;
+  tq_codec *k = nullptr, *v = nullptr;
+  tq_status st = tq_codec_create(head_dim, kb, seed, TQ_MODE_MSE, &k);
+  if (st != TQ_OK) return st;
+  st = tq_codec_create(head_dim, vb, seed + 1, TQ_MODE_MSE, &v);
+  if (st != TQ_OK) {
+    tq_codec_destroy(k);
+    return st;
+  }
+  *key_out = k;
+  *value_out = v;
+  return TQ_OK;
+}
+
+tq_status tq_codec_create_split(int32_t head_dim, double bits, uint64_t seed, tq_codec** out) {
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "tq_codec_create_split: out is NULL");
+  *out = nullptr;
+  if (!std::isfinite(bits) || std::fabs(bits - std::nearbyint(bits)) <= 1e-6)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_codec_create_split: bits must be fractional (not within 1e-6 of an integer)");
+  if (head_dim < 64 || head_dim > 256 || head_dim % 32)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_codec_create_split: head_dim must be a multiple of 32 in [64, 256]");
+  const int lo = (int)std::floor(bits), hi = lo + 1;
+  const int d_hi = (int)std::lround((bits - lo) * head_dim / 32.0) * 32;
+  const int d_lo = head_dim - d_hi;
+  if (lo < 1 || hi > 4 || d_hi < 32 || d_lo < 32)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_codec_create_split: each part needs 32..head_dim-32 channels and 1..4 bits");
+  tq::HostCodec hl, hh;
+  std::string err;
+  if (!tq::build_codec(d_lo, lo, seed, TQ_MODE_MSE, &hl, &err, 0) ||
+      !tq::build_codec(d_hi, hi, seed, TQ_MODE_MSE, &hh, &err, 2))
+    return fail(TQ_ERR_UNSUPPORTED, "tq_codec_create_split: " + err);
+  tq_codec* c = new (std::nothrow) tq_codec();
+  tq_codec* pl = new (std::nothrow) tq_codec();
+  tq_codec* ph = new (std::nothrow) tq_codec();
+  if (!c || !pl || !ph) {
+    delete c;
+    delete pl;
+    delete ph;
+    return fail(TQ_ERR_INVALID_ARG, "tq_codec_create_split: out of host memory");
+  }
+  tq::HostCodec& h = c->h;
+  h.d = head_dim;
+  h.bits = lo;
+  h.mode = TQ_MODE_SPLIT;
+  h.mse_bits = lo;
+  h.levels = 1 << lo;
+  h.grid_exp = hl.grid_exp;
+  h.seed = seed;
+  h.split_dhi = d_hi;
+  // the block-diagonal rotation and the low part's codebook, for export
+  h.rot.assign((size_t)head_dim * head_dim, 0.0f);
+  for (int i = 0; i < d_lo; ++i)
+    for (int j = 0; j < d_lo; ++j) h.rot[(size_t)i * head_dim + j] = hl.rot[(size_t)i * d_lo + j];
+  for (int i = 0; i < d_hi; ++i)
+    for (int j = 0; j < d_hi; ++j) h.rot[(size_t)(d_lo + i) * head_dim + d_lo + j] = hh.rot[(size_t)i * d_hi + j];
+  h.centroids = hl.centroids;
+  h.boundaries = hl.boundaries;
+  pl->h = std::move(hl);
+  ph->h = std::move(hh);
+  c->part[0] = pl;
+  c->part[1] = ph;
+  *out = c;
+  g_error.clear();
+  return TQ_OK;
+}
+
+tq_status tq_codec_part(const tq_codec* c, int32_t which, const tq_codec** out) {
+  if (!c || !out) return fail(TQ_ERR_INVALID_ARG, "tq_codec_part: NULL argument");
+  if (c->h.mode != TQ_MODE_SPLIT) return fail(TQ_ERR_INVALID_ARG, "tq_codec_part: not a split codec");
+  if (which != 0 && which != 1) return fail(TQ_ERR_INVALID_ARG, "tq_codec_part: which must be 0 (low) or 1 (high)");
+  *out = c->part[which];
+  return TQ_OK;
+}
+
 void tq_codec_destroy(tq_codec* c) {
   if (!c) return;
   for (int i = 0; i < tq::kMaxDevices; ++i)
     if (c->uploaded[i] && c->dev[i].block) (void)hipFree(c->dev[i].block);
+  tq_codec_destroy(c->part[0]);
+  tq_codec_destroy(c->part[1]);
   delete c;
 }
 
@@ -185,6 +300,7 @@ tq_status tq_codec_get_info(const tq_codec* c, tq_codec_info* info) {
   info->sign_words = sign_words(h);
   info->groups = group_count(h);
   info->grid_exp = h.grid_exp;
+  info->split_high_dim = h.mode == TQ_MODE_SPLIT ? h.split_dhi : 0;
   info->seed = h.seed;
   info->bytes_per_token = bytes_per_token(h);
   return TQ_OK;
@@ -269,6 +385,7 @@ static tq_status prepare_append(const char* who, const tq_codec* c, const void* 
                 (s2 * es) % 16 == 0;
   }
   p.idx = dst->idx;
+  p.idx_stride = p.words;
   p.norm = dst->norm;
   p.rnorm = dst->rnorm;
   p.sign = dst->sign;
@@ -281,6 +398,69 @@ static tq_status prepare_append(const char* who, const tq_codec* c, const void* 
 
 // After every argument of a call has been checked: the codec's device tables
 // (uploaded on first use on this device) go into its parameter block.
+static tq_status bind_tables(const tq_codec* c, tq::QuantizeParams* p);
+
+// The parameter blocks of one checked append: one, or for a split codec one
+// per part (each an MSE append of the part's channels into the part's words
+// of the shared token record and the part's norm array).  Tables bound.
+static tq_status append_blocks(const tq_codec* c, const tq::QuantizeParams& whole, std::vector<tq::QuantizeParams>* out,
+                               std::vector<const tq_codec*>* codecs) {
+  if (c->h.mode != TQ_MODE_SPLIT) {
+    out->push_back(whole);
+    codecs->push_back(c);
+    return TQ_OK;
+  }
+  const tq_codec* part[2] = {c->part[0], c->part[1]};
+  const int w_lo = idx_words(part[0]->h);
+  const int64_t es = whole.x_bf16 ? 2 : 4;
+  for (int q = 0; q < 2; ++q) {
+    const tq::HostCodec& h = part[q]->h;
+    tq::QuantizeParams p = whole;
+    p.d = h.d;
+    p.mode = TQ_MODE_MSE;
+    p.mse_bits = h.mse_bits;
+    p.levels = h.levels;
+    p.words = idx_words(h);
+    p.sign_words = 0;
+    p.groups = 0;
+    p.gbits = 0;
+    p.idx = whole.idx + (q == 0 ? 0 : w_lo);
+    p.idx_stride = whole.words;
+    p.norm = q == 0 ? whole.norm : whole.rnorm;
+    p.rnorm = nullptr;
+    if (q == 1) {
+      p.x = static_cast<const char*>(whole.x) + (int64_t)part[0]->h.d * es;
+      p.x_vec16 = whole.x_vec16 && ((int64_t)part[0]->h.d * es) % 16 == 0;
+    }
+    out->push_back(p);
+    codecs->push_back(part[q]);
+  }
+  return TQ_OK;
+}
+
+// Launch checked append blocks: neighbours with the same head_dim share one
+// launch (the kernel is chosen by sizes only, so grouping changes no bit).
+static tq_status launch_blocks(const char* who, std::vector<tq::QuantizeParams>& blocks,
+                               const std::vector<const tq_codec*>& codecs, void* stream) {
+  for (size_t i = 0; i < blocks.size(); ++i) {
+    tq_status st = bind_tables(codecs[i], &blocks[i]);
+    if (st != TQ_OK) return st;
+  }
+  for (size_t i = 0; i < blocks.size();) {
+    tq::QuantizeSets sets{};
+    int n = 1;
+    sets.s[0] = blocks[i];
+    if (i + 1 < blocks.size() && blocks[i + 1].d == blocks[i].d) {
+      sets.s[1] = blocks[i + 1];
+      n = 2;
+    }
+    const hipError_t e = tq::launch_quantize(sets, n, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, (std::string(who) + " launch").c_str());
+    i += n;
+  }
+  return TQ_OK;
+}
+
 static tq_status bind_tables(const tq_codec* c, tq::QuantizeParams* p) {
   if (c->h.mode == TQ_MODE_GROUP) return TQ_OK;
   tq::DevTables* t = nullptr;
@@ -306,11 +486,10 @@ tq_status tq_quantize_append(const tq_codec* c, const void* x, int32_t x_dtype, 
                                 pos_end, &sets.s[0], &empty);
   if (st != TQ_OK) return st;
   if (empty) return TQ_OK;
-  st = bind_tables(c, &sets.s[0]);
-  if (st != TQ_OK) return st;
-  hipError_t e = tq::launch_quantize(sets, 1, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "tq_quantize_append launch");
-  return TQ_OK;
+  std::vector<tq::QuantizeParams> blocks;
+  std::vector<const tq_codec*> codecs;
+  append_blocks(c, sets.s[0], &blocks, &codecs);
+  return launch_blocks("tq_quantize_append", blocks, codecs, stream);
 }
 
 tq_status tq_quantize_append_kv(const tq_codec* kc, const tq_codec* vc, const void* k, const void* v,
@@ -328,13 +507,11 @@ tq_status tq_quantize_append_kv(const tq_codec* kc, const tq_codec* vc, const vo
   if (kc->h.d != vc->h.d)
     return fail(TQ_ERR_CONFIG_MISMATCH, "tq_quantize_append_kv: key and value codecs have different head_dim");
   if (empty_k) return TQ_OK;
-  st = bind_tables(kc, &sets.s[0]);
-  if (st != TQ_OK) return st;
-  st = bind_tables(vc, &sets.s[1]);
-  if (st != TQ_OK) return st;
-  hipError_t e = tq::launch_quantize(sets, 2, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "tq_quantize_append_kv launch");
-  return TQ_OK;
+  std::vector<tq::QuantizeParams> blocks;
+  std::vector<const tq_codec*> codecs;
+  append_blocks(kc, sets.s[0], &blocks, &codecs);
+  append_blocks(vc, sets.s[1], &blocks, &codecs);
+  return launch_blocks("tq_quantize_append_kv", blocks, codecs, stream);
 }
 
 // Rows per launch: 16 up to head_dim 128, 8 above (the general kernel's
@@ -345,10 +522,10 @@ static int row_block(const tq_codec* kc) { return kc->h.d <= 128 ? 16 : 8; }
 static tq_status check_decode_shapes(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
                                      int32_t q_len, int64_t max_len, bool blocks = false) {
   if (!kc || !vc) return fail(TQ_ERR_INVALID_ARG, "decode: codec is NULL");
-  if (kc->h.mode != TQ_MODE_MSE && kc->h.mode != TQ_MODE_PROD)
-    return fail(TQ_ERR_UNSUPPORTED, "decode: the key codec must be MSE or Prod");
-  if (vc->h.mode != TQ_MODE_MSE && vc->h.mode != TQ_MODE_GROUP)
-    return fail(TQ_ERR_UNSUPPORTED, "decode: the value codec must be MSE or group");
+  if (kc->h.mode != TQ_MODE_MSE && kc->h.mode != TQ_MODE_PROD && kc->h.mode != TQ_MODE_SPLIT)
+    return fail(TQ_ERR_UNSUPPORTED, "decode: the key codec must be MSE, Prod or split");
+  if (vc->h.mode != TQ_MODE_MSE && vc->h.mode != TQ_MODE_GROUP && vc->h.mode != TQ_MODE_SPLIT)
+    return fail(TQ_ERR_UNSUPPORTED, "decode: the value codec must be MSE, group or split");
   if (kc->h.d != vc->h.d) return fail(TQ_ERR_CONFIG_MISMATCH, "decode: key and value codecs have different head_dim");
   if (batch <= 0 || hq <= 0 || hkv <= 0 || q_len <= 0)
     return fail(TQ_ERR_INVALID_ARG, "decode: batch, heads and q_len must be positive");
@@ -472,6 +649,13 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
   p.k_norm = k->norm;
   p.k_rnorm = k->rnorm;
   p.k_sign = k->sign;
+  const bool ksplit = kc->h.mode == TQ_MODE_SPLIT, vsplit = vc->h.mode == TQ_MODE_SPLIT;
+  p.ksplit_g = ksplit ? (kc->h.d - kc->h.split_dhi) / 32 : 0;
+  p.k_cent_hi = ksplit ? kt->cent2 : nullptr;
+  p.k_norm_hi = ksplit ? k->rnorm : nullptr;
+  p.vsplit_g = vsplit ? (vc->h.d - vc->h.split_dhi) / 32 : 0;
+  p.v_cent_hi = vsplit ? vt->cent2 : nullptr;
+  p.v_norm_hi = vsplit ? v->rnorm : nullptr;
   p.vmode = vc->h.mode;
   p.vbits = vc->h.mse_bits;
   p.vwords = idx_words(vc->h);
@@ -561,7 +745,7 @@ tq_status tq_cache_gather(const tq_codec* src_codec, const tq_cache* src, const 
     return fail(TQ_ERR_INVALID_ARG, "tq_cache_gather: NULL argument");
   const tq::HostCodec& a = src_codec->h;
   const tq::HostCodec& c = dst_codec->h;
-  if (a.d != c.d || a.bits != c.bits || a.mode != c.mode || a.seed != c.seed)
+  if (a.d != c.d || a.bits != c.bits || a.mode != c.mode || a.seed != c.seed || a.split_dhi != c.split_dhi)
     return fail(TQ_ERR_CONFIG_MISMATCH, "tq_cache_gather: the caches belong to codecs of different head_dim, bits, "
                                         "mode or seed");
   std::string why;
@@ -605,6 +789,7 @@ tq_status tq_cache_gather(const tq_codec* src_codec, const tq_cache* src, const 
     field(src->scale, dst->scale, group_count(a));
     field(src->gmin, dst->gmin, group_count(a));
   }
+  if (a.mode == TQ_MODE_SPLIT) field(src->rnorm, dst->rnorm, 1);  // the high part's norm
   g.heads = dst->heads;
   g.dst_batch = dst->batch;
   g.src_cap = src->cap;

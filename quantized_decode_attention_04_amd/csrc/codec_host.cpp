@@ -8,7 +8,8 @@
 // factorisation and density are this library's reading:
 //   * standard normals: counter-based SplitMix64 (Steele, Lea & Flood 2014)
 //     feeding Box-Muller; stream s of a seed starts at seed XOR s*GAMMA;
-//     stream 0 is the rotation's Gaussian, stream 1 is S; row-major fill;
+//     stream 0 is the rotation's Gaussian, stream 1 is S (stream 2: the
+//     high part's rotation of a split codec); row-major fill;
 //   * rotation: Householder QR G = QR, Pi = Q diag(sign R_ii) (positive
 //     diagonal, unique), y = Pi x;
 //   * codebook: Lloyd-Max for the density of one coordinate of a uniform unit
@@ -183,7 +184,7 @@ void lloyd_max(int d, int bits, std::vector<double>& c) {
 
 }  // namespace
 
-bool build_codec(int d, int bits, uint64_t seed, int mode, HostCodec* out, std::string* err) {
+bool build_codec(int d, int bits, uint64_t seed, int mode, HostCodec* out, std::string* err, int rot_stream) {
   if (d < 32 || d > 256 || d % 32 != 0) {
     *err = "head_dim must be a multiple of 32 in [32, 256]";
     return false;
@@ -215,7 +216,7 @@ bool build_codec(int d, int bits, uint64_t seed, int mode, HostCodec* out, std::
   h.levels = 1 << h.mse_bits;
 
   std::vector<double> g;
-  standard_normals(seed, 0, (size_t)d * d, g);
+  standard_normals(seed, (uint64_t)rot_stream, (size_t)d * d, g);
   const std::vector<double> pi = orthogonal_factor(g, d);
   h.rot.resize((size_t)d * d);
   for (size_t i = 0; i < pi.size(); ++i) h.rot[i] = (float)pi[i];

@@ -170,6 +170,49 @@ __device__ __forceinline__ void score_token(const DecodeParams& p, int64_t slot,
   for (int r = 0; r < RMAX; ++r) s[r] = n * am[r] + (PROD ? gq * aq[r] : 0.f);
 }
 
+// Scores of one token of a split key cache: the low part's groups (KB-bit
+// codes, centroids s_kc, norm k_norm) and the high part's (KB+1 bits, s_kc2,
+// k_norm_hi) against the rotated query (the block-diagonal rotation rotates
+// each part's channels by its own matrix).
+template <int D, int RMAX, int KB>
+__device__ __forceinline__ void score_token_split(const DecodeParams& p, int64_t slot, const float* s_q,
+                                                  const float* s_kc, const float* s_kc2, float (&s)[RMAX]) {
+  constexpr int KH = KB + 1;
+  float al[RMAX], ah[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) al[r] = ah[r] = 0.f;
+  const int glo = p.ksplit_g;
+  const uint32_t* kw = p.k_idx + slot * (int64_t)p.kwords;
+  for (int gi = 0; gi < glo; ++gi) {
+    uint32_t w[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) w[u] = kw[gi * KB + u];
+#pragma unroll
+    for (int rr = 0; rr < 32; ++rr) {
+      const int j = gi * 32 + rr;
+      const float c = s_kc[group_field<KB>(w, rr)];
+#pragma unroll
+      for (int r = 0; r < RMAX; ++r) al[r] = fmaf(s_q[r * D + j], c, al[r]);
+    }
+  }
+  const uint32_t* kh = kw + glo * KB;
+  for (int gi = glo; gi < D / 32; ++gi) {
+    uint32_t w[KH];
+#pragma unroll
+    for (int u = 0; u < KH; ++u) w[u] = kh[(gi - glo) * KH + u];
+#pragma unroll
+    for (int rr = 0; rr < 32; ++rr) {
+      const int j = gi * 32 + rr;
+      const float c = s_kc2[group_field<KH>(w, rr)];
+#pragma unroll
+      for (int r = 0; r < RMAX; ++r) ah[r] = fmaf(s_q[r * D + j], c, ah[r]);
+    }
+  }
+  const float nl = p.k_norm[slot], nh = p.k_norm_hi[slot];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) s[r] = fmaf(nl, al[r], nh * ah[r]);
+}
+
 template <int D, int RMAX>
 __device__ __forceinline__ void score_dispatch(const DecodeParams& p, int64_t slot, const float* s_q,
                                                const float* s_qs, const float* s_kc, float (&s)[RMAX]) {
@@ -237,6 +280,35 @@ __device__ __forceinline__ void accumulate_values(const DecodeParams& p, int64_t
   }
 }
 
+// Values of a split cache: coordinate j < d_lo reads the low part's VB-bit
+// codes (words 0 .. wlo-1 of the record), the rest the high part's VB+1-bit
+// codes; each part's norm multiplies its own coordinates (the softmax weights
+// in s_p carry no value norm for split values).
+template <int D, int RMAX, int VB>
+__device__ __forceinline__ void accumulate_values_split(const DecodeParams& p, int64_t slot0, int cnt, int j, int rg,
+                                                        const float* s_p, const float* s_vc, const float* s_vc2,
+                                                        const float* s_nv, const float* s_nv2, float* o,
+                                                        uint32_t* s_vw) {
+  constexpr int NRG = 256 / D;
+  constexpr int RPT = (RMAX + NRG - 1) / NRG;
+  const int vw = p.vwords, dlo = 32 * p.vsplit_g, wlo = p.vsplit_g * VB;
+  const uint32_t* src = p.v_idx + slot0 * vw;
+  for (int e = threadIdx.x; e < cnt * vw; e += 256) s_vw[e] = src[e];
+  __syncthreads();
+  if (rg >= NRG) return;
+  const bool low = j < dlo;
+  for (int t = 0; t < cnt; ++t) {
+    const uint32_t* tw = s_vw + t * vw;
+    const float cv = low ? s_vc[token_field<VB>(tw, j)] * s_nv[t]
+                         : s_vc2[token_field<VB + 1>(tw + wlo, j - dlo)] * s_nv2[t];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int r = rg + NRG * k;
+      if (r < RMAX) o[k] = fmaf(s_p[t * (RMAX + 1) + r], cv, o[k]);
+    }
+  }
+}
+
 template <int D, int RMAX>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr int NRG = 256 / D;
@@ -245,8 +317,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   __shared__ float s_qs[RMAX * D];
   __shared__ float s_p[kTile * (RMAX + 1)];
   __shared__ float s_nv[kTile];
+  __shared__ float s_nv2[kTile];                 // split values: the high part's norms
   __shared__ float s_m[RMAX], s_l[RMAX], s_alpha[RMAX];
   __shared__ float s_kc[16], s_vc[16];
+  __shared__ float s_kc2[16], s_vc2[16];         // split codecs: the high parts' centroids
   __shared__ uint32_t s_vw[kTile * D * 4 / 32];  // the tile's value words (up to 4 bits)
   __shared__ float s_vs[kTile * (D / 32) * 2];   // group scale and minimum pairs
 
@@ -255,6 +329,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   const int tid = threadIdx.x;
   const bool prod = p.kmode == TQ_MODE_PROD;
   const bool vgroup = p.vmode == TQ_MODE_GROUP;
+  const bool ksplit = p.ksplit_g > 0, vsplit = p.vsplit_g > 0;
   int64_t len = p.len[b];
   len = len < 0 ? 0 : (len > p.cap ? p.cap : len);
   const int64_t c0 = (int64_t)chunk_id * p.chunk;
@@ -268,6 +343,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   if (tid < 16) {
     s_kc[tid] = tid < (1 << p.kbits) ? p.k_cent[tid] : 0.f;
     s_vc[tid] = (!vgroup && tid < (1 << p.vbits)) ? p.v_cent[tid] : 0.f;
+    s_kc2[tid] = (ksplit && tid < (2 << p.kbits)) ? p.k_cent_hi[tid] : 0.f;
+    s_vc2[tid] = (vsplit && tid < (2 << p.vbits)) ? p.v_cent_hi[tid] : 0.f;
   }
   if (tid < RMAX) {
     s_m[tid] = -INFINITY;
@@ -290,8 +367,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int r = 0; r < RMAX; ++r) s[r] = 0.f;
       if (tid < cnt) {
-        score_dispatch<D, RMAX>(p, base + tok, s_q, s_qs, s_kc, s);
+        if (ksplit) {
+          switch (p.kbits) {
+            case 1: score_token_split<D, RMAX, 1>(p, base + tok, s_q, s_kc, s_kc2, s); break;
+            case 2: score_token_split<D, RMAX, 2>(p, base + tok, s_q, s_kc, s_kc2, s); break;
+            default: score_token_split<D, RMAX, 3>(p, base + tok, s_q, s_kc, s_kc2, s); break;
+          }
+        } else {
+          score_dispatch<D, RMAX>(p, base + tok, s_q, s_qs, s_kc, s);
+        }
         s_nv[tid] = vgroup ? 1.f : p.v_norm[base + tok];
+        if (vsplit) s_nv2[tid] = p.v_norm_hi[base + tok];
       }
 #pragma unroll
       for (int r = 0; r < RMAX; ++r) {
@@ -314,7 +400,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
           const float sv = s_p[k * (RMAX + 1) + r];
           const float pr = m_new == -INFINITY ? 0.f : exp2f(sv - m_new);
           sum += pr;
-          s_p[k * (RMAX + 1) + r] = pr * s_nv[k];
+          s_p[k * (RMAX + 1) + r] = vsplit ? pr : pr * s_nv[k];
         }
         sum = wave_sum(sum);
         if (lane == 0) {
@@ -336,6 +422,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         }
       }
       const int64_t slot0 = base + t0;
+      if (vsplit) {
+        switch (p.vbits) {
+          case 1: accumulate_values_split<D, RMAX, 1>(p, slot0, cnt, j, rg, s_p, s_vc, s_vc2, s_nv, s_nv2, o, s_vw); break;
+          case 2: accumulate_values_split<D, RMAX, 2>(p, slot0, cnt, j, rg, s_p, s_vc, s_vc2, s_nv, s_nv2, o, s_vw); break;
+          default: accumulate_values_split<D, RMAX, 3>(p, slot0, cnt, j, rg, s_p, s_vc, s_vc2, s_nv, s_nv2, o, s_vw); break;
+        }
+      } else
       switch (p.vbits * 2 + (vgroup ? 1 : 0)) {
         case 2: accumulate_values<D, RMAX, 1, false>(p, slot0, cnt, j, rg, s_p, s_vc, o, s_vw, s_vs); break;
         case 3: accumulate_values<D, RMAX, 1, true>(p, slot0, cnt, j, rg, s_p, s_vc, o, s_vw, s_vs); break;

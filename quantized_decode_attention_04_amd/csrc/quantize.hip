@@ -232,7 +232,7 @@ __device__ __forceinline__ void quantize_rotated(const QuantizeParams& p, BulkLd
   for (int e = tid; e < kMV * p.words; e += 256) {
     const int v = e / p.words, w = e % p.words;
     const int64_t slot = L.slot[v];
-    if (slot >= 0) p.idx[slot * p.words + w] = pack_word(L.codes[v], w, p.mse_bits);
+    if (slot >= 0) p.idx[slot * p.idx_stride + w] = pack_word(L.codes[v], w, p.mse_bits);
   }
   if (tid < kMV && L.slot[tid] >= 0) p.norm[L.slot[tid]] = L.nrm[tid];
   if (!prod) return;
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void quantize_bulk_kernel(Qu
     for (int e = tid; e < kMV * p.words; e += 256) {
       const int v = e / p.words, w = e % p.words;
       const int64_t slot = L.slot[v];
-      if (slot >= 0) p.idx[slot * p.words + w] = pack_word(L.codes[v], w, p.gbits);
+      if (slot >= 0) p.idx[slot * p.idx_stride + w] = pack_word(L.codes[v], w, p.gbits);
     }
     return;
   }
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(small_threads<D>()) void quantize_small_kernel(Quan
       }
     }
     __syncthreads();
-    if (tid < p.words) p.idx[tok * p.words + tid] = wbuf[tid];
+    if (tid < p.words) p.idx[tok * p.idx_stride + tid] = wbuf[tid];
     return;
   }
 
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(small_threads<D>()) void quantize_small_kernel(Quan
     pack_field(wbuf, tid, p.mse_bits, idx);
   }
   __syncthreads();
-  if (tid < p.words) p.idx[tok * p.words + tid] = wbuf[tid];
+  if (tid < p.words) p.idx[tok * p.idx_stride + tid] = wbuf[tid];
   if (tid == 0) p.norm[tok] = n;
   if (!prod) return;
 
@@ -644,7 +644,7 @@ __global__ __launch_bounds__(64) void quantize_mse_split_kernel(QuantizeSets set
   const int64_t pos = (int64_t)pos32 + t;
   if (pos < 0 || pos >= p.cap) return;  // nothing is written for this vector
   const int64_t tok = ((int64_t)b * p.heads + h) * p.cap + pos;
-  if (lane < p.mse_bits) p.idx[tok * p.words + g * p.mse_bits + lane] = wbuf[lane];
+  if (lane < p.mse_bits) p.idx[tok * p.idx_stride + g * p.mse_bits + lane] = wbuf[lane];
   if (g == 0 && lane == 0) p.norm[tok] = n;
 }
 

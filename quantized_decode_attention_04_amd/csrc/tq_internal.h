@@ -25,6 +25,7 @@ constexpr float kQjlConstNumer = 1.2533141373155003f;  // sqrt(pi/2)
 // Host tables of a codec (float32 as stored; see tq_codec_export).
 struct HostCodec {
   int d = 0, bits = 0, mode = 0, mse_bits = 0, levels = 0, grid_exp = 0;
+  int split_dhi = 0;              // SPLIT: channels of the high part (the parts are separate codecs)
   uint64_t seed = 0;
   std::vector<float> rot;         // Pi [d][d] row-major, y = Pi x
   std::vector<float> sketch;      // S  [d][d] row-major (Prod)
@@ -33,7 +34,9 @@ struct HostCodec {
 };
 
 // Builds the codec; returns false with a message on unsupported parameters.
-bool build_codec(int d, int bits, uint64_t seed, int mode, HostCodec* out, std::string* err);
+// The rotation's Gaussian is stream rot_stream of the seed (0; the high part of
+// a split codec uses 2).
+bool build_codec(int d, int bits, uint64_t seed, int mode, HostCodec* out, std::string* err, int rot_stream = 0);
 
 // Device copies of the tables on one device.
 struct DevTables {
@@ -41,8 +44,10 @@ struct DevTables {
   float* pi = nullptr;    // Pi   [d][d] row-major
   float* st = nullptr;    // S^T  [d][d]: st[j*d + i] = S[i][j] (Prod)
   float* s = nullptr;     // S    [d][d] row-major (Prod)
-  float* cent = nullptr;  // centroids [16]
+  float* cent = nullptr;  // centroids [16] (SPLIT: the low part's)
   float* bnd = nullptr;   // boundaries [16]
+  float* cent2 = nullptr; // SPLIT: the high part's centroids [16]
+  float* bnd2 = nullptr;  // SPLIT: the high part's boundaries [16]
   void* block = nullptr;  // single allocation holding all of the above
 };
 
@@ -53,6 +58,7 @@ struct tq_codec {
   std::mutex mu;
   bool uploaded[tq::kMaxDevices] = {};
   tq::DevTables dev[tq::kMaxDevices];
+  tq_codec* part[2] = {nullptr, nullptr};  // SPLIT: the low and high MSE codecs (owned)
 };
 
 namespace tq {
@@ -73,6 +79,7 @@ struct QuantizeParams {
   const float* cent;  // centroids
   const float* bnd;   // boundaries
   uint32_t* idx;
+  int idx_stride;     // words per token record of idx (= words, or a split cache's two parts' words)
   float* norm;
   float* rnorm;
   uint32_t* sign;
@@ -111,8 +118,16 @@ struct DecodeParams {
   const float* k_norm;
   const float* k_rnorm;
   const uint32_t* k_sign;
+  // split keys: the high part starts at group ksplit_g (0: not split), its
+  // codes have kbits + 1 bits, its centroids k_cent_hi, its norms k_norm_hi
+  int ksplit_g;
+  const float* k_cent_hi;
+  const float* k_norm_hi;
   // value codec / cache
   int vmode, vbits, vwords, vgroups;
+  int vsplit_g;               // as ksplit_g, for split values
+  const float* v_cent_hi;
+  const float* v_norm_hi;
   const float* v_pi;    // Pi_v row-major (inverse rotation of the output)
   const float* v_cent;
   const uint32_t* v_idx;

@@ -63,7 +63,39 @@ static void codecs() {
       }
     }
   }
+  // fractional widths: the key/value pair rule and split codecs with their parts
+  for (double b : {1.5, 2.5, 3.5, 3.25, 2.75, 3.0, 4.0000001}) {
+    tq_codec *k = nullptr, *v = nullptr;
+    CHECK(tq_codec_create_kv(128, b, 3, &k, &v) == TQ_OK);
+    tq_codec_info ki{}, vi{};
+    CHECK(tq_codec_get_info(k, &ki) == TQ_OK && tq_codec_get_info(v, &vi) == TQ_OK);
+    CHECK(ki.bits == (int)std::floor(b + 1e-6) && vi.bits == (int)std::ceil(b - 1e-6) && vi.seed == 4);
+    tq_codec_destroy(k);
+    tq_codec_destroy(v);
+    tq_codec* sp = nullptr;
+    const bool frac = std::fabs(b - std::nearbyint(b)) > 1e-6;
+    CHECK((tq_codec_create_split(128, b, 3, &sp) == TQ_OK) == frac);
+    if (sp) {
+      tq_codec_info si{}, li{}, hi{};
+      const tq_codec *lo = nullptr, *hp = nullptr;
+      CHECK(tq_codec_get_info(sp, &si) == TQ_OK && si.mode == TQ_MODE_SPLIT);
+      CHECK(tq_codec_part(sp, 0, &lo) == TQ_OK && tq_codec_part(sp, 1, &hp) == TQ_OK);
+      CHECK(tq_codec_get_info(lo, &li) == TQ_OK && tq_codec_get_info(hp, &hi) == TQ_OK);
+      CHECK(li.head_dim + hi.head_dim == 128 && hi.head_dim == si.split_high_dim && hi.bits == li.bits + 1);
+      CHECK(si.idx_words == li.idx_words + hi.idx_words && si.idx_words == (int)std::ceil(128 * b / 32));
+      CHECK(tq_codec_part(sp, 2, &lo) == TQ_ERR_INVALID_ARG);
+      std::vector<float> rot(128 * 128);
+      CHECK(tq_codec_export(sp, rot.data(), nullptr, nullptr, nullptr) == TQ_OK);
+      CHECK(rot[(size_t)0 * 128 + 127] == 0.0f && rot[(size_t)127 * 128 + 0] == 0.0f);  // block diagonal
+      tq_codec_destroy(sp);
+    }
+  }
   tq_codec* c = nullptr;
+  CHECK(tq_codec_create_split(128, 3.1, 0, &c) == TQ_ERR_UNSUPPORTED);   // a part below 32 channels
+  CHECK(tq_codec_create_split(128, 4.5, 0, &c) == TQ_ERR_UNSUPPORTED);   // 5 bits
+  CHECK(tq_codec_create_split(32, 2.5, 0, &c) == TQ_ERR_UNSUPPORTED);
+  CHECK(tq_codec_create_kv(128, 3.5, 0, nullptr, &c) == TQ_ERR_INVALID_ARG);
+  CHECK(tq_codec_part(nullptr, 0, nullptr) == TQ_ERR_INVALID_ARG);
   CHECK(tq_codec_create(100, 3, 0, TQ_MODE_MSE, &c) == TQ_ERR_UNSUPPORTED && c == nullptr);
   CHECK(tq_codec_create(288, 3, 0, TQ_MODE_MSE, &c) == TQ_ERR_UNSUPPORTED);
   CHECK(tq_codec_create(128, 5, 0, TQ_MODE_MSE, &c) == TQ_ERR_UNSUPPORTED);

@@ -57,6 +57,38 @@ def test_codec_tables_match_oracle(d, bits, seed, mode):
     assert np.abs(r.T @ r - np.eye(d)).max() < 1e-5
 
 
+@pytest.mark.parametrize("d,bits,seed", [(128, 3.5, 0), (128, 2.25, 7), (256, 2.5, 3), (96, 1.5, 1)])
+def test_split_codec_tables_match_oracle(d, bits, seed):
+    """Each part of a split codec is the oracle's MSE codec of that part (the
+    high part's rotation from stream 2 of the seed); the split codec exports
+    the block-diagonal rotation."""
+    c = tq.tq_codec_create_split(d, bits, seed)
+    o = ocodec.make_split_codec(d, bits, seed)
+    assert c.info["mode"] == tq.TQ_MODE_SPLIT and c.info["split_high_dim"] == o.d_hi
+    assert c.info["idx_words"] == o.d_lo * o.low.bits // 32 + o.d_hi * o.high.bits // 32
+    assert c.info["bytes_per_token"] == 4 * c.info["idx_words"] + 8
+    for which, oc in ((0, o.low), (1, o.high)):
+        part = tq.tq_codec_part(c, which)
+        t = tq.tq_codec_export(part)
+        assert part.info["head_dim"] == oc.head_dim and part.info["bits"] == oc.bits
+        assert np.abs(t["rot"] - oc.rot).max() <= 1e-6
+        assert np.array_equal(t["centroids"], oc.centroids.astype(np.float32))
+        assert np.array_equal(t["boundaries"], oc.boundaries.astype(np.float32))
+    whole = tq.tq_codec_export(c)["rot"]
+    assert np.array_equal(whole[:o.d_lo, :o.d_lo], tq.tq_codec_export(tq.tq_codec_part(c, 0))["rot"])
+    assert np.array_equal(whole[o.d_lo:, o.d_lo:], tq.tq_codec_export(tq.tq_codec_part(c, 1))["rot"])
+    assert not whole[:o.d_lo, o.d_lo:].any() and not whole[o.d_lo:, :o.d_lo].any()
+
+
+@pytest.mark.parametrize("bits", [3.5, 2.5, 3.0, 2.9999995, 3.25])
+def test_kv_codec_pair_follows_the_rebuild_rule(bits):
+    k, v = tq.tq_codec_create_kv(128, bits, 11)
+    ok, ov = ocodec.kv_codecs(128, bits, 11)
+    for g, o in ((k, ok), (v, ov)):
+        assert (g.info["bits"], g.info["mode"], g.info["seed"]) == (o.bits, ocodec.MODE_MSE, o.seed)
+        assert np.array_equal(tq.tq_codec_export(g)["centroids"], o.centroids.astype(np.float32))
+
+
 def test_codec_is_rebuilt_identically():
     a = tq.tq_codec_export(tq.tq_codec_create(128, 3, 42, 1))
     b = tq.tq_codec_export(tq.tq_codec_create(128, 3, 42, 1))

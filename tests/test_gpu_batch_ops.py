@@ -112,16 +112,24 @@ def _decode_check(gk, gv, kcache, vcache, kb, vb, q, tag):
     assert err.max() <= 1e-4, tag
 
 
-CODECS = [((3, 1), (4, 0)), ((3, 0), (3, 0))]   # (bits, mode) of K and V: general path, int8 path
+# (bits, mode) of K and V: general path, int8 path, split codecs (mode 3: a fractional width)
+CODECS = [((3, 1), (4, 0)), ((3, 0), (3, 0)), ((3.5, 3), (2.5, 3))]
 
 
-@pytest.mark.parametrize("kspec,vspec", CODECS, ids=["prod3_mse4", "mse3_mse3"])
+def _pair(spec, seed):
+    bits, mode = spec
+    if mode == 3:
+        return ocodec.make_split_codec(D, bits, seed), tq.tq_codec_create_split(D, bits, seed)
+    return ocodec.make_codec(D, bits, seed, mode), tq.tq_codec_create(D, bits, seed, mode)
+
+
+@pytest.mark.parametrize("kspec,vspec", CODECS, ids=["prod3_mse4", "mse3_mse3", "split35_split25"])
 def test_batch_ops_match_the_oracle(kspec, vspec):
     print(f"batch ops k={kspec} v={vspec}", flush=True)
     sys.stdout.flush()
     rng = np.random.default_rng(7)
-    okc, ovc = ocodec.make_codec(D, kspec[0], 0, kspec[1]), ocodec.make_codec(D, vspec[0], 1, vspec[1])
-    gk, gv = tq.tq_codec_create(D, kspec[0], 0, kspec[1]), tq.tq_codec_create(D, vspec[0], 1, vspec[1])
+    okc, gk = _pair(kspec, 0)
+    ovc, gv = _pair(vspec, 1)
     lens, cap = [37, 300, 5, 180], 320
     xk = [round_bf16(rng.standard_normal((H, n, D)).astype(np.float32) * np.float32(0.02)) for n in lens]
     xv = [round_bf16(rng.standard_normal((H, n, D)).astype(np.float32) * np.float32(0.02)) for n in lens]
@@ -187,9 +195,9 @@ def test_batch_ops_match_the_oracle(kspec, vspec):
     _decode_check(gk, gv, Km, Vm, Kom, Vom, q4[[3, 1, 2, 0]], "merged batch")
 
     # the pages' merge guard: caches of codecs with different bits or seed
-    other = tq.tq_codec_create(D, kspec[0], 5, kspec[1])
+    other = _pair(kspec, 5)[1]
     with pytest.raises(tq.TQError) as e:
         tq.tq_cache_gather(gk, Kd, other, Km, [0, -1, -1, -1], [0, 0, 0, 0], [5, 0, 0, 0])
     assert e.value.status == 3
     with pytest.raises(ValueError):
-        obatch.merge(K, obatch.from_inputs(xk[:1], ocodec.make_codec(D, kspec[0], 5, kspec[1])))
+        obatch.merge(K, obatch.from_inputs(xk[:1], _pair(kspec, 5)[0]))
