@@ -310,6 +310,47 @@ tq_status tq_cache_gather(const tq_codec* src_codec, const tq_cache* src, const 
                           const tq_cache* dst, const int32_t* src_batch, const int32_t* src_start,
                           const int32_t* count, void* stream);
 
+/* Hybrid cache ("turboquant validate_moe_phase2.py": Test 5's buffer_size
+ * and the commit note's hybrid decode): the most recent tokens of each
+ * sequence stay unquantised in a ring buffer of buf_size tokens per
+ * (sequence, KV head), caller-owned device memory [batch][heads][buf_size]
+ * [head_dim] of the tokens' dtype, one for keys and one for values.  A
+ * sequence of N tokens holds tokens 0 .. Nc-1, Nc = floor(N / buf_size) *
+ * buf_size, in the compressed caches and token t >= Nc in ring slot t - Nc;
+ * whenever appends fill a ring, its buf_size tokens are quantised into the
+ * compressed caches at Nc at once and the ring starts over.
+ *
+ * tq_hybrid_append: append n_new (<= buf_size) new key and value tokens per
+ * (sequence, head) -- k, v, strides and dtype as tq_quantize_append_kv -- to
+ * sequences holding d_len[b] tokens before the call (device int32[batch]);
+ * len_end is the caller's host bound on d_len[b] + n_new, and the compressed
+ * caches must hold floor(len_end / buf_size) * buf_size tokens (CAPACITY
+ * otherwise).  The caller then holds d_len[b] + n_new tokens per sequence.
+ * Errors: INVALID_ARG, UNSUPPORTED (n_new > buf_size), CONFIG_MISMATCH,
+ * CAPACITY, HIP. */
+tq_status tq_hybrid_append(const tq_codec* kc, const tq_codec* vc, const void* k, const void* v, int32_t x_dtype,
+                           int32_t batch, int32_t heads, int32_t n_new, const int64_t* k_strides,
+                           const int64_t* v_strides, const tq_cache* kdst, const tq_cache* vdst, void* kbuf,
+                           void* vbuf, int32_t buf_size, const int32_t* d_len, int64_t len_end, void* stream);
+
+/* Workspace bytes of tq_hybrid_decode_attention for these sizes. */
+tq_status tq_hybrid_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t n_q_heads,
+                                          int32_t n_kv_heads, int32_t q_len, int64_t max_len, int32_t buf_size,
+                                          size_t* bytes);
+
+/* Decode attention over a hybrid cache: every query row attends, with one
+ * softmax and the causal rule of tq_decode_attention counted from the whole
+ * length d_len[b] (device int32[batch], 1 <= d_len[b] <= max_len), to the
+ * compressed tokens through their codes and to the ring's tokens exactly (in
+ * float32 from buf_dtype values).  Arguments as tq_decode_attention plus the
+ * rings (kbuf, vbuf, buf_dtype, buf_size); ws holds
+ * tq_hybrid_decode_workspace_size(...) bytes.  Errors as tq_decode_attention. */
+tq_status tq_hybrid_decode_attention(const tq_codec* kc, const tq_codec* vc, const void* q, int32_t q_dtype,
+                                     int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t q_len,
+                                     const tq_cache* k, const tq_cache* v, const void* kbuf, const void* vbuf,
+                                     int32_t buf_dtype, int32_t buf_size, const int32_t* d_len, int64_t max_len,
+                                     float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* Measurement: read `bytes` of device memory once, as a plain streaming read
  * (16-byte loads, eight in flight per thread), the reference a decode
  * kernel's HBM rate is compared with.  Nothing in the library's path uses it.

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     TQError,
     allocate_cache,
     allocate_prefill_workspace,
+    allocate_ring,
     allocate_workspace,
     lib_path,
     tq_cache_gather,
@@ -32,6 +33,9 @@ from ._binding import (  # noqa: F401
     tq_decode_attention,
     tq_decode_attention_noalloc,
     tq_decode_workspace_size,
+    tq_hybrid_append,
+    tq_hybrid_decode_attention,
+    tq_hybrid_decode_workspace_size,
     tq_last_error,
     tq_prefill_attention,
     tq_prefill_workspace_size,

@@ -75,6 +75,12 @@ def _load() -> ctypes.CDLL:
         "tq_prefill_attention": (I32, [P, P, P, I32, I32, I32, I32, I32, ctypes.POINTER(_Cache),
                                        ctypes.POINTER(_Cache), P, I64, ctypes.c_float, P, P, SZ, P]),
         "tq_stream_read": (I32, [P, U64, P, I32, P]),
+        "tq_hybrid_append": (I32, [P, P, P, P, I32, I32, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                   ctypes.POINTER(_Cache), ctypes.POINTER(_Cache), P, P, I32, P, I64, P]),
+        "tq_hybrid_decode_workspace_size": (I32, [P, P, I32, I32, I32, I32, I64, I32, ctypes.POINTER(SZ)]),
+        "tq_hybrid_decode_attention": (I32, [P, P, P, I32, I32, I32, I32, I32, ctypes.POINTER(_Cache),
+                                             ctypes.POINTER(_Cache), P, P, I32, I32, P, I64, ctypes.c_float, P, P,
+                                             SZ, P]),
         "tq_decode_attention_noalloc": (I32, [P, P, P, I32, I32, I32, I32, I32, ctypes.POINTER(_Cache),
                                               ctypes.POINTER(_Cache), P, I64, ctypes.c_float, P, P]),
         "tq_last_error": (ctypes.c_char_p, []),
@@ -94,6 +100,7 @@ EXPORTED = (
     "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_workspace_size", "tq_decode_attention",
     "tq_prefill_workspace_size", "tq_prefill_attention", "tq_cache_gather", "tq_stream_read", "tq_last_error",
     "tq_status_string", "tq_decode_attention_noalloc", "tq_codec_create_kv", "tq_codec_create_split", "tq_codec_part",
+    "tq_hybrid_append", "tq_hybrid_decode_workspace_size", "tq_hybrid_decode_attention",
 )
 
 
@@ -428,3 +435,71 @@ def tq_stream_read(buf, sink, blocks: int, stream=None) -> None:
         raise ValueError("sink needs blocks * 256 32-bit elements")
     _check(_lib.tq_stream_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_uint64(nbytes),
                                ctypes.c_void_p(sink.data_ptr()), int(blocks), _stream(stream)))
+
+
+# ---- hybrid cache (recent-token rings in front of the compressed caches) -------
+
+def allocate_ring(batch: int, heads: int, buf_size: int, head_dim: int, dtype=None, device="cuda"):
+    """A zero-filled recent-token ring [batch, heads, buf_size, head_dim]."""
+    import torch
+    return torch.zeros((batch, heads, buf_size, head_dim), dtype=dtype or torch.bfloat16, device=device)
+
+
+def tq_hybrid_append(kc: Codec, vc: Codec, k, v, kcache: Cache, vcache: Cache, kbuf, vbuf, lens, len_end: int,
+                     stream=None) -> None:
+    """Append k, v [batch, heads, n_new, head_dim] to hybrid caches whose
+    sequences hold lens[b] tokens (int32 device tensor); the rings kbuf, vbuf
+    [batch, heads, buf_size, head_dim] have the inputs' dtype; len_end bounds
+    lens[b] + n_new on the host."""
+    import torch
+    _on_device(k, v, kbuf, vbuf, lens, *kcache.arrays().values(), *vcache.arrays().values())
+    for x in (k, v):
+        if x.dim() != 4 or x.stride(3) != 1:
+            raise ValueError("k and v must be [batch, heads, n_new, head_dim] with unit coordinate stride")
+    if tuple(k.shape) != tuple(v.shape) or k.dtype != v.dtype or kbuf.dtype != k.dtype or vbuf.dtype != k.dtype:
+        raise ValueError("k, v and the rings must share shape and dtype")
+    for r in (kbuf, vbuf):
+        if r.dim() != 4 or not r.is_contiguous() or r.shape[0] != k.shape[0] or r.shape[1] != k.shape[1] \
+                or r.shape[3] != k.shape[3]:
+            raise ValueError("rings must be contiguous [batch, heads, buf_size, head_dim]")
+    if lens.dtype != torch.int32 or lens.numel() != k.shape[0] or not lens.is_contiguous():
+        raise ValueError("lens must be a contiguous int32 tensor of length batch")
+    ks_, vs_ = (ctypes.c_int64 * 4)(*k.stride()), (ctypes.c_int64 * 4)(*v.stride())
+    kst, vst = kcache.as_struct(), vcache.as_struct()
+    _check(_lib.tq_hybrid_append(kc.handle, vc.handle, ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                 _dtype_code(k), int(k.shape[0]), int(k.shape[1]), int(k.shape[2]), ks_, vs_,
+                                 ctypes.byref(kst), ctypes.byref(vst), ctypes.c_void_p(kbuf.data_ptr()),
+                                 ctypes.c_void_p(vbuf.data_ptr()), int(kbuf.shape[2]),
+                                 ctypes.c_void_p(lens.data_ptr()), int(len_end), _stream(stream)))
+
+
+def tq_hybrid_decode_workspace_size(kc: Codec, vc: Codec, batch: int, n_q_heads: int, n_kv_heads: int, q_len: int,
+                                    max_len: int, buf_size: int) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.tq_hybrid_decode_workspace_size(kc.handle, vc.handle, int(batch), int(n_q_heads), int(n_kv_heads),
+                                                int(q_len), int(max_len), int(buf_size), ctypes.byref(n)))
+    return n.value
+
+
+def tq_hybrid_decode_attention(kc: Codec, vc: Codec, q, kcache: Cache, vcache: Cache, kbuf, vbuf, lens,
+                               max_len: int, scale: float, out, ws, stream=None) -> None:
+    """Decode attention over hybrid caches (lens: whole lengths, device int32)."""
+    import torch
+    _on_device(q, lens, out, ws, kbuf, vbuf, *kcache.arrays().values(), *vcache.arrays().values())
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [batch, n_q_heads, q_len, head_dim] tensor")
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must be a contiguous float32 tensor shaped like q")
+    if kbuf.dtype != vbuf.dtype or tuple(kbuf.shape) != tuple(vbuf.shape) or not kbuf.is_contiguous() \
+            or not vbuf.is_contiguous():
+        raise ValueError("rings must be contiguous tensors of one shape and dtype")
+    if lens.dtype != torch.int32 or lens.numel() != q.shape[0] or not lens.is_contiguous():
+        raise ValueError("lens must be a contiguous int32 tensor of length batch")
+    ks, vs = kcache.as_struct(), vcache.as_struct()
+    _check(_lib.tq_hybrid_decode_attention(kc.handle, vc.handle, ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
+                                           int(q.shape[0]), int(q.shape[1]), int(kcache.heads), int(q.shape[2]),
+                                           ctypes.byref(ks), ctypes.byref(vs), ctypes.c_void_p(kbuf.data_ptr()),
+                                           ctypes.c_void_p(vbuf.data_ptr()), _dtype_code(kbuf), int(kbuf.shape[2]),
+                                           ctypes.c_void_p(lens.data_ptr()), int(max_len), ctypes.c_float(scale),
+                                           ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                           ws.numel() * ws.element_size(), _stream(stream)))

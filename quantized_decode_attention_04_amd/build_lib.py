@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["capi.cpp", "dispatch.cpp", "codec_host.cpp", "quantize.hip", "decode.hip", "decode_fast.hip", "decode_mfma.hip", "decode_bf16.hip", "cache_ops.hip", "stream_read.hip", "noalloc.hip"]
+SOURCES = ["capi.cpp", "dispatch.cpp", "codec_host.cpp", "quantize.hip", "decode.hip", "decode_fast.hip", "decode_mfma.hip", "decode_bf16.hip", "cache_ops.hip", "stream_read.hip", "noalloc.hip", "hybrid.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

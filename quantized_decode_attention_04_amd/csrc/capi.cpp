@@ -594,7 +594,8 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
                                 int32_t q_dtype, int32_t batch, int32_t hq, int32_t hkv, int32_t q_len,
                                 const tq_cache* k, const tq_cache* v, const int32_t* d_len, int64_t max_len,
                                 float scale, float* out, void* ws, size_t ws_bytes, void* stream,
-                                bool may_upload = true) {
+                                bool may_upload = true, const int32_t* len_mask = nullptr,
+                                float* row_ml = nullptr) {
   const std::string fn(name);
   tq_status st = check_decode_shapes(kc, vc, batch, hq, hkv, q_len, max_len, blocks);
   if (st != TQ_OK) return st;
@@ -668,6 +669,8 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
   p.v_gmin = v->gmin;
   p.cap = k->cap;
   p.len = d_len;
+  p.len_mask = len_mask;
+  p.row_ml = row_ml;
   p.chunk = plan.chunk;
   p.n_chunks = plan.n_chunks;
   p.part_o = reinterpret_cast<float*>(w + plan.off_part_o);
@@ -726,6 +729,183 @@ tq_status tq_prefill_attention(const tq_codec* kc, const tq_codec* vc, const voi
                                size_t ws_bytes, void* stream) {
   return attention_impl("tq_prefill_attention", true, kc, vc, q, q_dtype, batch, hq, hkv, q_len, k, v, d_len,
                         max_len, scale, out, ws, ws_bytes, stream);
+}
+
+// ---- hybrid cache -------------------------------------------------------------
+
+static bool hybrid_buffers_ok(const void* kbuf, const void* vbuf, int32_t buf_dtype, int32_t buf_size,
+                              std::string* why) {
+  if (!kbuf || !vbuf) { *why = "buffer pointer is NULL"; return false; }
+  if (buf_dtype != TQ_F32 && buf_dtype != TQ_BF16) { *why = "bad buffer dtype"; return false; }
+  if (buf_size < 1 || buf_size > (1 << 16)) { *why = "buffer size must be in 1..65536"; return false; }
+  return true;
+}
+
+tq_status tq_hybrid_append(const tq_codec* kc, const tq_codec* vc, const void* k, const void* v, int32_t x_dtype,
+                           int32_t batch, int32_t heads, int32_t n_new, const int64_t* k_strides,
+                           const int64_t* v_strides, const tq_cache* kdst, const tq_cache* vdst, void* kbuf,
+                           void* vbuf, int32_t buf_size, const int32_t* d_len, int64_t len_end, void* stream) {
+  const char* who = "tq_hybrid_append";
+  std::string why;
+  if (!hybrid_buffers_ok(kbuf, vbuf, x_dtype, buf_size, &why)) return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": " + why);
+  if (n_new > buf_size) return fail(TQ_ERR_UNSUPPORTED, std::string(who) + ": more new tokens than the buffer holds");
+  if (len_end < n_new) return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": len_end is below n_new");
+  // the compressed cache holds floor(len / buf_size) * buf_size tokens
+  const int64_t comp_end = (len_end / buf_size) * buf_size;
+  tq::QuantizeSets sets{};
+  bool empty_k = false, empty_v = false;
+  if (!kc || !vc) return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": codec is NULL");
+  if (kc->h.d != vc->h.d) return fail(TQ_ERR_CONFIG_MISMATCH, std::string(who) + ": key and value codecs differ in head_dim");
+  const int d = kc->h.d;
+  // a flush appends a whole ring (buf_size tokens, read in its own layout)
+  // into the compressed cache, ending at most at comp_end; with comp_end 0 no
+  // ring can fill in this call
+  const bool may_flush = comp_end >= buf_size;
+  if (may_flush) {
+    const int64_t ring_strides[4] = {(int64_t)heads * buf_size * d, (int64_t)buf_size * d, d, 1};
+    tq_status st = prepare_append("tq_hybrid_append (keys)", kc, kbuf, x_dtype, batch, heads, buf_size, ring_strides,
+                                  kdst, d_len, comp_end, &sets.s[0], &empty_k);
+    if (st != TQ_OK) return st;
+    st = prepare_append("tq_hybrid_append (values)", vc, vbuf, x_dtype, batch, heads, buf_size, ring_strides, vdst,
+                        d_len, comp_end, &sets.s[1], &empty_v);
+    if (st != TQ_OK) return st;
+  } else if (batch <= 0 || heads <= 0 || n_new < 0 || !d_len) {
+    return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": bad sizes or NULL lengths");
+  }
+  if (!k || !v) return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": NULL input");
+  tq::HybridStage hs{};
+  hs.x[0] = k;
+  hs.x[1] = v;
+  for (int q = 0; q < 2; ++q) {
+    const int64_t* xs = q == 0 ? k_strides : v_strides;
+    if (xs) {
+      if (xs[3] != 1 || xs[0] < 0 || xs[1] < 0 || xs[2] < 0)
+        return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": bad input strides");
+      hs.xs[q][0] = xs[0];
+      hs.xs[q][1] = xs[1];
+      hs.xs[q][2] = xs[2];
+    } else {
+      hs.xs[q][2] = d;
+      hs.xs[q][1] = (int64_t)n_new * d;
+      hs.xs[q][0] = (int64_t)heads * n_new * d;
+    }
+  }
+  hs.buf[0] = kbuf;
+  hs.buf[1] = vbuf;
+  hs.n_sets = 2;
+  hs.bf16 = x_dtype == TQ_BF16;
+  hs.batch = batch;
+  hs.heads = heads;
+  hs.n_new = n_new;
+  hs.d = d;
+  hs.block = buf_size;
+  hs.len = d_len;
+  if (n_new == 0) return TQ_OK;
+  // every check passed: stage, flush full rings, stage the rest
+  hs.phase = 0;
+  hipError_t e = tq::launch_hybrid_stage(hs, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tq_hybrid_append stage launch");
+  if (!may_flush) return TQ_OK;
+  for (int q = 0; q < 2; ++q) {
+    sets.s[q].flush_block = buf_size;
+    sets.s[q].flush_new = n_new;
+  }
+  std::vector<tq::QuantizeParams> blocks;
+  std::vector<const tq_codec*> codecs;
+  append_blocks(kc, sets.s[0], &blocks, &codecs);
+  append_blocks(vc, sets.s[1], &blocks, &codecs);
+  tq_status st = launch_blocks("tq_hybrid_append flush", blocks, codecs, stream);
+  if (st != TQ_OK) return st;
+  hs.phase = 1;
+  e = tq::launch_hybrid_stage(hs, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tq_hybrid_append stage launch");
+  return TQ_OK;
+}
+
+// workspace: the compressed decode's, then the compressed lengths, then the
+// rows' (M, L)
+static tq_status hybrid_layout(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
+                               int32_t q_len, int64_t max_len, int32_t buf_size, size_t* base, size_t* off_lens,
+                               size_t* off_ml, size_t* total, bool* has_compressed) {
+  if (buf_size < 1 || buf_size > (1 << 16)) return fail(TQ_ERR_INVALID_ARG, "hybrid decode: bad buffer size");
+  const int64_t comp = (max_len / buf_size) * buf_size;
+  *has_compressed = comp > 0;
+  tq_status st = check_decode_shapes(kc, vc, batch, hq, hkv, q_len, std::max<int64_t>(comp, 1));
+  if (st != TQ_OK) return st;
+  if (max_len <= 0) return fail(TQ_ERR_INVALID_ARG, "hybrid decode: max_len must be positive");
+  *base = *has_compressed ? attention_workspace(kc, vc, batch, hq, hkv, q_len, comp) : 0;
+  *off_lens = align256(*base);
+  *off_ml = align256(*off_lens + 4 * (size_t)batch);
+  *total = align256(*off_ml + 8 * (size_t)batch * hq * q_len);
+  return TQ_OK;
+}
+
+tq_status tq_hybrid_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq,
+                                          int32_t hkv, int32_t q_len, int64_t max_len, int32_t buf_size,
+                                          size_t* bytes) {
+  if (!bytes) return fail(TQ_ERR_INVALID_ARG, "tq_hybrid_decode_workspace_size: bytes is NULL");
+  size_t base, ol, om, total;
+  bool hc;
+  tq_status st = hybrid_layout(kc, vc, batch, hq, hkv, q_len, max_len, buf_size, &base, &ol, &om, &total, &hc);
+  if (st != TQ_OK) return st;
+  *bytes = total;
+  return TQ_OK;
+}
+
+tq_status tq_hybrid_decode_attention(const tq_codec* kc, const tq_codec* vc, const void* q, int32_t q_dtype,
+                                     int32_t batch, int32_t hq, int32_t hkv, int32_t q_len, const tq_cache* k,
+                                     const tq_cache* v, const void* kbuf, const void* vbuf, int32_t buf_dtype,
+                                     int32_t buf_size, const int32_t* d_len, int64_t max_len, float scale,
+                                     float* out, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "tq_hybrid_decode_attention";
+  size_t base, off_lens, off_ml, total;
+  bool has_comp;
+  tq_status st = hybrid_layout(kc, vc, batch, hq, hkv, q_len, max_len, buf_size, &base, &off_lens, &off_ml, &total,
+                               &has_comp);
+  if (st != TQ_OK) return st;
+  std::string why;
+  if (!hybrid_buffers_ok(kbuf, vbuf, buf_dtype, buf_size, &why)) return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": " + why);
+  if (!q || !d_len || !out || !k || !v) return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": NULL argument");
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": bad q_dtype");
+  if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": scale is not finite");
+  if (!ws || ws_bytes < total)
+    return fail(TQ_ERR_WORKSPACE, std::string(who) + ": workspace needs " + std::to_string(total) + " bytes");
+  char* w = static_cast<char*>(ws);
+  int32_t* lens_c = reinterpret_cast<int32_t*>(w + off_lens);
+  float* row_ml = reinterpret_cast<float*>(w + off_ml);
+  if (has_comp) {
+    const int64_t comp = (max_len / buf_size) * buf_size;
+    // argument checks of the compressed decode before any launch
+    std::string cw;
+    if (!cache_ok(k, kc->h, &cw) || !cache_ok(v, vc->h, &cw)) return fail(TQ_ERR_INVALID_ARG, std::string(who) + ": " + cw);
+    if (comp > k->cap) return fail(TQ_ERR_CAPACITY, std::string(who) + ": the compressed part exceeds the cache capacity");
+    hipError_t e = tq::launch_hybrid_lens(d_len, lens_c, batch, buf_size, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "tq_hybrid_decode_attention lens launch");
+    st = attention_impl(who, false, kc, vc, q, q_dtype, batch, hq, hkv, q_len, k, v, lens_c, comp, scale, out, ws,
+                        base, stream, true, d_len, row_ml);
+    if (st != TQ_OK) return st;
+  }
+  tq::HybridAttn a{};
+  a.q = q;
+  a.q_bf16 = q_dtype == TQ_BF16;
+  a.batch = batch;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.q_len = q_len;
+  a.group = hq / hkv;
+  a.d = kc->h.d;
+  a.scale = scale;
+  a.kbuf = kbuf;
+  a.vbuf = vbuf;
+  a.buf_bf16 = buf_dtype == TQ_BF16;
+  a.block = buf_size;
+  a.has_compressed = has_comp ? 1 : 0;
+  a.len = d_len;
+  a.row_ml = row_ml;
+  a.out = out;
+  const hipError_t e = tq::launch_hybrid_combine(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tq_hybrid_decode_attention combine launch");
+  return TQ_OK;
 }
 
 tq_status tq_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, int32_t blocks, void* stream) {

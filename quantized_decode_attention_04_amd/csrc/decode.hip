@@ -332,6 +332,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   const bool ksplit = p.ksplit_g > 0, vsplit = p.vsplit_g > 0;
   int64_t len = p.len[b];
   len = len < 0 ? 0 : (len > p.cap ? p.cap : len);
+  // the causal rule's length (a hybrid cache's whole length; else len)
+  const int64_t lenm = p.len_mask ? (p.len_mask[b] < 0 ? 0 : (int64_t)p.len_mask[b]) : len;
   const int64_t c0 = (int64_t)chunk_id * p.chunk;
   const int64_t c1 = c0 + p.chunk < len ? c0 + p.chunk : len;
   const int rows = p.rows;
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       }
 #pragma unroll
       for (int r = 0; r < RMAX; ++r) {
-        const bool vis = tid < cnt && r < rows && tok < len - p.q_len + ((p.row0 + r) % p.q_len) + 1;
+        const bool vis = tid < cnt && r < rows && tok < lenm - p.q_len + ((p.row0 + r) % p.q_len) + 1;
         s_p[tid * (RMAX + 1) + r] = vis ? s[r] * sl2 : -INFINITY;
       }
     }
@@ -526,7 +528,12 @@ __global__ __launch_bounds__(4 * D) void merge_kernel(DecodeParams p) {
   __syncthreads();
   const int R = p.row0 + r;
   const int h = g * p.group + R / p.q_len, qi = R % p.q_len;
-  float* out = p.out + (((int64_t)b * p.hq + h) * p.q_len + qi) * D;
+  const int64_t orow = ((int64_t)b * p.hq + h) * p.q_len + qi;
+  float* out = p.out + orow * D;
+  if (p.row_ml && tid == 0) {  // the row's softmax reference and sum (log2 domain), for a later combine
+    p.row_ml[2 * orow] = M;
+    p.row_ml[2 * orow + 1] = L;
+  }
   if (!rotate) {
     if (k == 0) out[j] = s_o[j];
     return;

@@ -319,8 +319,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
   const int c0 = chunk_id * p.chunk;
   const int c1 = c0 + p.chunk < len ? c0 + p.chunk : len;
   const uint32_t ntok = c1 > c0 ? (uint32_t)(c1 - c0) : 0u;
-  const int lim = len - p.q_len + ((p.row0 + n) % p.q_len) + 1 - c0;  // row n sees tokens < lim
-  const int lim_all = len - p.q_len + 1 - c0;              // tokens every row sees
+  // the causal rule counts the q_len new tokens from the sequence's whole
+  // length, which a hybrid cache passes apart (its recent tokens are not in
+  // this cache)
+  const int lenm = p.len_mask ? (p.len_mask[b] < 0 ? 0 : p.len_mask[b]) : len;
+  const int lim = lenm - p.q_len + ((p.row0 + n) % p.q_len) + 1 - c0;  // row n sees tokens < lim
+  const int lim_all = lenm - p.q_len + 1 - c0;              // tokens every row sees
 
   // ---- loads: the query prologue's first, then the first two tiles
   QueryLoads ql;
@@ -660,7 +664,12 @@ __global__ __launch_bounds__(kD) void merge_fast_kernel(DecodeParams p) {
   for (int i = 0; i < kD; ++i) acc = fmaf(s_o[i], pv[i], acc);
   const int R = p.row0 + r;
   const int h = g * p.group + R / p.q_len, qi = R % p.q_len;
-  p.out[(((int64_t)b * p.hq + h) * p.q_len + qi) * kD + j] = acc;
+  const int64_t orow = ((int64_t)b * p.hq + h) * p.q_len + qi;
+  p.out[orow * kD + j] = acc;
+  if (p.row_ml && j == 0) {  // the row's softmax reference and sum (log2 domain), for a later combine
+    p.row_ml[2 * orow] = M;
+    p.row_ml[2 * orow + 1] = L;
+  }
 }
 
 }  // namespace

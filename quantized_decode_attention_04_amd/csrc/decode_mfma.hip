@@ -109,7 +109,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(DecodeParams p
   const int len = (int)len64;
   const int c0 = chunk_id * p.chunk;
   const int ntok = (c0 + p.chunk < len ? c0 + p.chunk : len) - c0;  // may be <= 0
-  const int lim = len - p.q_len + ((p.row0 + m) % p.q_len) + 1 - c0;  // row m sees tokens < lim
+  const int lenm = p.len_mask ? (p.len_mask[b] < 0 ? 0 : p.len_mask[b]) : len;  // the causal rule's length
+  const int lim = lenm - p.q_len + ((p.row0 + m) % p.q_len) + 1 - c0;  // row m sees tokens < lim
 
   for (int e = threadIdx.x; e < 16 * D; e += kWaves * 64) {
     const int r = e / D, j = e % D;

@@ -56,6 +56,18 @@ __device__ __forceinline__ void pack_field(uint32_t* w, int j, int b, uint32_t v
   }
 }
 
+// Cache slot position of token t of sequence b (negative: not written).  A
+// hybrid-cache flush writes the recent-token buffer's block only when this
+// step's appends complete it.
+__device__ __forceinline__ int64_t append_position(const QuantizeParams& p, int b, int t) {
+  const int64_t base = p.pos[b];
+  if (p.flush_block > 0) {
+    const int64_t blk = p.flush_block, start = base < 0 ? -1 : (base / blk) * blk;
+    return (start >= 0 && base - start + p.flush_new >= blk) ? start + t : -1;
+  }
+  return base + t;
+}
+
 // ---- bulk appends on the matrix cores --------------------------------------
 //
 // One 256-thread workgroup per tile of kMV = 64 vectors.  The tile is staged
@@ -287,13 +299,15 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void quantize_bulk_kernel(Qu
       const int64_t bh = vec / p.n_new;
       const int h = (int)(bh % p.heads), b = (int)(bh / p.heads);
       src = (int64_t)b * p.s0 + (int64_t)h * p.s1 + (int64_t)t * p.s2;
-      const int64_t pos = (int64_t)p.pos[b] + t;
+      const int64_t pos = append_position(p, b, t);
       if (pos >= 0 && pos < p.cap) slot = ((int64_t)b * p.heads + h) * p.cap + pos;
     }
     L.src[tid] = src;
     L.slot[tid] = slot;
   }
-  __syncthreads();
+  // a tile with nothing to write (a hybrid flush of sequences whose buffer is
+  // not full) stops here
+  if (!__syncthreads_or(tid < kMV && L.slot[tid] >= 0)) return;
 
   // ---- the x tile (zeros for rows past the end)
   if (p.x_vec16) {
@@ -416,7 +430,7 @@ __global__ __launch_bounds__(small_threads<D>()) void quantize_small_kernel(Quan
   const int t = (int)(vec % p.n_new);
   const int64_t bh = vec / p.n_new;
   const int h = (int)(bh % p.heads), b = (int)(bh / p.heads);
-  const int64_t pos = (int64_t)p.pos[b] + t;
+  const int64_t pos = append_position(p, b, t);
   if (pos < 0 || pos >= p.cap) return;  // whole workgroup: nothing is written for it
   const int64_t tok = ((int64_t)b * p.heads + h) * p.cap + pos;
   const bool prod = p.mode == TQ_MODE_PROD;
@@ -575,7 +589,9 @@ __global__ __launch_bounds__(64) void quantize_mse_split_kernel(QuantizeSets set
   const int h = (int)(bh % p.heads), b = (int)(bh / p.heads);
   // the write position is needed only by the stores: its load is in flight
   // with the others
-  const int32_t pos32 = p.pos[b];
+  const int64_t pos = append_position(p, b, t);
+  // a hybrid flush of a sequence whose buffer is not full writes nothing
+  if (p.flush_block > 0 && (pos < 0 || pos >= p.cap)) return;
 
   float4 pr[JN / 4];
   const float4* src = reinterpret_cast<const float4*>(p.pi + (size_t)(32 * g + c) * D + part * JN);
@@ -641,7 +657,6 @@ __global__ __launch_bounds__(64) void quantize_mse_split_kernel(QuantizeSets set
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int64_t pos = (int64_t)pos32 + t;
   if (pos < 0 || pos >= p.cap) return;  // nothing is written for this vector
   const int64_t tok = ((int64_t)b * p.heads + h) * p.cap + pos;
   if (lane < p.mse_bits) p.idx[tok * p.idx_stride + g * p.mse_bits + lane] = wbuf[lane];

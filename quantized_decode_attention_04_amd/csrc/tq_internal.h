@@ -87,6 +87,13 @@ struct QuantizeParams {
   float* gmin;
   int64_t cap;
   const int32_t* pos;
+  // hybrid-cache flush (0: an ordinary append at pos[b] + t): x is the
+  // recent-token buffer of flush_block tokens, pos[b] the sequence's length
+  // before the step's flush_new appended tokens; the buffer is quantised into
+  // slots start .. start+flush_block-1, start = floor(pos[b] / flush_block) *
+  // flush_block, when those tokens complete it, and nothing is written
+  // otherwise
+  int flush_block, flush_new;
 };
 
 // One or two parameter blocks (a key and a value append) in one launch;
@@ -136,6 +143,13 @@ struct DecodeParams {
   const float* v_gmin;
   int64_t cap;
   const int32_t* len;
+  // optional: the length the causal rule counts from (row i sees t <= lm -
+  // q_len + i), when it differs from len (a hybrid cache: len its compressed
+  // tokens, lm its whole length); NULL: len
+  const int32_t* len_mask;
+  // optional: the merge also writes each output row's softmax reference M and
+  // sum L (log2 domain) as [batch][hq][q_len][2]; NULL: not written
+  float* row_ml;
   // split over the token axis
   int chunk, n_chunks;
   // workspace pieces
@@ -213,6 +227,34 @@ tq_status decode_attention_in(const char* name, const tq_codec* kc, const tq_cod
                               float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 // Records msg as the thread's last error and returns s.
 tq_status set_error(tq_status s, const std::string& msg);
+
+// ---- hybrid cache: the recent-token buffer --------------------------------------
+
+// Copy of a step's new tokens into the rings (phase 0: the tokens of the block
+// being filled; phase 1: those after it, once the full block is flushed).
+struct HybridStage {
+  const void* x[2];
+  int64_t xs[2][3];   // element strides of batch, head, token (coordinate stride 1)
+  void* buf[2];       // rings [batch][heads][block][d]
+  int n_sets, bf16, batch, heads, n_new, d, block, phase;
+  const int32_t* len; // tokens of each sequence before the step
+};
+hipError_t launch_hybrid_stage(const HybridStage& s, hipStream_t stream);
+hipError_t launch_hybrid_lens(const int32_t* len, int32_t* lens_c, int batch, int block, hipStream_t stream);
+
+// Exact attention over the rings and the merge with the compressed decode.
+struct HybridAttn {
+  const void* q;
+  int q_bf16, batch, hq, hkv, q_len, group, d;
+  float scale;
+  const void* kbuf;
+  const void* vbuf;
+  int buf_bf16, block, has_compressed;
+  const int32_t* len;    // whole length N of each sequence
+  const float* row_ml;   // the compressed decode's (M, L) per output row
+  float* out;            // holds the compressed decode's output; overwritten with the merge
+};
+hipError_t launch_hybrid_combine(const HybridAttn& a, hipStream_t stream);
 
 // ---- measurement ------------------------------------------------------------
 

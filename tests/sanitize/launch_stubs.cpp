@@ -20,6 +20,12 @@ hipError_t launch_decode_bf16_kernel(const DecodeParams&, const dim3, hipStream_
 hipError_t launch_decode_mfma(const DecodeParams&, hipStream_t) { ++g_stub_launches; return hipErrorNoDevice; }
 hipError_t launch_decode_fast(const DecodeParams&, hipStream_t) { ++g_stub_launches; return hipErrorNoDevice; }
 hipError_t launch_cache_gather(const CacheGather&, int64_t, hipStream_t) { ++g_stub_launches; return hipErrorNoDevice; }
+hipError_t launch_hybrid_stage(const HybridStage&, hipStream_t) { ++g_stub_launches; return hipErrorNoDevice; }
+hipError_t launch_hybrid_lens(const int32_t*, int32_t*, int, int, hipStream_t) {
+  ++g_stub_launches;
+  return hipErrorNoDevice;
+}
+hipError_t launch_hybrid_combine(const HybridAttn&, hipStream_t) { ++g_stub_launches; return hipErrorNoDevice; }
 hipError_t launch_stream_read(const void*, uint64_t, uint32_t*, int, hipStream_t) {
   ++g_stub_launches;
   return hipErrorNoDevice;
