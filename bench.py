@@ -557,8 +557,9 @@ def main():
     rows = (hq // hkv) * qlen
     fast = d == 128 and (w.kmode, w.kbits, w.vmode, w.vbits) == (0, 3, 0, 3) and rows <= 16
     kcode_bits = w.kbits - 1 if w.kmode == 1 else w.kbits
-    bf16_path = (not fast and d == 128 and w.kmode in (0, 1) and kcode_bits in (1, 2) and w.vmode == 0
-                 and w.vbits in (1, 2, 4) and rows <= 16)
+    bf16_path = (not fast and d in (128, 256) and w.kmode in (0, 1) and kcode_bits in (1, 2)
+                 and ((w.vmode == 0 and w.vbits in (1, 2, 4)) or (w.vmode == 2 and w.vbits == 2))
+                 and rows <= (16 if d == 128 else 8))
     kernels = ("decode_fast_kernel + merge_fast_kernel" if fast
                else "qprep_kernel + decode_bf16_kernel + merge_kernel" if bf16_path
                else "qprep_kernel + decode_kernel + merge_kernel")

@@ -20,13 +20,14 @@ bool fast_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, in
   return d == 128 && kmode == TQ_MODE_MSE && kbits == 3 && vmode == TQ_MODE_MSE && vbits == 3 && rows <= 16;
 }
 
-// bf16 split-operand kernel (decode_bf16.hip): head_dim 128, key codes of 1
-// or 2 bits (MSE, or the MSE part of 2/3-bit Prod keys), MSE values of 1, 2
-// or 4 bits, up to 16 rows.
+// bf16 split-operand kernel (decode_bf16.hip): head_dim 128 or 256, key codes
+// of 1 or 2 bits (MSE, or the MSE part of 2/3-bit Prod keys), MSE values of
+// 1, 2 or 4 bits or 2-bit group values, up to 16 rows (8 at head_dim 256).
 bool bf16_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
   const bool kok = (kmode == TQ_MODE_MSE || kmode == TQ_MODE_PROD) && (kbits == 1 || kbits == 2);
-  const bool vok = vmode == TQ_MODE_MSE && (vbits == 1 || vbits == 2 || vbits == 4);
-  return d == 128 && kok && vok && rows >= 1 && rows <= 16;
+  const bool vok = (vmode == TQ_MODE_MSE && (vbits == 1 || vbits == 2 || vbits == 4)) ||
+                   (vmode == TQ_MODE_GROUP && vbits == 2);
+  return (d == 128 || d == 256) && kok && vok && rows >= 1 && rows <= (d == 128 ? 16 : 8);
 }
 
 // fp32 matrix-core kernel (decode_mfma.hip).
@@ -34,17 +35,17 @@ bool mfma_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, in
   const bool kok = (kmode == TQ_MODE_MSE || kmode == TQ_MODE_PROD) && kbits >= 1 && kbits <= 4;
   const bool vok = (vmode == TQ_MODE_MSE && (vbits == 1 || vbits == 2 || vbits == 4)) ||
                    (vmode == TQ_MODE_GROUP && (vbits == 2 || vbits == 4));
-  return (d == 128 || d == 256) && kok && vok && rows >= 1 && rows <= 16;
+  return (d == 128 || d == 256) && kok && vok && rows >= 1 && rows <= (d == 128 ? 16 : 8);
 }
 
 // Measured on MI355X: at head_dim 128 with more than 8 rows (prefill blocks,
 // multi-token decode) the fp32 matrix-core kernel takes half the general
 // kernel's time (whose work grows with the rows); at 8 rows or fewer, and at
 // head_dim 256, the general kernel is as fast or faster.  Launches the bf16
-// kernel covers go through launch_decode_mfma as well.
+// kernel covers (either head_dim) go through launch_decode_mfma as well.
 bool mfma_decode_preferred(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
-  return d == 128 && (rows > 8 || bf16_decode_supported(d, kmode, kbits, vmode, vbits, rows)) &&
-         mfma_decode_supported(d, kmode, kbits, vmode, vbits, rows);
+  if (bf16_decode_supported(d, kmode, kbits, vmode, vbits, rows)) return true;
+  return d == 128 && rows > 8 && mfma_decode_supported(d, kmode, kbits, vmode, vbits, rows);
 }
 
 // ---- chunk plans and workspace layouts ---------------------------------------
@@ -107,6 +108,7 @@ DecodePlan plan_decode_mfma(int batch, int hkv, int rows, int d, int64_t max_len
   // (chunks past a sequence's end exit at once)
   if (batch > 1) chunk = std::min<int64_t>(chunk, kRaggedChunk);
   chunk = std::max<int64_t>(step, ((chunk + step - 1) / step) * step);
+  chunk = std::min<int64_t>(chunk, (int64_t)1 << 24);  // the bf16 kernel's 24-bit token offsets
   chunk = std::max<int64_t>(chunk, ((max_len + 1023) / 1024 + step - 1) / step * step);  // <= 1024 chunks
   p.chunk = (int)chunk;
   p.n_chunks = (int)((max_len + chunk - 1) / chunk);

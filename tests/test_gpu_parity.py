@@ -245,12 +245,22 @@ DEC_CASES = [
     ("mfma_prod2_group4", 128, (2, 1), (4, 2), 1, 2, 8, 3, [777], 800, True, False),
     # general path at head_dim 256: 4-bit keys, 1-bit values
     ("d256_mse4_mse1", 256, (4, 0), (1, 0), 2, 1, 4, 2, [900, 40], 1000, False, False),
+    # bf16 split-operand path at head_dim 256 (32-token wave tiles): 2-bit MSE
+    # keys with 4-bit values (two value words per lane), ragged; 2-bit Prod
+    # keys (1-bit codes) with 2-bit group values and the causal rule of
+    # q_len 2; 1-bit keys and values; a sharp softmax over 3-bit Prod keys and
+    # group values
+    ("bf16_d256_mse2_mse4", 256, (2, 0), (4, 0), 2, 2, 8, 1, [1700, 333], 1800, True, False),
+    ("bf16_d256_prod2_group2_q2", 256, (2, 1), (2, 2), 1, 1, 4, 2, [2000], 2048, False, False),
+    ("bf16_d256_mse1_mse1", 256, (1, 0), (1, 0), 1, 2, 6, 1, [900], 900, False, False),
+    ("bf16_d256_prod3_group2_sharp", 256, (3, 1), (2, 2), 1, 2, 16, 1, [1500], 1536, True, False),
 ]
 
 # query scale per case (default 0.02, like the keys); larger scales make the
 # softmax sharp and stress the score precision
 Q_STD = {"fast_sharp_softmax": 200.0, "d32_mse1_mse2": 1.0, "d96_mse4_group3_q3": 1.0,
-         "d224_prod5_group4": 1.0, "d192_prod2_mse1": 1.0, "mfma_mse3_mse2": 20.0, "d256_mse4_mse1": 1.0}
+         "d224_prod5_group4": 1.0, "d192_prod2_mse1": 1.0, "mfma_mse3_mse2": 20.0, "d256_mse4_mse1": 1.0,
+         "bf16_d256_prod2_group2_q2": 1.0, "bf16_d256_prod3_group2_sharp": 30.0}
 
 
 def _oracle_states(name, d, kspec, vspec, B, Hkv, N, bf16, outliers, seed=0):
