@@ -60,7 +60,7 @@ tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out, bool may_upload
   if (!c->uploaded[dev] && c->h.mode != TQ_MODE_GROUP) {
     const int d = c->h.d;
     const size_t dd = (size_t)d * d;
-    const size_t nfl = 4 * dd + 64;
+    const size_t nfl = 5 * dd + 64;
     void* block = nullptr;
     e = hipMalloc(&block, nfl * sizeof(float));
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(codec tables)");
@@ -69,7 +69,8 @@ tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out, bool may_upload
     float* pi = pit + dd;
     float* st = pi + dd;
     float* sk = st + dd;
-    float* cent = sk + dd;
+    float* spt = sk + dd;
+    float* cent = spt + dd;
     float* bnd = cent + 16;
     float* cent2 = bnd + 16;
     float* bnd2 = cent2 + 16;
@@ -98,6 +99,20 @@ tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out, bool may_upload
         }
       float* ce = q == 0 ? cent : cent2;
       float* bo = q == 0 ? bnd : bnd2;
+      if (!hb.sketch.empty()) {
+        // (S Pi)^T, so that the query prologue forms S q_rot = (S Pi) q in
+        // the same pass as q_rot = Pi q (the product taken in double)
+        std::vector<double> row(db);
+        for (int i = 0; i < db; ++i) {
+          std::fill(row.begin(), row.end(), 0.0);
+          for (int k = 0; k < db; ++k) {
+            const double sik = hb.sketch[(size_t)i * db + k];
+            const float* rk = &hb.rot[(size_t)k * db];
+            for (int j = 0; j < db; ++j) row[j] += sik * (double)rk[j];
+          }
+          for (int j = 0; j < db; ++j) spt[(size_t)(o + j) * d + o + i] = (float)row[j];
+        }
+      }
       for (int k = 0; k < hb.levels; ++k) ce[k] = hb.centroids[k];
       for (int k = 0; k + 1 < hb.levels; ++k) bo[k] = hb.boundaries[k];
     }
@@ -112,10 +127,11 @@ tq_status ensure_tables(const tq_codec* cc, tq::DevTables** out, bool may_upload
     t.pi = base + dd;
     t.st = base + 2 * dd;
     t.s = base + 3 * dd;
-    t.cent = base + 4 * dd;
-    t.bnd = base + 4 * dd + 16;
-    t.cent2 = base + 4 * dd + 32;
-    t.bnd2 = base + 4 * dd + 48;
+    t.spt = base + 4 * dd;
+    t.cent = base + 5 * dd;
+    t.bnd = base + 5 * dd + 16;
+    t.cent2 = base + 5 * dd + 32;
+    t.bnd2 = base + 5 * dd + 48;
     c->uploaded[dev] = true;
   }
   *out = &t;
@@ -644,7 +660,7 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
   p.ksign_words = sign_words(kc->h);
   p.k_pit = kt->pit;
   p.k_pi = kt->pi;
-  p.k_st = kt->st;
+  p.k_spt = kt->spt;
   p.k_cent = kt->cent;
   p.k_idx = k->idx;
   p.k_norm = k->norm;

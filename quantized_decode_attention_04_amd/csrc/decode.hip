@@ -89,52 +89,42 @@ __device__ __forceinline__ uint32_t token_field(const uint32_t* tokw, int j) {
   }
 }
 
-// q_rot = Pi_k q (and S q_rot for Prod keys) for one query row: one
-// workgroup of 4 D threads per (row, sequence x KV head); thread (i, k) sums
-// the quarter k of coordinate i's D terms with all of its loads in flight
-// (coalesced across i), and the quarters are added through LDS.
+// q_rot = Pi_k q, and for Prod keys S q_rot = (S Pi_k) q, for one query row:
+// one workgroup of 4 D threads per (row, sequence x KV head, product), the
+// two products in parallel workgroups (blockIdx.z); thread (i, k) sums the
+// quarter k of coordinate i's D terms, with all of its table loads issued
+// before the query row is staged (coalesced across i), and the quarters are
+// added through LDS.
 template <int D>
 __global__ __launch_bounds__(4 * D) void qprep_kernel(DecodeParams p) {
-  constexpr int Q = D / 4, QB = Q <= 32 ? Q : Q / 2;  // terms per thread, per batch of loads
-  static_assert(D % 4 == 0 && Q % QB == 0 && QB <= 32, "batches must tile a quarter");
-  __shared__ float s_in[D], s_qr[D], s_part[4][D];
+  constexpr int Q = D / 4;  // terms per thread
+  static_assert(D % 4 == 0, "quarters");
+  __shared__ float s_in[D], s_part[4][D];
   const int r = blockIdx.x, bg = blockIdx.y;
+  const bool sq = blockIdx.z == 1;
   const int b = bg / p.hkv, g = bg % p.hkv;
   const int i = threadIdx.x % D, k = threadIdx.x / D;
   const int R = p.row0 + r;  // row among the KV head's group * q_len rows
   const int h = g * p.group + R / p.q_len, qi = R % p.q_len;
   const int64_t qoff = (((int64_t)b * p.hq + h) * p.q_len + qi) * D;
+  const float* mt = sq ? p.k_spt : p.k_pit;
+  float pv[Q];
+#pragma unroll
+  for (int t = 0; t < Q; ++t) pv[t] = mt[(size_t)(k * Q + t) * D + i];
   if (k == 0) s_in[i] = load_q(p.q, qoff + i, p.q_bf16);
   __syncthreads();
   float acc = 0.f;
-  for (int t0 = 0; t0 < Q; t0 += QB) {
-    float pv[QB];
 #pragma unroll
-    for (int t = 0; t < QB; ++t) pv[t] = p.k_pit[(size_t)(k * Q + t0 + t) * D + i];
-#pragma unroll
-    for (int t = 0; t < QB; ++t) acc = fmaf(pv[t], s_in[k * Q + t0 + t], acc);
-  }
+  for (int t = 0; t < Q; ++t) acc = fmaf(pv[t], s_in[k * Q + t], acc);
   s_part[k][i] = acc;
   __syncthreads();
   const size_t e = ((size_t)bg * p.rows + r) * D + i;
-  if (k == 0) {
-    const float qr = (s_part[0][i] + s_part[1][i]) + (s_part[2][i] + s_part[3][i]);
-    p.qrot[e] = qr;
-    s_qr[i] = qr;
-  }
-  if (p.kmode != TQ_MODE_PROD) return;
-  __syncthreads();
-  float acs = 0.f;
-  for (int t0 = 0; t0 < Q; t0 += QB) {
-    float sv[QB];
-#pragma unroll
-    for (int t = 0; t < QB; ++t) sv[t] = p.k_st[(size_t)(k * Q + t0 + t) * D + i];
-#pragma unroll
-    for (int t = 0; t < QB; ++t) acs = fmaf(sv[t], s_qr[k * Q + t0 + t], acs);
-  }
-  s_part[k][i] = acs;
-  __syncthreads();
-  if (k == 0) p.qs[e] = (s_part[0][i] + s_part[1][i]) + (s_part[2][i] + s_part[3][i]);
+  if (k == 0) (sq ? p.qs : p.qrot)[e] = (s_part[0][i] + s_part[1][i]) + (s_part[2][i] + s_part[3][i]);
+}
+
+// the prologue's grid: rows x (sequence x KV head) x (1, or 2 for Prod keys)
+inline dim3 qprep_grid(const DecodeParams& p) {
+  return dim3(p.rows, p.batch * p.hkv, p.kmode == TQ_MODE_PROD ? 2 : 1);
 }
 
 // Scores of one token against all rows (rows beyond p.rows read zeros).
@@ -548,7 +538,7 @@ __global__ __launch_bounds__(4 * D) void merge_kernel(DecodeParams p) {
 
 template <int D>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
-  qprep_kernel<D><<<dim3(p.rows, p.batch * p.hkv), dim3(4 * D), 0, stream>>>(p);
+  qprep_kernel<D><<<qprep_grid(p), dim3(4 * D), 0, stream>>>(p);
   const dim3 grid(p.n_chunks, p.hkv, p.batch);
   if (p.rows <= 4) {
     decode_kernel<D, 4><<<grid, dim3(256), 0, stream>>>(p);
@@ -567,8 +557,8 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_qprep(const DecodeParams& p, hipStream_t stream) {
   switch (p.d) {
-    case 128: qprep_kernel<128><<<dim3(p.rows, p.batch * p.hkv), dim3(4 * 128), 0, stream>>>(p); break;
-    case 256: qprep_kernel<256><<<dim3(p.rows, p.batch * p.hkv), dim3(4 * 256), 0, stream>>>(p); break;
+    case 128: qprep_kernel<128><<<qprep_grid(p), dim3(4 * 128), 0, stream>>>(p); break;
+    case 256: qprep_kernel<256><<<qprep_grid(p), dim3(4 * 256), 0, stream>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -44,6 +44,7 @@ struct DevTables {
   float* pi = nullptr;    // Pi   [d][d] row-major
   float* st = nullptr;    // S^T  [d][d]: st[j*d + i] = S[i][j] (Prod)
   float* s = nullptr;     // S    [d][d] row-major (Prod)
+  float* spt = nullptr;   // (S Pi)^T [d][d]: spt[j*d + i] = (S Pi)[i][j] (Prod)
   float* cent = nullptr;  // centroids [16] (SPLIT: the low part's)
   float* bnd = nullptr;   // boundaries [16]
   float* cent2 = nullptr; // SPLIT: the high part's centroids [16]
@@ -119,7 +120,7 @@ struct DecodeParams {
   int kmode, kbits, kwords, ksign_words;
   const float* k_pit;   // Pi_k^T
   const float* k_pi;    // Pi_k row-major
-  const float* k_st;    // S^T
+  const float* k_spt;   // (S Pi)^T (Prod): the prologue's S q_rot = (S Pi) q
   const float* k_cent;
   const uint32_t* k_idx;
   const float* k_norm;
