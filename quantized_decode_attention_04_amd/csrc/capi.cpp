@@ -692,10 +692,11 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
   p.part_o = reinterpret_cast<float*>(w + plan.off_part_o);
   p.part_ml = reinterpret_cast<float*>(w + plan.off_part_ml);
   p.out = out;
+  // int8 centroid pieces (the matrix-core paths; centroids lie on the 2^-E grid)
+  piece_tables(kc->h, p.klut);
+  p.kgrid = kc->h.grid_exp;
   if (fast) {
-    piece_tables(kc->h, p.klut);
     piece_tables(vc->h, p.vlut);
-    p.kgrid = kc->h.grid_exp;
     p.vgrid = vc->h.grid_exp;
   } else {
     p.qrot = reinterpret_cast<float*>(w + plan.off_qrot);

@@ -57,11 +57,13 @@ namespace {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kStep = 256;  // chunks are multiples of this many tokens
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFlushGap = 8.f;  // log2 headroom of the lazy softmax reference
+constexpr float kQMax = 8355711.f;  // three-digit query bound (2^23 - 0x8081)
 
 __device__ __forceinline__ v4f mfma(const v4u& a, const v4u& b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0,
@@ -70,6 +72,26 @@ __device__ __forceinline__ v4f mfma(const v4u& a, const v4u& b, v4f c) {
 
 __device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
   return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+__device__ __forceinline__ v4i mfma8(const v4i& a, const v4i& b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// Coordinate (within a lane group's D/4) of byte f = 4 e + b of the int8
+// K-step ks fragments: the key selectors below put the codes in this order.
+template <int KB>
+__device__ __forceinline__ int kstep_coord(int ks, int e, int b) {
+  if constexpr (KB == 2) return 16 * ks + 4 * b + e;
+  return 32 * (ks >> 1) + 8 * b + 4 * (ks & 1) + e;
+}
+
+// int8 K-step ks selectors of a lane's key words: byte b of dword e is the
+// code of coordinate kstep_coord(ks, e, b)
+template <int KB>
+__device__ __forceinline__ uint32_t key_sel8(const uint32_t* w, int ks, int e) {
+  if constexpr (KB == 2) return (w[ks] >> (2 * e)) & 0x03030303u;
+  return (w[ks >> 1] >> (4 * (ks & 1) + e)) & 0x01010101u;
 }
 
 // A value loaded from a valid address (the caller clamps it), or zero; the
@@ -113,38 +135,6 @@ __device__ __forceinline__ float rowmax4(float v) {
   return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
-// Twice the code of coordinate (8/KB) k + t of word w, in byte k (t < 8/KB).
-template <int KB>
-__device__ __forceinline__ uint32_t spread(uint32_t w, int t) {
-  constexpr uint32_t mask = KB == 2 ? 0x06060606u : 0x02020202u;
-  const int sh = KB * t;
-  return (sh == 0 ? (w << 1) : (w >> (sh - 1))) & mask;
-}
-
-// Byte selectors of k-step s (coordinates 8 s .. 8 s + 7 of the lane's run):
-// dword e covers the coordinates 8 s + 2e and 8 s + 2e + 1.
-template <int KB>
-__device__ __forceinline__ void key_selectors(const uint32_t* w, int s, uint32_t (&sel)[4]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    uint32_t lo, hi;
-    int k;
-    if constexpr (KB == 2) {
-      const uint32_t word = w[s >> 1];
-      k = 2 * (s & 1) + (e >> 1);
-      lo = spread<2>(word, 2 * (e & 1));
-      hi = spread<2>(word, 2 * (e & 1) + 1);
-    } else {
-      const uint32_t word = w[s >> 2];
-      k = s & 3;
-      lo = spread<1>(word, 2 * e);
-      hi = spread<1>(word, 2 * e + 1);
-    }
-    const uint32_t dup = perm(hi, lo, 0x04040000u + 0x01010101u * (uint32_t)k);
-    sel[e] = dup | 0x01000100u;
-  }
-}
-
 // v_perm selector of two entries of a 4-entry bf16 table (entry c at bytes
 // 2c, 2c+1 of the 8-byte pool): the 2-bit codes of run coordinates u (low
 // half of the result) and u + NU/2 (high half); run = the lane's codes from
@@ -162,7 +152,8 @@ __device__ __forceinline__ uint32_t pair_selector(uint32_t run, int u) {
 
 template <int D, int KB, int VB, bool PROD, bool VGROUP>
 __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParams p) {
-  constexpr int KS = D / 32;          // k-steps of the score product
+  constexpr int KS = D / 32;          // bf16 k-steps of the QJL product
+  constexpr int KS8 = D / 64;         // int8 K-steps of the MSE product
   constexpr int LC = D / 4;           // key coordinates of a lane group
   constexpr int KW = KB * LC / 32;    // key index words of a lane group's coordinates
   constexpr int SW = LC / 32;         // QJL sign words of them
@@ -179,8 +170,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
   static_assert(D == 128 || D == 256, "head_dim 128 or 256");
   static_assert(kStep % (kWaves * kTile) == 0, "chunks hold whole workgroup steps");
   static_assert(!VGROUP || VB == 2, "group values of 2 bits");
-  // the query operands during the tiles, the waves' partial outputs after them
-  constexpr int kQopBytes = KS * 4 * 64 * 16;
+  // the query operands during the tiles (int8 digits, then the QJL pieces),
+  // the waves' partial outputs after them
+  constexpr int kQdBytes = KS8 * 3 * 64 * 16;
+  constexpr int kQopBytes = kQdBytes + (PROD ? KS * 2 * 64 * 16 : 0);
   // the waves' outputs: kRows rows of kRS floats, coordinate j at
   // j + 16 (j / GW) (GW = 4 NU coordinates per lane group): kRS = 1 mod 64
   // and the 16-float step per lane group put the 64 lanes of one store
@@ -193,7 +186,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
   __shared__ __attribute__((aligned(16))) uint8_t s_raw[kRawBytes];
   __shared__ uint32_t s_vt[16];           // MSE value centroid c: bf16 hi | lo << 16
   __shared__ float s_ml[kWaves][16][2];   // the waves' (m, l) per row
-  v4u* s_qop = reinterpret_cast<v4u*>(s_raw);     // [k-step][q hi, q lo, S q hi, S q lo][lane]
+  v4i* s_qd = reinterpret_cast<v4i*>(s_raw);                 // [K-step][digit a, b, c][lane]
+  v4u* s_qop = reinterpret_cast<v4u*>(s_raw + kQdBytes);     // [k-step][S q hi, S q lo][lane]
   float* s_o = reinterpret_cast<float*>(s_raw);   // [wave][row][kRS]
 
   const int lane = threadIdx.x & 63;
@@ -217,46 +211,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
       s_vt[threadIdx.x] = hi | (lo << 16);
     }
   }
-  // key centroid pools of v_perm: entries 0, 1 in the low word, 2, 3 in the high
-  uint32_t kh[2] = {0u, 0u}, kl[2] = {0u, 0u};
-#pragma unroll
-  for (int c = 0; c < (1 << KB); ++c) {
-    uint32_t hi, lo;
-    split_rne(p.k_cent[c], hi, lo);
-    kh[c >> 1] |= hi << (16 * (c & 1));
-    kl[c >> 1] |= lo << (16 * (c & 1));
-  }
-  // query operands of row m, per k-step s and lane, in LDS (the same for
-  // every wave): MSE term q_rot[(D/4) g + 8 s + v] (hi, lo), QJL term
-  // (S q_rot)[(D/4) g + 32 (s/4) + 4 (s%4) + e] and [.. + 16] as the pair e
-  // (hi, lo); wave w builds the k-steps w, w + 4, ...
-  for (int s = wave; s < KS; s += kWaves) {
-    const bool rok = m < rows;
-    const size_t qoff = ((size_t)bg * rows + (rok ? m : 0)) * D + LC * g;
-    v4u qh, ql, ch, cl;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t h, l;
-      split_pair(pick(p.qrot[qoff + 8 * s + 2 * e], rok), pick(p.qrot[qoff + 8 * s + 2 * e + 1], rok), h, l);
-      qh[e] = h;
-      ql[e] = l;
-      ch[e] = cl[e] = 0u;
-      if constexpr (PROD) {
-        const int c = 32 * (s >> 2) + 4 * (s & 3) + e;
-        split_pair(pick(p.qs[qoff + c], rok), pick(p.qs[qoff + c + 16], rok), h, l);
-        ch[e] = h;
-        cl[e] = l;
-      }
-    }
-    s_qop[(4 * s + 0) * 64 + lane] = qh;
-    s_qop[(4 * s + 1) * 64 + lane] = ql;
-    s_qop[(4 * s + 2) * 64 + lane] = ch;
-    s_qop[(4 * s + 3) * 64 + lane] = cl;
-  }
-  __syncthreads();
-
-  const float sl2 = p.scale * kLog2e;
-  const float qjl = kQjlConstNumer / (float)D;
+  const float qjl = p.scale * kLog2e * kQjlConstNumer / (float)D;  // log2-domain QJL factor
   const size_t base = (size_t)bg * (size_t)p.cap + (size_t)c0;  // slot of token 0 of the chunk
   // the chunk's fields (uniform bases); a token index t < ntok (< 2^24)
   // addresses them with 24-bit products and 32-bit byte offsets
@@ -273,17 +228,16 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
   const uint32_t koff = 4u * g * KW, soff = 4u * g * SW, voff = 4u * ((m * VRB) >> 5);
   const uint32_t goff = 4u * ((m * NU) >> 5);  // the group of the lane's value run
   const int vshift = (m * VRB) & 31;
-  float m_ref = -1e30f, l_run = 0.f;
-  v4f acc[NU];
-#pragma unroll
-  for (int u = 0; u < NU; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // Tokens past the chunk's end read the last token instead: every load is
-  // valid, and their scores are masked, so they weigh nothing.
-  // ---- key words of token T0 + 16 tg + m, coordinates (D/4) g .. (D/4) g +
-  // D/4 - 1: each tile's are loaded one tile ahead (the scores need them
-  // first; the other fields are used only after the scores)
+  // ---- tile loads, one tile ahead of their use.  Key words of token T0 +
+  // 16 tg + m, coordinates (D/4) g .. (D/4) g + D/4 - 1; key norms and value
+  // fields of the lane's tokens T0 + 16 tg + 4 g + r (token i: tg = i / 4,
+  // r = i % 4).  Tokens past the chunk's end read the last token instead
+  // (token 0 of an empty chunk, a slot below the cache's capacity): every
+  // load is valid, and their scores are masked, so they weigh nothing.
   uint32_t nkw[TG][KW], nksw[TG][SW];
+  float kn[NT], kq[NT], vn[NT], vs[NT];
+  uint32_t vw[NT][VW];
   auto load_keys = [&](int T0) {
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) {
@@ -297,7 +251,119 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
       }
     }
   };
-  if (wave * kTile < ntok) load_keys(wave * kTile);
+  auto load_fields = [&](int T0) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const uint32_t t = (uint32_t)max(min(T0 + 16 * (i >> 2) + 4 * g + (i & 3), ntok - 1), 0);
+      kn[i] = ld<float>(knrm, 4u * t);
+      kq[i] = 0.f;
+      if constexpr (PROD) kq[i] = ld<float>(krnm, 4u * t) * qjl;
+      if constexpr (VGROUP) {
+        vs[i] = ld<float>(vscl, __umul24(t, gstride) + goff);
+        vn[i] = ld<float>(vmin, __umul24(t, gstride) + goff);
+      } else {
+        vn[i] = ld<float>(vnrm, 4u * t);
+        vs[i] = 0.f;
+      }
+#pragma unroll
+      for (int w = 0; w < VW; ++w) vw[i][w] = ld<uint32_t>(vidx, __umul24(t, vstride) + voff + 4u * w);
+    }
+  };
+
+  // ---- the prologue's reads of the query rows first, then the first
+  // tile's: loads complete in issue order, so the prologue waits for its own
+  // reads alone and the tile's arrive while it computes
+  const bool rok = m < rows;
+  const size_t qoff = ((size_t)bg * rows + (rok ? m : 0)) * D + LC * g;
+  float qv[LC];
+#pragma unroll
+  for (int c = 0; c < LC; ++c) qv[c] = p.qrot[qoff + c];
+  // this wave's QJL k-steps s = wave + 4 j: coordinates 32 j + 4 wave + e and + 16
+  constexpr int KSW = (KS + kWaves - 1) / kWaves;
+  float qsv[KSW][4][2];
+#pragma unroll
+  for (int jj = 0; jj < KSW; ++jj)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        qsv[jj][e][hh] = 0.f;
+        if constexpr (PROD) qsv[jj][e][hh] = p.qs[qoff + 32 * jj + 4 * wave + e + 16 * hh];
+      }
+  __builtin_amdgcn_sched_barrier(0);
+  load_keys(wave * kTile);
+  load_fields(wave * kTile);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // key centroid pieces: centroid c * 2^E = 256 hi + lo (int8 hi, lo),
+  // entries 0..3 in the bytes of one dword each
+  const uint32_t kth = p.klut[0], ktl = p.klut[2];
+  // Query operands, the same for every wave, in LDS.  MSE term: row m of
+  // q_rot quantised to 24 bits, q = round(q_rot sc) = 65536 a + 256 b + c
+  // with balanced int8 digits, sc = kQMax / max_j |q_rot[m][j]|; byte f =
+  // 4 e + b of K-step ks is coordinate (D/4) g + kstep_coord(ks, e, b).  QJL
+  // term: (S q_rot)[(D/4) g + 32 (s/4) + 4 (s%4) + e] and [.. + 16] as the
+  // bf16 pair e (hi, lo) of k-step s.  Every wave finds the row maximum; wave
+  // w writes the K-steps and k-steps w, w + 4, ...
+  float rowc;  // log2-domain score per unit of 2^16 t24 + 2^8 t16 + t8, 0 for a zero row
+  {
+    float mx = 0.f;
+#pragma unroll
+    for (int c = 0; c < LC; ++c) mx = fmaxf(mx, fabsf(qv[c]));
+    mx = rok ? rowmax4(mx) : 0.f;
+    const float sc = mx > 0.f ? kQMax / mx : 0.f;
+    // (with the log2-domain score scale folded in)
+    rowc = mx > 0.f ? p.scale * kLog2e * 256.f * exp2f(-(float)p.kgrid) / sc : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks) {
+      if (ks % kWaves != wave) continue;
+      v4i da, db, dc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t u[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          // the product may round one past the bound: clamp so the top digit fits
+          const float q = rok ? qv[kstep_coord<KB>(ks, e, bb)] : 0.f;
+          const float x = fminf(fmaxf(rintf(q * sc), -kQMax), kQMax);
+          u[bb] = (uint32_t)((int)x + 0x808080);  // bytes 2, 1, 0: a, b, c, each + 128
+        }
+        const uint32_t lo01 = perm(u[1], u[0], 0x05010400u);  // u0.b0 u1.b0 u0.b1 u1.b1
+        const uint32_t lo23 = perm(u[3], u[2], 0x05010400u);
+        const uint32_t hi01 = perm(u[1], u[0], 0x0c0c0602u);  // u0.b2 u1.b2 0 0
+        const uint32_t hi23 = perm(u[3], u[2], 0x0c0c0602u);
+        da[e] = (int)(perm(hi23, hi01, 0x05040100u) ^ 0x80808080u);
+        db[e] = (int)(perm(lo23, lo01, 0x07060302u) ^ 0x80808080u);
+        dc[e] = (int)(perm(lo23, lo01, 0x05040100u) ^ 0x80808080u);
+      }
+      s_qd[(3 * ks + 0) * 64 + lane] = da;
+      s_qd[(3 * ks + 1) * 64 + lane] = db;
+      s_qd[(3 * ks + 2) * 64 + lane] = dc;
+    }
+  }
+  if constexpr (PROD) {
+#pragma unroll
+    for (int jj = 0; jj < KSW; ++jj) {
+      const int s = wave + kWaves * jj;
+      if (s >= KS) continue;
+      v4u ch, cl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t h, l;
+        split_pair(rok ? qsv[jj][e][0] : 0.f, rok ? qsv[jj][e][1] : 0.f, h, l);
+        ch[e] = h;
+        cl[e] = l;
+      }
+      s_qop[(2 * s + 0) * 64 + lane] = ch;
+      s_qop[(2 * s + 1) * 64 + lane] = cl;
+    }
+  }
+  __syncthreads();
+
+  float m_ref = -1e30f, l_run = 0.f;
+  v4f acc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
 
   for (int T0 = wave * kTile; T0 < ntok; T0 += kWaves * kTile) {
     uint32_t kw[TG][KW], ksw[TG][SW];
@@ -308,84 +374,89 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
 #pragma unroll
       for (int w = 0; w < SW; ++w) ksw[tg][w] = nksw[tg][w];
     }
-    // ---- key norms and value fields of the lane's tokens T0 + 16 tg + 4 g
-    // + r (token i: tg = i / 4, r = i % 4)
-    float kn[NT], kq[NT], vn[NT], vs[NT];
-    uint32_t vw[NT][VW];
-    auto token_of = [&](int i) { return (uint32_t)min(T0 + 16 * (i >> 2) + 4 * g + (i & 3), ntok - 1); };
-    auto load_values = [&](int i) {
-      const uint32_t t = token_of(i);
-      if constexpr (VGROUP) {
-        vs[i] = ld<float>(vscl, __umul24(t, gstride) + goff);
-        vn[i] = ld<float>(vmin, __umul24(t, gstride) + goff);
-      } else {
-        vn[i] = ld<float>(vnrm, 4u * t);
-        vs[i] = 0.f;
-      }
-#pragma unroll
-      for (int w = 0; w < VW; ++w) vw[i][w] = ld<uint32_t>(vidx, __umul24(t, vstride) + voff + 4u * w);
-      if constexpr (VW == 1) vw[i][0] >>= vshift;
-    };
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const uint32_t t = token_of(i);
-      kn[i] = ld<float>(knrm, 4u * t);
-      kq[i] = 0.f;
-      if constexpr (PROD) kq[i] = ld<float>(krnm, 4u * t) * qjl;
-      load_values(i);
-    }
     // the next tile's key words (the last tile's reads of the chunk's last
     // token are never used)
     load_keys(T0 + kWaves * kTile);
+    uint32_t run[NT][VW];  // the value runs of this tile, from bit 0
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int w = 0; w < VW; ++w) run[i][w] = VW == 1 ? vw[i][w] >> vshift : vw[i][w];
 
-    // ---- scores
+    // ---- scores.  MSE term on the int8 matrix cores: sm[tg][i] = rowc (2^16
+    // t24 + 2^8 t16 + t8), exact integer digit products; the query operands
+    // of K-step ks + 1 are read while K-step ks computes, and the scheduling
+    // barriers keep the compiler from hoisting every step's reads (their
+    // registers) to the top
     v4f sm[TG], sq[TG];
+    {
+      v4i t24[TG], t16[TG], t8[TG];
 #pragma unroll
-    for (int tg = 0; tg < TG; ++tg) sm[tg] = sq[tg] = v4f{0.f, 0.f, 0.f, 0.f};
-    // the query operands of k-step s + 1 are read while k-step s computes;
-    // the scheduling barrier at the end of each k-step keeps the compiler from
-    // hoisting every k-step's reads (their registers) to the top
-    v4u nbh = s_qop[0 * 64 + lane], nbl = s_qop[1 * 64 + lane];
-    v4u nch = v4u{0u, 0u, 0u, 0u}, ncl = v4u{0u, 0u, 0u, 0u};
-    if constexpr (PROD) {
-      nch = s_qop[2 * 64 + lane];
-      ncl = s_qop[3 * 64 + lane];
-    }
+      for (int tg = 0; tg < TG; ++tg) t24[tg] = t16[tg] = t8[tg] = v4i{0, 0, 0, 0};
+      v4i na = s_qd[0 * 64 + lane], nb = s_qd[1 * 64 + lane], nc = s_qd[2 * 64 + lane];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const v4u bh = nbh, bl = nbl, ch = nch, cl = ncl;
-      if (s + 1 < KS) {
-        nbh = s_qop[(4 * s + 4) * 64 + lane];
-        nbl = s_qop[(4 * s + 5) * 64 + lane];
-        if constexpr (PROD) {
-          nch = s_qop[(4 * s + 6) * 64 + lane];
-          ncl = s_qop[(4 * s + 7) * 64 + lane];
+      for (int ks = 0; ks < KS8; ++ks) {
+        const v4i qa = na, qb = nb, qc = nc;
+        if (ks + 1 < KS8) {
+          na = s_qd[(3 * ks + 3) * 64 + lane];
+          nb = s_qd[(3 * ks + 4) * 64 + lane];
+          nc = s_qd[(3 * ks + 5) * 64 + lane];
         }
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
+          v4i ah, al;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t x = key_sel8<KB>(kw[tg], ks, e);
+            ah[e] = (int)perm(0u, kth, x);
+            al[e] = (int)perm(0u, ktl, x);
+          }
+          // Q C = 2^24 a Ch + 2^16 (a Cl + b Ch) + 2^8 (b Cl + c Ch) [+ c Cl,
+          // below 2^-23 of the product]
+          t24[tg] = mfma8(ah, qa, t24[tg]);
+          t16[tg] = mfma8(al, qa, t16[tg]);
+          t8[tg] = mfma8(al, qb, t8[tg]);
+          t16[tg] = mfma8(ah, qb, t16[tg]);
+          t8[tg] = mfma8(ah, qc, t8[tg]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      // 2^8 t16 + t8 stays below 2^31 (|t16|, |t8| <= D 64 128 + D 128 128)
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg) {
-        uint32_t sel[4];
-        key_selectors<KB>(kw[tg], s, sel);
-        v4u ah, al;
+      for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ah[e] = perm(kh[1], kh[0], sel[e]);
-          al[e] = perm(kl[1], kl[0], sel[e]);
+        for (int i = 0; i < 4; ++i) {
+          const int lo = (int)(((uint32_t)t16[tg][i] << 8) + (uint32_t)t8[tg][i]);
+          sm[tg][i] = rowc * fmaf(65536.f, (float)t24[tg][i], (float)lo);
         }
-        sm[tg] = mfma(ah, bh, sm[tg]);
-        sm[tg] = mfma(ah, bl, sm[tg]);
-        sm[tg] = mfma(al, bh, sm[tg]);
-        if constexpr (PROD) {
+    }
+    // QJL term on the bf16 matrix cores (the signs are exact in bf16)
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) sq[tg] = v4f{0.f, 0.f, 0.f, 0.f};
+    if constexpr (PROD) {
+      v4u nch = s_qop[0 * 64 + lane], ncl = s_qop[1 * 64 + lane];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const v4u ch = nch, cl = ncl;
+        if (s + 1 < KS) {
+          nch = s_qop[(2 * s + 2) * 64 + lane];
+          ncl = s_qop[(2 * s + 3) * 64 + lane];
+        }
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
           const uint32_t ns = ~ksw[tg][s >> 2];
-          const int sb = 4 * (s & 3);
           v4u as;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) as[e] = ((ns << (15 - (sb + e))) & 0x80008000u) | 0x3f803f80u;
+          for (int e = 0; e < 4; ++e) {
+            // bits k and k + 16 of the negated signs become the bf16 sign bits
+            const int k = 4 * (s & 3) + e;
+            as[e] = ((ns & (0x00010001u << k)) << (15 - k)) | 0x3f803f80u;
+          }
           sq[tg] = mfma(as, ch, sq[tg]);
           sq[tg] = mfma(as, cl, sq[tg]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- online softmax of row m over this lane's NT tokens
@@ -395,7 +466,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
     for (int i = 0; i < NT; ++i) {
       const int tok = T0 + 16 * (i >> 2) + 4 * g + (i & 3);
       const float raw = PROD ? fmaf(kn[i], sm[i >> 2][i & 3], kq[i] * sq[i >> 2][i & 3]) : kn[i] * sm[i >> 2][i & 3];
-      const float v = (tok < ntok && tok < lim) ? raw * sl2 : -INFINITY;
+      const float v = (tok < ntok && tok < lim) ? raw : -INFINITY;
       sc[i] = v;
       tmax = fmaxf(tmax, v);
     }
@@ -447,8 +518,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int ia = 2 * e, ib = 2 * e + 1;
-            const uint32_t sa = pair_selector<NU>(vw[8 * h + ia][0], u);
-            const uint32_t sb = pair_selector<NU>(vw[8 * h + ib][0], u);
+            const uint32_t sa = pair_selector<NU>(run[8 * h + ia][0], u);
+            const uint32_t sb = pair_selector<NU>(run[8 * h + ib][0], u);
             const uint32_t xa = perm(th[ia][1], th[ia][0], sa), xb = perm(th[ib][1], th[ib][0], sb);
             const uint32_t ya = perm(tl[ia][1], tl[ia][0], sa), yb = perm(tl[ib][1], tl[ib][0], sb);
             ah0[e] = perm(xb, xa, 0x05040100u);
@@ -475,7 +546,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
 #pragma unroll
             for (int t = 0; t < TPB; ++t) {
               const int sh = 2 - VB * t;
-              const uint32_t x = vw[8 * h + i][w];
+              const uint32_t x = run[8 * h + i][w];
               va[i][w][t] = (sh >= 0 ? (x << sh) : (x >> -sh)) & (0x01010101u * (VMASK << 2));
             }
 #pragma unroll
@@ -500,6 +571,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
         }
       }
     }
+    // the next tile's key norms and value fields (into registers whose
+    // contents this tile no longer needs)
+    load_fields(T0 + kWaves * kTile);
   }
 
   // ---- the workgroup's partial: the four waves' (m, l, o) of each row,
