@@ -271,28 +271,32 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
   };
 
   // ---- the prologue's reads of the query rows first, then the first
-  // tile's: loads complete in issue order, so the prologue waits for its own
-  // reads alone and the tile's arrive while it computes
+  // tile's key words: loads complete in issue order, so the prologue waits
+  // for its own reads alone and the key words arrive while it computes
   const bool rok = m < rows;
   const size_t qoff = ((size_t)bg * rows + (rok ? m : 0)) * D + LC * g;
+  // (16-byte reads: the rows are 16-byte aligned)
   float qv[LC];
 #pragma unroll
-  for (int c = 0; c < LC; ++c) qv[c] = p.qrot[qoff + c];
+  for (int c = 0; c < LC; c += 4) {
+    const v4f x = *reinterpret_cast<const v4f*>(p.qrot + qoff + c);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qv[c + t] = x[t];
+  }
   // this wave's QJL k-steps s = wave + 4 j: coordinates 32 j + 4 wave + e and + 16
   constexpr int KSW = (KS + kWaves - 1) / kWaves;
   float qsv[KSW][4][2];
 #pragma unroll
   for (int jj = 0; jj < KSW; ++jj)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int hh = 0; hh < 2; ++hh) {
+      v4f x = v4f{0.f, 0.f, 0.f, 0.f};
+      if constexpr (PROD) x = *reinterpret_cast<const v4f*>(p.qs + qoff + 32 * jj + 4 * wave + 16 * hh);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        qsv[jj][e][hh] = 0.f;
-        if constexpr (PROD) qsv[jj][e][hh] = p.qs[qoff + 32 * jj + 4 * wave + e + 16 * hh];
-      }
+      for (int e = 0; e < 4; ++e) qsv[jj][e][hh] = x[e];
+    }
   __builtin_amdgcn_sched_barrier(0);
   load_keys(wave * kTile);
-  load_fields(wave * kTile);
   __builtin_amdgcn_sched_barrier(0);
 
   // key centroid pieces: centroid c * 2^E = 256 hi + lo (int8 hi, lo),
@@ -358,6 +362,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
       s_qop[(2 * s + 1) * 64 + lane] = cl;
     }
   }
+  // the first tile's other fields (the wait counter tracks at most 63 loads:
+  // issued after the prologue's waits, they do not hold them up)
+  load_fields(wave * kTile);
   __syncthreads();
 
   float m_ref = -1e30f, l_run = 0.f;
