@@ -564,12 +564,23 @@ static tq_status check_decode_shapes(const tq_codec* kc, const tq_codec* vc, int
 // The decode path and its plan for these sizes: one function for the
 // workspace size queries and the calls, so that a workspace sized through the
 // API always fits the call.
-enum class DecodePath { kFast, kMfma, kGeneral };
+enum class DecodePath { kFast, kMfma, kGeneral, kPrefillFast };
 
 static tq::DecodePlan choose_plan(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
-                                  int32_t q_len, int64_t max_len, DecodePath* path) {
-  const int rows = (int)std::min<int64_t>((int64_t)(hq / hkv) * q_len, row_block(kc));
+                                  int32_t q_len, int64_t max_len, DecodePath* path, bool blocks = false) {
+  const int64_t rows_total = (int64_t)(hq / hkv) * q_len;
+  const int rows = (int)std::min<int64_t>(rows_total, row_block(kc));
   const bool prod = kc->h.mode == TQ_MODE_PROD;
+  // prefill on the 3-bit int8 path: one launch takes up to kPrefillRows rows
+  // of every KV head and reads each tile once per 128 of them
+  if (blocks && rows_total > 16 && use_fast(kc, vc, 16)) {
+    const int prows = (int)std::min<int64_t>(rows_total, tq::kPrefillRows);
+    const tq::DecodePlan pp = tq::plan_prefill_fast(batch, hkv, prows, max_len);
+    if (pp.n_chunks > 0) {
+      *path = DecodePath::kPrefillFast;
+      return pp;
+    }
+  }
   if (use_fast(kc, vc, rows)) {
     *path = DecodePath::kFast;
     return tq::plan_decode_fast(batch, hkv, rows, kc->h.d, max_len);
@@ -583,9 +594,9 @@ static tq::DecodePlan choose_plan(const tq_codec* kc, const tq_codec* vc, int32_
 }
 
 static size_t attention_workspace(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
-                                  int32_t q_len, int64_t max_len) {
+                                  int32_t q_len, int64_t max_len, bool blocks = false) {
   DecodePath path;
-  return choose_plan(kc, vc, batch, hq, hkv, q_len, max_len, &path).total;
+  return choose_plan(kc, vc, batch, hq, hkv, q_len, max_len, &path, blocks).total;
 }
 
 tq_status tq_decode_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
@@ -602,7 +613,7 @@ tq_status tq_prefill_workspace_size(const tq_codec* kc, const tq_codec* vc, int3
   if (!bytes) return fail(TQ_ERR_INVALID_ARG, "tq_prefill_workspace_size: bytes is NULL");
   tq_status st = check_decode_shapes(kc, vc, batch, hq, hkv, q_len, max_len, true);
   if (st != TQ_OK) return st;
-  *bytes = attention_workspace(kc, vc, batch, hq, hkv, q_len, max_len);
+  *bytes = attention_workspace(kc, vc, batch, hq, hkv, q_len, max_len, true);
   return TQ_OK;
 }
 
@@ -629,8 +640,9 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
   const int rows = (int)std::min<int64_t>(rows_total, row_block(kc));  // rows per launch
   const bool prod = kc->h.mode == TQ_MODE_PROD;
   DecodePath path;
-  const tq::DecodePlan plan = choose_plan(kc, vc, batch, hq, hkv, q_len, max_len, &path);
-  const bool fast = path == DecodePath::kFast;
+  const tq::DecodePlan plan = choose_plan(kc, vc, batch, hq, hkv, q_len, max_len, &path, blocks);
+  const bool prefill = path == DecodePath::kPrefillFast;
+  const bool fast = path == DecodePath::kFast || prefill;
   const bool mfma = path == DecodePath::kMfma;
   if (!ws || ws_bytes < plan.total)
     return fail(TQ_ERR_WORKSPACE, fn + ": workspace needs " + std::to_string(plan.total) + " bytes");
@@ -698,17 +710,20 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
   if (fast) {
     piece_tables(vc->h, p.vlut);
     p.vgrid = vc->h.grid_exp;
-  } else {
+  }
+  if (!fast || prefill) {
     p.qrot = reinterpret_cast<float*>(w + plan.off_qrot);
     p.qs = prod ? reinterpret_cast<float*>(w + plan.off_qs) : nullptr;
   }
   // one launch per block of rows; the blocks reuse the workspace in stream order
-  for (int64_t r0 = 0; r0 < rows_total; r0 += rows) {
+  const int block = prefill ? plan.rows : rows;
+  for (int64_t r0 = 0; r0 < rows_total; r0 += block) {
     p.row0 = (int)r0;
-    p.rows = (int)std::min<int64_t>(rows, rows_total - r0);
-    const hipError_t e = fast   ? tq::launch_decode_fast(p, static_cast<hipStream_t>(stream))
-                         : mfma ? tq::launch_decode_mfma(p, static_cast<hipStream_t>(stream))
-                                : tq::launch_decode(p, static_cast<hipStream_t>(stream));
+    p.rows = (int)std::min<int64_t>(block, rows_total - r0);
+    const hipError_t e = prefill ? tq::launch_prefill_fast(p, static_cast<hipStream_t>(stream))
+                         : fast  ? tq::launch_decode_fast(p, static_cast<hipStream_t>(stream))
+                         : mfma  ? tq::launch_decode_mfma(p, static_cast<hipStream_t>(stream))
+                                 : tq::launch_decode(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, (fn + " launch").c_str());
   }
   return TQ_OK;

@@ -672,6 +672,312 @@ __global__ __launch_bounds__(kD) void merge_fast_kernel(DecodeParams p) {
   }
 }
 
+// ---- prefill: many query rows over shared tiles ------------------------------
+//
+// A launch with more query rows per KV head than one decode workgroup takes
+// (prefill, long q_len) would read the state and expand its codes once per 16
+// rows.  Here the eight waves of a workgroup each own 16 rows of the same KV
+// head and walk the chunk's tiles together.  Per tile, wave w expands one
+// eighth of the shared operands into LDS -- the int8 key pieces of score tile
+// w/2, K-step w%2 (the selectors and look-ups a decode wave does for a whole
+// tile), half of each of its tokens' value selectors, and eight tokens'
+// norms -- and after one barrier every wave runs its own rows' score and value
+// products over all of them, as the decode kernel does.  Two LDS buffers
+// alternate: a wave that reaches the barrier of tile t has finished reading
+// tile t-1's buffer, and the next write to that buffer (tile t+1) comes after
+// the barrier of tile t, so one barrier per tile suffices.  The rotated query
+// rows come from qprep_kernel; every wave writes its own rows' partial (m, l,
+// o) for the chunk, merged by merge_fast_kernel.
+constexpr int kPfRowsWave = 16;
+constexpr int kPfRows = kWaves * kPfRowsWave;           // rows per workgroup
+constexpr int kPfKeyLds = 4 * 2 * 2 * 64 * 16;          // [score tile][K-step][hi, lo][lane] int8 pieces
+constexpr int kPfBuf = kPfKeyLds + kSelLds + kNormLds;  // one tile's shared operands
+constexpr int kPfLds = 2 * kPfBuf + kWaves * kAccLds;
+// every wave takes every tile of its chunk: at most 1024 tiles between
+// flushes of its int32 value accumulators (the decode kernel's bound)
+constexpr int kPfMaxChunk = 1 << 16;
+
+__global__ __launch_bounds__(kThreads, 1) void prefill_fast_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[kPfLds];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 15, h = lane >> 4;  // query row of the wave, lane group
+  const int chunk_id = blockIdx.x % p.n_chunks, rg = blockIdx.x / p.n_chunks;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int bg = b * p.hkv + g;
+  const int rows = p.rows;
+  const int rl = rg * kPfRows + wave * kPfRowsWave + n;  // this lane's row among the launch's rows
+  const bool rok = rl < rows;
+  int64_t len64 = p.len[b];
+  len64 = len64 < 0 ? 0 : (len64 > p.cap ? p.cap : len64);
+  const int len = (int)len64;
+  const int c0 = chunk_id * p.chunk;
+  const int c1 = c0 + p.chunk < len ? c0 + p.chunk : len;
+  const uint32_t ntok = c1 > c0 ? (uint32_t)(c1 - c0) : 0u;
+  const int lenm = p.len_mask ? (p.len_mask[b] < 0 ? 0 : p.len_mask[b]) : len;
+  const int lim = lenm - p.q_len + ((p.row0 + rl) % p.q_len) + 1 - c0;  // row rl sees tokens < lim
+  const int lim_all = lenm - p.q_len + 1 - c0;                        // tokens every row sees
+
+  // ---- this wave's share of each tile: lane (n, h) holds the key and value
+  // words of token tt, 32-coordinate group h (score tile pst = wave/2, whose
+  // token order puts a lane's scores on 16 consecutive tokens), and lanes
+  // 0..7 the norms of tokens 8 wave .. 8 wave + 7
+  const int pst = wave >> 1, pks = wave & 1;
+  const uint32_t tt = (uint32_t)(16 * (n >> 2) + 4 * pst + (n & 3));
+  const uint32_t lwo = tt * 48u + 12u * (uint32_t)h;
+  const uint32_t ln4 = (uint32_t)(8 * wave + (lane & 7)) * 4u;
+  const size_t base = (size_t)bg * (size_t)p.cap + (size_t)(ntok > 0 ? c0 : 0);
+  const __amdgpu_buffer_rsrc_t rk = rsrc(p.k_idx + base * 12, ntok * 48u);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(p.v_idx + base * 12, ntok * 48u);
+  const __amdgpu_buffer_rsrc_t rkn = rsrc(p.k_norm + base, ntok * 4u);
+  const __amdgpu_buffer_rsrc_t rvn = rsrc(p.v_norm + base, ntok * 4u);
+  // the first tile's words are requested before the query row (loads
+  // complete in order: the digits below wait for them too, which the
+  // prologue's own latency covers)
+  v3u kw = __builtin_amdgcn_raw_buffer_load_b96(rk, lwo, 0, 0);
+  v3u vw = __builtin_amdgcn_raw_buffer_load_b96(rv, lwo, 0, 0);
+  float kn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rkn, ln4, 0, 0));
+  float vn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvn, ln4, 0, 0));
+
+  // ---- query digits of row rl (zero for rows past the launch's): lane
+  // (n, h) holds coordinates 32 h .. 32 h + 31, the B operand of K-step ks is
+  // coordinates 32 h + 16 ks + s (byte s of the fragment); q = 65536 a + 256 b + c
+  v4i qa[2], qb[2], qc[2];
+  float rowc;
+  {
+    const float* qr = p.qrot + ((size_t)bg * rows + (rok ? rl : 0)) * kD + 32 * h;
+    v4f x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = rok ? *reinterpret_cast<const v4f*>(qr + 4 * i) : v4f{0.f, 0.f, 0.f, 0.f};
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x[i][0]), fabsf(x[i][1])), fmaxf(fabsf(x[i][2]), fabsf(x[i][3]))));
+    mx = rowmax4(mx);
+    const float sc = mx > 0.f ? kQMax / mx : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // the product may round one past the bound: clamp so the top digit fits
+          const float v = fminf(fmaxf(rintf(x[4 * ks + e][i] * sc), -kQMax), kQMax);
+          u[i] = (uint32_t)((int)v + 0x808080);  // bytes 2, 1, 0: a, b, c, each + 128
+        }
+        const uint32_t lo01 = perm(u[1], u[0], 0x05010400u);  // u0.b0 u1.b0 u0.b1 u1.b1
+        const uint32_t lo23 = perm(u[3], u[2], 0x05010400u);
+        const uint32_t hi01 = perm(u[1], u[0], 0x0c0c0602u);  // u0.b2 u1.b2 0 0
+        const uint32_t hi23 = perm(u[3], u[2], 0x0c0c0602u);
+        qa[ks][e] = (int)(perm(hi23, hi01, 0x05040100u) ^ 0x80808080u);
+        qb[ks][e] = (int)(perm(lo23, lo01, 0x07060302u) ^ 0x80808080u);
+        qc[ks][e] = (int)(perm(lo23, lo01, 0x05040100u) ^ 0x80808080u);
+      }
+    // score = sum_j Q_j C_j / (sc 2^E) = 256 [(256 t24 + t16) 256 + t8] / (sc 2^E)
+    rowc = sc > 0.f ? 256.f * p.scale * kLog2e * exp2f(-(float)p.kgrid) / sc : 0.f;
+    rowc = fmaxf(rowc, 1e-30f);  // keeps -inf * rowc = -inf for a zero query row
+  }
+  const uint32_t kh1 = p.klut[1], kh0 = p.klut[0], kl1 = p.klut[3], kl0 = p.klut[2];
+  const uint32_t vh1 = p.vlut[1], vh0 = p.vlut[0], vl1 = p.vlut[3], vl0 = p.vlut[2];
+  const float kappa = 256.f * exp2f(-(float)p.vgrid);
+
+  v4f* so = reinterpret_cast<v4f*>(s_buf + 2 * kPfBuf + wave * kAccLds);  // [16 rows][kAccRow] x 4 coords
+  auto oref = [&](int u) -> v4f& { return so[n * kAccRow + 4 * u + h]; };
+#pragma unroll
+  for (int u = 0; u < 8; ++u) oref(u) = v4f{0.f, 0.f, 0.f, 0.f};
+
+  float m_ref = -1e30f, l_run = 0.f;
+  float nref = 0.f, lsig = 0.f, isig = 1.f, kflush = kappa;
+  bool empty = true;
+  v4i ahh[8], ax[8], all[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) ahh[u] = ax[u] = all[u] = v4i{0, 0, 0, 0};
+
+  // ---- stage A: this wave's share of tile T's operands into its buffer,
+  // then the request for the words of the tile after it (past the chunk the
+  // loads read zeros, fetching nothing, and the expanded operands are never read)
+  auto stage_a = [&](uint32_t T) {
+    uint8_t* buf = s_buf + ((T / kTile) & 1u) * kPfBuf;
+    v4i* kk = reinterpret_cast<v4i*>(buf);
+    uint8_t* sb = buf + kPfKeyLds;
+    float* sn = reinterpret_cast<float*>(sb + kSelLds);
+    // (the K-step half is picked with selects: a register array takes no
+    // run-time index)
+    uint32_t s8[8], k4[4];
+    selectors3(kw.x, kw.y, kw.z, s8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k4[i] = pks ? s8[4 + i] : s8[i];
+    kk[((2 * pst + pks) * 2 + 0) * 64 + lane] = lookup(k4, kh1, kh0);
+    kk[((2 * pst + pks) * 2 + 1) * 64 + lane] = lookup(k4, kl1, kl0);
+    uint32_t v8[8];
+    selectors3(vw.x, vw.y, vw.z, v8);
+    v4u* dst = reinterpret_cast<v4u*>(sb + tt * kRow + sel_group_offset((int)(tt >> 4)) + 32 * h + 16 * pks);
+    *dst = pks ? v4u{v8[4], v8[5], v8[6], v8[7]} : v4u{v8[0], v8[1], v8[2], v8[3]};
+    if (lane < 8) {
+      sn[8 * wave + lane] = kn;
+      sn[kTile + 8 * wave + lane] = vn;
+    }
+    const uint32_t Tn = T + kTile;
+    kw = __builtin_amdgcn_raw_buffer_load_b96(rk, lwo + Tn * 48u, 0, 0);
+    vw = __builtin_amdgcn_raw_buffer_load_b96(rv, lwo + Tn * 48u, 0, 0);
+    kn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rkn, ln4 + Tn * 4u, 0, 0));
+    vn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvn, ln4 + Tn * 4u, 0, 0));
+  };
+  if (ntok > 0) stage_a(0);
+
+  // Tile T's buffer was written by stage A of the previous iteration (the
+  // barrier completes it); stage A of tile T + 64 runs between the score and
+  // the value products of tile T, into the other buffer, whose last reader
+  // (tile T - 64) every wave finished before the barrier.
+  for (uint32_t T0 = 0; T0 < ntok; T0 += kTile) {
+    uint8_t* buf = s_buf + ((T0 / kTile) & 1u) * kPfBuf;
+    const v4i* kk = reinterpret_cast<const v4i*>(buf);  // [tile st][K-step][hi, lo][lane]
+    const uint8_t* sb = buf + kPfKeyLds;                // value selectors [token][coordinate]
+    const float* sn = reinterpret_cast<const float*>(sb + kSelLds);  // key norms [64], value norms [64]
+    __syncthreads();
+
+    // ---- stage B: this wave's rows.  Scores: lane (n, h) ends with row n's
+    // scores of tokens 16 h + 4 st + i
+    float sc[16];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      v4i t24 = v4i{0, 0, 0, 0}, t16 = v4i{0, 0, 0, 0}, t8 = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const v4i ah = kk[((2 * st + ks) * 2 + 0) * 64 + lane];
+        const v4i al = kk[((2 * st + ks) * 2 + 1) * 64 + lane];
+        // Q C = 2^24 a Ch + 2^16 (a Cl + b Ch) + 2^8 (b Cl + c Ch) [+ c Cl, below 2^-23 of the product]
+        t24 = mfma(ah, qa[ks], t24);
+        t16 = mfma(al, qa[ks], t16);
+        t8 = mfma(al, qb[ks], t8);
+        t16 = mfma(ah, qb[ks], t16);
+        t8 = mfma(ah, qc[ks], t8);
+      }
+      // 256 t24 + t16 is exact in int32; then one float rounding (2^-24)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[4 * st + i] = fmaf((float)(t24[i] * 256 + t16[i]), 256.f, (float)t8[i]);
+    }
+    stage_a(T0 + kTile);
+
+    // ---- online softmax for row n over tokens tb .. tb+15 held by this lane
+    const int tb = (int)T0 + 16 * h;
+    const v4f* snk = reinterpret_cast<const v4f*>(sn + 16 * h);
+    const v4f* snv = reinterpret_cast<const v4f*>(sn + kTile + 16 * h);
+    float s[16], wv[16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const v4f nk4 = snk[c], nv4 = snv[c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[4 * c + i] = sc[4 * c + i] * nk4[i];  // score / rowc
+        wv[4 * c + i] = nv4[i];
+      }
+    }
+    const bool full = T0 + kTile <= ntok && (int)T0 + kTile <= lim_all;  // no token of the tile is masked
+    if (!full) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int tok = tb + j;
+        if (!(tok < (int)ntok && tok < lim)) s[j] = -INFINITY;
+      }
+    }
+    float tmax = s[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, s[j]);
+    tmax = rowmax4(tmax) * rowc;
+    float vmax = wv[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) vmax = fmaxf(vmax, wv[j]);
+    const bool grow = tmax > m_ref + kFlushGap;
+    const bool vgrow = vmax > nref;
+    if (__ballot(grow || vgrow) != 0) {
+      const float nnew = __ballot(vgrow) != 0 ? kNormHeadroom * wave_max(vmax) : nref;
+      const float m_new = grow ? tmax : m_ref;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+      if (!empty) {  // nothing to move before the wave's first tile
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          v4f o = oref(u);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = fmaf(flushed(ahh[u][i], ax[u][i], all[u][i]), kflush, o[i]) * alpha;
+          oref(u) = o;
+          ahh[u] = v4i{0, 0, 0, 0};
+          ax[u] = v4i{0, 0, 0, 0};
+          all[u] = v4i{0, 0, 0, 0};
+        }
+      }
+      l_run *= alpha;
+      m_ref = m_new;
+      if (nnew > nref) {
+        nref = nnew;
+        const float sig = kQMax / (nref * kProbBound);
+        lsig = __log2f(sig);
+        isig = 1.f / sig;
+        kflush = kappa * isig;
+      }
+    }
+    // p sig = exp2(s - m_ref + lsig); the digits carry p n_v sig
+    const float off = lsig - m_ref;
+    float psum = 0.f;
+    uint32_t qv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float pr = __builtin_amdgcn_exp2f(fmaf(s[j], rowc, off));
+      psum += pr;
+      qv[j] = __float_as_uint(fmaf(pr, wv[j], kDigitBias));
+    }
+    l_run = fmaf(psum, isig, l_run);
+    empty = false;
+    v4i ba, bb, bc;  // digits of 2^16, 2^8 and 1
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t a01 = perm(qv[4 * c + 1], qv[4 * c], 0x05010400u);  // q0.b0 q1.b0 q0.b1 q1.b1
+      const uint32_t a23 = perm(qv[4 * c + 3], qv[4 * c + 2], 0x05010400u);
+      const uint32_t b01 = perm(qv[4 * c + 1], qv[4 * c], 0x0c0c0602u);  // q0.b2 q1.b2 0 0
+      const uint32_t b23 = perm(qv[4 * c + 3], qv[4 * c + 2], 0x0c0c0602u);
+      bc[c] = (int)(perm(a23, a01, 0x05040100u) ^ 0x80808080u);
+      bb[c] = (int)(perm(a23, a01, 0x07060302u) ^ 0x80808080u);
+      ba[c] = (int)perm(b23, b01, 0x05040100u);
+    }
+
+    // ---- values on the matrix cores: coordinates 16u + n of tokens tb..tb+15
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint8_t* a0 = sb + (16 * h + (n >> 1)) * kRow + sel_group_offset(h) + 16 * u + 8 * (n & 1);
+      const v2i r0 = read_tr8(a0);
+      const v2i r1 = read_tr8(a0 + 8 * kRow);
+      const uint32_t sv[4] = {(uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r1.x, (uint32_t)r1.y};
+      const v4i vh = lookup(sv, vh1, vh0), vl = lookup(sv, vl1, vl0);
+      // P' V = 2^24 a Vh + 2^16 (a Vl + b Vh) + 2^8 (b Vl + c Vh) [+ c Vl]
+      ahh[u] = mfma(vh, ba, ahh[u]);
+      ax[u] = mfma(vl, ba, ax[u]);
+      ax[u] = mfma(vh, bb, ax[u]);
+      all[u] = mfma(vl, bb, all[u]);
+      all[u] = mfma(vh, bc, all[u]);
+    }
+  }
+
+  // ---- this wave's rows' partial for the chunk
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (rok) {
+    float* po = p.part_o + (((size_t)bg * p.n_chunks + chunk_id) * rows + rl) * kD;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v4f o = oref(u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = fmaf(flushed(ahh[u][i], ax[u][i], all[u][i]), kflush, o[i]);
+      *reinterpret_cast<v4f*>(po + 16 * u + 4 * h) = o;
+    }
+    if (h == 0) {
+      float* pml = p.part_ml + (((size_t)bg * p.n_chunks + chunk_id) * rows + rl) * 2;
+      pml[0] = m_ref;
+      pml[1] = l_run;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode_fast(const DecodeParams& p, hipStream_t stream) {
@@ -682,6 +988,18 @@ hipError_t launch_decode_fast(const DecodeParams& p, hipStream_t stream) {
       p.rows > 16 || p.chunk > kMaxChunk)
     return hipErrorInvalidValue;
   decode_fast_kernel<<<dim3(p.n_chunks, p.hkv, p.batch), dim3(kThreads), 0, stream>>>(p);
+  merge_fast_kernel<<<dim3(p.rows, p.hkv, p.batch), dim3(kD), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_fast(const DecodeParams& p, hipStream_t stream) {
+  const int n_rg = (p.rows + kPfRows - 1) / kPfRows;
+  if (p.n_chunks < 1 || p.n_chunks > kMaxChunks || p.hkv > 65535 || p.batch > 65535 || p.d != kD || p.rows < 1 ||
+      p.chunk > kPfMaxChunk || p.chunk % kTile || (int64_t)p.n_chunks * n_rg > 65535 || !p.qrot)
+    return hipErrorInvalidValue;
+  hipError_t e = launch_qprep(p, stream);
+  if (e != hipSuccess) return e;
+  prefill_fast_kernel<<<dim3(p.n_chunks * n_rg, p.hkv, p.batch), dim3(kThreads), 0, stream>>>(p);
   merge_fast_kernel<<<dim3(p.rows, p.hkv, p.batch), dim3(kD), 0, stream>>>(p);
   return hipGetLastError();
 }

@@ -198,6 +198,14 @@ bool fast_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, in
 DecodePlan plan_decode_fast(int batch, int hkv, int rows, int d, int64_t max_len);
 hipError_t launch_decode_fast(const DecodeParams& p, hipStream_t stream);
 
+// Prefill on the same codecs: query rows per launch (128 per workgroup), the
+// plan (n_chunks = 0: the lengths need more chunks than the merge takes, and
+// the caller uses the decode path per row block) and the launcher (query
+// prologue, prefill kernel, merge).
+constexpr int kPrefillRows = 1024;
+DecodePlan plan_prefill_fast(int batch, int hkv, int rows, int64_t max_len);
+hipError_t launch_prefill_fast(const DecodeParams& p, hipStream_t stream);
+
 // ---- token-record copies between caches of one codec ----------------------
 
 constexpr int kMaxGatherBatch = 256;  // destination sequences per call

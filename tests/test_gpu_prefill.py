@@ -39,6 +39,11 @@ CASES = [
     ("fast_sharp_q33", 128, (3, 0), (3, 0), 1, 1, 1, 33, [600], 640, False, 200.0),
     # a sequence shorter than q_len: its first rows see no token
     ("fast_short_sequence", 128, (3, 0), (3, 0), 2, 1, 4, 8, [5, 300], 320, True, 0.02),
+    # 512 rows per KV head (four 128-row workgroups) over a ragged batch of
+    # several chunks of 64-token tiles
+    ("fast_512_rows_ragged", 128, (3, 0), (3, 0), 2, 2, 16, 32, [5000, 2100], 5000, True, 0.02),
+    # 1100 rows: two launches (1024 + 76 rows), the second's row groups partly empty
+    ("fast_1100_rows_two_launches", 128, (3, 0), (3, 0), 1, 1, 4, 275, [300], 320, False, 1.0),
     # general path: Prod keys, 4-bit values, 36 rows
     ("general_prod3_mse4_q9", 128, (3, 1), (4, 0), 2, 2, 8, 9, [513, 77], 600, True, 0.02),
     # general path at head_dim 256 (8-row blocks): Prod keys, group values
