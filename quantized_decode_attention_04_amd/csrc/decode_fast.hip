@@ -456,6 +456,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
     }
     const bool full = T0 + kTile <= ntok && (int)T0 + kTile <= lim_all;  // no token of the tile is masked
     if (!full) {
+      // (an empty asm statement keeps the selects behind the wave-uniform
+      // branch: only the last tiles of a chunk take them)
+      asm volatile("");
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int tok = tb + j;
@@ -470,7 +473,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
     const bool grow = tmax > m_ref + kFlushGap;
     const bool vgrow = cur.vn > nref;
     if (__ballot(grow || vgrow) != 0) {
-      const float nnew = __ballot(vgrow) != 0 ? kNormHeadroom * wave_max(cur.vn) : nref;
+      // the tile's largest value norm from this lane's sixteen, then across
+      // the four lane groups (every lane holds the same maximum: the
+      // reference stays wave-uniform)
+      float vmax = fmaxf(fmaxf(wv[0], wv[1]), wv[2]);
+#pragma unroll
+      for (int j = 3; j < 15; j += 2) vmax = fmaxf(fmaxf(vmax, wv[j]), wv[j + 1]);
+      vmax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, rowmax4(fmaxf(vmax, wv[15])))));
+      const float nnew = vmax > nref ? kNormHeadroom * vmax : nref;
       const float m_new = grow ? tmax : m_ref;
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
       if (!empty) {  // nothing to move before the wave's first tile
