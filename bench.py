@@ -342,6 +342,32 @@ def stream_read_reference(tq, dev, stream, reps: int = 10, gib: int = 4) -> dict
     return best
 
 
+def decode_read_reference(tq, kc, vc, kcs, vcs, lens, max_len, dev, stream, reps: int) -> dict:
+    """The decode call's own state reads alone: tq_decode_read_reference over
+    the same layer caches in turn (the int8 decode kernel's grid, chunks, tile
+    loads and prefetch depth, no arithmetic), timed with HIP events on the
+    launch stream around each call."""
+    import torch
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    for K, V in zip(kcs, vcs):
+        tq.tq_decode_read_reference(kc, vc, K, V, lens, max_len, sink)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps) for _ in kcs]
+    i = 0
+    for _ in range(reps):
+        for K, V in zip(kcs, vcs):
+            ev[i][0].record(stream)
+            tq.tq_decode_read_reference(kc, vc, K, V, lens, max_len, sink)
+            ev[i][1].record(stream)
+            i += 1
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1000.0
+    nbytes = int(lens.sum().item()) * kcs[0].heads * (kc.info["bytes_per_token"] + vc.info["bytes_per_token"])
+    return {"kernel": "tq_decode_read_reference: decode_fast_kernel's grid and tile loads with no arithmetic",
+            "state_bytes": nbytes, "us": us, "gbps": nbytes / (us / 1e6) / 1e9}
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -542,6 +568,12 @@ def main():
                   "frac": sbytes / (sms / 1000.0) / 1e9 / HBM_PEAK_GBPS}
         del ws_all, out_all
     stream_ref = stream_read_reference(tq, dev, stream)
+    # the library takes the int8 matrix-core path for d 128 with 3-bit MSE keys
+    # and values and at most 16 query rows per KV head (a label only)
+    rows = (hq // hkv) * qlen
+    fast = d == 128 and (w.kmode, w.kbits, w.vmode, w.vbits) == (0, 3, 0, 3) and rows <= 16
+    read_ref = (decode_read_reference(tq, kc, vc, kcs, vcs, lens, max_len, dev, stream, max(3, args.steps))
+                if fast else None)
 
     tokens_per_step = float(lens_h.sum()) * layers
     value = tokens_per_step / (ms_per_step / 1000.0)
@@ -552,10 +584,6 @@ def main():
     table_bytes = 2 * d * d * 4 + (d * d * 4 if w.kmode == 1 else 0)
     alg_bytes = layer_state_bytes + q_bytes + out_bytes + table_bytes
     achieved = alg_bytes / (dec_ms_avg / 1000.0) / 1e9
-    # the library takes the matrix-core path for d 128 with 3-bit MSE keys and
-    # values and at most 16 query rows per KV head (a label only)
-    rows = (hq // hkv) * qlen
-    fast = d == 128 and (w.kmode, w.kbits, w.vmode, w.vbits) == (0, 3, 0, 3) and rows <= 16
     kcode_bits = w.kbits - 1 if w.kmode == 1 else w.kbits
     bf16_path = (not fast and d in (128, 256) and w.kmode in (0, 1) and kcode_bits in (1, 2)
                  and ((w.vmode == 0 and w.vbits in (1, 2, 4)) or (w.vmode == 2 and w.vbits == 2))
@@ -624,6 +652,8 @@ def main():
             "cache_gather": gather,
             "stream_read_reference": stream_ref,
             "achieved_vs_stream_read": achieved / stream_ref["gbps"],
+            "decode_read_reference": read_ref,
+            "decode_call_vs_its_reads": (read_ref["us"] / (dec_ms_avg * 1000.0)) if read_ref else None,
             "single_launch_all_layers": single,
         },
     }

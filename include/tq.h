@@ -361,6 +361,23 @@ tq_status tq_hybrid_decode_attention(const tq_codec* kc, const tq_codec* vc, con
  * Errors: INVALID_ARG, HIP. */
 tq_status tq_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, int32_t blocks, void* stream);
 
+/* Measurement: read the packed K and V state that tq_decode_attention reads
+ * for these caches (indices and norms of the first len[b] tokens of every
+ * sequence and KV head), once, in the int8 decode kernel's own grid, chunks,
+ * tile loads and prefetch depth, with no arithmetic: the rate that the decode
+ * kernel's access pattern reaches by itself.  Nothing in the library's path
+ * uses it.  Codecs: 3-bit MSE keys and values at head_dim 128 only.
+ *   k, v        device caches [batch][n_kv_heads][cap] (as for decode)
+ *   d_len       device int32 [batch], clamped to 0..cap
+ *   max_len     1..cap, the largest length (sets the chunk plan)
+ *   sink        device uint32[sink_words], caller-owned; written only in the
+ *               rare case that a thread's folded words equal one fixed value
+ * Errors: INVALID_ARG, UNSUPPORTED (other codecs), CONFIG_MISMATCH, CAPACITY,
+ * HIP. */
+tq_status tq_decode_read_reference(const tq_codec* k_codec, const tq_codec* v_codec, int32_t batch,
+                                   int32_t n_kv_heads, const tq_cache* k, const tq_cache* v, const int32_t* d_len,
+                                   int64_t max_len, uint32_t* sink, uint32_t sink_words, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* tq_last_error(void);
 

@@ -32,6 +32,7 @@ from ._binding import (  # noqa: F401
     tq_codec_upload,
     tq_decode_attention,
     tq_decode_attention_noalloc,
+    tq_decode_read_reference,
     tq_decode_workspace_size,
     tq_hybrid_append,
     tq_hybrid_decode_attention,

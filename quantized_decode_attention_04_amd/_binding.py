@@ -75,6 +75,8 @@ def _load() -> ctypes.CDLL:
         "tq_prefill_attention": (I32, [P, P, P, I32, I32, I32, I32, I32, ctypes.POINTER(_Cache),
                                        ctypes.POINTER(_Cache), P, I64, ctypes.c_float, P, P, SZ, P]),
         "tq_stream_read": (I32, [P, U64, P, I32, P]),
+        "tq_decode_read_reference": (I32, [P, P, I32, I32, ctypes.POINTER(_Cache), ctypes.POINTER(_Cache), P, I64,
+                                           P, ctypes.c_uint32, P]),
         "tq_hybrid_append": (I32, [P, P, P, P, I32, I32, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(I64),
                                    ctypes.POINTER(_Cache), ctypes.POINTER(_Cache), P, P, I32, P, I64, P]),
         "tq_hybrid_decode_workspace_size": (I32, [P, P, I32, I32, I32, I32, I64, I32, ctypes.POINTER(SZ)]),
@@ -100,7 +102,7 @@ EXPORTED = (
     "tq_quantize_append", "tq_quantize_append_kv", "tq_decode_workspace_size", "tq_decode_attention",
     "tq_prefill_workspace_size", "tq_prefill_attention", "tq_cache_gather", "tq_stream_read", "tq_last_error",
     "tq_status_string", "tq_decode_attention_noalloc", "tq_codec_create_kv", "tq_codec_create_split", "tq_codec_part",
-    "tq_hybrid_append", "tq_hybrid_decode_workspace_size", "tq_hybrid_decode_attention",
+    "tq_hybrid_append", "tq_hybrid_decode_workspace_size", "tq_hybrid_decode_attention", "tq_decode_read_reference",
 )
 
 
@@ -435,6 +437,26 @@ def tq_stream_read(buf, sink, blocks: int, stream=None) -> None:
         raise ValueError("sink needs blocks * 256 32-bit elements")
     _check(_lib.tq_stream_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_uint64(nbytes),
                                ctypes.c_void_p(sink.data_ptr()), int(blocks), _stream(stream)))
+
+
+def tq_decode_read_reference(kc: Codec, vc: Codec, kcache: Cache, vcache: Cache, lens, max_len: int, sink,
+                             stream=None) -> None:
+    """Measurement: the packed K/V state that tq_decode_attention reads for
+    these caches, read once in the int8 decode kernel's own grid and load
+    pattern with no arithmetic (3-bit MSE head_dim 128 codecs only).
+    ``sink``: a device tensor of 32-bit elements (any length >= 1)."""
+    import torch
+    _on_device(lens, sink, *kcache.arrays().values(), *vcache.arrays().values())
+    if lens.dtype != torch.int32 or not lens.is_contiguous():
+        raise ValueError("lens must be a contiguous int32 tensor of length batch")
+    words = sink.numel() * sink.element_size() // 4
+    if words < 1:
+        raise ValueError("sink needs at least one 32-bit element")
+    ks, vs = kcache.as_struct(), vcache.as_struct()
+    _check(_lib.tq_decode_read_reference(kc.handle, vc.handle, int(kcache.batch), int(kcache.heads),
+                                         ctypes.byref(ks), ctypes.byref(vs), ctypes.c_void_p(lens.data_ptr()),
+                                         int(max_len), ctypes.c_void_p(sink.data_ptr()), ctypes.c_uint32(words),
+                                         _stream(stream)))
 
 
 # ---- hybrid cache (recent-token rings in front of the compressed caches) -------

@@ -950,6 +950,37 @@ tq_status tq_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, int32_
   return TQ_OK;
 }
 
+tq_status tq_decode_read_reference(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t n_kv_heads,
+                                   const tq_cache* k, const tq_cache* v, const int32_t* d_len, int64_t max_len,
+                                   uint32_t* sink, uint32_t sink_words, void* stream) {
+  const std::string fn = "tq_decode_read_reference";
+  if (!kc || !vc || !k || !v || !d_len || !sink) return fail(TQ_ERR_INVALID_ARG, fn + ": NULL argument");
+  if (!k->idx || !k->norm || !v->idx || !v->norm) return fail(TQ_ERR_INVALID_ARG, fn + ": cache buffers missing");
+  if (!use_fast(kc, vc, 16))
+    return fail(TQ_ERR_UNSUPPORTED, fn + ": only the 3-bit MSE head_dim 128 key and value codecs (the int8 decode kernel)");
+  if (batch < 1 || n_kv_heads < 1 || batch > 65535 || n_kv_heads > 65535 || sink_words < 1)
+    return fail(TQ_ERR_INVALID_ARG, fn + ": batch, heads or sink_words out of range");
+  if (k->batch != batch || v->batch != batch || k->heads != n_kv_heads || v->heads != n_kv_heads || k->cap != v->cap)
+    return fail(TQ_ERR_CONFIG_MISMATCH, fn + ": caches disagree with batch / heads");
+  if (max_len < 1 || max_len > k->cap) return fail(TQ_ERR_CAPACITY, fn + ": max_len outside 1..cap");
+  const tq::DecodePlan plan = tq::plan_decode_fast(batch, n_kv_heads, 16, kc->h.d, max_len);
+  tq::DecodeParams p{};
+  p.batch = batch;
+  p.hkv = n_kv_heads;
+  p.d = kc->h.d;
+  p.k_idx = k->idx;
+  p.k_norm = k->norm;
+  p.v_idx = v->idx;
+  p.v_norm = v->norm;
+  p.cap = k->cap;
+  p.len = d_len;
+  p.chunk = plan.chunk;
+  p.n_chunks = plan.n_chunks;
+  const hipError_t e = tq::launch_decode_read(p, sink, sink_words, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, (fn + " launch").c_str());
+  return TQ_OK;
+}
+
 tq_status tq_cache_gather(const tq_codec* src_codec, const tq_cache* src, const tq_codec* dst_codec,
                           const tq_cache* dst, const int32_t* src_batch, const int32_t* src_start,
                           const int32_t* count, void* stream) {

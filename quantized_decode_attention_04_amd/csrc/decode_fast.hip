@@ -988,7 +988,61 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fast_kernel(DecodeParams 
   }
 }
 
+// ---- measurement: the decode kernel's reads alone ----------------------------
+//
+// The same grid, chunks, per-wave tiles, load instructions and two tiles in
+// flight per wave as decode_fast_kernel, reading the packed state of every
+// sequence once and folding the words instead of computing attention: the
+// rate the decode kernel's own access pattern reaches with no arithmetic.
+__global__ __launch_bounds__(kThreads, 1) void decode_read_kernel(DecodeParams p, uint32_t* sink, uint32_t sink_words) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 15, h = lane >> 4;
+  const int chunk_id = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  int64_t len64 = p.len[b];
+  len64 = len64 < 0 ? 0 : (len64 > p.cap ? p.cap : len64);
+  const int len = (int)len64;
+  const int c0 = chunk_id * p.chunk;
+  const int c1 = c0 + p.chunk < len ? c0 + p.chunk : len;
+  const uint32_t ntok = c1 > c0 ? (uint32_t)(c1 - c0) : 0u;
+  const size_t base = (size_t)(b * p.hkv + g) * (size_t)p.cap + (size_t)(ntok > 0 ? c0 : 0);
+  const __amdgpu_buffer_rsrc_t rk = rsrc(p.k_idx + base * 12, ntok * 48u);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(p.v_idx + base * 12, ntok * 48u);
+  const __amdgpu_buffer_rsrc_t rkn = rsrc(p.k_norm + base, ntok * 4u);
+  const __amdgpu_buffer_rsrc_t rvn = rsrc(p.v_norm + base, ntok * 4u);
+  uint32_t lw[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) lw[st] = (uint32_t)(16 * (n >> 2) + 4 * st + (n & 3)) * 48u + 12u * h;
+  const uint32_t ln4 = (uint32_t)lane * 4u;
+  const uint32_t t_first = (uint32_t)(wave * kTile);
+  Tile ta, tb;
+  load_tile(ta, rk, rv, rkn, rvn, lw, ln4, t_first);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(tb, rk, rv, rkn, rvn, lw, ln4, t_first + kStep);
+  uint32_t acc = 0;
+  auto fold = [&](const Tile& t) {
+    uint32_t x = __float_as_uint(t.kn) ^ __float_as_uint(t.vn);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) x ^= t.kw[st].x ^ t.kw[st].y ^ t.kw[st].z ^ t.vw[st].x ^ t.vw[st].y ^ t.vw[st].z;
+    acc = acc * 31u + x;
+  };
+  for (uint32_t T0 = t_first; T0 < ntok; T0 += 2 * kStep) {
+    fold(ta);
+    load_tile(ta, rk, rv, rkn, rvn, lw, ln4, T0 + 2 * kStep);
+    if (T0 + kStep >= ntok) break;
+    fold(tb);
+    load_tile(tb, rk, rv, rkn, rvn, lw, ln4, T0 + 3 * kStep);
+  }
+  if (acc == 0x9E3779B9u) sink[((((size_t)b * p.hkv + g) * gridDim.x + chunk_id) * kThreads + threadIdx.x) % sink_words] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_decode_read(const DecodeParams& p, uint32_t* sink, uint32_t sink_words, hipStream_t stream) {
+  if (p.n_chunks < 1 || p.hkv > 65535 || p.batch > 65535 || p.d != kD || p.chunk < 1 || sink_words < 1)
+    return hipErrorInvalidValue;
+  decode_read_kernel<<<dim3(p.n_chunks, p.hkv, p.batch), dim3(kThreads), 0, stream>>>(p, sink, sink_words);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_fast(const DecodeParams& p, hipStream_t stream) {
   // each wave takes at most chunk / 512 tiles between flushes of its int32

@@ -270,5 +270,8 @@ hipError_t launch_hybrid_combine(const HybridAttn& a, hipStream_t stream);
 // Threads per workgroup of the streaming-read kernel.
 constexpr int kStreamThreads = 256;
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
+// decode_fast_kernel's loads (grid, chunks, tiles, two tiles in flight per
+// wave) over the packed K/V state, with no arithmetic
+hipError_t launch_decode_read(const DecodeParams& p, uint32_t* sink, uint32_t sink_words, hipStream_t stream);
 
 }  // namespace tq

@@ -31,5 +31,9 @@ hipError_t launch_stream_read(const void*, uint64_t, uint32_t*, int, hipStream_t
   ++g_stub_launches;
   return hipErrorNoDevice;
 }
+hipError_t launch_decode_read(const DecodeParams&, uint32_t*, uint32_t, hipStream_t) {
+  ++g_stub_launches;
+  return hipErrorNoDevice;
+}
 
 }  // namespace tq

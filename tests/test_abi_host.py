@@ -271,3 +271,30 @@ def test_cache_gather_argument_errors(no_gpu):
     bad = _fake_cache(3, 2, 100, 0)
     bad.idx = None
     assert gather(s=bad) == 1
+
+
+def test_decode_read_reference_argument_errors(no_gpu):
+    """The decode-pattern read reference refuses other codecs, mismatched
+    caches and lengths outside 1..cap before any launch."""
+    lib = _binding._lib
+    kc = tq.tq_codec_create(128, 3, 0, tq.TQ_MODE_MSE)
+    vc = tq.tq_codec_create(128, 3, 1, tq.TQ_MODE_MSE)
+    k4 = tq.tq_codec_create(128, 4, 0, tq.TQ_MODE_MSE)
+    P = ctypes.c_void_p(0x1000)
+    k, v = _fake_cache(1, 8, 100, 0), _fake_cache(1, 8, 100, 0)
+
+    def rd(kcodec=kc, kcache=k, vcache=v, max_len=100, sink=P, words=1, batch=1, heads=8):
+        return lib.tq_decode_read_reference(kcodec.handle, vc.handle, batch, heads, ctypes.byref(kcache),
+                                            ctypes.byref(vcache), P, max_len, sink, words, None)
+
+    assert rd(sink=None) == 1
+    assert rd(words=0) == 1
+    assert rd(kcodec=k4) == 2
+    assert "3-bit MSE" in tq.tq_last_error()
+    assert rd(heads=4) == 3
+    assert rd(vcache=_fake_cache(1, 8, 99, 0), max_len=50) == 3
+    assert rd(max_len=101) == 4
+    assert rd(max_len=0) == 4
+    bad = _fake_cache(1, 8, 100, 0)
+    bad.idx = None
+    assert rd(kcache=bad) == 1

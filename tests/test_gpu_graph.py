@@ -76,3 +76,28 @@ def test_graph_replays_match_eager(kspec, vspec, n):
         torch.cuda.synchronize()
         assert torch.equal(outs[1], ref[1])
     assert np.isfinite(ref[0].cpu().numpy()).all()
+
+
+def test_decode_read_reference_runs_and_refuses_other_codecs():
+    """The measurement kernel behind bench.py's decode_read_reference reads a
+    ragged batch's state without error (its one possible write stays inside
+    the sink) and refuses codecs the int8 decode kernel does not take."""
+    print("decode read reference", flush=True)
+    dev = torch.device("cuda")
+    B, hkv, d, cap = 3, 2, 128, 5000
+    kc = tq.tq_codec_create(d, 3, 0, tq.TQ_MODE_MSE)
+    vc = tq.tq_codec_create(d, 3, 1, tq.TQ_MODE_MSE)
+    K = tq.allocate_cache(kc, B, hkv, cap, dev)
+    V = tq.allocate_cache(vc, B, hkv, cap, dev)
+    pos0 = torch.zeros(B, dtype=torch.int32, device=dev)
+    kx = wl.device_normal((B, hkv, cap, d), 5, 0, 100, True, dev)
+    vx = wl.device_normal((B, hkv, cap, d), 5, 0, 101, True, dev)
+    tq.tq_quantize_append_kv(kc, vc, kx, vx, K, V, pos0, cap)
+    lens = torch.tensor([5000, 0, 777], dtype=torch.int32, device=dev)
+    sink = torch.zeros(7, dtype=torch.int32, device=dev)
+    tq.tq_decode_read_reference(kc, vc, K, V, lens, cap, sink)
+    torch.cuda.synchronize()
+    k4 = tq.tq_codec_create(d, 4, 0, tq.TQ_MODE_MSE)
+    K4 = tq.allocate_cache(k4, B, hkv, cap, dev)
+    with pytest.raises(tq.TQError, match="3-bit MSE"):
+        tq.tq_decode_read_reference(k4, vc, K4, V, lens, cap, sink)
