@@ -564,7 +564,7 @@ static tq_status check_decode_shapes(const tq_codec* kc, const tq_codec* vc, int
 // The decode path and its plan for these sizes: one function for the
 // workspace size queries and the calls, so that a workspace sized through the
 // API always fits the call.
-enum class DecodePath { kFast, kMfma, kGeneral, kPrefillFast };
+enum class DecodePath { kFast, kMfma, kGeneral, kPrefillFast, kPrefillBf16 };
 
 static tq::DecodePlan choose_plan(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t hq, int32_t hkv,
                                   int32_t q_len, int64_t max_len, DecodePath* path, bool blocks = false) {
@@ -578,6 +578,16 @@ static tq::DecodePlan choose_plan(const tq_codec* kc, const tq_codec* vc, int32_
     const tq::DecodePlan pp = tq::plan_prefill_fast(batch, hkv, prows, max_len);
     if (pp.n_chunks > 0) {
       *path = DecodePath::kPrefillFast;
+      return pp;
+    }
+  }
+  // prefill on the bf16 / int8 kernel's codecs at head_dim 128: likewise
+  if (blocks && rows_total > 16 && kc->h.d == 128 &&
+      tq::bf16_decode_supported(kc->h.d, kc->h.mode, kc->h.mse_bits, vc->h.mode, vc->h.mse_bits, 1)) {
+    const int prows = (int)std::min<int64_t>(rows_total, tq::kPrefillRows);
+    const tq::DecodePlan pp = tq::plan_prefill_bf16(batch, hkv, prows, max_len);
+    if (pp.n_chunks > 0) {
+      *path = DecodePath::kPrefillBf16;
       return pp;
     }
   }
@@ -641,8 +651,9 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
   const bool prod = kc->h.mode == TQ_MODE_PROD;
   DecodePath path;
   const tq::DecodePlan plan = choose_plan(kc, vc, batch, hq, hkv, q_len, max_len, &path, blocks);
-  const bool prefill = path == DecodePath::kPrefillFast;
-  const bool fast = path == DecodePath::kFast || prefill;
+  const bool prefill_bf16 = path == DecodePath::kPrefillBf16;
+  const bool prefill = path == DecodePath::kPrefillFast || prefill_bf16;
+  const bool fast = path == DecodePath::kFast || path == DecodePath::kPrefillFast;
   const bool mfma = path == DecodePath::kMfma;
   if (!ws || ws_bytes < plan.total)
     return fail(TQ_ERR_WORKSPACE, fn + ": workspace needs " + std::to_string(plan.total) + " bytes");
@@ -720,7 +731,8 @@ static tq_status attention_impl(const char* name, bool blocks, const tq_codec* k
   for (int64_t r0 = 0; r0 < rows_total; r0 += block) {
     p.row0 = (int)r0;
     p.rows = (int)std::min<int64_t>(block, rows_total - r0);
-    const hipError_t e = prefill ? tq::launch_prefill_fast(p, static_cast<hipStream_t>(stream))
+    const hipError_t e = prefill_bf16 ? tq::launch_prefill_bf16(p, static_cast<hipStream_t>(stream))
+                         : prefill ? tq::launch_prefill_fast(p, static_cast<hipStream_t>(stream))
                          : fast  ? tq::launch_decode_fast(p, static_cast<hipStream_t>(stream))
                          : mfma  ? tq::launch_decode_mfma(p, static_cast<hipStream_t>(stream))
                                  : tq::launch_decode(p, static_cast<hipStream_t>(stream));

@@ -627,6 +627,448 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
   }
 }
 
+// ---- prefill: many query rows over shared tiles ------------------------------
+//
+// A launch with more query rows per KV head than the decode kernel takes
+// would expand every tile's codes once per 16 rows.  Here the eight waves of a
+// workgroup each own 16 rows of the same KV head (head_dim 128) and walk the
+// chunk's 64-token tiles together.  Per tile, wave w expands its share of the
+// operands the decode kernel's lanes build for themselves -- the int8 key
+// pieces of (token group w/2, K-step w%2), the QJL sign operands of two
+// (token group, k-step) pairs, the value operands of two (half, coordinate)
+// pairs -- into one of two LDS buffers, and wave 0 the tile's per-token norms;
+// after one barrier every wave runs its own rows' products, softmax and value
+// products over all of them.  A wave that reaches the barrier of tile t has
+// finished with tile t-1's buffer, which the expansion of tile t+1 (after
+// that barrier) then overwrites.  The rows' operands (int8 query digits, the
+// QJL pieces) come from qprep_kernel's rotated rows and stay in registers;
+// each wave writes its rows' partial (m, l, o) for the chunk, merged by
+// merge_kernel.
+constexpr int kPbWaves = 8;
+constexpr int kPbRows = kPbWaves * 16;  // rows per workgroup
+
+template <int KB, int VB, bool PROD, bool VGROUP>
+struct PbLayout {
+  static constexpr int D = 128, KS = D / 32, KS8 = D / 64, TG = 4, kTile = 64, NU = D / 16;
+  static constexpr int kKey = TG * KS8 * 2 * 64 * 16;             // [tg][ks][hi, lo][lane] v4i
+  static constexpr int kQjl = PROD ? TG * KS * 64 * 16 : 0;       // [tg][s][lane] v4u
+  static constexpr int kVal = (TG / 2) * NU * 2 * 64 * 16;        // [h][u][hi, lo][lane] v4u
+  static constexpr int kFld = 3 * kTile * 4;                      // kn, kq, vn per token
+  static constexpr int kBuf = kKey + kQjl + kVal + kFld;
+};
+
+template <int KB, int VB, bool PROD, bool VGROUP>
+__global__ __launch_bounds__(kPbWaves * 64, 1) void prefill_bf16_kernel(DecodeParams p) {
+  using Lay = PbLayout<KB, VB, PROD, VGROUP>;
+  constexpr int D = 128;
+  constexpr int KS = Lay::KS, KS8 = Lay::KS8, TG = Lay::TG, kTile = Lay::kTile, NU = Lay::NU;
+  constexpr int LC = D / 4;
+  constexpr int KW = KB * LC / 32;
+  constexpr int SW = LC / 32;
+  constexpr int NT = 4 * TG;
+  constexpr int VRB = NU * VB;
+  constexpr int VW = (VRB + 31) / 32;
+  constexpr uint32_t VMASK = (1u << VB) - 1u;
+  constexpr int kBuf = Lay::kBuf;
+  static_assert(!VGROUP || VB == 2, "group values of 2 bits");
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[2 * kBuf];
+  __shared__ uint32_t s_vt[16];  // MSE value centroid c: bf16 hi | lo << 16
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  const int chunk_id = blockIdx.x % p.n_chunks, rg = blockIdx.x / p.n_chunks;
+  const int gh = blockIdx.y, b = blockIdx.z;
+  const int bg = b * p.hkv + gh;
+  const int rows = p.rows;
+  const int rl = rg * kPbRows + wave * 16 + m;  // this lane's row among the launch's rows
+  const bool rok = rl < rows;
+  int64_t len64 = p.len[b];
+  len64 = len64 < 0 ? 0 : (len64 > p.cap ? p.cap : len64);
+  const int len = (int)len64;
+  const int c0 = chunk_id * p.chunk;
+  const int ntok = (c0 + p.chunk < len ? c0 + p.chunk : len) - c0;  // may be <= 0
+  const int lenm = p.len_mask ? (p.len_mask[b] < 0 ? 0 : p.len_mask[b]) : len;
+  const int lim = lenm - p.q_len + ((p.row0 + rl) % p.q_len) + 1 - c0;  // row rl sees tokens < lim
+
+  if constexpr (!VGROUP) {
+    if (threadIdx.x < 16) {
+      uint32_t hi = 0, lo = 0;
+      if (threadIdx.x <= VMASK) split_rne(p.v_cent[threadIdx.x], hi, lo);
+      s_vt[threadIdx.x] = hi | (lo << 16);
+    }
+  }
+  const float qjl = p.scale * kLog2e * kQjlConstNumer / (float)D;
+  const size_t base = (size_t)bg * (size_t)p.cap + (size_t)(c0 > 0 ? c0 : 0);
+  const char* kidx = reinterpret_cast<const char*>(p.k_idx + base * p.kwords);
+  const char* ksgn = PROD ? reinterpret_cast<const char*>(p.k_sign + base * p.ksign_words) : nullptr;
+  const char* knrm = reinterpret_cast<const char*>(p.k_norm + base);
+  const char* krnm = PROD ? reinterpret_cast<const char*>(p.k_rnorm + base) : nullptr;
+  const char* vnrm = VGROUP ? nullptr : reinterpret_cast<const char*>(p.v_norm + base);
+  const char* vscl = VGROUP ? reinterpret_cast<const char*>(p.v_scale + base * p.vgroups) : nullptr;
+  const char* vmin = VGROUP ? reinterpret_cast<const char*>(p.v_gmin + base * p.vgroups) : nullptr;
+  const char* vidx = reinterpret_cast<const char*>(p.v_idx + base * p.vwords);
+  const uint32_t kstride = 4u * p.kwords, sstride = 4u * p.ksign_words, vstride = 4u * p.vwords;
+  const uint32_t gstride = 4u * p.vgroups;
+  const uint32_t koff = 4u * g * KW, soff = 4u * g * SW, voff = 4u * ((m * VRB) >> 5);
+  const uint32_t goff = 4u * ((m * NU) >> 5);
+  const int vshift = (m * VRB) & 31;
+  // a token index of the chunk, clamped to a valid one (tokens past the end
+  // are read from the last token, or token 0 of an empty chunk, and masked)
+  auto tok = [&](int t) -> uint32_t { return (uint32_t)max(min(t, ntok - 1), 0); };
+
+  // ---- this wave's share of the expansion: key group ktg, K-step kks; QJL
+  // pairs (tg, s) = (w/2, 2(w%2) + j); value pairs (h, u) = (w/4, 2(w%4) + j)
+  const int ktg = wave >> 1, kks = wave & 1;
+  const int qtg = wave >> 1, qs0 = 2 * (wave & 1);
+  const int vh = wave >> 2, vu0 = 2 * (wave & 3);
+  uint32_t rkw[KW], rsw = 0u;
+  uint32_t rvw[8][VW];
+  float rvs[8], rvm[8];
+  float rfk = 0.f, rfq = 0.f, rfv = 0.f;
+  auto stage_load = [&](int T0) {
+    {
+      const uint32_t t = tok(T0 + 16 * ktg + m);
+#pragma unroll
+      for (int w = 0; w < KW; ++w) rkw[w] = ld<uint32_t>(kidx, __umul24(t, kstride) + koff + 4u * w);
+    }
+    if constexpr (PROD) {
+      const uint32_t t = tok(T0 + 16 * qtg + m);
+      rsw = ld<uint32_t>(ksgn, __umul24(t, sstride) + soff + 4u * (qs0 >> 2));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t t = tok(T0 + 16 * (2 * vh + (i >> 2)) + 4 * g + (i & 3));
+#pragma unroll
+      for (int w = 0; w < VW; ++w) rvw[i][w] = ld<uint32_t>(vidx, __umul24(t, vstride) + voff + 4u * w);
+      if constexpr (VGROUP) {
+        rvs[i] = ld<float>(vscl, __umul24(t, gstride) + goff);
+        rvm[i] = ld<float>(vmin, __umul24(t, gstride) + goff);
+      }
+    }
+    if (wave == 0) {
+      const uint32_t t = tok(T0 + lane);
+      rfk = ld<float>(knrm, 4u * t);
+      if constexpr (PROD) rfq = ld<float>(krnm, 4u * t) * qjl;
+      if constexpr (!VGROUP) rfv = ld<float>(vnrm, 4u * t);
+    }
+  };
+  const uint32_t kth = p.klut[0], ktl = p.klut[2];
+  auto stage_expand = [&](int T0) {
+    uint8_t* buf = s_buf + ((T0 / kTile) & 1) * kBuf;
+    v4i* kop = reinterpret_cast<v4i*>(buf);
+    v4u* qop = reinterpret_cast<v4u*>(buf + Lay::kKey);
+    v4u* vop = reinterpret_cast<v4u*>(buf + Lay::kKey + Lay::kQjl);
+    float* fld = reinterpret_cast<float*>(buf + Lay::kKey + Lay::kQjl + Lay::kVal);
+    {
+      v4i ah, al;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = key_sel8<KB>(rkw, kks, e);
+        ah[e] = (int)perm(0u, kth, x);
+        al[e] = (int)perm(0u, ktl, x);
+      }
+      kop[((ktg * KS8 + kks) * 2 + 0) * 64 + lane] = ah;
+      kop[((ktg * KS8 + kks) * 2 + 1) * 64 + lane] = al;
+    }
+    if constexpr (PROD) {
+      const uint32_t ns = ~rsw;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int s = qs0 + j;
+        v4u as;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // bits k and k + 16 of the negated signs become the bf16 sign bits
+          const int k = 4 * (s & 3) + e;
+          as[e] = ((ns & (0x00010001u << k)) << (15 - k)) | 0x3f803f80u;
+        }
+        qop[(qtg * KS + s) * 64 + lane] = as;
+      }
+    }
+    uint32_t run[8][VW];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int w = 0; w < VW; ++w) run[i][w] = VW == 1 ? rvw[i][w] >> vshift : rvw[i][w];
+    if constexpr (VGROUP) {
+      uint32_t th[8][2], tl[8][2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float sg = rvs[i], mn = rvm[i];
+        split_pair(mn, mn + sg, th[i][0], tl[i][0]);
+        split_pair(fmaf(2.f, sg, mn), fmaf(3.f, sg, mn), th[i][1], tl[i][1]);
+      }
+      // coordinates u and u + NU/2 of the run (the wave's one u of NU/2 = 4),
+      // stored as (h, u) and (h, u + NU/2)
+      {
+        const int u = wave & 3;
+        v4u ah0, al0, ah1, al1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ia = 2 * e, ib = 2 * e + 1;
+          const uint32_t sa = pair_selector<NU>(run[ia][0], u);
+          const uint32_t sb = pair_selector<NU>(run[ib][0], u);
+          const uint32_t xa = perm(th[ia][1], th[ia][0], sa), xb = perm(th[ib][1], th[ib][0], sb);
+          const uint32_t ya = perm(tl[ia][1], tl[ia][0], sa), yb = perm(tl[ib][1], tl[ib][0], sb);
+          ah0[e] = perm(xb, xa, 0x05040100u);
+          ah1[e] = perm(xb, xa, 0x07060302u);
+          al0[e] = perm(yb, ya, 0x05040100u);
+          al1[e] = perm(yb, ya, 0x07060302u);
+        }
+        vop[((vh * NU + u) * 2 + 0) * 64 + lane] = ah0;
+        vop[((vh * NU + u) * 2 + 1) * 64 + lane] = al0;
+        vop[((vh * NU + u + NU / 2) * 2 + 0) * 64 + lane] = ah1;
+        vop[((vh * NU + u + NU / 2) * 2 + 1) * 64 + lane] = al1;
+      }
+    } else {
+      constexpr int TPB = 8 / VB;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int u = vu0 + j;
+        constexpr int kBitsPerWord = 32;
+        const int bit = u * VB, w = bit / kBitsPerWord, byte = (bit % kBitsPerWord) / 8;
+        const int t = u % TPB;
+        const int sh = 2 - VB * t;
+        v4u ah, al;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // LDS byte offsets of the two tokens' codes (4 x the code), byte
+          // `byte` zero-extended (selector 0x0c gives a zero byte)
+          const uint32_t xa = run[2 * e][w], xc = run[2 * e + 1][w];
+          const uint32_t va = (sh >= 0 ? (xa << sh) : (xa >> -sh)) & (0x01010101u * (VMASK << 2));
+          const uint32_t vc = (sh >= 0 ? (xc << sh) : (xc >> -sh)) & (0x01010101u * (VMASK << 2));
+          const uint32_t bsel = 0x0c0c0c00u + (uint32_t)byte;
+          const uint32_t oa = perm(0u, va, bsel), oc = perm(0u, vc, bsel);
+          const uint32_t ta = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(s_vt) + oa);
+          const uint32_t tc = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(s_vt) + oc);
+          ah[e] = perm(tc, ta, 0x05040100u);
+          al[e] = perm(tc, ta, 0x07060302u);
+        }
+        vop[((vh * NU + u) * 2 + 0) * 64 + lane] = ah;
+        vop[((vh * NU + u) * 2 + 1) * 64 + lane] = al;
+      }
+    }
+    if (wave == 0) {
+      fld[lane] = rfk;
+      fld[kTile + lane] = rfq;
+      fld[2 * kTile + lane] = rfv;
+    }
+  };
+
+  // ---- the rows' operands (registers): int8 digits of q_rot row rl, and the
+  // QJL pieces of (S q_rot) row rl, in the decode kernel's lane layout
+  v4i qa[KS8], qb[KS8], qc[KS8];
+  v4u qh[KS], ql[KS];
+  float rowc;
+  {
+    const size_t qoff = ((size_t)bg * rows + (rok ? rl : 0)) * D + LC * g;
+    float qv[LC];
+#pragma unroll
+    for (int c = 0; c < LC; c += 4) {
+      const v4f x = rok ? *reinterpret_cast<const v4f*>(p.qrot + qoff + c) : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qv[c + t] = x[t];
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int c = 0; c < LC; ++c) mx = fmaxf(mx, fabsf(qv[c]));
+    mx = rowmax4(mx);
+    const float sc = mx > 0.f ? kQMax / mx : 0.f;
+    rowc = mx > 0.f ? p.scale * kLog2e * 256.f * exp2f(-(float)p.kgrid) / sc : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t u[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          // the product may round one past the bound: clamp so the top digit fits
+          const float x = fminf(fmaxf(rintf(qv[kstep_coord<KB>(ks, e, bb)] * sc), -kQMax), kQMax);
+          u[bb] = (uint32_t)((int)x + 0x808080);  // bytes 2, 1, 0: a, b, c, each + 128
+        }
+        const uint32_t lo01 = perm(u[1], u[0], 0x05010400u);
+        const uint32_t lo23 = perm(u[3], u[2], 0x05010400u);
+        const uint32_t hi01 = perm(u[1], u[0], 0x0c0c0602u);
+        const uint32_t hi23 = perm(u[3], u[2], 0x0c0c0602u);
+        qa[ks][e] = (int)(perm(hi23, hi01, 0x05040100u) ^ 0x80808080u);
+        qb[ks][e] = (int)(perm(lo23, lo01, 0x07060302u) ^ 0x80808080u);
+        qc[ks][e] = (int)(perm(lo23, lo01, 0x05040100u) ^ 0x80808080u);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qh[s] = v4u{0u, 0u, 0u, 0u};
+      ql[s] = v4u{0u, 0u, 0u, 0u};
+      if constexpr (PROD) {
+        const float* qsr = p.qs + qoff + 32 * (s >> 2) + 4 * (s & 3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t h, l;
+          split_pair(rok ? qsr[e] : 0.f, rok ? qsr[e + 16] : 0.f, h, l);
+          qh[s][e] = h;
+          ql[s][e] = l;
+        }
+      }
+    }
+  }
+
+  if (ntok > 0) {
+    stage_load(0);
+    __syncthreads();  // s_vt
+    stage_expand(0);
+    stage_load(kTile);
+  }
+  float m_ref = -1e30f, l_run = 0.f;
+  v4f acc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int T0 = 0; T0 < ntok; T0 += kTile) {
+    const uint8_t* buf = s_buf + ((T0 / kTile) & 1) * kBuf;
+    const v4i* kop = reinterpret_cast<const v4i*>(buf);
+    const v4u* qop = reinterpret_cast<const v4u*>(buf + Lay::kKey);
+    const v4u* vop = reinterpret_cast<const v4u*>(buf + Lay::kKey + Lay::kQjl);
+    const float* fld = reinterpret_cast<const float*>(buf + Lay::kKey + Lay::kQjl + Lay::kVal);
+    __syncthreads();
+
+    // ---- scores of this wave's rows: MSE term on the int8 matrix cores, QJL
+    // term on the bf16 ones (lane (m, g) ends with row m's scores of tokens
+    // 16 tg + 4 g + r)
+    v4f sm[TG], sq[TG];
+    {
+      v4i t24[TG], t16[TG], t8[TG];
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) t24[tg] = t16[tg] = t8[tg] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < KS8; ++ks) {
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
+          const v4i ah = kop[((tg * KS8 + ks) * 2 + 0) * 64 + lane];
+          const v4i al = kop[((tg * KS8 + ks) * 2 + 1) * 64 + lane];
+          t24[tg] = mfma8(ah, qa[ks], t24[tg]);
+          t16[tg] = mfma8(al, qa[ks], t16[tg]);
+          t8[tg] = mfma8(al, qb[ks], t8[tg]);
+          t16[tg] = mfma8(ah, qb[ks], t16[tg]);
+          t8[tg] = mfma8(ah, qc[ks], t8[tg]);
+        }
+      }
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int lo = (int)(((uint32_t)t16[tg][i] << 8) + (uint32_t)t8[tg][i]);
+          sm[tg][i] = rowc * fmaf(65536.f, (float)t24[tg][i], (float)lo);
+        }
+    }
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) sq[tg] = v4f{0.f, 0.f, 0.f, 0.f};
+    if constexpr (PROD) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
+          const v4u as = qop[(tg * KS + s) * 64 + lane];
+          sq[tg] = mfma(as, qh[s], sq[tg]);
+          sq[tg] = mfma(as, ql[s], sq[tg]);
+        }
+    }
+
+    // the next tile's share, into the other buffer (every wave finished with
+    // it before this tile's barrier), and the loads of the one after
+    if (T0 + kTile < ntok) {
+      stage_expand(T0 + kTile);
+      stage_load(T0 + 2 * kTile);
+    }
+
+    // ---- online softmax of row m over this lane's NT tokens
+    float sc[NT];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int tk = T0 + 16 * (i >> 2) + 4 * g + (i & 3);
+      const float kn = fld[tk - T0], kq = fld[kTile + tk - T0];
+      const float raw = PROD ? fmaf(kn, sm[i >> 2][i & 3], kq * sq[i >> 2][i & 3]) : kn * sm[i >> 2][i & 3];
+      const float v = (tk < ntok && tk < lim) ? raw : -INFINITY;
+      sc[i] = v;
+      tmax = fmaxf(tmax, v);
+    }
+    tmax = rowmax4(tmax);
+    if (__ballot(tmax > m_ref + kFlushGap) != 0) {
+      const float m_new = fmaxf(m_ref, tmax);
+      const float alpha = exp2f(m_ref - m_new);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) acc[u] *= alpha;
+      l_run *= alpha;
+      m_ref = m_new;
+    }
+    float pv[NT];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const float pr = exp2f(sc[i] - m_ref);
+      psum += pr;
+      pv[i] = VGROUP ? pr : pr * fld[2 * kTile + 16 * (i >> 2) + 4 * g + (i & 3)];
+    }
+    l_run += psum;
+
+    // ---- values: half h takes the lane's tokens i = 8 h .. 8 h + 7
+#pragma unroll
+    for (int h = 0; h < TG / 2; ++h) {
+      v4u bh, bl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t a = __float_as_uint(pv[8 * h + 2 * e]), c = __float_as_uint(pv[8 * h + 2 * e + 1]);
+        bh[e] = perm(c, a, 0x07060302u);
+        const float ra = pv[8 * h + 2 * e] - __uint_as_float(a & 0xffff0000u);
+        const float rc = pv[8 * h + 2 * e + 1] - __uint_as_float(c & 0xffff0000u);
+        bl[e] = perm(__float_as_uint(rc), __float_as_uint(ra), 0x07060302u);
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const v4u ah = vop[((h * NU + u) * 2 + 0) * 64 + lane];
+        const v4u al = vop[((h * NU + u) * 2 + 1) * 64 + lane];
+        acc[u] = mfma(ah, bh, acc[u]);
+        acc[u] = mfma(ah, bl, acc[u]);
+        acc[u] = mfma(al, bh, acc[u]);
+      }
+    }
+  }
+
+  // ---- this wave's rows' partial for the chunk
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (rok) {
+    const size_t slot = ((size_t)bg * p.n_chunks + chunk_id) * rows + rl;
+    float* po = p.part_o + slot * D;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) po[(4 * g + r) * NU + u] = acc[u][r];
+    if (g == 0) {
+      p.part_ml[2 * slot] = m_ref;
+      p.part_ml[2 * slot + 1] = l_run;
+    }
+  }
+}
+
+template <int KB, bool PROD>
+hipError_t launch_pb_vb(const DecodeParams& p, const dim3 grid, hipStream_t stream) {
+  const dim3 block(kPbWaves * 64);
+  if (p.vmode == TQ_MODE_GROUP) {
+    if (p.vbits != 2) return hipErrorInvalidValue;
+    prefill_bf16_kernel<KB, 2, PROD, true><<<grid, block, 0, stream>>>(p);
+    return hipGetLastError();
+  }
+  switch (p.vbits) {
+    case 1: prefill_bf16_kernel<KB, 1, PROD, false><<<grid, block, 0, stream>>>(p); break;
+    case 2: prefill_bf16_kernel<KB, 2, PROD, false><<<grid, block, 0, stream>>>(p); break;
+    case 4: prefill_bf16_kernel<KB, 4, PROD, false><<<grid, block, 0, stream>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int D, int KB, bool PROD>
 hipError_t launch_vb(const DecodeParams& p, const dim3 grid, hipStream_t stream) {
   const dim3 block(kWaves * 64);
@@ -656,6 +1098,28 @@ hipError_t launch_d(const DecodeParams& p, const dim3 grid, hipStream_t stream) 
 // The decode kernel of this file for a launch that bf16_decode_supported
 // accepts; the query prologue and the merge are the caller's.  Token indices
 // inside a chunk use 24-bit products: chunks hold at most 2^24 tokens.
+// qprep_kernel (the rotated rows), prefill_bf16_kernel over row groups of 128
+// and chunks of the plan, merge_kernel; head_dim 128 and the codecs
+// bf16_decode_supported accepts.  Token indices inside a chunk use 24-bit
+// products: chunks hold at most 2^24 tokens.
+hipError_t launch_prefill_bf16(const DecodeParams& p, hipStream_t stream) {
+  if (p.d != 128 || !bf16_decode_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits, 1) || p.rows < 1 ||
+      p.n_chunks < 1 || p.chunk % 64 || p.chunk > (1 << 24) || p.hkv > 65535 || p.batch > 65535)
+    return hipErrorInvalidValue;
+  const int64_t n_rg = (p.rows + kPbRows - 1) / kPbRows;
+  if ((int64_t)p.n_chunks * n_rg > 0x7fffffff) return hipErrorInvalidValue;
+  hipError_t e = launch_qprep(p, stream);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)(p.n_chunks * n_rg), p.hkv, p.batch);
+  const bool prod = p.kmode == TQ_MODE_PROD;
+  if (p.kbits == 1)
+    e = prod ? launch_pb_vb<1, true>(p, grid, stream) : launch_pb_vb<1, false>(p, grid, stream);
+  else
+    e = prod ? launch_pb_vb<2, true>(p, grid, stream) : launch_pb_vb<2, false>(p, grid, stream);
+  if (e != hipSuccess) return e;
+  return launch_merge(p, stream);
+}
+
 hipError_t launch_decode_bf16_kernel(const DecodeParams& p, const dim3 grid, hipStream_t stream) {
   if (!bf16_decode_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits, p.rows) || p.chunk % kStep ||
       p.chunk > (1 << 24))

@@ -189,4 +189,37 @@ DecodePlan plan_prefill_fast(int batch, int hkv, int rows, int64_t max_len) {
   return p;
 }
 
+DecodePlan plan_prefill_bf16(int batch, int hkv, int rows, int64_t max_len) {
+  DecodePlan p{};
+  p.rows = rows;
+  const int64_t tile = 64;                    // every wave walks every tile of its chunk
+  const int64_t max_chunks = 4096;            // the merge kernel's weights in LDS
+  const int64_t row_groups = (rows + 127) / 128;
+  const int64_t units = (int64_t)batch * hkv * row_groups;
+  // about one workgroup per compute unit (one fits, at 130 KB of LDS)
+  const int64_t per = std::max<int64_t>(1, (device_cus() + units - 1) / units);
+  int64_t chunk = (max_len + per - 1) / per;
+  if (batch > 1) chunk = std::min<int64_t>(chunk, kRaggedChunk);  // as in plan_decode_mfma
+  chunk = std::max<int64_t>(tile, (chunk + tile - 1) / tile * tile);
+  chunk = std::max<int64_t>(chunk, ((max_len + max_chunks - 1) / max_chunks + tile - 1) / tile * tile);
+  if (chunk > ((int64_t)1 << 24) || ((max_len + chunk - 1) / chunk) * row_groups > 0x7fffffff) {
+    p.n_chunks = 0;  // the caller falls back to row blocks
+    return p;
+  }
+  p.chunk = (int)chunk;
+  p.n_chunks = (int)((max_len + chunk - 1) / chunk);
+  const size_t bg = (size_t)batch * hkv;
+  size_t off = 0;
+  p.off_qrot = off;
+  off = align256(off + bg * rows * 128 * sizeof(float));
+  p.off_qs = off;
+  off = align256(off + bg * rows * 128 * sizeof(float));
+  p.off_part_o = off;
+  off = align256(off + bg * p.n_chunks * rows * 128 * sizeof(float));
+  p.off_part_ml = off;
+  off = align256(off + bg * p.n_chunks * rows * 2 * sizeof(float));
+  p.total = off;
+  return p;
+}
+
 }  // namespace tq

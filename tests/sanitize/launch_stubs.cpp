@@ -20,6 +20,7 @@ hipError_t launch_decode_bf16_kernel(const DecodeParams&, const dim3, hipStream_
 hipError_t launch_decode_mfma(const DecodeParams&, hipStream_t) { ++g_stub_launches; return hipErrorNoDevice; }
 hipError_t launch_decode_fast(const DecodeParams&, hipStream_t) { ++g_stub_launches; return hipErrorNoDevice; }
 hipError_t launch_prefill_fast(const DecodeParams&, hipStream_t) { ++g_stub_launches; return hipErrorNoDevice; }
+hipError_t launch_prefill_bf16(const DecodeParams&, hipStream_t) { ++g_stub_launches; return hipErrorNoDevice; }
 hipError_t launch_cache_gather(const CacheGather&, int64_t, hipStream_t) { ++g_stub_launches; return hipErrorNoDevice; }
 hipError_t launch_hybrid_stage(const HybridStage&, hipStream_t) { ++g_stub_launches; return hipErrorNoDevice; }
 hipError_t launch_hybrid_lens(const int32_t*, int32_t*, int, int, hipStream_t) {

@@ -48,6 +48,17 @@ CASES = [
     ("general_prod3_mse4_q9", 128, (3, 1), (4, 0), 2, 2, 8, 9, [513, 77], 600, True, 0.02),
     # general path at head_dim 256 (8-row blocks): Prod keys, group values
     ("general_d256_prod3_group2_q7", 256, (3, 1), (2, 2), 1, 1, 2, 7, [300], 320, True, 0.02),
+    # shared-tile kernel of the bf16 / int8 codecs (head_dim 128): 256 rows per
+    # KV head (two 128-row workgroups) over a ragged batch of several chunks
+    ("bf16_prod3_mse4_256_rows_ragged", 128, (3, 1), (4, 0), 2, 2, 16, 16, [5000, 2100], 5000, True, 0.02),
+    # group values, MSE keys of 2 bits, 40 rows (one workgroup, its last 88 rows empty)
+    ("bf16_mse2_group2_q5", 128, (2, 0), (2, 2), 1, 2, 16, 5, [1500], 1536, True, 0.02),
+    # 1-bit key codes with QJL signs, 1-bit values, a sharp softmax over 33 rows
+    ("bf16_prod2_mse1_sharp_q33", 128, (2, 1), (1, 0), 1, 1, 1, 33, [777], 800, False, 200.0),
+    # 2-bit values; every token new (row i sees tokens 0..i), 130 rows
+    ("bf16_prod3_mse2_self_attention_q130", 128, (3, 1), (2, 0), 1, 1, 1, 130, [130], 160, False, 1.0),
+    # 1100 rows: two launches (1024 + 76 rows)
+    ("bf16_prod3_mse4_1100_rows_two_launches", 128, (3, 1), (4, 0), 1, 1, 4, 275, [300], 320, False, 1.0),
 ]
 
 
