@@ -581,11 +581,12 @@ static tq::DecodePlan choose_plan(const tq_codec* kc, const tq_codec* vc, int32_
       return pp;
     }
   }
-  // prefill on the bf16 / int8 kernel's codecs at head_dim 128: likewise
-  if (blocks && rows_total > 16 && kc->h.d == 128 &&
+  // prefill on the bf16 / int8 kernel's codecs: likewise, per 128 rows at
+  // head_dim 128 and per 64 at 256
+  if (blocks && rows_total > row_block(kc) &&
       tq::bf16_decode_supported(kc->h.d, kc->h.mode, kc->h.mse_bits, vc->h.mode, vc->h.mse_bits, 1)) {
     const int prows = (int)std::min<int64_t>(rows_total, tq::kPrefillRows);
-    const tq::DecodePlan pp = tq::plan_prefill_bf16(batch, hkv, prows, max_len);
+    const tq::DecodePlan pp = tq::plan_prefill_bf16(batch, hkv, prows, kc->h.d, max_len);
     if (pp.n_chunks > 0) {
       *path = DecodePath::kPrefillBf16;
       return pp;

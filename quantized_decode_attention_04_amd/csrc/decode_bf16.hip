@@ -630,37 +630,45 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
 // ---- prefill: many query rows over shared tiles ------------------------------
 //
 // A launch with more query rows per KV head than the decode kernel takes
-// would expand every tile's codes once per 16 rows.  Here the eight waves of a
-// workgroup each own 16 rows of the same KV head (head_dim 128) and walk the
-// chunk's 64-token tiles together.  Per tile, wave w expands its share of the
-// operands the decode kernel's lanes build for themselves -- the int8 key
-// pieces of (token group w/2, K-step w%2), the QJL sign operands of two
-// (token group, k-step) pairs, the value operands of two (half, coordinate)
-// pairs -- into one of two LDS buffers, and wave 0 the tile's per-token norms;
-// after one barrier every wave runs its own rows' products, softmax and value
-// products over all of them.  A wave that reaches the barrier of tile t has
-// finished with tile t-1's buffer, which the expansion of tile t+1 (after
-// that barrier) then overwrites.  The rows' operands (int8 query digits, the
-// QJL pieces) come from qprep_kernel's rotated rows and stay in registers;
-// each wave writes its rows' partial (m, l, o) for the chunk, merged by
-// merge_kernel.
-constexpr int kPbWaves = 8;
-constexpr int kPbRows = kPbWaves * 16;  // rows per workgroup
+// would expand every tile's codes once per 16 rows.  Here the waves of a
+// workgroup each own 16 rows of the same KV head and walk the chunk's tiles
+// together: eight waves over 64-token tiles at head_dim 128, four waves over
+// 32-token tiles at head_dim 256 (the same operand bytes per tile, so two
+// tile buffers fit in LDS either way; and at head_dim 256 the wave's query
+// operands and value accumulators take twice the registers, which four waves
+// of 512 leave room for).  A tile's operands come in eight key pieces (token
+// group, K-step), sixteen QJL sign operands (token group, k-step) and sixteen
+// value operands (half, coordinate); wave w expands its equal share of each
+// -- the ones the decode kernel's lanes build for themselves -- into one of
+// two LDS buffers, and wave 0 the tile's per-token norms; after one barrier
+// every wave runs its own rows' products, softmax and value products over all
+// of them.  A wave that reaches the barrier of tile t has finished with tile
+// t-1's buffer, which the expansion of tile t+1 (after that barrier) then
+// overwrites.  The rows' operands (int8 query digits, the QJL pieces) come
+// from qprep_kernel's rotated rows and stay in registers; each wave writes
+// its rows' partial (m, l, o) for the chunk, merged by merge_kernel.
+template <int D>
+struct PbShape {
+  static constexpr int kWaves = D == 128 ? 8 : 4;
+  static constexpr int kRows = kWaves * 16;   // rows per workgroup
+  static constexpr int TG = D == 128 ? 4 : 2; // 16-token groups per tile
+};
 
-template <int KB, int VB, bool PROD, bool VGROUP>
+template <int D, int KB, int VB, bool PROD, bool VGROUP>
 struct PbLayout {
-  static constexpr int D = 128, KS = D / 32, KS8 = D / 64, TG = 4, kTile = 64, NU = D / 16;
+  static constexpr int KS = D / 32, KS8 = D / 64, TG = PbShape<D>::TG, kTile = 16 * TG, NU = D / 16;
   static constexpr int kKey = TG * KS8 * 2 * 64 * 16;             // [tg][ks][hi, lo][lane] v4i
   static constexpr int kQjl = PROD ? TG * KS * 64 * 16 : 0;       // [tg][s][lane] v4u
   static constexpr int kVal = (TG / 2) * NU * 2 * 64 * 16;        // [h][u][hi, lo][lane] v4u
   static constexpr int kFld = 3 * kTile * 4;                      // kn, kq, vn per token
   static constexpr int kBuf = kKey + kQjl + kVal + kFld;
+  static_assert(TG * KS8 == 8 && TG * KS == 16 && (TG / 2) * NU == 16, "operand pieces per tile");
 };
 
-template <int KB, int VB, bool PROD, bool VGROUP>
-__global__ __launch_bounds__(kPbWaves * 64, 1) void prefill_bf16_kernel(DecodeParams p) {
-  using Lay = PbLayout<KB, VB, PROD, VGROUP>;
-  constexpr int D = 128;
+template <int D, int KB, int VB, bool PROD, bool VGROUP>
+__global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kernel(DecodeParams p) {
+  using Lay = PbLayout<D, KB, VB, PROD, VGROUP>;
+  constexpr int kPbWaves = PbShape<D>::kWaves, kPbRows = PbShape<D>::kRows;
   constexpr int KS = Lay::KS, KS8 = Lay::KS8, TG = Lay::TG, kTile = Lay::kTile, NU = Lay::NU;
   constexpr int LC = D / 4;
   constexpr int KW = KB * LC / 32;
@@ -717,11 +725,15 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void prefill_bf16_kernel(DecodePa
   // are read from the last token, or token 0 of an empty chunk, and masked)
   auto tok = [&](int t) -> uint32_t { return (uint32_t)max(min(t, ntok - 1), 0); };
 
-  // ---- this wave's share of the expansion: key group ktg, K-step kks; QJL
-  // pairs (tg, s) = (w/2, 2(w%2) + j); value pairs (h, u) = (w/4, 2(w%4) + j)
-  const int ktg = wave >> 1, kks = wave & 1;
-  const int qtg = wave >> 1, qs0 = 2 * (wave & 1);
-  const int vh = wave >> 2, vu0 = 2 * (wave & 3);
+  // ---- this wave's share of the expansion: of the tile's pieces numbered
+  // (tg, ks), (tg, s) and (h, u) in that order, the KJ key pieces, QJ QJL
+  // operands and VJ value operands from wave x the count (one token group or
+  // half, and for the QJL operands one sign word, per wave); group values go
+  // by pairs (u, u + NU/2), GJ of them
+  constexpr int KJ = 8 / kPbWaves, QJ = 16 / kPbWaves, VJ = 16 / kPbWaves, GJ = VJ / 2;
+  const int ktg = wave * KJ / KS8, kks0 = wave * KJ % KS8;
+  const int qtg = wave * QJ / KS, qs0 = wave * QJ % KS;
+  const int vh = wave * VJ / NU, vu0 = wave * VJ % NU;
   uint32_t rkw[KW], rsw = 0u;
   uint32_t rvw[8][VW];
   float rvs[8], rvm[8];
@@ -747,7 +759,7 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void prefill_bf16_kernel(DecodePa
       }
     }
     if (wave == 0) {
-      const uint32_t t = tok(T0 + lane);
+      const uint32_t t = tok(T0 + (lane & (kTile - 1)));
       rfk = ld<float>(knrm, 4u * t);
       if constexpr (PROD) rfq = ld<float>(krnm, 4u * t) * qjl;
       if constexpr (!VGROUP) rfv = ld<float>(vnrm, 4u * t);
@@ -760,7 +772,9 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void prefill_bf16_kernel(DecodePa
     v4u* qop = reinterpret_cast<v4u*>(buf + Lay::kKey);
     v4u* vop = reinterpret_cast<v4u*>(buf + Lay::kKey + Lay::kQjl);
     float* fld = reinterpret_cast<float*>(buf + Lay::kKey + Lay::kQjl + Lay::kVal);
-    {
+#pragma unroll
+    for (int i = 0; i < KJ; ++i) {
+      const int kks = kks0 + i;
       v4i ah, al;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -774,7 +788,7 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void prefill_bf16_kernel(DecodePa
     if constexpr (PROD) {
       const uint32_t ns = ~rsw;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < QJ; ++j) {
         const int s = qs0 + j;
         v4u as;
 #pragma unroll
@@ -799,10 +813,11 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void prefill_bf16_kernel(DecodePa
         split_pair(mn, mn + sg, th[i][0], tl[i][0]);
         split_pair(fmaf(2.f, sg, mn), fmaf(3.f, sg, mn), th[i][1], tl[i][1]);
       }
-      // coordinates u and u + NU/2 of the run (the wave's one u of NU/2 = 4),
-      // stored as (h, u) and (h, u + NU/2)
-      {
-        const int u = wave & 3;
+      // coordinates u and u + NU/2 of the run, stored as (h, u) and
+      // (h, u + NU/2)
+#pragma unroll
+      for (int j = 0; j < GJ; ++j) {
+        const int u = (wave * GJ + j) % (NU / 2);
         v4u ah0, al0, ah1, al1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -824,7 +839,7 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void prefill_bf16_kernel(DecodePa
     } else {
       constexpr int TPB = 8 / VB;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < VJ; ++j) {
         const int u = vu0 + j;
         constexpr int kBitsPerWord = 32;
         const int bit = u * VB, w = bit / kBitsPerWord, byte = (bit % kBitsPerWord) / 8;
@@ -849,7 +864,7 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void prefill_bf16_kernel(DecodePa
         vop[((vh * NU + u) * 2 + 1) * 64 + lane] = al;
       }
     }
-    if (wave == 0) {
+    if (wave == 0 && lane < kTile) {
       fld[lane] = rfk;
       fld[kTile + lane] = rfq;
       fld[2 * kTile + lane] = rfv;
@@ -1052,21 +1067,31 @@ __global__ __launch_bounds__(kPbWaves * 64, 1) void prefill_bf16_kernel(DecodePa
   }
 }
 
-template <int KB, bool PROD>
-hipError_t launch_pb_vb(const DecodeParams& p, const dim3 grid, hipStream_t stream) {
-  const dim3 block(kPbWaves * 64);
+template <int D, int KB, bool PROD>
+hipError_t launch_pb_vb(const DecodeParams& p, hipStream_t stream) {
+  const int64_t n_rg = (p.rows + PbShape<D>::kRows - 1) / PbShape<D>::kRows;
+  if ((int64_t)p.n_chunks * n_rg > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p.n_chunks * n_rg), p.hkv, p.batch);
+  const dim3 block(PbShape<D>::kWaves * 64);
   if (p.vmode == TQ_MODE_GROUP) {
     if (p.vbits != 2) return hipErrorInvalidValue;
-    prefill_bf16_kernel<KB, 2, PROD, true><<<grid, block, 0, stream>>>(p);
+    prefill_bf16_kernel<D, KB, 2, PROD, true><<<grid, block, 0, stream>>>(p);
     return hipGetLastError();
   }
   switch (p.vbits) {
-    case 1: prefill_bf16_kernel<KB, 1, PROD, false><<<grid, block, 0, stream>>>(p); break;
-    case 2: prefill_bf16_kernel<KB, 2, PROD, false><<<grid, block, 0, stream>>>(p); break;
-    case 4: prefill_bf16_kernel<KB, 4, PROD, false><<<grid, block, 0, stream>>>(p); break;
+    case 1: prefill_bf16_kernel<D, KB, 1, PROD, false><<<grid, block, 0, stream>>>(p); break;
+    case 2: prefill_bf16_kernel<D, KB, 2, PROD, false><<<grid, block, 0, stream>>>(p); break;
+    case 4: prefill_bf16_kernel<D, KB, 4, PROD, false><<<grid, block, 0, stream>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_pb_d(const DecodeParams& p, hipStream_t stream) {
+  const bool prod = p.kmode == TQ_MODE_PROD;
+  if (p.kbits == 1) return prod ? launch_pb_vb<D, 1, true>(p, stream) : launch_pb_vb<D, 1, false>(p, stream);
+  return prod ? launch_pb_vb<D, 2, true>(p, stream) : launch_pb_vb<D, 2, false>(p, stream);
 }
 
 template <int D, int KB, bool PROD>
@@ -1095,31 +1120,24 @@ hipError_t launch_d(const DecodeParams& p, const dim3 grid, hipStream_t stream) 
 
 }  // namespace
 
-// The decode kernel of this file for a launch that bf16_decode_supported
-// accepts; the query prologue and the merge are the caller's.  Token indices
-// inside a chunk use 24-bit products: chunks hold at most 2^24 tokens.
-// qprep_kernel (the rotated rows), prefill_bf16_kernel over row groups of 128
-// and chunks of the plan, merge_kernel; head_dim 128 and the codecs
-// bf16_decode_supported accepts.  Token indices inside a chunk use 24-bit
-// products: chunks hold at most 2^24 tokens.
+// qprep_kernel (the rotated rows), prefill_bf16_kernel over row groups (128
+// rows at head_dim 128, 64 at 256) and chunks of the plan, merge_kernel; the
+// codecs bf16_decode_supported accepts.  Token indices inside a chunk use
+// 24-bit products: chunks hold at most 2^24 tokens.
 hipError_t launch_prefill_bf16(const DecodeParams& p, hipStream_t stream) {
-  if (p.d != 128 || !bf16_decode_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits, 1) || p.rows < 1 ||
-      p.n_chunks < 1 || p.chunk % 64 || p.chunk > (1 << 24) || p.hkv > 65535 || p.batch > 65535)
+  if (!bf16_decode_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits, 1) || p.rows < 1 || p.n_chunks < 1 ||
+      p.chunk % 64 || p.chunk > (1 << 24) || p.hkv > 65535 || p.batch > 65535)
     return hipErrorInvalidValue;
-  const int64_t n_rg = (p.rows + kPbRows - 1) / kPbRows;
-  if ((int64_t)p.n_chunks * n_rg > 0x7fffffff) return hipErrorInvalidValue;
   hipError_t e = launch_qprep(p, stream);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)(p.n_chunks * n_rg), p.hkv, p.batch);
-  const bool prod = p.kmode == TQ_MODE_PROD;
-  if (p.kbits == 1)
-    e = prod ? launch_pb_vb<1, true>(p, grid, stream) : launch_pb_vb<1, false>(p, grid, stream);
-  else
-    e = prod ? launch_pb_vb<2, true>(p, grid, stream) : launch_pb_vb<2, false>(p, grid, stream);
+  e = p.d == 128 ? launch_pb_d<128>(p, stream) : launch_pb_d<256>(p, stream);
   if (e != hipSuccess) return e;
   return launch_merge(p, stream);
 }
 
+// The decode kernel of this file for a launch that bf16_decode_supported
+// accepts; the query prologue and the merge are the caller's.  Token indices
+// inside a chunk use 24-bit products: chunks hold at most 2^24 tokens.
 hipError_t launch_decode_bf16_kernel(const DecodeParams& p, const dim3 grid, hipStream_t stream) {
   if (!bf16_decode_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits, p.rows) || p.chunk % kStep ||
       p.chunk > (1 << 24))

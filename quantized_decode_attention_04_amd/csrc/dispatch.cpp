@@ -189,12 +189,13 @@ DecodePlan plan_prefill_fast(int batch, int hkv, int rows, int64_t max_len) {
   return p;
 }
 
-DecodePlan plan_prefill_bf16(int batch, int hkv, int rows, int64_t max_len) {
+DecodePlan plan_prefill_bf16(int batch, int hkv, int rows, int d, int64_t max_len) {
   DecodePlan p{};
   p.rows = rows;
-  const int64_t tile = 64;                    // every wave walks every tile of its chunk
+  const int64_t tile = 64;                    // a multiple of both kernels' tiles
   const int64_t max_chunks = 4096;            // the merge kernel's weights in LDS
-  const int64_t row_groups = (rows + 127) / 128;
+  const int64_t group = d == 128 ? 128 : 64;  // rows per workgroup
+  const int64_t row_groups = (rows + group - 1) / group;
   const int64_t units = (int64_t)batch * hkv * row_groups;
   // about one workgroup per compute unit (one fits, at 130 KB of LDS)
   const int64_t per = std::max<int64_t>(1, (device_cus() + units - 1) / units);
@@ -211,11 +212,11 @@ DecodePlan plan_prefill_bf16(int batch, int hkv, int rows, int64_t max_len) {
   const size_t bg = (size_t)batch * hkv;
   size_t off = 0;
   p.off_qrot = off;
-  off = align256(off + bg * rows * 128 * sizeof(float));
+  off = align256(off + bg * rows * d * sizeof(float));
   p.off_qs = off;
-  off = align256(off + bg * rows * 128 * sizeof(float));
+  off = align256(off + bg * rows * d * sizeof(float));
   p.off_part_o = off;
-  off = align256(off + bg * p.n_chunks * rows * 128 * sizeof(float));
+  off = align256(off + bg * p.n_chunks * rows * d * sizeof(float));
   p.off_part_ml = off;
   off = align256(off + bg * p.n_chunks * rows * 2 * sizeof(float));
   p.total = off;

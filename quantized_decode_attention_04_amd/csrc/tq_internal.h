@@ -205,9 +205,10 @@ hipError_t launch_decode_fast(const DecodeParams& p, hipStream_t stream);
 constexpr int kPrefillRows = 1024;
 DecodePlan plan_prefill_fast(int batch, int hkv, int rows, int64_t max_len);
 hipError_t launch_prefill_fast(const DecodeParams& p, hipStream_t stream);
-// prefill on the bf16 / int8 kernel's codecs at head_dim 128: 128 rows per
-// workgroup over shared tiles (decode_bf16.hip), qprep and merge around it
-DecodePlan plan_prefill_bf16(int batch, int hkv, int rows, int64_t max_len);
+// prefill on the bf16 / int8 kernel's codecs (head_dim 128 or 256): 128 or
+// 64 rows per workgroup over shared tiles (decode_bf16.hip), qprep and merge
+// around it
+DecodePlan plan_prefill_bf16(int batch, int hkv, int rows, int d, int64_t max_len);
 hipError_t launch_prefill_bf16(const DecodeParams& p, hipStream_t stream);
 
 // ---- token-record copies between caches of one codec ----------------------

@@ -165,7 +165,7 @@ def test_decode_shape_validation():
 def test_prefill_workspace_is_one_row_block():
     """Prefill takes any q_len and plans its workspace for one launch of rows,
     which the launches reuse: a decode block (16 rows up to head_dim 128, 8
-    above), or on the 3-bit int8 path above 16 rows up to 1024 rows (the
+    above), or on the shared-tile kernels above that up to 1024 rows (the
     rotated queries and every chunk's partial of each row)."""
     kc = tq.tq_codec_create(128, 3, 0, tq.TQ_MODE_MSE)
     vc = tq.tq_codec_create(128, 3, 1, tq.TQ_MODE_MSE)
@@ -177,7 +177,9 @@ def test_prefill_workspace_is_one_row_block():
     assert many == pre(kc, vc, 1, 8, 1, 128, 5000)                            # 1024 rows
     assert many >= 1024 * 128 * 4 * 2                                         # q_rot + at least one chunk
     assert pre(kc, vc, 1, 8, 1, 5, 5000) < many                               # 40 rows
-    assert pre(kp, vg, 1, 2, 1, 300, 5000) == dec(kp, vg, 1, 8, 1, 1, 5000)    # d 256: 8-row blocks
+    assert pre(kp, vg, 1, 2, 1, 4, 5000) == dec(kp, vg, 1, 8, 1, 1, 5000)      # d 256, 8 rows: one block
+    big = pre(kp, vg, 1, 2, 1, 300, 5000)                                     # 600 rows: shared tiles
+    assert big >= 600 * 256 * 4 * 3                                           # q_rot, S q_rot, one chunk
     with pytest.raises(tq.TQError) as e:
         dec(kc, vc, 1, 8, 1, 3, 5000)                                         # 24 rows: not a decode step
     assert e.value.status == 2

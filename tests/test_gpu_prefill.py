@@ -46,8 +46,6 @@ CASES = [
     ("fast_1100_rows_two_launches", 128, (3, 0), (3, 0), 1, 1, 4, 275, [300], 320, False, 1.0),
     # general path: Prod keys, 4-bit values, 36 rows
     ("general_prod3_mse4_q9", 128, (3, 1), (4, 0), 2, 2, 8, 9, [513, 77], 600, True, 0.02),
-    # general path at head_dim 256 (8-row blocks): Prod keys, group values
-    ("general_d256_prod3_group2_q7", 256, (3, 1), (2, 2), 1, 1, 2, 7, [300], 320, True, 0.02),
     # shared-tile kernel of the bf16 / int8 codecs (head_dim 128): 256 rows per
     # KV head (two 128-row workgroups) over a ragged batch of several chunks
     ("bf16_prod3_mse4_256_rows_ragged", 128, (3, 1), (4, 0), 2, 2, 16, 16, [5000, 2100], 5000, True, 0.02),
@@ -59,6 +57,19 @@ CASES = [
     ("bf16_prod3_mse2_self_attention_q130", 128, (3, 1), (2, 0), 1, 1, 1, 130, [130], 160, False, 1.0),
     # 1100 rows: two launches (1024 + 76 rows)
     ("bf16_prod3_mse4_1100_rows_two_launches", 128, (3, 1), (4, 0), 1, 1, 4, 275, [300], 320, False, 1.0),
+    # the same kernel at head_dim 256 (64-row workgroups over 32-token tiles):
+    # Prod keys and group values, 14 rows (one workgroup, its last 50 rows empty)
+    ("bf16_d256_prod3_group2_q7", 256, (3, 1), (2, 2), 1, 1, 2, 7, [300], 320, True, 0.02),
+    # 192 rows per KV head (three workgroups) over a ragged batch of several chunks
+    ("bf16_d256_prod3_group2_192_rows_ragged", 256, (3, 1), (2, 2), 2, 2, 16, 24, [3000, 1100], 3000, True, 0.02),
+    # MSE keys of 2 bits, 4-bit values, 80 rows
+    ("bf16_d256_mse2_mse4_q40", 256, (2, 0), (4, 0), 1, 1, 2, 40, [900], 960, False, 1.0),
+    # 1-bit key codes with QJL signs, 1-bit values, a sharp softmax over 33 rows
+    ("bf16_d256_prod2_mse1_sharp_q33", 256, (2, 1), (1, 0), 1, 1, 1, 33, [700], 704, False, 200.0),
+    # 2-bit values; every token new, 70 rows
+    ("bf16_d256_prod3_mse2_self_attention_q70", 256, (3, 1), (2, 0), 1, 1, 1, 70, [70], 96, False, 1.0),
+    # 1100 rows: two launches (1024 + 76 rows)
+    ("bf16_d256_prod3_group2_1100_rows_two_launches", 256, (3, 1), (2, 2), 1, 1, 4, 275, [300], 320, False, 1.0),
 ]
 
 
