@@ -246,10 +246,12 @@ def bulk_prefill(tq, wl, w, kc, vc, dev, stream, warmup: int, reps: int, tokens:
 
 def prefill_timing(tq, wl, w, kc, vc, K, V, lens, max_len, dev, stream, reps: int, q_len: int = 64) -> dict:
     """tq_prefill_attention of ``q_len`` new tokens per sequence over one
-    layer's cache (the rows of each KV head run in blocks of 16 through the
-    decode kernels, each block reading the layer's state once), timed with HIP
-    events on the launch stream: microseconds per call, query tokens per
-    second, and the state bytes the blocks read per second."""
+    layer's cache, timed with HIP events on the launch stream: microseconds per
+    call, query tokens per second, and the layer's state bytes per second.  On
+    every workload here the rows of each KV head run on a shared-tile kernel in
+    groups of 128 (head_dim 128) or 64 (head_dim 256), each group walking the
+    whole state: ``row_groups`` passes over it (served in part by the caches),
+    and ``state_gbps`` counts the state once."""
     import torch
     q = wl.device_normal((w.batch, w.hq, q_len, w.d), 0, 0, 902, w.bf16, dev)
     out = torch.empty((w.batch, w.hq, q_len, w.d), dtype=torch.float32, device=dev)
@@ -265,12 +267,11 @@ def prefill_timing(tq, wl, w, kc, vc, K, V, lens, max_len, dev, stream, reps: in
     torch.cuda.synchronize()
     us = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1000.0
     rows = (w.hq // w.hkv) * q_len
-    block = 16 if w.d <= 128 else 8
-    blocks = -(-rows // block)
+    group = 128 if w.d <= 128 else 64
     state = int(w.lens().sum()) * w.hkv * (kc.info["bytes_per_token"] + vc.info["bytes_per_token"])
-    return {"q_len": q_len, "rows_per_kv_head": rows, "row_blocks": blocks, "us": us,
+    return {"q_len": q_len, "rows_per_kv_head": rows, "row_groups": -(-rows // group), "us": us,
             "query_tokens_per_s": w.batch * q_len / (us * 1e-6),
-            "state_read_gbps": blocks * state / (us * 1e-6) / 1e9}
+            "state_gbps": state / (us * 1e-6) / 1e9}
 
 
 def gather_timing(tq, w, kc, vc, K, V, dev, stream, reps: int) -> dict:

@@ -27,6 +27,7 @@
 //                  invalidates the L2 of every XCD).
 // Scores are kept in the log2 domain (multiplied by log2 e) so that the
 // softmax uses exp2.
+#include "chunk_order.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -314,7 +315,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   __shared__ uint32_t s_vw[kTile * D * 4 / 32];  // the tile's value words (up to 4 bits)
   __shared__ float s_vs[kTile * (D / 32) * 2];   // group scale and minimum pairs
 
-  const int chunk_id = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int chunk_id = rotated_chunk(blockIdx.x, blockIdx.y, blockIdx.z, p.hkv, p.n_chunks);
+  const int g = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.hkv + g;
   const int tid = threadIdx.x;
   const bool prod = p.kmode == TQ_MODE_PROD;

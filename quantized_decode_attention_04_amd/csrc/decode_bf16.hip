@@ -49,6 +49,7 @@
 // four waves' (m, l, o) are combined in LDS (the query operands' space,
 // reused once the tiles are done) into the chunk's partial, which the
 // general path's merge kernel merges across chunks.
+#include "chunk_order.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -193,7 +194,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, g = lane >> 4;
-  const int chunk_id = blockIdx.x, gh = blockIdx.y, b = blockIdx.z;
+  const int chunk_id = rotated_chunk(blockIdx.x, blockIdx.y, blockIdx.z, p.hkv, p.n_chunks);
+  const int gh = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.hkv + gh;
   const int rows = p.rows;
   int64_t len64 = p.len[b];
@@ -685,7 +687,8 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, g = lane >> 4;
-  const int chunk_id = blockIdx.x % p.n_chunks, rg = blockIdx.x / p.n_chunks;
+  const int chunk_id = rotated_chunk(blockIdx.x % p.n_chunks, blockIdx.y, blockIdx.z, p.hkv, p.n_chunks);
+  const int rg = blockIdx.x / p.n_chunks;
   const int gh = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.hkv + gh;
   const int rows = p.rows;

@@ -37,6 +37,7 @@
 //   cores) while the first two tiles of every wave are already in flight, and
 //   each workgroup's buffer resources end at its chunk, so no byte outside the
 //   chunk is fetched.
+#include "chunk_order.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -308,7 +309,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fast_kernel(DecodeParams p
   // the wave index is uniform: a scalar register keeps the tile loop uniform
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, h = lane >> 4;  // query row, lane group
-  const int chunk_id = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int chunk_id = rotated_chunk(blockIdx.x, blockIdx.y, blockIdx.z, p.hkv, p.n_chunks);
+  const int g = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.hkv + g;
   const int rows = p.rows;
   int64_t len64 = p.len[b];
@@ -712,7 +714,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fast_kernel(DecodeParams 
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, h = lane >> 4;  // query row of the wave, lane group
-  const int chunk_id = blockIdx.x % p.n_chunks, rg = blockIdx.x / p.n_chunks;
+  const int chunk_id = rotated_chunk(blockIdx.x % p.n_chunks, blockIdx.y, blockIdx.z, p.hkv, p.n_chunks);
+  const int rg = blockIdx.x / p.n_chunks;
   const int g = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.hkv + g;
   const int rows = p.rows;
@@ -997,7 +1000,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fast_kernel(DecodeParams 
 __global__ __launch_bounds__(kThreads, 1) void decode_read_kernel(DecodeParams p, uint32_t* sink, uint32_t sink_words) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, h = lane >> 4;
-  const int chunk_id = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int chunk_id = rotated_chunk(blockIdx.x, blockIdx.y, blockIdx.z, p.hkv, p.n_chunks);
+  const int g = blockIdx.y, b = blockIdx.z;
   int64_t len64 = p.len[b];
   len64 = len64 < 0 ? 0 : (len64 > p.cap ? p.cap : len64);
   const int len = (int)len64;

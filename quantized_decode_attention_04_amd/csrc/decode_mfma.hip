@@ -29,6 +29,7 @@
 // writes its own partial (m, l, o) (4 per chunk), merged by the general
 // path's merge kernel.  The query rows (rotated by the general path's qprep
 // kernel) sit in LDS.
+#include "chunk_order.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -99,7 +100,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(DecodeParams p
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, g = lane >> 4;  // token slot / query row, lane group
-  const int chunk_id = blockIdx.x, gh = blockIdx.y, b = blockIdx.z;
+  const int chunk_id = rotated_chunk(blockIdx.x, blockIdx.y, blockIdx.z, p.hkv, p.n_chunks);
+  const int gh = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.hkv + gh;
   const int rows = p.rows;
   const bool prod = p.kmode == TQ_MODE_PROD;
