@@ -443,6 +443,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) sq[tg] = v4f{0.f, 0.f, 0.f, 0.f};
     if constexpr (PROD) {
+      // the sign-bit mask in a register, so that mask and +1.0 bits make one
+      // v_and_or_b32 (its three-operand form takes no literal constant)
+      uint32_t sgn = 0x80008000u;
+      asm volatile("" : "+v"(sgn));
       v4u nch = s_qop[0 * 64 + lane], ncl = s_qop[1 * 64 + lane];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -459,7 +463,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
           for (int e = 0; e < 4; ++e) {
             // bits k and k + 16 of the negated signs become the bf16 sign bits
             const int k = 4 * (s & 3) + e;
-            as[e] = ((ns & (0x00010001u << k)) << (15 - k)) | 0x3f803f80u;
+            as[e] = ((ns << (15 - k)) & sgn) | 0x3f803f80u;
           }
           sq[tg] = mfma(as, ch, sq[tg]);
           sq[tg] = mfma(as, cl, sq[tg]);
@@ -482,7 +486,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
     tmax = rowmax4(tmax);
     if (__ballot(tmax > m_ref + kFlushGap) != 0) {
       const float m_new = fmaxf(m_ref, tmax);
-      const float alpha = exp2f(m_ref - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
 #pragma unroll
       for (int u = 0; u < NU; ++u) acc[u] *= alpha;
       l_run *= alpha;
@@ -492,7 +496,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      const float pr = exp2f(sc[i] - m_ref);
+      // the hardware exp2: arguments are at most kFlushGap, or -inf (masked)
+      const float pr = __builtin_amdgcn_exp2f(sc[i] - m_ref);
       psum += pr;
       pv[i] = VGROUP ? pr : pr * vn[i];
     }
@@ -790,6 +795,8 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
     }
     if constexpr (PROD) {
       const uint32_t ns = ~rsw;
+      uint32_t sgn = 0x80008000u;  // in a register: one v_and_or_b32 below
+      asm volatile("" : "+v"(sgn));
 #pragma unroll
       for (int j = 0; j < QJ; ++j) {
         const int s = qs0 + j;
@@ -798,7 +805,7 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
         for (int e = 0; e < 4; ++e) {
           // bits k and k + 16 of the negated signs become the bf16 sign bits
           const int k = 4 * (s & 3) + e;
-          as[e] = ((ns & (0x00010001u << k)) << (15 - k)) | 0x3f803f80u;
+          as[e] = ((ns << (15 - k)) & sgn) | 0x3f803f80u;
         }
         qop[(qtg * KS + s) * 64 + lane] = as;
       }
@@ -1014,7 +1021,7 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
     tmax = rowmax4(tmax);
     if (__ballot(tmax > m_ref + kFlushGap) != 0) {
       const float m_new = fmaxf(m_ref, tmax);
-      const float alpha = exp2f(m_ref - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
 #pragma unroll
       for (int u = 0; u < NU; ++u) acc[u] *= alpha;
       l_run *= alpha;
@@ -1024,7 +1031,8 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      const float pr = exp2f(sc[i] - m_ref);
+      // the hardware exp2: arguments are at most kFlushGap, or -inf (masked)
+      const float pr = __builtin_amdgcn_exp2f(sc[i] - m_ref);
       psum += pr;
       pv[i] = VGROUP ? pr : pr * fld[2 * kTile + 16 * (i >> 2) + 4 * g + (i & 3)];
     }
