@@ -205,6 +205,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
   const int ntok = (c0 + p.chunk < len ? c0 + p.chunk : len) - c0;  // may be <= 0
   const int lenm = p.len_mask ? (p.len_mask[b] < 0 ? 0 : p.len_mask[b]) : len;  // the causal rule's length
   const int lim = lenm - p.q_len + ((p.row0 + m) % p.q_len) + 1 - c0;  // row m sees tokens < lim
+  const int lim_all = lenm - p.q_len + 1 - c0;                           // tokens every row sees
 
   if constexpr (!VGROUP) {
     if (threadIdx.x < 16) {
@@ -474,15 +475,22 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
 
     // ---- online softmax of row m over this lane's NT tokens
     float sc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+      sc[i] = PROD ? fmaf(kn[i], sm[i >> 2][i & 3], kq[i] * sq[i >> 2][i & 3]) : kn[i] * sm[i >> 2][i & 3];
+    if (!(T0 + kTile <= ntok && T0 + kTile <= lim_all)) {
+      // a tile with masked tokens (the chunk's end, the causal edge); the
+      // empty asm statement keeps the selects behind the wave-uniform branch
+      asm volatile("");
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        const int tok = T0 + 16 * (i >> 2) + 4 * g + (i & 3);
+        if (!(tok < ntok && tok < lim)) sc[i] = -INFINITY;
+      }
+    }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int tok = T0 + 16 * (i >> 2) + 4 * g + (i & 3);
-      const float raw = PROD ? fmaf(kn[i], sm[i >> 2][i & 3], kq[i] * sq[i >> 2][i & 3]) : kn[i] * sm[i >> 2][i & 3];
-      const float v = (tok < ntok && tok < lim) ? raw : -INFINITY;
-      sc[i] = v;
-      tmax = fmaxf(tmax, v);
-    }
+    for (int i = 0; i < NT; ++i) tmax = fmaxf(tmax, sc[i]);
     tmax = rowmax4(tmax);
     if (__ballot(tmax > m_ref + kFlushGap) != 0) {
       const float m_new = fmaxf(m_ref, tmax);
@@ -706,6 +714,7 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
   const int ntok = (c0 + p.chunk < len ? c0 + p.chunk : len) - c0;  // may be <= 0
   const int lenm = p.len_mask ? (p.len_mask[b] < 0 ? 0 : p.len_mask[b]) : len;
   const int lim = lenm - p.q_len + ((p.row0 + rl) % p.q_len) + 1 - c0;  // row rl sees tokens < lim
+  const int lim_all = lenm - p.q_len + 1 - c0;                            // tokens every row sees
 
   if constexpr (!VGROUP) {
     if (threadIdx.x < 16) {
@@ -1008,16 +1017,25 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
 
     // ---- online softmax of row m over this lane's NT tokens
     float sc[NT];
-    float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      const int tk = T0 + 16 * (i >> 2) + 4 * g + (i & 3);
-      const float kn = fld[tk - T0], kq = fld[kTile + tk - T0];
-      const float raw = PROD ? fmaf(kn, sm[i >> 2][i & 3], kq * sq[i >> 2][i & 3]) : kn * sm[i >> 2][i & 3];
-      const float v = (tk < ntok && tk < lim) ? raw : -INFINITY;
-      sc[i] = v;
-      tmax = fmaxf(tmax, v);
+      const int ti = 16 * (i >> 2) + 4 * g + (i & 3);
+      const float kn = fld[ti], kq = fld[kTile + ti];
+      sc[i] = PROD ? fmaf(kn, sm[i >> 2][i & 3], kq * sq[i >> 2][i & 3]) : kn * sm[i >> 2][i & 3];
     }
+    if (!(T0 + kTile <= ntok && T0 + kTile <= lim_all)) {
+      // masked tokens (the chunk's end, the causal edge) behind a
+      // wave-uniform branch, kept there by the empty asm statement
+      asm volatile("");
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        const int tk = T0 + 16 * (i >> 2) + 4 * g + (i & 3);
+        if (!(tk < ntok && tk < lim)) sc[i] = -INFINITY;
+      }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) tmax = fmaxf(tmax, sc[i]);
     tmax = rowmax4(tmax);
     if (__ballot(tmax > m_ref + kFlushGap) != 0) {
       const float m_new = fmaxf(m_ref, tmax);
