@@ -749,6 +749,8 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
   // by pairs (u, u + NU/2), GJ of them
   constexpr int KJ = 8 / kPbWaves, QJ = 16 / kPbWaves, VJ = 16 / kPbWaves, GJ = VJ / 2;
   const int ktg = wave * KJ / KS8, kks0 = wave * KJ % KS8;
+  const bool early = kPbWaves == 8 && (wave & 4) != 0;  // expands before its products
+  const bool late = kPbWaves == 8 && (wave & 4) == 0;   // after them
   const int qtg = wave * QJ / KS, qs0 = wave * QJ % KS;
   const int vh = wave * VJ / NU, vu0 = wave * VJ % NU;
   uint32_t rkw[KW], rsw = 0u;
@@ -966,6 +968,19 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
     const float* fld = reinterpret_cast<const float*>(buf + Lay::kKey + Lay::kQjl + Lay::kVal);
     __syncthreads();
 
+    // the next tile's share, into the other buffer (every wave finished with
+    // it before this tile's barrier), and the loads of the one after.  With
+    // eight waves, half expand before their products and half after them, so
+    // that the two waves sharing a SIMD (w and w + 4) tend to run matrix-core
+    // and VALU phases side by side rather than in step after the barrier;
+    // with four (one per SIMD) every wave expands between its score and
+    // value products.
+    const bool more = T0 + kTile < ntok;
+    if (early && more) {
+      stage_expand(T0 + kTile);
+      stage_load(T0 + 2 * kTile);
+    }
+
     // ---- scores of this wave's rows: MSE term on the int8 matrix cores, QJL
     // term on the bf16 ones (lane (m, g) ends with row m's scores of tokens
     // 16 tg + 4 g + r)
@@ -1007,10 +1022,7 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
           sq[tg] = mfma(as, ql[s], sq[tg]);
         }
     }
-
-    // the next tile's share, into the other buffer (every wave finished with
-    // it before this tile's barrier), and the loads of the one after
-    if (T0 + kTile < ntok) {
+    if (!early && !late && more) {
       stage_expand(T0 + kTile);
       stage_load(T0 + 2 * kTile);
     }
@@ -1076,6 +1088,10 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
         acc[u] = mfma(ah, bl, acc[u]);
         acc[u] = mfma(al, bh, acc[u]);
       }
+    }
+    if (late && more) {
+      stage_expand(T0 + kTile);
+      stage_load(T0 + 2 * kTile);
     }
   }
 
