@@ -108,6 +108,19 @@ __device__ __forceinline__ T ld(const char* base, uint32_t off) {
   return *reinterpret_cast<const T*>(base + off);
 }
 
+// A raw buffer resource over `bytes` bytes from `base`: loads at offsets
+// past the end return zero without touching memory.
+constexpr int kBufWord3 = 0x00020000;  // raw buffer resource, gfx9 data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+__device__ __forceinline__ uint32_t bld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ float bldf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // bf16 bits of x, rounded to nearest even (finite x)
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -231,45 +244,54 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
   const uint32_t koff = 4u * g * KW, soff = 4u * g * SW, voff = 4u * ((m * VRB) >> 5);
   const uint32_t goff = 4u * ((m * NU) >> 5);  // the group of the lane's value run
   const int vshift = (m * VRB) & 31;
+  // the chunk's fields as buffer resources that end at its last token
+  const uint32_t nt = ntok > 0 ? (uint32_t)ntok : 0u;
+  const __amdgpu_buffer_rsrc_t rki = rsrc(kidx, nt * kstride);
+  const __amdgpu_buffer_rsrc_t rks = rsrc(PROD ? ksgn : kidx, PROD ? nt * sstride : 0u);
+  const __amdgpu_buffer_rsrc_t rkn = rsrc(knrm, nt * 4u);
+  const __amdgpu_buffer_rsrc_t rkr = rsrc(PROD ? krnm : knrm, PROD ? nt * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t rvn = rsrc(VGROUP ? vidx : vnrm, VGROUP ? 0u : nt * 4u);
+  const __amdgpu_buffer_rsrc_t rvs = rsrc(VGROUP ? vscl : vidx, VGROUP ? nt * gstride : 0u);
+  const __amdgpu_buffer_rsrc_t rvm = rsrc(VGROUP ? vmin : vidx, VGROUP ? nt * gstride : 0u);
+  const __amdgpu_buffer_rsrc_t rvi = rsrc(vidx, nt * vstride);
 
   // ---- tile loads, one tile ahead of their use.  Key words of token T0 +
   // 16 tg + m, coordinates (D/4) g .. (D/4) g + D/4 - 1; key norms and value
   // fields of the lane's tokens T0 + 16 tg + 4 g + r (token i: tg = i / 4,
-  // r = i % 4).  Tokens past the chunk's end read the last token instead
-  // (token 0 of an empty chunk, a slot below the cache's capacity): every
-  // load is valid, and their scores are masked, so they weigh nothing.
+  // r = i % 4).  Tokens past the chunk's end read zeros, without touching
+  // memory; their scores are masked, so they weigh nothing.
   uint32_t nkw[TG][KW], nksw[TG][SW];
   float kn[NT], kq[NT], vn[NT], vs[NT];
   uint32_t vw[NT][VW];
   auto load_keys = [&](int T0) {
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) {
-      const uint32_t t = (uint32_t)max(min(T0 + 16 * tg + m, ntok - 1), 0);
+      const uint32_t t = (uint32_t)(T0 + 16 * tg + m);
 #pragma unroll
-      for (int w = 0; w < KW; ++w) nkw[tg][w] = ld<uint32_t>(kidx, __umul24(t, kstride) + koff + 4u * w);
+      for (int w = 0; w < KW; ++w) nkw[tg][w] = bld(rki, __umul24(t, kstride) + koff + 4u * w);
 #pragma unroll
       for (int w = 0; w < SW; ++w) {
         nksw[tg][w] = 0u;
-        if constexpr (PROD) nksw[tg][w] = ld<uint32_t>(ksgn, __umul24(t, sstride) + soff + 4u * w);
+        if constexpr (PROD) nksw[tg][w] = bld(rks, __umul24(t, sstride) + soff + 4u * w);
       }
     }
   };
   auto load_fields = [&](int T0) {
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      const uint32_t t = (uint32_t)max(min(T0 + 16 * (i >> 2) + 4 * g + (i & 3), ntok - 1), 0);
-      kn[i] = ld<float>(knrm, 4u * t);
+      const uint32_t t = (uint32_t)(T0 + 16 * (i >> 2) + 4 * g + (i & 3));
+      kn[i] = bldf(rkn, 4u * t);
       kq[i] = 0.f;
-      if constexpr (PROD) kq[i] = ld<float>(krnm, 4u * t) * qjl;
+      if constexpr (PROD) kq[i] = bldf(rkr, 4u * t) * qjl;
       if constexpr (VGROUP) {
-        vs[i] = ld<float>(vscl, __umul24(t, gstride) + goff);
-        vn[i] = ld<float>(vmin, __umul24(t, gstride) + goff);
+        vs[i] = bldf(rvs, __umul24(t, gstride) + goff);
+        vn[i] = bldf(rvm, __umul24(t, gstride) + goff);
       } else {
-        vn[i] = ld<float>(vnrm, 4u * t);
+        vn[i] = bldf(rvn, 4u * t);
         vs[i] = 0.f;
       }
 #pragma unroll
-      for (int w = 0; w < VW; ++w) vw[i][w] = ld<uint32_t>(vidx, __umul24(t, vstride) + voff + 4u * w);
+      for (int w = 0; w < VW; ++w) vw[i][w] = bld(rvi, __umul24(t, vstride) + voff + 4u * w);
     }
   };
 
