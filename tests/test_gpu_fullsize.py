@@ -2,7 +2,8 @@
 
 Each case builds one layer of a benchmark workload at its real size on the
 device, in the launch configuration bench.py times (bulk 65536-token appends,
-then one decode call over every KV head):
+then one decode call over every KV head, and one prefill call of 64 new
+tokens per sequence):
 
 * one sampled KV head's whole history is taken from the device *inputs*
   (seeded synthetic K and V, before quantisation) and quantised by the
@@ -10,7 +11,8 @@ then one decode call over every KV head):
   the decision window (norms to 1e-6 relative);
 * the oracle's state for that head is then written over the GPU's, the decode
   runs over all heads, and the sampled head's output rows must match the
-  oracle's decode of its own state to relative L2 1e-4.
+  oracle's decode of its own state to relative L2 1e-4, and so must sampled
+  rows of the prefill call (the first and last positions of the 64).
 
 No oracle input comes from the HIP path: the oracle sees the generated
 inputs only, and the GPU decodes the oracle's state.
@@ -185,3 +187,24 @@ def test_full_size_layer_sampled_head(name, b, g, layer):
     cos = np.sum(got * ref, -1) / (np.linalg.norm(got, axis=-1) * np.linalg.norm(ref, axis=-1))
     _say(f"  cos-sim to unquantised attention: mean {cos.mean():.6f} min {cos.min():.6f}")
     assert cos.mean() >= QUALITY_FLOOR[name]
+
+    # prefill at the bench's size: 64 new tokens of every sequence (the last
+    # 64 cached positions, causal among themselves) over the same cache, every
+    # row of every KV head in one call; the sampled head's first and last four
+    # positions of its first and last query head against the oracle.  A slice
+    # of rows i0 .. i0+3 goes to the oracle as a 4-row call over the first
+    # n_b - 64 + i0 + 4 tokens, which gives its rows the same visible tokens.
+    pq = 64
+    qp = wl.device_normal((B, Hq, pq, d), 0, 0, 902, w.bf16, dev)
+    outp = torch.zeros((B, Hq, pq, d), dtype=torch.float32, device=dev)
+    wsp = tq.allocate_prefill_workspace(gk, gv, B, Hq, Hkv, pq, max_len, dev)
+    tq.tq_prefill_attention(gk, gv, qp, K, V, ld, max_len, scale, outp, wsp)
+    torch.cuda.synchronize()
+    heads = [g * G, g * G + G - 1]
+    for i0 in (0, pq - 4):
+        gotp = outp[b, heads, i0:i0 + 4].cpu().numpy().astype(np.float64)[None]
+        qs_ = qp[b, heads, i0:i0 + 4].float().cpu().numpy().astype(np.float64)[None]
+        wantp = oatt.decode_attention_rotated(qs_, ks, kc, vs, vc, np.array([n_b - pq + i0 + 4]), scale)
+        errp = rel_l2_rows(gotp, wantp)
+        _say(f"  prefill rows {i0}..{i0 + 3} of query heads {heads}: max row rel L2 {errp.max():.3e}")
+        assert errp.max() <= 1e-4
