@@ -304,6 +304,115 @@ def gather_timing(tq, w, kc, vc, K, V, dev, stream, reps: int) -> dict:
             "gbps": nbytes / (us * 1e-6) / 1e9}
 
 
+def hybrid_timing(tq, wl, w, kc, vc, K, V, lens_h, max_len, dev, stream, reps: int, buf: int = 128) -> dict:
+    """Hybrid cache of the recent-token ring in front of one layer's
+    compressed caches ("turboquant validate_moe_phase2.py", Test 5's
+    buffer_size): each sequence is taken to hold N = len - 64 tokens, its first
+    floor(N / buf) * buf in the layer's compressed records and the rest (64 at
+    these lengths) in a ring of seeded values.  Timed with HIP events on the
+    launch stream: tq_hybrid_append of the step's new tokens that only stage
+    into the rings, one that fills each ring (its buf tokens quantised into
+    copies of the compressed caches, one ring below each sequence's length, so
+    the layer's own records stay as the rest of the bench reads them), and
+    tq_hybrid_decode_attention over both parts; bytes of the decode =
+    compressed records + ring tokens read."""
+    import dataclasses
+    import torch
+    B, hkv, hq, d, qlen = w.batch, w.hkv, w.hq, w.d, w.q_len
+    dt = torch.bfloat16 if w.bf16 else torch.float32
+    n_h = np.maximum(lens_h - 64, 1).astype(np.int64)
+    nc = (n_h // buf) * buf
+    kb = tq.allocate_ring(B, hkv, buf, d, dtype=dt, device=dev)
+    vb = tq.allocate_ring(B, hkv, buf, d, dtype=dt, device=dev)
+    kb.copy_(wl.device_normal((B, hkv, buf, d), 0, 0, 903, w.bf16, dev))
+    vb.copy_(wl.device_normal((B, hkv, buf, d), 0, 0, 904, w.bf16, dev))
+    kn = wl.device_normal((B, hkv, qlen, d), 0, 0, 905, w.bf16, dev)
+    vn = wl.device_normal((B, hkv, qlen, d), 0, 0, 906, w.bf16, dev)
+    q = wl.device_normal((B, hq, qlen, d), 0, 0, 907, w.bf16, dev)
+    out = torch.empty((B, hq, qlen, d), dtype=torch.float32, device=dev)
+    ln = torch.tensor(n_h, dtype=torch.int32, device=dev)
+    # lengths at which the step's tokens complete every ring (a ring below N)
+    nf = np.maximum(n_h // buf - 1, 0) * buf + (buf - qlen)
+    lf = torch.tensor(nf, dtype=torch.int32, device=dev)
+    clone = lambda c: dataclasses.replace(c, **{f: getattr(c, f).clone() for f in
+                                                ("idx", "norm", "rnorm", "sign", "scale", "gmin")
+                                                if getattr(c, f) is not None})
+    Kc, Vc = clone(K), clone(V)
+    ws = torch.zeros(tq.tq_hybrid_decode_workspace_size(kc, vc, B, hq, hkv, qlen, max_len, buf), dtype=torch.uint8,
+                     device=dev)
+    scale = 1.0 / math.sqrt(d)
+
+    def timed(fn):
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1000.0
+
+    stage_us = timed(lambda: tq.tq_hybrid_append(kc, vc, kn, vn, K, V, kb, vb, ln, int(n_h.max()) + qlen))
+    flush_us = timed(lambda: tq.tq_hybrid_append(kc, vc, kn, vn, Kc, Vc, kb, vb, lf, int(nf.max()) + qlen))
+    del Kc, Vc
+    dec_us = timed(lambda: tq.tq_hybrid_decode_attention(kc, vc, q, K, V, kb, vb, ln, max_len, scale, out, ws))
+    esz = 2 if w.bf16 else 4
+    nbytes = (int(nc.sum()) * (kc.info["bytes_per_token"] + vc.info["bytes_per_token"])
+              + int((n_h - nc).sum()) * 2 * d * esz) * hkv
+    del kb, vb, ws, out
+    return {"buf_size": buf, "compressed_tokens": int(nc.sum()), "ring_tokens": int((n_h - nc).sum()),
+            "append_stage_us": stage_us, "append_fill_flush_us": flush_us, "decode_us": dec_us,
+            "decode_bytes": nbytes, "decode_gbps": nbytes / (dec_us * 1e-6) / 1e9,
+            "decode_frac": nbytes / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+
+
+def split_timing(tq, wl, w, dev, stream, reps: int) -> dict:
+    """Fractional bit-widths and the split state at the workload's shape, over
+    one layer filled with bulk appends: keys and values of a 3.5-bit cache
+    (tq_codec_create_kv: 3-bit keys, 4-bit values) and of 2.5-bit split codecs
+    (tq_codec_create_split, keys and values alike).  Timed with HIP events on
+    the launch stream: one decode call of the workload's query rows; bytes =
+    the packed records of every attended token-head."""
+    import torch
+    B, hkv, hq, d, qlen = w.batch, w.hkv, w.hq, w.d, w.q_len
+    lens_h = w.lens()
+    max_len = int(lens_h.max())
+    lens = torch.tensor(lens_h, dtype=torch.int32, device=dev)
+    q = wl.device_normal((B, hq, qlen, d), 0, 0, 908, w.bf16, dev)
+    out = torch.empty((B, hq, qlen, d), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    res = {}
+    for label, (kc, vc) in (("fractional_3.5", tq.tq_codec_create_kv(d, 3.5, 0)),
+                            ("split_2.5", (tq.tq_codec_create_split(d, 2.5, 0), tq.tq_codec_create_split(d, 2.5, 1)))):
+        K, V = tq.allocate_cache(kc, B, hkv, max_len, dev), tq.allocate_cache(vc, B, hkv, max_len, dev)
+        for s0 in range(0, max_len, 65536):
+            n = min(65536, max_len - s0)
+            pos = torch.full((B,), s0, dtype=torch.int32, device=dev)
+            kx = wl.device_normal((B, hkv, n, d), 0, 0, 100 + s0 // 65536, w.bf16, dev)
+            vx = wl.device_normal((B, hkv, n, d), 0, 0, 200000 + s0 // 65536, w.bf16, dev)
+            tq.tq_quantize_append_kv(kc, vc, kx, vx, K, V, pos, s0 + n)
+            del kx, vx
+        ws = tq.allocate_workspace(kc, vc, B, hq, hkv, qlen, max_len, dev)
+        tq.tq_decode_attention(kc, vc, q, K, V, lens, max_len, scale, out, ws)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record(stream)
+            tq.tq_decode_attention(kc, vc, q, K, V, lens, max_len, scale, out, ws)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1000.0
+        nbytes = int(lens_h.sum()) * hkv * (kc.info["bytes_per_token"] + vc.info["bytes_per_token"])
+        res[label] = {"k_bits": kc.info["bits"], "v_bits": vc.info["bits"],
+                      "split_high_dims": [kc.info["split_high_dim"], vc.info["split_high_dim"]],
+                      "bytes_per_token_head": kc.info["bytes_per_token"] + vc.info["bytes_per_token"],
+                      "decode_us": us, "gbps": nbytes / (us * 1e-6) / 1e9,
+                      "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        del K, V, ws
+    return res
+
+
 def layer_view(c, l: int):
     """Layer l of a cache allocated with the layers as its batch: the same
     arrays sliced to batch 1 (contiguous, so only the base pointers move)."""
@@ -542,6 +651,8 @@ def main():
     gather = gather_timing(tq, w, kc, vc, kcs[0], vcs[0], dev, stream, max(3, args.steps // 2))
     prefill_attn = prefill_timing(tq, wl, w, kc, vc, kcs[0], vcs[0], lens, max_len, dev, stream,
                                   max(3, args.steps // 2))
+    hybrid = hybrid_timing(tq, wl, w, kc, vc, kcs[0], vcs[0], lens_h, max_len, dev, stream, max(3, args.steps // 2))
+    split = split_timing(tq, wl, w, dev, stream, max(3, args.steps // 2))
 
     single = "not run (bench.py --all-layers-call)" if stacked else None
     if stacked and args.all_layers_call:
@@ -651,6 +762,8 @@ def main():
             "bulk_prefill": prefill,
             "prefill_attention": prefill_attn,
             "cache_gather": gather,
+            "hybrid_decode": hybrid,
+            "split_decode": split,
             "stream_read_reference": stream_ref,
             "achieved_vs_stream_read": achieved / stream_ref["gbps"],
             "decode_read_reference": read_ref,

@@ -314,7 +314,8 @@ tq_status tq_cache_gather(const tq_codec* src_codec, const tq_cache* src, const 
  * and the commit note's hybrid decode): the most recent tokens of each
  * sequence stay unquantised in a ring buffer of buf_size tokens per
  * (sequence, KV head), caller-owned device memory [batch][heads][buf_size]
- * [head_dim] of the tokens' dtype, one for keys and one for values.  A
+ * [head_dim] of the tokens' dtype, one for keys and one for values, each
+ * 16-byte aligned (INVALID_ARG otherwise).  A
  * sequence of N tokens holds tokens 0 .. Nc-1, Nc = floor(N / buf_size) *
  * buf_size, in the compressed caches and token t >= Nc in ring slot t - Nc;
  * whenever appends fill a ring, its buf_size tokens are quantised into the

@@ -783,6 +783,10 @@ static bool hybrid_buffers_ok(const void* kbuf, const void* vbuf, int32_t buf_dt
   if (!kbuf || !vbuf) { *why = "buffer pointer is NULL"; return false; }
   if (buf_dtype != TQ_F32 && buf_dtype != TQ_BF16) { *why = "bad buffer dtype"; return false; }
   if (buf_size < 1 || buf_size > (1 << 16)) { *why = "buffer size must be in 1..65536"; return false; }
+  if ((reinterpret_cast<uintptr_t>(kbuf) | reinterpret_cast<uintptr_t>(vbuf)) & 15u) {
+    *why = "buffers must be 16-byte aligned";  // the combine kernel's 16-byte key reads
+    return false;
+  }
   return true;
 }
 

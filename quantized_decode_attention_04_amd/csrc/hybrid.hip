@@ -13,8 +13,9 @@
 //                          flush -- those that start the next block;
 //   hybrid_lens_kernel     Nc of every sequence, for the compressed decode;
 //   hybrid_combine_kernel  exact attention of each query row over the ring's
-//                          tokens, merged with the compressed decode's output
-//                          through its softmax reference and sum.
+//                          tokens (one workgroup per row), merged with the
+//                          compressed decode's output through its softmax
+//                          reference and sum.
 #include "tq_internal.h"
 
 namespace tq {
@@ -58,113 +59,121 @@ __global__ __launch_bounds__(256) void hybrid_lens_kernel(const int32_t* len, in
   }
 }
 
-constexpr int kTok = 16;  // ring tokens per round
+constexpr int kThreads = 256;  // combine workgroup
+constexpr int kRound = 64;     // ring tokens per round (four threads score one)
 
-// One workgroup of 256 threads per (KV head, sequence): the G * q_len query
-// rows of the head against the ring's tokens, online softmax in the log2
-// domain (as the compressed decode), then the merge with the compressed
-// output: out = (O_c L_c 2^(M_c - M) + o_b 2^(m_b - M)) / (L_c 2^(M_c - M) +
-// l_b 2^(m_b - M)), M = max(M_c, m_b).
+// Coordinates j .. j+7 of a ring row as floats (16-byte reads of bf16, two of
+// float32; rows of D >= 32 coordinates stay 16-byte aligned).
+__device__ __forceinline__ void load8(const void* base, int64_t off, int bf16, float* x) {
+  if (bf16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    const float4 c = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+  }
+}
+
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* s_red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float u = __shfl_xor(v, o, 64);
+    v = is_max ? fmaxf(v, u) : v + u;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();  // s_red's previous use is over
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  v = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) v = is_max ? fmaxf(v, s_red[w]) : v + s_red[w];
+  return v;
+}
+
+// One workgroup of 256 threads per (query row, KV head, sequence): the row
+// against the ring's tokens with an online softmax in the log2 domain (the
+// compressed decode's), 64 tokens per round -- four threads score a token,
+// each over a quarter of the coordinates, while the round's value rows are
+// staged in LDS with 16-byte reads; thread j < D accumulates coordinate j --
+// then the merge with the compressed output: out = (O_c L_c 2^(M_c - M) +
+// o_b 2^(m_b - M)) / (L_c 2^(M_c - M) + l_b 2^(m_b - M)), M = max(M_c, m_b).
 template <int D>
-__global__ __launch_bounds__(256) void hybrid_combine_kernel(HybridAttn a) {
-  constexpr int NRG = 256 / D;                 // row groups (thread j % D owns coordinate j)
-  constexpr int RPT = (16 + NRG - 1) / NRG;    // rows per thread
-  __shared__ float s_q[16][D + 1];
-  __shared__ float s_k[kTok][D + 1];
-  __shared__ float s_v[kTok][D];
-  __shared__ float s_s[16][kTok];
-  __shared__ float s_m[16], s_l[16], s_alpha[16];
-  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int rows = a.group * a.q_len;
+__global__ __launch_bounds__(kThreads) void hybrid_combine_kernel(HybridAttn a) {
+  constexpr int Q4 = D / 4;  // coordinates per scoring thread (a multiple of 8)
+  __shared__ float s_q[D];
+  __shared__ float s_p[kRound];
+  __shared__ float s_red[kThreads / 64];
+  __shared__ __attribute__((aligned(16))) float s_v[kRound][D];
+  const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int h = g * a.group + r / a.q_len, qi = r % a.q_len;
+  const int64_t orow = ((int64_t)b * a.hq + h) * a.q_len + qi;
   const int64_t n = a.len[b] < 0 ? 0 : a.len[b];
   const int64_t nc = (n / a.block) * a.block;
   const int nb = (int)(n - nc);
+  const int64_t vis = n - a.q_len + qi + 1 - nc;  // ring tokens 0 .. vis-1 are seen by the row
   const float sl2 = a.scale * kLog2e;
-  for (int e = tid; e < rows * D; e += 256) {
-    const int r = e / D, j = e % D;
-    const int h = g * a.group + r / a.q_len, qi = r % a.q_len;
-    s_q[r][j] = load_elem(a.q, (((int64_t)b * a.hq + h) * a.q_len + qi) * D + j, a.q_bf16) * sl2;
-  }
-  if (tid < 16) {
-    s_m[tid] = -INFINITY;
-    s_l[tid] = 0.f;
-  }
-  const int j = tid % D, rg = tid / D;
-  float o[RPT];
-#pragma unroll
-  for (int k = 0; k < RPT; ++k) o[k] = 0.f;
+  for (int j = tid; j < D; j += kThreads) s_q[j] = load_elem(a.q, orow * D + j, a.q_bf16) * sl2;
   const int64_t ring = ((int64_t)b * a.hkv + g) * a.block * D;
+  const int tt = tid >> 2, part = tid & 3;  // scoring: token tt of the round, coordinates part * Q4 ..
+  float m_run = -INFINITY, l_run = 0.f, o = 0.f;
   __syncthreads();
-  for (int t0 = 0; t0 < nb; t0 += kTok) {
-    const int cnt = nb - t0 < kTok ? nb - t0 : kTok;
-    for (int e = tid; e < cnt * D; e += 256) {
-      const int i = e / D, jj = e % D;
-      s_k[i][jj] = load_elem(a.kbuf, ring + (int64_t)(t0 + i) * D + jj, a.buf_bf16);
-      s_v[i][jj] = load_elem(a.vbuf, ring + (int64_t)(t0 + i) * D + jj, a.buf_bf16);
+  for (int t0 = 0; t0 < nb; t0 += kRound) {
+    const int cnt = nb - t0 < kRound ? nb - t0 : kRound;
+    // the round's value rows into LDS (as float), eight coordinates a read
+    for (int e = tid; e < cnt * (D / 8); e += kThreads) {
+      const int i = e / (D / 8), j0 = 8 * (e % (D / 8));
+      float x[8];
+      load8(a.vbuf, ring + (int64_t)(t0 + i) * D + j0, a.buf_bf16, x);
+      *reinterpret_cast<float4*>(&s_v[i][j0]) = make_float4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<float4*>(&s_v[i][j0 + 4]) = make_float4(x[4], x[5], x[6], x[7]);
     }
-    __syncthreads();
-    {
-      const int r = tid / kTok, i = tid % kTok;
-      if (r < rows) {
-        // token nc + t0 + i is seen by row r when it is at most n - q_len + r % q_len
-        const bool vis = i < cnt && nc + t0 + i <= n - a.q_len + r % a.q_len;
-        float dot = 0.f;
-        if (vis)
-          for (int jj = 0; jj < D; ++jj) dot = fmaf(s_q[r][jj], s_k[i][jj], dot);
-        s_s[r][i] = vis ? dot : -INFINITY;
-      }
-    }
-    __syncthreads();
-    if (tid < rows) {
-      const int r = tid;
-      float mx = -INFINITY;
-      for (int i = 0; i < cnt; ++i) mx = fmaxf(mx, s_s[r][i]);
-      const float m_old = s_m[r], m_new = fmaxf(m_old, mx);
-      float sum = 0.f;
-      for (int i = 0; i < cnt; ++i) {
-        const float pr = m_new == -INFINITY ? 0.f : exp2f(s_s[r][i] - m_new);
-        s_s[r][i] = pr;
-        sum += pr;
-      }
-      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_old - m_new);
-      s_alpha[r] = alpha;
-      s_m[r] = m_new;
-      s_l[r] = s_l[r] * alpha + sum;
-    }
-    __syncthreads();
-    if (rg < NRG) {
+    float dot = 0.f;
+    const bool seen = tt < cnt && t0 + tt < vis;
+    if (seen) {
+      float x[Q4];
 #pragma unroll
-      for (int k = 0; k < RPT; ++k) {
-        const int r = rg + NRG * k;
-        if (r < rows) {
-          float acc = o[k] * s_alpha[r];
-          for (int i = 0; i < cnt; ++i) acc = fmaf(s_s[r][i], s_v[i][j], acc);
-          o[k] = acc;
-        }
-      }
-    }
-    __syncthreads();
-  }
-  if (rg >= NRG) return;
+      for (int j0 = 0; j0 < Q4; j0 += 8) load8(a.kbuf, ring + (int64_t)(t0 + tt) * D + part * Q4 + j0, a.buf_bf16, x + j0);
 #pragma unroll
-  for (int k = 0; k < RPT; ++k) {
-    const int r = rg + NRG * k;
-    if (r >= rows) continue;
-    const int h = g * a.group + r / a.q_len, qi = r % a.q_len;
-    const int64_t orow = ((int64_t)b * a.hq + h) * a.q_len + qi;
-    float mc = -INFINITY, lc = 0.f, oc = 0.f;
-    if (a.has_compressed) {
-      mc = a.row_ml[2 * orow];
-      lc = a.row_ml[2 * orow + 1];
-      oc = a.out[orow * D + j];
+      for (int j = 0; j < Q4; ++j) dot = fmaf(s_q[part * Q4 + j], x[j], dot);
     }
-    const float mb = s_m[r], lb = s_l[r];
-    const float mm = fmaxf(mc, mb);
-    const float wc = lc > 0.f ? lc * exp2f(mc - mm) : 0.f;
-    const float wb = lb > 0.f ? exp2f(mb - mm) : 0.f;
-    const float den = wc + lb * wb;
-    a.out[orow * D + j] = den > 0.f ? (oc * wc + o[k] * wb) / den : 0.f;
+    dot += __shfl_xor(dot, 1, 64);
+    dot += __shfl_xor(dot, 2, 64);
+    const float sc = seen ? dot : -INFINITY;
+    const float mx = block_reduce(sc, true, s_red);
+    const float m_new = fmaxf(m_run, mx);
+    const float pr = (m_new == -INFINITY || sc == -INFINITY) ? 0.f : exp2f(sc - m_new);
+    const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+    if (part == 0 && tt < kRound) s_p[tt] = pr;
+    // each token's probability counted once (the four scoring threads agree)
+    const float sum = block_reduce(part == 0 ? pr : 0.f, false, s_red);  // (its barriers publish s_p, s_v)
+    l_run = l_run * alpha + sum;
+    m_run = m_new;
+    if (tid < D) {
+      float acc = o * alpha;
+      for (int i = 0; i < cnt; ++i) acc = fmaf(s_p[i], s_v[i][tid], acc);
+      o = acc;
+    }
+    __syncthreads();  // s_p and s_v are rewritten by the next round
   }
+  if (tid >= D) return;
+  float mc = -INFINITY, lc = 0.f, oc = 0.f;
+  if (a.has_compressed) {
+    mc = a.row_ml[2 * orow];
+    lc = a.row_ml[2 * orow + 1];
+    oc = a.out[orow * D + tid];
+  }
+  const float mm = fmaxf(mc, m_run);
+  const float wc = lc > 0.f ? lc * exp2f(mc - mm) : 0.f;
+  const float wb = l_run > 0.f ? exp2f(m_run - mm) : 0.f;
+  const float den = wc + l_run * wb;
+  a.out[orow * D + tid] = den > 0.f ? (oc * wc + o * wb) / den : 0.f;
 }
 
 }  // namespace
@@ -184,7 +193,7 @@ hipError_t launch_hybrid_lens(const int32_t* len, int32_t* lens_c, int batch, in
 
 hipError_t launch_hybrid_combine(const HybridAttn& a, hipStream_t stream) {
   if (a.group * a.q_len > 16 || a.hkv > 65535 || a.batch > 65535) return hipErrorInvalidValue;
-  const dim3 grid(a.hkv, a.batch), block(256);
+  const dim3 grid(a.group * a.q_len, a.hkv, a.batch), block(kThreads);
   switch (a.d) {
     case 32: hybrid_combine_kernel<32><<<grid, block, 0, stream>>>(a); break;
     case 64: hybrid_combine_kernel<64><<<grid, block, 0, stream>>>(a); break;

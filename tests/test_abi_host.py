@@ -300,3 +300,34 @@ def test_decode_read_reference_argument_errors(no_gpu):
     bad = _fake_cache(1, 8, 100, 0)
     bad.idx = None
     assert rd(kcache=bad) == 1
+
+
+def test_hybrid_argument_errors(no_gpu):
+    """The hybrid entry points refuse NULL or misaligned rings, a bad ring
+    dtype or size and a short workspace on the host, before any launch."""
+    lib = _binding._lib
+    kc = tq.tq_codec_create(128, 3, 0, tq.TQ_MODE_MSE)
+    vc = tq.tq_codec_create(128, 3, 1, tq.TQ_MODE_MSE)
+    P = ctypes.c_void_p(0x1000)
+    k, v = _fake_cache(1, 8, 256, 0), _fake_cache(1, 8, 256, 0)
+    need = tq.tq_hybrid_decode_workspace_size(kc, vc, 1, 64, 8, 1, 256, 128)
+
+    def dec(kbuf=P, vbuf=P, dtype=tq.TQ_BF16, buf=128, ws_bytes=need):
+        return lib.tq_hybrid_decode_attention(kc.handle, vc.handle, P, tq.TQ_BF16, 1, 64, 8, 1, ctypes.byref(k),
+                                              ctypes.byref(v), kbuf, vbuf, dtype, buf, P, 256, ctypes.c_float(0.1),
+                                              P, P, ws_bytes, None)
+
+    strides = (ctypes.c_int64 * 4)(8 * 128, 128, 128, 1)
+
+    def app(kbuf=P, vbuf=P, buf=128, n_new=1):
+        return lib.tq_hybrid_append(kc.handle, vc.handle, P, P, tq.TQ_BF16, 1, 8, n_new, strides, strides,
+                                    ctypes.byref(k), ctypes.byref(v), kbuf, vbuf, buf, P, 200, None)
+
+    for call in (dec, app):
+        assert call(kbuf=None) == 1
+        assert call(vbuf=ctypes.c_void_p(0x1008)) == 1
+        assert "16-byte aligned" in tq.tq_last_error()
+        assert call(buf=0) == 1
+    assert dec(dtype=7) == 1
+    assert dec(ws_bytes=need - 1) == 5  # TQ_ERR_WORKSPACE
+    assert app(n_new=129) == 2  # TQ_ERR_UNSUPPORTED
