@@ -1,6 +1,6 @@
 // Decode attention over the compressed cache on the bf16 matrix cores, with
 // every fp32 operand split into two bf16 pieces, for head_dim 128 or 256 keys
-// whose MSE part has 1 or 2 bits (MSE keys, or Prod keys of 2 or 3 bits) and
+// whose MSE part has 1, 2 or 3 bits (MSE keys, or Prod keys of 2 to 4 bits) and
 // MSE values of 1, 2 or 4 bits or 2-bit group values, at up to 16 query rows
 // per KV head.
 //
@@ -83,16 +83,54 @@ __device__ __forceinline__ v4i mfma8(const v4i& a, const v4i& b, v4i c) {
 // K-step ks fragments: the key selectors below put the codes in this order.
 template <int KB>
 __device__ __forceinline__ int kstep_coord(int ks, int e, int b) {
+  if constexpr (KB == 3) return 16 * ks + 4 * e + b;
   if constexpr (KB == 2) return 16 * ks + 4 * b + e;
   return 32 * (ks >> 1) + 8 * b + 4 * (ks & 1) + e;
+}
+
+// The eight selector dwords (dword q: byte k = the code of coordinate 4 q + k)
+// of 32 coordinates stored in the 3-bit byte-lane layout, words X, Y, Z:
+// bytes of X and Y hold codes at bits 0-2 and 3-5 and two bits of a third
+// code at bits 6-7, whose third bit is in Z's byte (bit 6 for X's, bit 7 for
+// Y's), and Z's bits 0-2 and 3-5 hold two more.
+__device__ __forceinline__ void selectors3(uint32_t X, uint32_t Y, uint32_t Z, uint32_t* s) {
+  const uint32_t m3 = 0x07070707u, m2 = 0x03030303u, m4 = 0x04040404u;
+  s[0] = X & m3;
+  s[1] = (X >> 3) & m3;
+  s[2] = ((X >> 6) & m2) | ((Z >> 4) & m4);
+  s[3] = Y & m3;
+  s[4] = (Y >> 3) & m3;
+  s[5] = ((Y >> 6) & m2) | ((Z >> 5) & m4);
+  s[6] = Z & m3;
+  s[7] = (Z >> 3) & m3;
 }
 
 // int8 K-step ks selectors of a lane's key words: byte b of dword e is the
 // code of coordinate kstep_coord(ks, e, b)
 template <int KB>
 __device__ __forceinline__ uint32_t key_sel8(const uint32_t* w, int ks, int e) {
+  if constexpr (KB == 3) {
+    // K-steps 2 j and 2 j + 1 take the two halves of 32-coordinate group j
+    uint32_t s[8];
+    selectors3(w[3 * (ks >> 1)], w[3 * (ks >> 1) + 1], w[3 * (ks >> 1) + 2], s);
+    return s[4 * (ks & 1) + e];
+  }
   if constexpr (KB == 2) return (w[ks] >> (2 * e)) & 0x03030303u;
   return (w[ks >> 1] >> (4 * (ks & 1) + e)) & 0x01010101u;
+}
+
+// key_sel8 at a run-time K-step ks < KS8: every K-step's selectors with
+// compile-time indices, then a select (a register array takes no run-time
+// index without going through scratch memory)
+template <int KB, int KS8>
+__device__ __forceinline__ uint32_t key_sel8_rt(const uint32_t* w, int ks, int e) {
+  uint32_t x = 0u;
+#pragma unroll
+  for (int kk = 0; kk < KS8; ++kk) {
+    const uint32_t y = key_sel8<KB>(w, kk, e);
+    x = kk == ks ? y : x;
+  }
+  return x;
 }
 
 // A value loaded from a valid address (the caller clamps it), or zero; the
@@ -326,7 +364,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
 
   // key centroid pieces: centroid c * 2^E = 256 hi + lo (int8 hi, lo),
   // entries 0..3 in the bytes of one dword each
-  const uint32_t kth = p.klut[0], ktl = p.klut[2];
+  // (up to 8 entries: the high dwords hold entries 4..7 of 3-bit codes)
+  const uint32_t kth = p.klut[0], ktl = p.klut[2], kth1 = KB == 3 ? p.klut[1] : 0u, ktl1 = KB == 3 ? p.klut[3] : 0u;
   // Query operands, the same for every wave, in LDS.  MSE term: row m of
   // q_rot quantised to 24 bits, q = round(q_rot sc) = 65536 a + 256 b + c
   // with balanced int8 digits, sc = kQMax / max_j |q_rot[m][j]|; byte f =
@@ -440,8 +479,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t x = key_sel8<KB>(kw[tg], ks, e);
-            ah[e] = (int)perm(0u, kth, x);
-            al[e] = (int)perm(0u, ktl, x);
+            ah[e] = (int)perm(kth1, kth, x);
+            al[e] = (int)perm(ktl1, ktl, x);
           }
           // Q C = 2^24 a Ch + 2^16 (a Cl + b Ch) + 2^8 (b Cl + c Ch) [+ c Cl,
           // below 2^-23 of the product]
@@ -806,7 +845,7 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
       if constexpr (!VGROUP) rfv = ld<float>(vnrm, 4u * t);
     }
   };
-  const uint32_t kth = p.klut[0], ktl = p.klut[2];
+  const uint32_t kth = p.klut[0], ktl = p.klut[2], kth1 = KB == 3 ? p.klut[1] : 0u, ktl1 = KB == 3 ? p.klut[3] : 0u;
   auto stage_expand = [&](int T0) {
     uint8_t* buf = s_buf + ((T0 / kTile) & 1) * kBuf;
     v4i* kop = reinterpret_cast<v4i*>(buf);
@@ -819,9 +858,9 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
       v4i ah, al;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t x = key_sel8<KB>(rkw, kks, e);
-        ah[e] = (int)perm(0u, kth, x);
-        al[e] = (int)perm(0u, ktl, x);
+        const uint32_t x = KB == 3 ? key_sel8_rt<KB, KS8>(rkw, kks, e) : key_sel8<KB>(rkw, kks, e);
+        ah[e] = (int)perm(kth1, kth, x);
+        al[e] = (int)perm(ktl1, ktl, x);
       }
       kop[((ktg * KS8 + kks) * 2 + 0) * 64 + lane] = ah;
       kop[((ktg * KS8 + kks) * 2 + 1) * 64 + lane] = al;
@@ -1158,6 +1197,7 @@ template <int D>
 hipError_t launch_pb_d(const DecodeParams& p, hipStream_t stream) {
   const bool prod = p.kmode == TQ_MODE_PROD;
   if (p.kbits == 1) return prod ? launch_pb_vb<D, 1, true>(p, stream) : launch_pb_vb<D, 1, false>(p, stream);
+  if (p.kbits == 3) return prod ? launch_pb_vb<D, 3, true>(p, stream) : launch_pb_vb<D, 3, false>(p, stream);
   return prod ? launch_pb_vb<D, 2, true>(p, stream) : launch_pb_vb<D, 2, false>(p, stream);
 }
 
@@ -1182,6 +1222,7 @@ template <int D>
 hipError_t launch_d(const DecodeParams& p, const dim3 grid, hipStream_t stream) {
   const bool prod = p.kmode == TQ_MODE_PROD;
   if (p.kbits == 1) return prod ? launch_vb<D, 1, true>(p, grid, stream) : launch_vb<D, 1, false>(p, grid, stream);
+  if (p.kbits == 3) return prod ? launch_vb<D, 3, true>(p, grid, stream) : launch_vb<D, 3, false>(p, grid, stream);
   return prod ? launch_vb<D, 2, true>(p, grid, stream) : launch_vb<D, 2, false>(p, grid, stream);
 }
 

@@ -240,9 +240,18 @@ DEC_CASES = [
     ("fast_sharp_softmax", 128, (3, 0), (3, 0), 1, 2, 16, 1, [3000], 3000, False, False),
     ("fast_growing_value_norms", 128, (3, 0), (3, 0), 1, 2, 32, 1, [4100], 4100, True, False),
     # fp32 matrix-core path (head_dim 128, more than 8 rows): 3-bit byte-lane keys with
-    # 2-bit values (16 rows); 1-bit Prod keys (2 bits) with 4-bit group values (12 rows)
-    ("mfma_mse3_mse2", 128, (3, 0), (2, 0), 1, 2, 16, 2, [1500], 1600, True, False),
+    # 4-bit group values (16 rows); 1-bit Prod keys (2 bits) with 4-bit group values (12 rows)
+    ("mfma_mse3_group4", 128, (3, 0), (4, 2), 1, 2, 16, 2, [1500], 1600, True, False),
     ("mfma_prod2_group4", 128, (2, 1), (4, 2), 1, 2, 8, 3, [777], 800, True, False),
+    # bf16 split-operand path with 3-bit key codes in the byte-lane layout: 2-bit
+    # values (16 rows, q_len 2); the 3.5-bit cache of the fractional rule (3-bit
+    # keys, 4-bit values); 4-bit Prod keys (3-bit codes and QJL signs) over a
+    # ragged batch; head_dim 256 with group values and with 1-bit values
+    ("bf16_mse3_mse2", 128, (3, 0), (2, 0), 1, 2, 16, 2, [1500], 1600, True, False),
+    ("bf16_mse3_mse4_fractional", 128, (3, 0), (4, 0), 1, 8, 64, 1, [3000], 3072, True, False),
+    ("bf16_prod4_mse4_ragged", 128, (4, 1), (4, 0), 3, 2, 16, 1, [1234, 7, 2000], 2048, True, False),
+    ("bf16_d256_mse3_group2_q2", 256, (3, 0), (2, 2), 1, 2, 8, 2, [1100], 1152, True, False),
+    ("bf16_d256_prod4_mse1", 256, (4, 1), (1, 0), 1, 1, 8, 1, [1700], 1800, False, False),
     # general path at head_dim 256: 4-bit keys, 1-bit values
     ("d256_mse4_mse1", 256, (4, 0), (1, 0), 2, 1, 4, 2, [900, 40], 1000, False, False),
     # bf16 split-operand path at head_dim 256 (32-token wave tiles): 2-bit MSE
@@ -259,7 +268,8 @@ DEC_CASES = [
 # query scale per case (default 0.02, like the keys); larger scales make the
 # softmax sharp and stress the score precision
 Q_STD = {"fast_sharp_softmax": 200.0, "d32_mse1_mse2": 1.0, "d96_mse4_group3_q3": 1.0,
-         "d224_prod5_group4": 1.0, "d192_prod2_mse1": 1.0, "mfma_mse3_mse2": 20.0, "d256_mse4_mse1": 1.0,
+         "d224_prod5_group4": 1.0, "d192_prod2_mse1": 1.0, "mfma_mse3_group4": 20.0, "bf16_mse3_mse2": 20.0,
+         "bf16_d256_prod4_mse1": 1.0, "d256_mse4_mse1": 1.0,
          "bf16_d256_prod2_group2_q2": 1.0, "bf16_d256_prod3_group2_sharp": 30.0}
 
 

@@ -70,6 +70,11 @@ CASES = [
     ("bf16_d256_prod3_mse2_self_attention_q70", 256, (3, 1), (2, 0), 1, 1, 1, 70, [70], 96, False, 1.0),
     # 1100 rows: two launches (1024 + 76 rows)
     ("bf16_d256_prod3_group2_1100_rows_two_launches", 256, (3, 1), (2, 2), 1, 1, 4, 275, [300], 320, False, 1.0),
+    # 3-bit key codes (byte-lane layout) on the shared-tile kernel: the 3.5-bit
+    # cache (3-bit keys, 4-bit values), 160 rows; 4-bit Prod keys with group
+    # values at head_dim 256, 80 rows
+    ("bf16_mse3_mse4_q20", 128, (3, 0), (4, 0), 1, 2, 16, 20, [900], 960, True, 0.02),
+    ("bf16_d256_prod4_group2_q40", 256, (4, 1), (2, 2), 1, 1, 2, 40, [700], 768, True, 0.02),
 ]
 
 
