@@ -703,7 +703,10 @@ __global__ __launch_bounds__(kD) void merge_fast_kernel(DecodeParams p) {
 constexpr int kPfRowsWave = 16;
 constexpr int kPfRows = kWaves * kPfRowsWave;           // rows per workgroup
 constexpr int kPfKeyLds = 4 * 2 * 2 * 64 * 16;          // [score tile][K-step][hi, lo][lane] int8 pieces
-constexpr int kPfBuf = kPfKeyLds + kSelLds + kNormLds;  // one tile's shared operands
+// one tile's shared operands: key pieces, value hi pieces (in the decode
+// kernel's selector layout), norms, value lo pieces (the same layout)
+constexpr int kPfLoOff = kSelLds + kNormLds;  // lo pieces, from the hi pieces' start
+constexpr int kPfBuf = kPfKeyLds + 2 * kSelLds + kNormLds;
 constexpr int kPfLds = 2 * kPfBuf + kWaves * kAccLds;
 // every wave takes every tile of its chunk: at most 1024 tiles between
 // flushes of its int32 value accumulators (the decode kernel's bound)
@@ -823,10 +826,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fast_kernel(DecodeParams 
     for (int i = 0; i < 4; ++i) k4[i] = pks ? s8[4 + i] : s8[i];
     kk[((2 * pst + pks) * 2 + 0) * 64 + lane] = lookup(k4, kh1, kh0);
     kk[((2 * pst + pks) * 2 + 1) * 64 + lane] = lookup(k4, kl1, kl0);
-    uint32_t v8[8];
+    // the value codes' int8 hi and lo pieces, looked up once per tile for
+    // every wave
+    uint32_t v8[8], v4s[4];
     selectors3(vw.x, vw.y, vw.z, v8);
-    v4u* dst = reinterpret_cast<v4u*>(sb + tt * kRow + sel_group_offset((int)(tt >> 4)) + 32 * h + 16 * pks);
-    *dst = pks ? v4u{v8[4], v8[5], v8[6], v8[7]} : v4u{v8[0], v8[1], v8[2], v8[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v4s[i] = pks ? v8[4 + i] : v8[i];
+    uint8_t* dst = sb + tt * kRow + sel_group_offset((int)(tt >> 4)) + 32 * h + 16 * pks;
+    *reinterpret_cast<v4i*>(dst) = lookup(v4s, vh1, vh0);
+    *reinterpret_cast<v4i*>(dst + kPfLoOff) = lookup(v4s, vl1, vl0);
     if (lane < 8) {
       sn[8 * wave + lane] = kn;
       sn[kTile + 8 * wave + lane] = vn;
@@ -846,7 +854,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fast_kernel(DecodeParams 
   for (uint32_t T0 = 0; T0 < ntok; T0 += kTile) {
     uint8_t* buf = s_buf + ((T0 / kTile) & 1u) * kPfBuf;
     const v4i* kk = reinterpret_cast<const v4i*>(buf);  // [tile st][K-step][hi, lo][lane]
-    const uint8_t* sb = buf + kPfKeyLds;                // value selectors [token][coordinate]
+    const uint8_t* sb = buf + kPfKeyLds;                // value hi pieces [token][coordinate], lo at kPfLoOff
     const float* sn = reinterpret_cast<const float*>(sb + kSelLds);  // key norms [64], value norms [64]
     __syncthreads();
 
@@ -958,10 +966,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fast_kernel(DecodeParams 
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const uint8_t* a0 = sb + (16 * h + (n >> 1)) * kRow + sel_group_offset(h) + 16 * u + 8 * (n & 1);
-      const v2i r0 = read_tr8(a0);
-      const v2i r1 = read_tr8(a0 + 8 * kRow);
-      const uint32_t sv[4] = {(uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r1.x, (uint32_t)r1.y};
-      const v4i vh = lookup(sv, vh1, vh0), vl = lookup(sv, vl1, vl0);
+      // the pieces, transposed as the decode kernel transposes its selectors
+      // (a byte-wise look-up commutes with the transposition)
+      const v2i h0 = read_tr8(a0), h1 = read_tr8(a0 + 8 * kRow);
+      const v2i l0 = read_tr8(a0 + kPfLoOff), l1 = read_tr8(a0 + kPfLoOff + 8 * kRow);
+      const v4i vh = v4i{h0.x, h0.y, h1.x, h1.y}, vl = v4i{l0.x, l0.y, l1.x, l1.y};
       // P' V = 2^24 a Vh + 2^16 (a Vl + b Vh) + 2^8 (b Vl + c Vh) [+ c Vl]
       ahh[u] = mfma(vh, ba, ahh[u]);
       ax[u] = mfma(vl, ba, ax[u]);
