@@ -38,6 +38,7 @@
 //   each workgroup's buffer resources end at its chunk, so no byte outside the
 //   chunk is fetched.
 #include "chunk_order.h"
+#include "codes3.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -91,20 +92,6 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 
 __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-}
-
-// The eight selector dwords (quads 0..7, byte k = coordinate 4*quad + k) of a
-// 32-coordinate group stored in the 3-bit byte-lane layout (words X, Y, Z).
-__device__ __forceinline__ void selectors3(uint32_t X, uint32_t Y, uint32_t Z, uint32_t* s) {
-  const uint32_t m3 = 0x07070707u, m2 = 0x03030303u, m4 = 0x04040404u;
-  s[0] = X & m3;
-  s[1] = (X >> 3) & m3;
-  s[2] = ((X >> 6) & m2) | ((Z >> 4) & m4);
-  s[3] = Y & m3;
-  s[4] = (Y >> 3) & m3;
-  s[5] = ((Y >> 6) & m2) | ((Z >> 5) & m4);
-  s[6] = Z & m3;
-  s[7] = (Z >> 3) & m3;
 }
 
 // int8 pieces of sixteen codes (four selector dwords) from an 8-entry table.
