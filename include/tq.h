@@ -269,18 +269,23 @@ tq_status tq_decode_attention_noalloc(const tq_codec* kc, const tq_codec* vc, co
                                       float scale, float* out, void* stream);
 
 /* Bytes of device workspace tq_prefill_attention needs for these sizes (one
- * block of rows at a time reuses it). */
+ * launch of rows at a time reuses it). */
 tq_status tq_prefill_workspace_size(const tq_codec* kc, const tq_codec* vc, int32_t batch, int32_t n_q_heads,
                                     int32_t n_kv_heads, int32_t q_len, int64_t max_len, size_t* bytes);
 
 /* Prefill attention over the compressed cache ([omlx] prefill_attention:
  * many new tokens attend to the cache and, causally, to each other, as in
  * make_mask).  Same arguments, layouts, masking, ownership and errors as
- * tq_decode_attention, with any q_len >= 1: the (n_q_heads / n_kv_heads) *
- * q_len rows of each KV head are processed in blocks of 16 (8 above
- * head_dim 128), one block after the other on the stream, so the cost grows
- * with the number of blocks.  ws must hold tq_prefill_workspace_size(...)
- * bytes.  UNSUPPORTED above 2^30 rows per KV head. */
+ * tq_decode_attention, with any q_len >= 1.  The (n_q_heads / n_kv_heads) *
+ * q_len rows of each KV head run in launches of up to 1024 rows, one after
+ * the other on the stream: on the 3-bit MSE head_dim 128 codecs and on the
+ * codecs of the bf16 decode kernel (key codes of 1 to 3 bits, 1/2/4-bit MSE
+ * or 2-bit group values, head_dim 128 or 256) a workgroup takes 128 rows (64
+ * at head_dim 256) and reads each tile of the state once for them; other
+ * codecs run the rows in blocks of 16 (8 above head_dim 128) through the
+ * decode kernels, so their cost grows with the number of blocks.  ws must
+ * hold tq_prefill_workspace_size(...) bytes.  UNSUPPORTED above 2^30 rows per
+ * KV head. */
 tq_status tq_prefill_attention(const tq_codec* kc, const tq_codec* vc, const void* q, int32_t q_dtype, int32_t batch,
                                int32_t n_q_heads, int32_t n_kv_heads, int32_t q_len, const tq_cache* k,
                                const tq_cache* v, const int32_t* d_len, int64_t max_len, float scale, float* out,
