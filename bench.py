@@ -369,9 +369,10 @@ def hybrid_timing(tq, wl, w, kc, vc, K, V, lens_h, max_len, dev, stream, reps: i
 
 def split_timing(tq, wl, w, dev, stream, reps: int) -> dict:
     """Fractional bit-widths and the split state at the workload's shape, over
-    one layer filled with bulk appends: keys and values of a 3.5-bit cache
-    (tq_codec_create_kv: 3-bit keys, 4-bit values) and of 2.5-bit split codecs
-    (tq_codec_create_split, keys and values alike).  Timed with HIP events on
+    one layer filled with bulk appends: keys and values of a 3.5-bit and a
+    2.5-bit cache (tq_codec_create_kv: 3-bit keys and 4-bit values, 2-bit keys
+    and 3-bit values) and of 2.5-bit split codecs (tq_codec_create_split, keys
+    and values alike).  Timed with HIP events on
     the launch stream: one decode call of the workload's query rows; bytes =
     the packed records of every attended token-head."""
     import torch
@@ -384,6 +385,7 @@ def split_timing(tq, wl, w, dev, stream, reps: int) -> dict:
     scale = 1.0 / math.sqrt(d)
     res = {}
     for label, (kc, vc) in (("fractional_3.5", tq.tq_codec_create_kv(d, 3.5, 0)),
+                            ("fractional_2.5", tq.tq_codec_create_kv(d, 2.5, 0)),
                             ("split_2.5", (tq.tq_codec_create_split(d, 2.5, 0), tq.tq_codec_create_split(d, 2.5, 1)))):
         K, V = tq.allocate_cache(kc, B, hkv, max_len, dev), tq.allocate_cache(vc, B, hkv, max_len, dev)
         for s0 in range(0, max_len, 65536):

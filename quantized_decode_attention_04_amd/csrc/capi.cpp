@@ -584,7 +584,7 @@ static tq::DecodePlan choose_plan(const tq_codec* kc, const tq_codec* vc, int32_
   // prefill on the bf16 / int8 kernel's codecs: likewise, per 128 rows at
   // head_dim 128 and per 64 at 256
   if (blocks && rows_total > row_block(kc) &&
-      tq::bf16_decode_supported(kc->h.d, kc->h.mode, kc->h.mse_bits, vc->h.mode, vc->h.mse_bits, 1)) {
+      tq::bf16_prefill_supported(kc->h.d, kc->h.mode, kc->h.mse_bits, vc->h.mode, vc->h.mse_bits)) {
     const int prows = (int)std::min<int64_t>(rows_total, tq::kPrefillRows);
     const tq::DecodePlan pp = tq::plan_prefill_bf16(batch, hkv, prows, kc->h.d, max_len);
     if (pp.n_chunks > 0) {

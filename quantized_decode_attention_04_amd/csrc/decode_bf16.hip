@@ -186,6 +186,32 @@ __device__ __forceinline__ uint32_t pair_selector(uint32_t run, int u) {
   }
 }
 
+// 3-bit values (byte-lane layout, 32 coordinates in words X, Y, Z): lane
+// slot i at value step u takes coordinate 32 G + 4 (u % 8) + i % 4 of the
+// cache, G = i / 4 at head_dim 128 and 2 (i / 4) + u / 8 at 256 -- byte i % 4
+// of selector dword u % 8 of one group, so every lane extracts its codes
+// with the same instructions at a lane-dependent bit offset.
+template <int D>
+__device__ __forceinline__ int coord3(int i, int u) {
+  const int grp = D == 128 ? i / 4 : 2 * (i / 4) + u / 8;
+  return 32 * grp + 4 * (u % 8) + (i % 4);
+}
+
+// 4 x the code of selector dword q (a compile-time constant), byte k, of a
+// 3-bit byte-lane group; kb = 8 k
+__device__ __forceinline__ uint32_t code3x4(uint32_t X, uint32_t Y, uint32_t Z, int q, uint32_t kb) {
+  switch (q) {
+    case 0: return __builtin_amdgcn_ubfe(X, kb, 3) << 2;
+    case 1: return __builtin_amdgcn_ubfe(X, kb + 3, 3) << 2;
+    case 2: return (__builtin_amdgcn_ubfe(X, kb + 6, 2) << 2) | (__builtin_amdgcn_ubfe(Z, kb + 6, 1) << 4);
+    case 3: return __builtin_amdgcn_ubfe(Y, kb, 3) << 2;
+    case 4: return __builtin_amdgcn_ubfe(Y, kb + 3, 3) << 2;
+    case 5: return (__builtin_amdgcn_ubfe(Y, kb + 6, 2) << 2) | (__builtin_amdgcn_ubfe(Z, kb + 7, 1) << 4);
+    case 6: return __builtin_amdgcn_ubfe(Z, kb, 3) << 2;
+    default: return __builtin_amdgcn_ubfe(Z, kb + 3, 3) << 2;
+  }
+}
+
 template <int D, int KB, int VB, bool PROD, bool VGROUP>
 __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParams p) {
   constexpr int KS = D / 32;          // bf16 k-steps of the QJL product
@@ -194,8 +220,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
   constexpr int KW = KB * LC / 32;    // key index words of a lane group's coordinates
   constexpr int SW = LC / 32;         // QJL sign words of them
   constexpr int NU = D / 16;          // value coordinates per lane
+  constexpr bool V3 = VB == 3;        // 3-bit MSE values (byte-lane groups)
   constexpr int VRB = NU * VB;        // bits of a lane's value run (8 .. 64)
-  constexpr int VW = (VRB + 31) / 32; // words of it
+  // words of it (3-bit values: the lane's one or two whole 32-coordinate groups)
+  constexpr int VW = V3 ? 3 * (D / 128) : (VRB + 31) / 32;
   constexpr uint32_t VMASK = (1u << VB) - 1u;
   // 16-token groups of a wave's tile: 64 tokens at head_dim 128, 32 at 256
   // (the wider head's operands and accumulators leave registers for half as
@@ -263,7 +291,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
   const char* vidx = reinterpret_cast<const char*>(p.v_idx + base * p.vwords);
   const uint32_t kstride = 4u * p.kwords, sstride = 4u * p.ksign_words, vstride = 4u * p.vwords;
   const uint32_t gstride = 4u * p.vgroups;
-  const uint32_t koff = 4u * g * KW, soff = 4u * g * SW, voff = 4u * ((m * VRB) >> 5);
+  const uint32_t koff = 4u * g * KW, soff = 4u * g * SW;
+  const uint32_t voff = V3 ? 12u * (uint32_t)((D / 128) * (m / 4)) : 4u * ((m * VRB) >> 5);
   const uint32_t goff = 4u * ((m * NU) >> 5);  // the group of the lane's value run
   const int vshift = (m * VRB) & 31;
   // the chunk's fields as buffer resources that end at its last token
@@ -436,7 +465,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int w = 0; w < VW; ++w) run[i][w] = VW == 1 ? vw[i][w] >> vshift : vw[i][w];
+      for (int w = 0; w < VW; ++w) run[i][w] = (VW == 1 && !V3) ? vw[i][w] >> vshift : vw[i][w];
 
     // ---- scores.  MSE term on the int8 matrix cores: sm[tg][i] = rowc (2^16
     // t24 + 2^8 t16 + t8), exact integer digit products; the query operands
@@ -601,6 +630,29 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
           acc[u + NU / 2] = mfma(ah1, bl, acc[u + NU / 2]);
           acc[u + NU / 2] = mfma(al1, bh, acc[u + NU / 2]);
         }
+      } else if constexpr (V3) {
+        // 3-bit values: slot m's code at step u (coord3) from its group's
+        // words, as an LDS byte offset (4 x the code) into the centroid table
+        const uint32_t kb = 8u * (uint32_t)(m & 3);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int w0 = 3 * (u / 8);
+          v4u ah, al;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t* xa = run[8 * h + 2 * e];
+            const uint32_t* xc = run[8 * h + 2 * e + 1];
+            const uint32_t oa = code3x4(xa[w0], xa[w0 + 1], xa[w0 + 2], u % 8, kb);
+            const uint32_t oc = code3x4(xc[w0], xc[w0 + 1], xc[w0 + 2], u % 8, kb);
+            const uint32_t ta = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(s_vt) + oa);
+            const uint32_t tc = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(s_vt) + oc);
+            ah[e] = perm(tc, ta, 0x05040100u);
+            al[e] = perm(tc, ta, 0x07060302u);
+          }
+          acc[u] = mfma(ah, bh, acc[u]);
+          acc[u] = mfma(ah, bl, acc[u]);
+          acc[u] = mfma(al, bh, acc[u]);
+        }
       } else {
         // LDS byte offsets of the value codes: byte k of va[i][w][t] is 4 x
         // the code of run coordinate (32 w + 8 k) / VB + t of token i
@@ -657,7 +709,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_bf16_kernel(DecodeParam
   for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int j = (4 * g + r) * NU + u;
+      const int j = V3 ? coord3<D>(4 * g + r, u) : (4 * g + r) * NU + u;
       if (m < rows) s_o[(wave * kRows + m) * kRS + j + 16 * (j / GW)] = acc[u][r];
     }
   __syncthreads();
@@ -1196,6 +1248,7 @@ hipError_t launch_vb(const DecodeParams& p, const dim3 grid, hipStream_t stream)
   switch (p.vbits) {
     case 1: decode_bf16_kernel<D, KB, 1, PROD, false><<<grid, block, 0, stream>>>(p); break;
     case 2: decode_bf16_kernel<D, KB, 2, PROD, false><<<grid, block, 0, stream>>>(p); break;
+    case 3: decode_bf16_kernel<D, KB, 3, PROD, false><<<grid, block, 0, stream>>>(p); break;
     case 4: decode_bf16_kernel<D, KB, 4, PROD, false><<<grid, block, 0, stream>>>(p); break;
     default: return hipErrorInvalidValue;
   }
@@ -1217,7 +1270,7 @@ hipError_t launch_d(const DecodeParams& p, const dim3 grid, hipStream_t stream) 
 // codecs bf16_decode_supported accepts.  Token indices inside a chunk use
 // 24-bit products: chunks hold at most 2^24 tokens.
 hipError_t launch_prefill_bf16(const DecodeParams& p, hipStream_t stream) {
-  if (!bf16_decode_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits, 1) || p.rows < 1 || p.n_chunks < 1 ||
+  if (!bf16_prefill_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits) || p.rows < 1 || p.n_chunks < 1 ||
       p.chunk % 64 || p.chunk > (1 << 24) || p.hkv > 65535 || p.batch > 65535)
     return hipErrorInvalidValue;
   hipError_t e = launch_qprep(p, stream);

@@ -298,13 +298,13 @@ hipError_t launch_dd(const DecodeParams& p, const dim3 grid, hipStream_t stream)
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
-  if (!mfma_decode_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits, p.rows) || p.hkv > 65535 ||
+  const bool bf16 = bf16_decode_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits, p.rows);
+  if (!(bf16 || mfma_decode_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits, p.rows)) || p.hkv > 65535 ||
       p.batch > 65535 || p.n_chunks < 1 || (int64_t)p.n_chunks * kWaves > 4096 || p.chunk % (kWaves * kTile))
     return hipErrorInvalidValue;
   hipError_t e = launch_qprep(p, stream);
   if (e != hipSuccess) return e;
   const dim3 grid(p.n_chunks, p.hkv, p.batch);
-  const bool bf16 = bf16_decode_supported(p.d, p.kmode, p.kbits, p.vmode, p.vbits, p.rows);
   if (bf16)
     e = launch_decode_bf16_kernel(p, grid, stream);
   else

@@ -22,12 +22,16 @@ bool fast_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, in
 
 // bf16 split-operand kernel (decode_bf16.hip): head_dim 128 or 256, key codes
 // of 1, 2 or 3 bits (MSE, or the MSE part of 2- to 4-bit Prod keys), MSE values of
-// 1, 2 or 4 bits or 2-bit group values, up to 16 rows (8 at head_dim 256).
+// 1 to 4 bits or 2-bit group values, up to 16 rows (8 at head_dim 256).
 bool bf16_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows) {
   const bool kok = (kmode == TQ_MODE_MSE || kmode == TQ_MODE_PROD) && kbits >= 1 && kbits <= 3;
-  const bool vok = (vmode == TQ_MODE_MSE && (vbits == 1 || vbits == 2 || vbits == 4)) ||
-                   (vmode == TQ_MODE_GROUP && vbits == 2);
+  const bool vok = (vmode == TQ_MODE_MSE && vbits >= 1 && vbits <= 4) || (vmode == TQ_MODE_GROUP && vbits == 2);
   return (d == 128 || d == 256) && kok && vok && rows >= 1 && rows <= (d == 128 ? 16 : 8);
+}
+
+// Its shared-tile prefill kernel: the same codecs except 3-bit values.
+bool bf16_prefill_supported(int d, int kmode, int kbits, int vmode, int vbits) {
+  return bf16_decode_supported(d, kmode, kbits, vmode, vbits, 1) && !(vmode == TQ_MODE_MSE && vbits == 3);
 }
 
 // fp32 matrix-core kernel (decode_mfma.hip).

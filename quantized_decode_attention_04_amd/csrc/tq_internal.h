@@ -189,6 +189,7 @@ bool mfma_decode_preferred(int d, int kmode, int kbits, int vmode, int vbits, in
 // bf16 split-operand matrix-core kernel (head_dim 128, 1/2-bit MSE key codes,
 // 1/2/4-bit MSE values), launched by launch_decode_mfma when it applies
 bool bf16_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows);
+bool bf16_prefill_supported(int d, int kmode, int kbits, int vmode, int vbits);
 hipError_t launch_decode_bf16_kernel(const DecodeParams& p, const dim3 grid, hipStream_t stream);
 DecodePlan plan_decode_mfma(int batch, int hkv, int rows, int d, int64_t max_len, bool prod);
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);

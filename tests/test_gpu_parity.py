@@ -252,6 +252,14 @@ DEC_CASES = [
     ("bf16_prod4_mse4_ragged", 128, (4, 1), (4, 0), 3, 2, 16, 1, [1234, 7, 2000], 2048, True, False),
     ("bf16_d256_mse3_group2_q2", 256, (3, 0), (2, 2), 1, 2, 8, 2, [1100], 1152, True, False),
     ("bf16_d256_prod4_mse1", 256, (4, 1), (1, 0), 1, 1, 8, 1, [1700], 1800, False, False),
+    # 3-bit values on the same path (byte-lane groups, lane slots mapped through
+    # the group's selector dwords): 3-bit Prod keys; the 2.5-bit cache of the
+    # fractional rule (2-bit keys, 3-bit values), ragged, q_len 2; head_dim 256
+    # with 3-bit keys and with 4-bit Prod keys
+    ("bf16_prod3_mse3", 128, (3, 1), (3, 0), 1, 2, 16, 1, [2000], 2048, True, False),
+    ("bf16_fractional_2p5_q2", 128, (2, 0), (3, 0), 2, 2, 16, 2, [1500, 777], 1600, True, False),
+    ("bf16_d256_mse3_mse3", 256, (3, 0), (3, 0), 1, 2, 8, 1, [1300], 1300, False, False),
+    ("bf16_d256_prod4_mse3_q2", 256, (4, 1), (3, 0), 1, 1, 4, 2, [999], 1024, True, False),
     # general path at head_dim 256: 4-bit keys, 1-bit values
     ("d256_mse4_mse1", 256, (4, 0), (1, 0), 2, 1, 4, 2, [900, 40], 1000, False, False),
     # bf16 split-operand path at head_dim 256 (32-token wave tiles): 2-bit MSE
@@ -269,7 +277,7 @@ DEC_CASES = [
 # softmax sharp and stress the score precision
 Q_STD = {"fast_sharp_softmax": 200.0, "d32_mse1_mse2": 1.0, "d96_mse4_group3_q3": 1.0,
          "d224_prod5_group4": 1.0, "d192_prod2_mse1": 1.0, "mfma_mse3_group4": 20.0, "bf16_mse3_mse2": 20.0,
-         "bf16_d256_prod4_mse1": 1.0, "d256_mse4_mse1": 1.0,
+         "bf16_d256_prod4_mse1": 1.0, "bf16_d256_mse3_mse3": 1.0, "d256_mse4_mse1": 1.0,
          "bf16_d256_prod2_group2_q2": 1.0, "bf16_d256_prod3_group2_sharp": 30.0}
 
 

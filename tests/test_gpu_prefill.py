@@ -75,6 +75,8 @@ CASES = [
     # values at head_dim 256, 80 rows
     ("bf16_mse3_mse4_q20", 128, (3, 0), (4, 0), 1, 2, 16, 20, [900], 960, True, 0.02),
     ("bf16_d256_prod4_group2_q40", 256, (4, 1), (2, 2), 1, 1, 2, 40, [700], 768, True, 0.02),
+    # 3-bit values: row blocks of 16 through the bf16 decode kernel (160 rows)
+    ("rowblocks_prod3_mse3_q20", 128, (3, 1), (3, 0), 1, 1, 8, 20, [700], 768, True, 0.02),
 ]
 
 
