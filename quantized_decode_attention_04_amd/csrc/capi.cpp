@@ -171,6 +171,9 @@ bool use_fast(const tq_codec* kc, const tq_codec* vc, int rows) {
 }
 
 bool use_mfma(const tq_codec* kc, const tq_codec* vc, int rows) {
+  if (kc->h.mode == TQ_MODE_SPLIT || vc->h.mode == TQ_MODE_SPLIT)
+    return tq::mfma_split_supported(kc->h.d, kc->h.mode, kc->h.mse_bits, kc->h.d - kc->h.split_dhi, vc->h.mode,
+                                    vc->h.mse_bits, vc->h.d - vc->h.split_dhi, rows);
   return !use_fast(kc, vc, rows) &&
          tq::mfma_decode_preferred(kc->h.d, kc->h.mode, kc->h.mse_bits, vc->h.mode, vc->h.mse_bits, rows);
 }

@@ -93,13 +93,35 @@ DECODE_CASES = [
     ("prod3_split25", 128, ("prod", 3), ("split", 2.5), 1, 2, 8, 1, [1800]),
     ("d256_split25_split35", 256, ("split", 2.5), ("split", 3.5), 1, 2, 8, 1, [2500]),
     ("d64_split15_ragged", 64, ("split", 1.5), ("split", 1.5), 3, 1, 4, 2, [0, 1, 900]),
+    # split keys and values with 64-channel parts at head_dim 128 take the fp32
+    # matrix-core kernel's split variant: low parts of 2, 1 and 2/3 bits (3-bit
+    # and 4-bit high parts), 16, 4 and 8 rows, a ragged batch of several chunks
+    ("split25_split25_mtp2_ragged", 128, ("split", 2.5), ("split", 2.5), 2, 2, 16, 2, [3000, 1234]),
+    ("split15_split15", 128, ("split", 1.5), ("split", 1.5), 1, 2, 4, 1, [2000]),
+    ("split25_split35_mtp2", 128, ("split", 2.5), ("split", 3.5), 1, 1, 4, 2, [1500]),
 ]
 
 
 @pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
 def test_split_decode_parity_on_oracle_state(case):
+    _split_attention_case(case, prefill=False)
+
+
+# prefill over split caches: 80 and 48 rows per KV head, in row blocks of 16
+PREFILL_CASES = [
+    ("prefill_split25_split25_q20", 128, ("split", 2.5), ("split", 2.5), 1, 2, 8, 10, [900]),
+    ("prefill_split35_split35_q12_ragged", 128, ("split", 3.5), ("split", 3.5), 2, 1, 4, 12, [700, 40]),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_split_prefill_parity_on_oracle_state(case):
+    _split_attention_case(case, prefill=True)
+
+
+def _split_attention_case(case, prefill):
     name, d, kspec, vspec, B, Hkv, Hq, q_len, lens = case
-    _say(f"split decode {name}")
+    _say(f"split {'prefill' if prefill else 'decode'} {name}")
     rng = np.random.default_rng(zlib.crc32(name.encode()))
     N = max(lens)
     k = round_bf16(rng.standard_normal((B, Hkv, N, d)).astype(np.float32) * np.float32(0.02))
@@ -117,10 +139,14 @@ def test_split_decode_parity_on_oracle_state(case):
         if oc.mode == ocodec.MODE_PROD:
             cache.sign.copy_(torch.from_numpy(words_i32(st["sign_words"])).to("cuda"))
     out = torch.zeros((B, Hq, q_len, d), dtype=torch.float32, device="cuda")
-    ws = tq.allocate_workspace(gk, gv, B, Hq, Hkv, q_len, N)
     scale = 1 / math.sqrt(d)
-    tq.tq_decode_attention(gk, gv, to_device_f(q, True), K, V, torch.tensor(lens, dtype=torch.int32, device="cuda"),
-                           N, scale, out, ws)
+    ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    if prefill:
+        ws = tq.allocate_prefill_workspace(gk, gv, B, Hq, Hkv, q_len, N)
+        tq.tq_prefill_attention(gk, gv, to_device_f(q, True), K, V, ld, N, scale, out, ws)
+    else:
+        ws = tq.allocate_workspace(gk, gv, B, Hq, Hkv, q_len, N)
+        tq.tq_decode_attention(gk, gv, to_device_f(q, True), K, V, ld, N, scale, out, ws)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     want = oatt.decode_attention_rotated(q.astype(np.float64), ks, okc, vs, ovc, np.array(lens), scale)
