@@ -374,7 +374,7 @@ struct SplitValueLane {
 };
 
 template <int KB, int VB>
-__global__ __launch_bounds__(kWaves * 64) void decode_mfma_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kWaves * 64, kSplitWgPerCu) void decode_mfma_split_kernel(DecodeParams p) {
   constexpr int D = 128, NU = 8, QSTR = D + 4;
   constexpr int KH = KB + 1, VH = VB + 1;
   constexpr int KLW = split_klw<KB>(), KHW = split_klw<KH>();
@@ -481,42 +481,38 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_split_kernel(DecodePa
       l_run *= alpha;
       m_ref = m_new;
     }
-    // probabilities times each part's value norm
-    float pl[16], ph[16];
+    // ---- values: token 16 tg + 4 g + s; lane m's coordinates 4 m .. 4 m + 3
+    // of each part, the probabilities times each part's value norm formed one
+    // token group at a time (fewer live registers: four waves per SIMD)
     float psum = 0.f;
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
       const int t0 = T0 + 16 * tg + 4 * g;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pr = exp2f(sc[4 * tg + i] - m_ref);
-        psum += pr;
-        const bool ok = t0 + i < ntok;
-        const size_t slot = base + (ok ? t0 + i : 0);
-        pl[4 * tg + i] = pr * pick(p.v_norm[slot], ok);
-        ph[4 * tg + i] = pr * pick(p.v_norm_hi[slot], ok);
-      }
-    }
-    l_run += psum;
-
-    // ---- values: token 16 tg + 4 g + s; lane m's coordinates 4 m .. 4 m + 3 of each part
-#pragma unroll
-    for (int tg = 0; tg < 4; ++tg) {
+      float pl[4], ph[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int tok = T0 + 16 * tg + 4 * g + s;
-        const bool ok = tok < ntok;
-        const size_t slot = base + (ok ? tok : 0);
+        const float pr = exp2f(sc[4 * tg + s] - m_ref);
+        psum += pr;
+        const bool ok = t0 + s < ntok;
+        const size_t slot = base + (ok ? t0 + s : 0);
+        pl[s] = pr * pick(p.v_norm[slot], ok);
+        ph[s] = pr * pick(p.v_norm_hi[slot], ok);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bool ok = t0 + s < ntok;
+        const size_t slot = base + (ok ? t0 + s : 0);
         const uint32_t* rec = p.v_idx + slot * p.vwords;
         const uint32_t rl = vl.run(pick(rec[vl.w0], ok), VB == 3 ? pick(rec[vl.wz], ok) : 0u);
         const uint32_t rh = vh.run(pick(rec[vhw + vh.w0], ok), VH == 3 ? pick(rec[vhw + vh.wz], ok) : 0u);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          acc[u] = mfma4(s_vc[SplitValueLane<VB>::code(rl, u)], pl[4 * tg + s], acc[u]);
-          acc[4 + u] = mfma4(s_vc[16 + SplitValueLane<VH>::code(rh, u)], ph[4 * tg + s], acc[4 + u]);
+          acc[u] = mfma4(s_vc[SplitValueLane<VB>::code(rl, u)], pl[s], acc[u]);
+          acc[4 + u] = mfma4(s_vc[16 + SplitValueLane<VH>::code(rh, u)], ph[s], acc[4 + u]);
         }
       }
     }
+    l_run += psum;
   }
 
   // ---- this wave's partial: o[row m][64 (u / 4) + 4 (4 g + i) + u % 4], m and l of row m

@@ -112,14 +112,15 @@ constexpr int64_t kRaggedChunk = 8192;
 // 3072..6144, 551 us at 2048 (more partials for the merge).
 constexpr int64_t kRaggedDecodeChunk = 4096;
 
-DecodePlan plan_decode_mfma(int batch, int hkv, int rows, int d, int64_t max_len, bool prod) {
+DecodePlan plan_decode_mfma(int batch, int hkv, int rows, int d, int64_t max_len, bool prod, int wg_per_cu) {
   DecodePlan p{};
   p.rows = rows;
   const int64_t step = 256;  // four waves x 64-token tiles
   const int64_t heads = (int64_t)batch * hkv;
-  // about two workgroups per compute unit; every wave writes a partial and
-  // the merge takes at most 4096 of them per row
-  const int64_t per_head = std::max<int64_t>(1, (2 * device_cus() + heads - 1) / heads);
+  // about wg_per_cu workgroups per compute unit (as many as the kernel keeps
+  // resident); every wave writes a partial and the merge takes at most 4096
+  // of them per row
+  const int64_t per_head = std::max<int64_t>(1, (wg_per_cu * device_cus() + heads - 1) / heads);
   int64_t chunk = (max_len + per_head - 1) / per_head;
   // a batch may be ragged: the host knows only the longest sequence, so the
   // chunk is capped and a long sequence spreads over several workgroups

@@ -190,12 +190,15 @@ bool mfma_decode_preferred(int d, int kmode, int kbits, int vmode, int vbits, in
 // part 64 channels, low parts of 1 to 3 bits); k_dlo, v_dlo: the low parts'
 // channels
 bool mfma_split_supported(int d, int kmode, int kbits, int k_dlo, int vmode, int vbits, int v_dlo, int rows);
+// its resident 256-thread workgroups per compute unit (the launch bound and
+// the chunk plan)
+constexpr int kSplitWgPerCu = 4;
 // bf16 split-operand matrix-core kernel (head_dim 128, 1/2-bit MSE key codes,
 // 1/2/4-bit MSE values), launched by launch_decode_mfma when it applies
 bool bf16_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows);
 bool bf16_prefill_supported(int d, int kmode, int kbits, int vmode, int vbits);
 hipError_t launch_decode_bf16_kernel(const DecodeParams& p, const dim3 grid, hipStream_t stream);
-DecodePlan plan_decode_mfma(int batch, int hkv, int rows, int d, int64_t max_len, bool prod);
+DecodePlan plan_decode_mfma(int batch, int hkv, int rows, int d, int64_t max_len, bool prod, int wg_per_cu = 2);
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 
 // MFMA decode path: which shapes it covers, its plan and its launcher.
