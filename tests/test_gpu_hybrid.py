@@ -63,7 +63,18 @@ CASES = [
     ("mse3_mse3_int8_path", 128, (3, 0), (3, 0), 2, 16, 16),
     ("prod3_mse4_bf16_path", 128, (3, 1), (4, 0), 2, 16, 16),
     ("d256_prod3_group2_general_path", 256, (3, 1), (2, 2), 1, 4, 32),
+    # split caches of 2.5 bits (mode 3): the fp32 matrix-core split kernel
+    ("split25_split25_split_path", 128, (2.5, 3), (2.5, 3), 2, 16, 16),
 ]
+
+
+def _codecs(spec, d, seed):
+    """(bits, mode) -> (oracle codec, device codec); mode 3 is a split codec
+    of fractional width bits."""
+    bits, mode = spec
+    if mode == 3:
+        return ocodec.make_split_codec(d, bits, seed), tq.tq_codec_create_split(d, bits, seed)
+    return ocodec.make_codec(d, bits, seed, mode), tq.tq_codec_create(d, bits, seed, mode)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
@@ -76,8 +87,7 @@ def test_hybrid_steps_through_flushes(case):
     start = [5, ring - 1, 2 * ring - 2]
     final = [s + steps * n_new for s in start]
     cap = max(final)
-    okc, ovc = ocodec.make_codec(d, kspec[0], 0, kspec[1]), ocodec.make_codec(d, vspec[0], 1, vspec[1])
-    gk, gv = tq.tq_codec_create(d, kspec[0], 0, kspec[1]), tq.tq_codec_create(d, vspec[0], 1, vspec[1])
+    (okc, gk), (ovc, gv) = _codecs(kspec, d, 0), _codecs(vspec, d, 1)
     k = _window_free_tokens(rng, (B, Hkv, cap, d), [okc])
     v = _window_free_tokens(rng, (B, Hkv, cap, d), [ovc])
     K, V = tq.allocate_cache(gk, B, Hkv, cap), tq.allocate_cache(gv, B, Hkv, cap)
@@ -113,6 +123,8 @@ def test_hybrid_steps_through_flushes(case):
                     assert np.array_equal(got["idx"][b, :, :nc], st["words"][0]), f"{name} step {step} row {b}"
                     if oc.mode != 2:
                         np.testing.assert_allclose(got["norm"][b, :, :nc], st["norm"][0], rtol=1e-6, atol=0)
+                    if oc.mode == 3:
+                        np.testing.assert_allclose(got["rnorm"][b, :, :nc], st["rnorm"][0], rtol=1e-6, atol=0)
             assert np.array_equal(krh[b, :, :n - nc], k[b, :, nc:n]), f"{name} step {step}: key ring of row {b}"
             assert np.array_equal(vrh[b, :, :n - nc], v[b, :, nc:n]), f"{name} step {step}: value ring of row {b}"
         # decode: every row over its compressed tokens and its ring
