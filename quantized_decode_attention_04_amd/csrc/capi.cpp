@@ -602,7 +602,7 @@ static tq::DecodePlan choose_plan(const tq_codec* kc, const tq_codec* vc, int32_
   if (use_mfma(kc, vc, rows)) {
     *path = DecodePath::kMfma;
     const bool split = kc->h.mode == TQ_MODE_SPLIT || vc->h.mode == TQ_MODE_SPLIT;
-    return tq::plan_decode_mfma(batch, hkv, rows, kc->h.d, max_len, prod, split ? tq::kSplitWgPerCu : 2);
+    return tq::plan_decode_mfma(batch, hkv, rows, kc->h.d, max_len, prod, (split && kc->h.d == 128) ? tq::kSplitWgPerCu : 2);
   }
   *path = DecodePath::kGeneral;
   return tq::plan_decode(batch, hkv, rows, kc->h.d, max_len, prod);

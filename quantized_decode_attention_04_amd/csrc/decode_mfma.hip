@@ -3,8 +3,8 @@
 // included), 1/2/4-bit MSE values, group values.  Taken at head_dim 128 when
 // a launch has more than 8 query rows per KV head (prefill blocks,
 // multi-token decode), where it halves the general kernel's time.  A variant
-// below takes split keys and values (two 64-channel parts at head_dim 128)
-// at any row count.
+// below takes split keys and values (two parts of half the head each) at any
+// row count.
 //
 // What is computed is the general kernel's ("turboquant validate_moe_phase2.py",
 // Tests 1 and 5; "omlx turboquant_kv.py", make_mask):
@@ -273,52 +273,57 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(DecodeParams p
 }
 
 // ---- split caches ("omlx turboquant_kv.py", TurboQuantSplitState): a low part
-// of channels 0..63 with KB-bit codes and a high part of channels 64..127
-// with KB+1-bit codes, each an MSE instance with its own norm and centroids
-// (head_dim 128, keys and values both split this way).  The products are the
-// kernel above's; only which lane supplies which coordinate changes, so that
-// every k-step (keys) and every value product reads one part, with a code
-// extraction the same for all lanes up to a per-lane shift:
-//   keys    k-steps 0..15 take the low part, 16..31 the high part; in a
-//           part of B-bit codes k-step s of lane group g takes coordinate
-//           16 g + s (B = 1, 2, 4: a run of 16 codes of the part's LSB-first
-//           stream) or, for B = 3, 32 (g/2) + 4 (s/2) + 2 (g%2) + s%2 (field
-//           s/2 of byte 2 (g%2) + s%2 of the byte-lane group g/2).  The query
-//           rows are staged in LDS in this order.  A = n_part c_part[code].
-//   values  products 0..3 take the low part, 4..7 the high part; in a part
-//           lane m owns coordinates 4 m .. 4 m + 3 (B = 1, 2, 4: 4 B bits of
-//           the stream; B = 3: field m%8 of the four bytes of group m/8), and
-//           the part's norm scales the probability operand.
-// Words of a B-bit code group (32 channels) and of a 64-channel part: B, 2 B.
+// of channels 0 .. D/2 - 1 with KB-bit codes and a high part of the other D/2
+// channels with KB+1-bit codes, each an MSE instance with its own norm and
+// centroids (head_dim 128 or 256, keys and values both split this way).  The
+// products are the kernel above's; only which lane supplies which coordinate
+// changes, so that every k-step (keys) and every value product reads one
+// part, with a code extraction the same for all lanes up to a per-lane shift:
+//   keys    k-steps 0 .. D/8 - 1 take the low part, the rest the high part.
+//           In a part of B-bit codes k-step s of lane group g takes
+//           coordinate 32 g + s at head_dim 256 (the lane group's own code
+//           group); at 128, 16 g + s (B = 1, 2, 4: a run of 16 codes of the
+//           part's LSB-first stream) or, for B = 3, 32 (g/2) + 4 (s/2) +
+//           2 (g%2) + s%2 (field s/2 of byte 2 (g%2) + s%2 of the byte-lane
+//           group g/2).  The query rows are staged in LDS in this order.
+//           A = n_part c_part[code].
+//   values  products 0 .. D/32 - 1 take the low part, the rest the high part;
+//           in a part lane m owns the coordinates NP m .. NP m + NP - 1 (NP =
+//           D/32; B = 1, 2, 4: NP B bits of the stream; B = 3: NP/4 fields
+//           of the four bytes of one group, see SplitValueLane), and the
+//           part's norm scales the probability operand.
+// Words of a B-bit code group (32 channels): B.
 
 // key coordinate (within a part) of k-step s of lane group g
-template <int B>
+template <int D, int B>
 __device__ __forceinline__ int split_kcoord(int g, int s) {
+  if constexpr (D == 256) return 32 * g + s;
   if constexpr (B == 3) return 32 * (g >> 1) + 4 * (s >> 1) + 2 * (g & 1) + (s & 1);
   return 16 * g + s;
 }
 
 // words of a part a lane group loads per token, the first one's index in the
 // part, and the right shift that brings its codes to bit 0 (byte 0 for B = 3)
-template <int B>
+template <int D, int B>
 constexpr int split_klw() {
-  return B == 3 ? 3 : (B == 4 ? 2 : 1);
+  return D == 256 ? B : (B == 3 ? 3 : (B == 4 ? 2 : 1));
 }
-template <int B>
+template <int D, int B>
 __device__ __forceinline__ int split_kword0(int g) {
-  if constexpr (B == 3) return 3 * (g >> 1);
+  if constexpr (D == 256 || B == 3) return B * (D == 256 ? g : (g >> 1));
   if constexpr (B == 4) return 2 * g;
   if constexpr (B == 2) return g;
   return g >> 1;
 }
-template <int B>
+template <int D, int B>
 __device__ __forceinline__ uint32_t split_kshift(int g) {
-  return (B == 3 || B == 1) ? 16u * (uint32_t)(g & 1) : 0u;
+  return (D == 128 && (B == 3 || B == 1)) ? 16u * (uint32_t)(g & 1) : 0u;
 }
 
 // code of k-step s (compile-time) from the lane group's shifted words
-template <int B>
+template <int D, int B>
 __device__ __forceinline__ uint32_t split_kcode(const uint32_t* w, int s) {
+  if constexpr (D == 256) return group_code<B>(w, s);
   if constexpr (B == 3) {
     const int kb = 8 * (s & 1);
     switch (s >> 1) {
@@ -338,46 +343,68 @@ __device__ __forceinline__ uint32_t split_kcode(const uint32_t* w, int s) {
   }
 }
 
-// A lane's value codes of one part: the word(s) to load and how to bring
-// its four codes to fixed places (code u at bits B u; for B = 3 in byte u)
-template <int B>
+// A lane's NP value codes of one part (NP = 4 or 8): the word(s) to load and
+// how to bring its codes to fixed places.  B = 1, 2, 4: code u at bits B u of
+// one shifted word.  B = 3: NP / 4 fields of the four bytes of group G (field
+// a of byte k is coordinate 32 G + 4 a + k): at NP = 4 field m % 8 of group
+// m / 8, at NP = 8 fields 2 (m % 4) and 2 (m % 4) + 1 of group m / 4, so that
+// lane m's coordinates are NP m .. NP m + NP - 1 either way; code u in byte
+// u % 4 of selector f = u / 4.  A field a lies at bits 3 (a % 3) of word a / 3
+// of the group, and fields 2 and 5 take two bits there plus bit 6 or 7 of the
+// third word.
+template <int B, int NP>
 struct SplitValueLane {
-  int w0, wz;  // word indices in the part (wz: the group's third word, B = 3)
-  uint32_t sh, m1, m2, zsh;
+  static constexpr int NF = B == 3 ? NP / 4 : 1;  // words (selectors) per token
+  int w[NF], wz;
+  uint32_t sh[NF], m1[NF], m2[NF], zsh[NF];
   __device__ __forceinline__ explicit SplitValueLane(int m) {
     if constexpr (B == 3) {
-      // field a of the four bytes of group G: bits 3 (a%3) of word a/3, and
-      // for fields 2 and 5 two bits there plus bit 6 or 7 of the third word
-      const int G = m >> 3, a = m & 7;
-      w0 = 3 * G + a / 3;
+      const int G = NP == 4 ? (m >> 3) : (m >> 2);
       wz = 3 * G + 2;
-      sh = 3u * (uint32_t)(a % 3);
-      const bool two = a % 3 == 2;
-      m1 = two ? 0x03030303u : 0x07070707u;
-      m2 = two ? 0x04040404u : 0u;
-      zsh = a == 5 ? 5u : 4u;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int a = NP == 4 ? (m & 7) : 2 * (m & 3) + f;
+        w[f] = 3 * G + a / 3;
+        sh[f] = 3u * (uint32_t)(a % 3);
+        const bool two = a % 3 == 2;
+        m1[f] = two ? 0x03030303u : 0x07070707u;
+        m2[f] = two ? 0x04040404u : 0u;
+        zsh[f] = a == 5 ? 5u : 4u;
+      }
     } else {
-      const int bit = 4 * m * B;
-      w0 = wz = bit >> 5;
-      sh = (uint32_t)(bit & 31);
-      m1 = m2 = zsh = 0u;
+      const int bit = NP * m * B;
+      w[0] = wz = bit >> 5;
+      sh[0] = (uint32_t)(bit & 31);
+      m1[0] = m2[0] = zsh[0] = 0u;
     }
   }
-  __device__ __forceinline__ uint32_t run(uint32_t w, uint32_t z) const {
-    if constexpr (B == 3) return ((w >> sh) & m1) | ((z >> zsh) & m2);
-    return w >> sh;
+  __device__ __forceinline__ uint32_t run(int f, uint32_t x, uint32_t z) const {
+    if constexpr (B == 3) return ((x >> sh[f]) & m1[f]) | ((z >> zsh[f]) & m2[f]);
+    return x >> sh[0];
   }
-  __device__ __forceinline__ static uint32_t code(uint32_t run, int u) {
-    if constexpr (B == 3) return (run >> (8 * u)) & 7u;
-    return (run >> (B * u)) & ((1u << B) - 1u);
+  // code u from the runs
+  __device__ __forceinline__ static uint32_t code(const uint32_t* r, int u) {
+    if constexpr (B == 3) return (r[u >> 2] >> (8 * (u & 3))) & 7u;
+    return (r[0] >> (B * u)) & ((1u << B) - 1u);
   }
 };
 
-template <int KB, int VB>
-__global__ __launch_bounds__(kWaves * 64, kSplitWgPerCu) void decode_mfma_split_kernel(DecodeParams p) {
-  constexpr int D = 128, NU = 8, QSTR = D + 4;
+// resident 256-thread workgroups per CU: at head_dim 128 kSplitWgPerCu, at
+// 256 two (twice the accumulators)
+template <int D>
+constexpr int split_wg_per_cu() {
+  return D == 128 ? kSplitWgPerCu : 2;
+}
+
+template <int D, int KB, int VB>
+__global__ __launch_bounds__(kWaves * 64, split_wg_per_cu<D>()) void decode_mfma_split_kernel(DecodeParams p) {
+  constexpr int KS = D / 4;       // k-steps; the first KS / 2 take the low part
+  constexpr int NU = D / 16;      // value products; the first NU / 2 take the low part
+  constexpr int NP = D / 32;      // coordinates a lane owns in each part
+  constexpr int QSTR = D + 4;
   constexpr int KH = KB + 1, VH = VB + 1;
-  constexpr int KLW = split_klw<KB>(), KHW = split_klw<KH>();
+  constexpr int KLW = split_klw<D, KB>(), KHW = split_klw<D, KH>();
+  constexpr int LO_W = D * KB / 64, VLO_W = D * VB / 64;  // words of the low parts
   __shared__ __attribute__((aligned(16))) float s_q[16 * QSTR];
   __shared__ float s_kc[32], s_vc[32];  // low part's centroids at 0, high part's at 16
 
@@ -396,12 +423,12 @@ __global__ __launch_bounds__(kWaves * 64, kSplitWgPerCu) void decode_mfma_split_
   const int lenm = p.len_mask ? (p.len_mask[b] < 0 ? 0 : p.len_mask[b]) : len;  // the causal rule's length
   const int lim = lenm - p.q_len + ((p.row0 + m) % p.q_len) + 1 - c0;  // row m sees tokens < lim
 
-  // query rows in k-step order: entry g 32 + s of a row is the coordinate
+  // query rows in k-step order: entry KS g + s of a row is the coordinate
   // that k-step s of lane group g takes
   for (int e = threadIdx.x; e < 16 * D; e += kWaves * 64) {
     const int r = e / D, c = e % D;
-    const int gg = c >> 5, s = c & 31;
-    const int j = s < 16 ? split_kcoord<KB>(gg, s) : 64 + split_kcoord<KH>(gg, s - 16);
+    const int gg = c / KS, s = c % KS;
+    const int j = s < KS / 2 ? split_kcoord<D, KB>(gg, s) : D / 2 + split_kcoord<D, KH>(gg, s - KS / 2);
     s_q[r * QSTR + c] = r < rows ? p.qrot[((size_t)bg * rows + r) * D + j] : 0.f;
   }
   if (threadIdx.x < 32) {
@@ -414,11 +441,11 @@ __global__ __launch_bounds__(kWaves * 64, kSplitWgPerCu) void decode_mfma_split_
 
   const float sl2 = p.scale * kLog2e;
   const size_t base = (size_t)bg * (size_t)p.cap + (size_t)c0;  // slot of token 0 of the chunk
-  const int klo = split_kword0<KB>(g), khi = 2 * KB + split_kword0<KH>(g);
-  const uint32_t kslo = split_kshift<KB>(g), kshi = split_kshift<KH>(g);
-  const SplitValueLane<VB> vl(m);
-  const SplitValueLane<VH> vh(m);
-  const int vhw = 2 * VB;  // the high part's first word in a value record
+  const int klo = split_kword0<D, KB>(g), khi = LO_W + split_kword0<D, KH>(g);
+  const uint32_t kslo = split_kshift<D, KB>(g), kshi = split_kshift<D, KH>(g);
+  const SplitValueLane<VB, NP> vl(m);
+  const SplitValueLane<VH, NP> vh(m);
+  constexpr int VLF = SplitValueLane<VB, NP>::NF, VHF = SplitValueLane<VH, NP>::NF;
   float m_ref = -1e30f, l_run = 0.f;
   v4f acc[NU];
 #pragma unroll
@@ -446,15 +473,15 @@ __global__ __launch_bounds__(kWaves * 64, kSplitWgPerCu) void decode_mfma_split_
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) sacc[tg] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t4 = 0; t4 < 8; ++t4) {
-      const v4f qv = *reinterpret_cast<const v4f*>(&s_q[m * QSTR + g * 32 + 4 * t4]);
+    for (int t4 = 0; t4 < KS / 4; ++t4) {
+      const v4f qv = *reinterpret_cast<const v4f*>(&s_q[m * QSTR + g * KS + 4 * t4]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s = 4 * t4 + e;
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
-          const float a = s < 16 ? nl[tg] * s_kc[split_kcode<KB>(kl[tg], s)]
-                                 : nh[tg] * s_kc[16 + split_kcode<KH>(kh[tg], s - 16)];
+          const float a = s < KS / 2 ? nl[tg] * s_kc[split_kcode<D, KB>(kl[tg], s)]
+                                     : nh[tg] * s_kc[16 + split_kcode<D, KH>(kh[tg], s - KS / 2)];
           sacc[tg] = mfma4(a, qv[e], sacc[tg]);
         }
       }
@@ -481,9 +508,9 @@ __global__ __launch_bounds__(kWaves * 64, kSplitWgPerCu) void decode_mfma_split_
       l_run *= alpha;
       m_ref = m_new;
     }
-    // ---- values: token 16 tg + 4 g + s; lane m's coordinates 4 m .. 4 m + 3
-    // of each part, the probabilities times each part's value norm formed one
-    // token group at a time (fewer live registers: four waves per SIMD)
+    // ---- values: token 16 tg + 4 g + s; lane m's coordinates NP m ..
+    // NP m + NP - 1 of each part, the probabilities times each part's value
+    // norm formed one token group at a time (fewer live registers)
     float psum = 0.f;
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
@@ -503,19 +530,24 @@ __global__ __launch_bounds__(kWaves * 64, kSplitWgPerCu) void decode_mfma_split_
         const bool ok = t0 + s < ntok;
         const size_t slot = base + (ok ? t0 + s : 0);
         const uint32_t* rec = p.v_idx + slot * p.vwords;
-        const uint32_t rl = vl.run(pick(rec[vl.w0], ok), VB == 3 ? pick(rec[vl.wz], ok) : 0u);
-        const uint32_t rh = vh.run(pick(rec[vhw + vh.w0], ok), VH == 3 ? pick(rec[vhw + vh.wz], ok) : 0u);
+        uint32_t rl[VLF], rh[VHF];
+        const uint32_t zl = VB == 3 ? pick(rec[vl.wz], ok) : 0u;
+        const uint32_t zh = VH == 3 ? pick(rec[VLO_W + vh.wz], ok) : 0u;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          acc[u] = mfma4(s_vc[SplitValueLane<VB>::code(rl, u)], pl[s], acc[u]);
-          acc[4 + u] = mfma4(s_vc[16 + SplitValueLane<VH>::code(rh, u)], ph[s], acc[4 + u]);
+        for (int f = 0; f < VLF; ++f) rl[f] = vl.run(f, pick(rec[vl.w[f]], ok), zl);
+#pragma unroll
+        for (int f = 0; f < VHF; ++f) rh[f] = vh.run(f, pick(rec[VLO_W + vh.w[f]], ok), zh);
+#pragma unroll
+        for (int u = 0; u < NU / 2; ++u) {
+          acc[u] = mfma4(s_vc[SplitValueLane<VB, NP>::code(rl, u)], pl[s], acc[u]);
+          acc[NU / 2 + u] = mfma4(s_vc[16 + SplitValueLane<VH, NP>::code(rh, u)], ph[s], acc[NU / 2 + u]);
         }
       }
     }
     l_run += psum;
   }
 
-  // ---- this wave's partial: o[row m][64 (u / 4) + 4 (4 g + i) + u % 4], m and l of row m
+  // ---- this wave's partial: o[row m][(D/2) (u / (NU/2)) + NP (4 g + i) + u % (NU/2)], m and l of row m
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   const int part = chunk_id * kWaves + wave;
@@ -525,7 +557,8 @@ __global__ __launch_bounds__(kWaves * 64, kSplitWgPerCu) void decode_mfma_split_
 #pragma unroll
     for (int u = 0; u < NU; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) po[64 * (u >> 2) + 4 * (4 * g + i) + (u & 3)] = acc[u][i];
+      for (int i = 0; i < 4; ++i)
+        po[(D / 2) * (u / (NU / 2)) + NP * (4 * g + i) + (u % (NU / 2))] = acc[u][i];
     if (g == 0) {
       float* pml = p.part_ml + (((size_t)bg * n_parts + part) * rows + m) * 2;
       pml[0] = m_ref;
@@ -534,24 +567,29 @@ __global__ __launch_bounds__(kWaves * 64, kSplitWgPerCu) void decode_mfma_split_
   }
 }
 
-template <int KB>
+template <int D, int KB>
 hipError_t launch_split_kb(const DecodeParams& p, const dim3 grid, hipStream_t stream) {
   switch (p.vbits) {
-    case 1: decode_mfma_split_kernel<KB, 1><<<grid, dim3(kWaves * 64), 0, stream>>>(p); break;
-    case 2: decode_mfma_split_kernel<KB, 2><<<grid, dim3(kWaves * 64), 0, stream>>>(p); break;
-    case 3: decode_mfma_split_kernel<KB, 3><<<grid, dim3(kWaves * 64), 0, stream>>>(p); break;
+    case 1: decode_mfma_split_kernel<D, KB, 1><<<grid, dim3(kWaves * 64), 0, stream>>>(p); break;
+    case 2: decode_mfma_split_kernel<D, KB, 2><<<grid, dim3(kWaves * 64), 0, stream>>>(p); break;
+    case 3: decode_mfma_split_kernel<D, KB, 3><<<grid, dim3(kWaves * 64), 0, stream>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_split(const DecodeParams& p, const dim3 grid, hipStream_t stream) {
+template <int D>
+hipError_t launch_split_d(const DecodeParams& p, const dim3 grid, hipStream_t stream) {
   switch (p.kbits) {
-    case 1: return launch_split_kb<1>(p, grid, stream);
-    case 2: return launch_split_kb<2>(p, grid, stream);
-    case 3: return launch_split_kb<3>(p, grid, stream);
+    case 1: return launch_split_kb<D, 1>(p, grid, stream);
+    case 2: return launch_split_kb<D, 2>(p, grid, stream);
+    case 3: return launch_split_kb<D, 3>(p, grid, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_split(const DecodeParams& p, const dim3 grid, hipStream_t stream) {
+  return p.d == 128 ? launch_split_d<128>(p, grid, stream) : launch_split_d<256>(p, grid, stream);
 }
 
 template <int D, int KB>

@@ -42,11 +42,12 @@ bool mfma_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, in
   return (d == 128 || d == 256) && kok && vok && rows >= 1 && rows <= (d == 128 ? 16 : 8);
 }
 
-// Split keys and values, each part 64 channels of head_dim 128: the fp32
+// Split keys and values, each part half of head_dim 128 or 256: the fp32
 // matrix-core kernel's split variant (decode_mfma.hip), at any row count.
 bool mfma_split_supported(int d, int kmode, int kbits, int k_dlo, int vmode, int vbits, int v_dlo, int rows) {
-  return d == 128 && kmode == TQ_MODE_SPLIT && vmode == TQ_MODE_SPLIT && k_dlo == 64 && v_dlo == 64 &&
-         kbits >= 1 && kbits <= 3 && vbits >= 1 && vbits <= 3 && rows >= 1 && rows <= 16;
+  return (d == 128 || d == 256) && kmode == TQ_MODE_SPLIT && vmode == TQ_MODE_SPLIT && k_dlo == d / 2 &&
+         v_dlo == d / 2 && kbits >= 1 && kbits <= 3 && vbits >= 1 && vbits <= 3 && rows >= 1 &&
+         rows <= (d == 128 ? 16 : 8);
 }
 
 // Measured on MI355X: at head_dim 128 with more than 8 rows (prefill blocks,

@@ -186,12 +186,12 @@ hipError_t launch_merge(const DecodeParams& p, hipStream_t stream);
 // partial, so the merge sees 4 partials per chunk.
 bool mfma_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, int rows);
 bool mfma_decode_preferred(int d, int kmode, int kbits, int vmode, int vbits, int rows);
-// fp32 matrix-core kernel over split keys and values (head_dim 128, each
-// part 64 channels, low parts of 1 to 3 bits); k_dlo, v_dlo: the low parts'
-// channels
+// fp32 matrix-core kernel over split keys and values (head_dim 128 or 256,
+// each part half the channels, low parts of 1 to 3 bits); k_dlo, v_dlo: the
+// low parts' channels
 bool mfma_split_supported(int d, int kmode, int kbits, int k_dlo, int vmode, int vbits, int v_dlo, int rows);
-// its resident 256-thread workgroups per compute unit (the launch bound and
-// the chunk plan)
+// its resident 256-thread workgroups per compute unit at head_dim 128 (the
+// launch bound and the chunk plan; two at 256)
 constexpr int kSplitWgPerCu = 4;
 // bf16 split-operand matrix-core kernel (head_dim 128, 1/2-bit MSE key codes,
 // 1/2/4-bit MSE values), launched by launch_decode_mfma when it applies

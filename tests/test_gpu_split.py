@@ -99,6 +99,12 @@ DECODE_CASES = [
     ("split25_split25_mtp2_ragged", 128, ("split", 2.5), ("split", 2.5), 2, 2, 16, 2, [3000, 1234]),
     ("split15_split15", 128, ("split", 1.5), ("split", 1.5), 1, 2, 4, 1, [2000]),
     ("split25_split35_mtp2", 128, ("split", 2.5), ("split", 3.5), 1, 1, 4, 2, [1500]),
+    # the same kernel at head_dim 256 (128-channel parts; d256_split25_split35
+    # above too): 1-bit and 3-bit low parts, 8 and 4 rows, a ragged batch
+    ("d256_split35_split35_mtp2", 256, ("split", 3.5), ("split", 3.5), 1, 2, 8, 2, [2600]),
+    ("d256_split15_split15_ragged", 256, ("split", 1.5), ("split", 1.5), 2, 1, 4, 1, [1900, 300]),
+    # 3.25 bits at head_dim 256 (a 64-channel high part): the general kernel
+    ("d256_split325_split325", 256, ("split", 3.25), ("split", 3.25), 1, 1, 4, 1, [1000]),
 ]
 
 
@@ -107,10 +113,11 @@ def test_split_decode_parity_on_oracle_state(case):
     _split_attention_case(case, prefill=False)
 
 
-# prefill over split caches: 80 and 48 rows per KV head, in row blocks of 16
+# prefill over split caches: 80, 48 and 36 rows per KV head, in row blocks of 16 (8 at head_dim 256)
 PREFILL_CASES = [
     ("prefill_split25_split25_q20", 128, ("split", 2.5), ("split", 2.5), 1, 2, 8, 10, [900]),
     ("prefill_split35_split35_q12_ragged", 128, ("split", 3.5), ("split", 3.5), 2, 1, 4, 12, [700, 40]),
+    ("prefill_d256_split25_split25_q9", 256, ("split", 2.5), ("split", 2.5), 1, 1, 4, 9, [800]),
 ]
 
 
