@@ -279,8 +279,8 @@ tq_status tq_prefill_workspace_size(const tq_codec* kc, const tq_codec* vc, int3
  * tq_decode_attention, with any q_len >= 1.  The (n_q_heads / n_kv_heads) *
  * q_len rows of each KV head run in launches of up to 1024 rows, one after
  * the other on the stream: on the 3-bit MSE head_dim 128 codecs and on the
- * codecs of the bf16 decode kernel (key codes of 1 to 3 bits, 1/2/4-bit MSE
- * or 2-bit group values, head_dim 128 or 256) a workgroup takes 128 rows (64
+ * codecs of the bf16 decode kernel (key codes of 1 to 3 bits, 1- to 4-bit
+ * MSE or 2-bit group values, head_dim 128 or 256) a workgroup takes 128 rows (64
  * at head_dim 256) and reads each tile of the state once for them; other
  * codecs run the rows in blocks of 16 (8 above head_dim 128) through the
  * decode kernels, so their cost grows with the number of blocks.  ws must

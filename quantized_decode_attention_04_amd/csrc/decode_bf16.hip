@@ -787,7 +787,8 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
   constexpr int SW = LC / 32;
   constexpr int NT = 4 * TG;
   constexpr int VRB = NU * VB;
-  constexpr int VW = (VRB + 31) / 32;
+  constexpr bool V3 = VB == 3;  // 3-bit MSE values (byte-lane groups, the decode kernel's coord3 slots)
+  constexpr int VW = V3 ? 3 * (D / 128) : (VRB + 31) / 32;
   constexpr uint32_t VMASK = (1u << VB) - 1u;
   constexpr int kBuf = Lay::kBuf;
   static_assert(!VGROUP || VB == 2, "group values of 2 bits");
@@ -832,7 +833,7 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
   const char* vidx = reinterpret_cast<const char*>(p.v_idx + base * p.vwords);
   const uint32_t kstride = 4u * p.kwords, sstride = 4u * p.ksign_words, vstride = 4u * p.vwords;
   const uint32_t gstride = 4u * p.vgroups;
-  const uint32_t koff = 4u * g * KW, soff = 4u * g * SW, voff = 4u * ((m * VRB) >> 5);
+  const uint32_t koff = 4u * g * KW, soff = 4u * g * SW, voff = V3 ? 12u * (uint32_t)((D / 128) * (m / 4)) : 4u * ((m * VRB) >> 5);
   const uint32_t goff = 4u * ((m * NU) >> 5);
   const int vshift = (m * VRB) & 31;
   // a token index of the chunk, clamped to a valid one (tokens past the end
@@ -953,6 +954,39 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
         vop[((vh * NU + u) * 2 + 1) * 64 + lane] = al0;
         vop[((vh * NU + u + NU / 2) * 2 + 0) * 64 + lane] = ah1;
         vop[((vh * NU + u + NU / 2) * 2 + 1) * 64 + lane] = al1;
+      }
+    } else if constexpr (V3) {
+      // slot m's code at step u (coord3) from its group's words, as an LDS
+      // byte offset (4 x the code) into the centroid table; u is the same on
+      // every lane of the wave
+      const uint32_t kb = 8u * (uint32_t)(m & 3);
+#pragma unroll
+      for (int j = 0; j < VJ; ++j) {
+        const int u = vu0 + j;
+        const bool g1 = D == 256 && u >= 8;  // a head_dim-256 lane's second group
+        v4u ah, al;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t* xa = run[2 * e];
+          const uint32_t* xc = run[2 * e + 1];
+          uint32_t a0 = xa[0], a1 = xa[1], a2 = xa[2], c0 = xc[0], c1 = xc[1], c2 = xc[2];
+          if constexpr (D == 256) {
+            a0 = g1 ? xa[3] : a0;
+            a1 = g1 ? xa[4] : a1;
+            a2 = g1 ? xa[5] : a2;
+            c0 = g1 ? xc[3] : c0;
+            c1 = g1 ? xc[4] : c1;
+            c2 = g1 ? xc[5] : c2;
+          }
+          const uint32_t oa = code3x4(a0, a1, a2, u % 8, kb);
+          const uint32_t oc = code3x4(c0, c1, c2, u % 8, kb);
+          const uint32_t ta = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(s_vt) + oa);
+          const uint32_t tc = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(s_vt) + oc);
+          ah[e] = perm(tc, ta, 0x05040100u);
+          al[e] = perm(tc, ta, 0x07060302u);
+        }
+        vop[((vh * NU + u) * 2 + 0) * 64 + lane] = ah;
+        vop[((vh * NU + u) * 2 + 1) * 64 + lane] = al;
       }
     } else {
       constexpr int TPB = 8 / VB;
@@ -1201,7 +1235,7 @@ __global__ __launch_bounds__(PbShape<D>::kWaves * 64, 1) void prefill_bf16_kerne
 #pragma unroll
     for (int u = 0; u < NU; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) po[(4 * g + r) * NU + u] = acc[u][r];
+      for (int r = 0; r < 4; ++r) po[V3 ? coord3<D>(4 * g + r, u) : (4 * g + r) * NU + u] = acc[u][r];
     if (g == 0) {
       p.part_ml[2 * slot] = m_ref;
       p.part_ml[2 * slot + 1] = l_run;
@@ -1223,6 +1257,7 @@ hipError_t launch_pb_vb(const DecodeParams& p, hipStream_t stream) {
   switch (p.vbits) {
     case 1: prefill_bf16_kernel<D, KB, 1, PROD, false><<<grid, block, 0, stream>>>(p); break;
     case 2: prefill_bf16_kernel<D, KB, 2, PROD, false><<<grid, block, 0, stream>>>(p); break;
+    case 3: prefill_bf16_kernel<D, KB, 3, PROD, false><<<grid, block, 0, stream>>>(p); break;
     case 4: prefill_bf16_kernel<D, KB, 4, PROD, false><<<grid, block, 0, stream>>>(p); break;
     default: return hipErrorInvalidValue;
   }

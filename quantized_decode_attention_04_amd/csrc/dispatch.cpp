@@ -29,9 +29,9 @@ bool bf16_decode_supported(int d, int kmode, int kbits, int vmode, int vbits, in
   return (d == 128 || d == 256) && kok && vok && rows >= 1 && rows <= (d == 128 ? 16 : 8);
 }
 
-// Its shared-tile prefill kernel: the same codecs except 3-bit values.
+// Its shared-tile prefill kernel: the same codecs.
 bool bf16_prefill_supported(int d, int kmode, int kbits, int vmode, int vbits) {
-  return bf16_decode_supported(d, kmode, kbits, vmode, vbits, 1) && !(vmode == TQ_MODE_MSE && vbits == 3);
+  return bf16_decode_supported(d, kmode, kbits, vmode, vbits, 1);
 }
 
 // fp32 matrix-core kernel (decode_mfma.hip).

@@ -75,8 +75,13 @@ CASES = [
     # values at head_dim 256, 80 rows
     ("bf16_mse3_mse4_q20", 128, (3, 0), (4, 0), 1, 2, 16, 20, [900], 960, True, 0.02),
     ("bf16_d256_prod4_group2_q40", 256, (4, 1), (2, 2), 1, 1, 2, 40, [700], 768, True, 0.02),
-    # 3-bit values: row blocks of 16 through the bf16 decode kernel (160 rows)
-    ("rowblocks_prod3_mse3_q20", 128, (3, 1), (3, 0), 1, 1, 8, 20, [700], 768, True, 0.02),
+    # 3-bit values (byte-lane groups) on the shared-tile kernel: Prod keys, 160
+    # rows; the 2.5-bit cache (2-bit keys, 3-bit values) over a ragged batch of
+    # several chunks, 256 rows per KV head; 3-bit keys and values at head_dim
+    # 256, 80 rows
+    ("bf16_prod3_mse3_q20", 128, (3, 1), (3, 0), 1, 1, 8, 20, [700], 768, True, 0.02),
+    ("bf16_mse2_mse3_256_rows_ragged", 128, (2, 0), (3, 0), 2, 2, 16, 16, [4100, 1900], 4100, True, 0.02),
+    ("bf16_d256_mse3_mse3_q40", 256, (3, 0), (3, 0), 1, 1, 2, 40, [900], 960, False, 1.0),
 ]
 
 
