@@ -485,6 +485,10 @@ __global__ __launch_bounds__(kWaves * 64, split_wg_per_cu<D>()) void decode_mfma
           sacc[tg] = mfma4(a, qv[e], sacc[tg]);
         }
       }
+      // keep each group of four k-steps' look-ups next to its products: at
+      // four waves per SIMD (128 registers) the look-ups the compiler
+      // otherwise hoists ahead spill to scratch memory
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- online softmax of row m over this lane's 16 tokens
